@@ -1,0 +1,226 @@
+"""CPU oracle for RaZeR-NVFP4 -- test infrastructure only.
+
+A ctypes wrapper around ``razer_oracle.c``: a plain single-threaded C statement
+of the RaZeR-NVFP4 encoder, decoder and W4A16 product, written from the pages
+("RaZeR: Pushing the Limits of NVFP4 Quantization with Redundant Zero
+Remapping", papernotes.org notes; and the gist.science technical summary of the
+same paper).  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  The GPU library
+never imports, links or calls it, and the two share no code.
+
+All arrays are numpy host arrays.  fp16/bf16 inputs are widened to fp32 by the
+caller (exact).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "razer_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+WEIGHT = 0
+ACT = 1
+
+
+def build_oracle() -> str:
+    """Compile the oracle with gcc: -O2, no fast-math, no FP contraction."""
+    tmp = _LIB + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+           "-Wall", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    """Load liboracle.so, building it first only if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build_oracle()
+        L = ctypes.CDLL(_LIB)
+        d, i, i64, f = ctypes.c_double, ctypes.c_int, ctypes.c_int64, ctypes.c_float
+        vp = ctypes.c_void_p
+        L.rzo_fp4_value.restype = d
+        L.rzo_fp4_value.argtypes = [i]
+        L.rzo_fp4_round_mag.restype = i
+        L.rzo_fp4_round_mag.argtypes = [d]
+        L.rzo_scale_value.restype = d
+        L.rzo_scale_value.argtypes = [i, i]
+        L.rzo_scale_round.restype = i
+        L.rzo_scale_round.argtypes = [i, f]
+        L.rzo_scale_max.restype = d
+        L.rzo_scale_max.argtypes = [i]
+        L.rzo_special_value.restype = d
+        L.rzo_special_value.argtypes = [i, i]
+        L.rzo_encode_block_scaled.restype = None
+        L.rzo_encode_block_scaled.argtypes = [vp, i, vp, i, i, vp, vp]
+        L.rzo_quantize.restype = i
+        L.rzo_quantize.argtypes = [i, vp, i64, i64, vp, i, vp, vp, vp]
+        L.rzo_decode_value.restype = d
+        L.rzo_decode_value.argtypes = [i, i, i, vp]
+        L.rzo_block_scale.restype = d
+        L.rzo_block_scale.argtypes = [i, i]
+        L.rzo_dequant_f64.restype = None
+        L.rzo_dequant_f64.argtypes = [i, vp, vp, f, vp, i64, i64, vp]
+        L.rzo_dequant_f32.restype = None
+        L.rzo_dequant_f32.argtypes = [i, vp, vp, f, vp, i64, i64, vp]
+        L.rzo_gemm.restype = None
+        L.rzo_gemm.argtypes = [vp, i64, i64, i, vp, vp, f, vp, i64, vp, i64, vp, vp]
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _offsets(kind: int, offsets) -> np.ndarray:
+    off = np.zeros(2, dtype=np.int8)
+    vals = list(offsets)
+    if kind == WEIGHT and len(vals) != 2:
+        raise ValueError("weights take two offsets")
+    if kind == ACT and len(vals) != 1:
+        raise ValueError("activations take one offset")
+    off[: len(vals)] = vals
+    return off
+
+
+# ---- scalar helpers ---------------------------------------------------------
+
+def fp4_value(code: int) -> float:
+    return lib().rzo_fp4_value(code)
+
+
+def fp4_round_mag(a: float) -> int:
+    return lib().rzo_fp4_round_mag(float(a))
+
+
+def scale_value(kind: int, code: int) -> float:
+    return lib().rzo_scale_value(kind, code)
+
+
+def scale_round(kind: int, v: float) -> int:
+    return lib().rzo_scale_round(kind, float(np.float32(v)))
+
+
+def scale_max(kind: int) -> float:
+    return lib().rzo_scale_max(kind)
+
+
+def special_value(neg: int, off_half: int) -> float:
+    return lib().rzo_special_value(neg, off_half)
+
+
+def decode_value(kind: int, code: int, sbyte: int, offsets) -> float:
+    off = _offsets(kind, offsets)
+    return lib().rzo_decode_value(kind, code, sbyte, _ptr(off))
+
+
+def block_scale(kind: int, sbyte: int) -> float:
+    return lib().rzo_block_scale(kind, sbyte)
+
+
+# ---- block and tensor entry points -------------------------------------------
+
+def encode_block_scaled(y, candidates, remap: bool = True):
+    """Remap one block of already-scaled values; returns (codes[n], sel)."""
+    y = np.ascontiguousarray(np.asarray(y, dtype=np.float32))
+    cand = np.ascontiguousarray(np.asarray(candidates, dtype=np.float64))
+    if y.size > 64:
+        raise ValueError("at most 64 values per block")
+    codes = np.zeros(y.size, dtype=np.uint8)
+    sel = ctypes.c_int(0)
+    lib().rzo_encode_block_scaled(_ptr(y), y.size, _ptr(cand), cand.size, int(remap), _ptr(codes),
+                                  ctypes.byref(sel))
+    return codes, sel.value
+
+
+class Packed:
+    """Host copy of a packed RaZeR tensor."""
+
+    def __init__(self, kind, rows, cols, offsets, codes, scales, tensor_scale):
+        self.kind, self.rows, self.cols = kind, rows, cols
+        self.offsets = tuple(int(o) for o in offsets)
+        self.codes, self.scales = codes, scales
+        self.tensor_scale = np.float32(tensor_scale)
+
+    def unpacked_codes(self) -> np.ndarray:
+        c = self.codes.reshape(self.rows, self.cols // 2)
+        out = np.empty((self.rows, self.cols), dtype=np.uint8)
+        out[:, 0::2] = c & 15
+        out[:, 1::2] = c >> 4
+        return out
+
+
+def quantize(kind: int, x, offsets, remap: bool = True) -> Packed:
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    if x.ndim != 2:
+        raise ValueError("x must be 2-D")
+    rows, cols = x.shape
+    off = _offsets(kind, offsets)
+    codes = np.zeros(rows * cols // 2, dtype=np.uint8)
+    scales = np.zeros(rows * cols // 16, dtype=np.uint8)
+    ts = np.zeros(1, dtype=np.float32)
+    rc = lib().rzo_quantize(kind, _ptr(x), rows, cols, _ptr(off), int(remap), _ptr(codes),
+                            _ptr(scales), _ptr(ts))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments")
+    return Packed(kind, rows, cols, offsets, codes, scales, ts[0])
+
+
+def quantize_weight(w, offsets=(-2, 4), remap: bool = True) -> Packed:
+    return quantize(WEIGHT, w, offsets, remap)
+
+
+def quantize_act(x, offsets=(-2,), remap: bool = True) -> Packed:
+    return quantize(ACT, x, offsets, remap)
+
+
+def dequant_f64(p: Packed) -> np.ndarray:
+    out = np.empty((p.rows, p.cols), dtype=np.float64)
+    off = _offsets(p.kind, p.offsets)
+    lib().rzo_dequant_f64(p.kind, _ptr(p.codes), _ptr(p.scales), float(p.tensor_scale), _ptr(off),
+                          p.rows, p.cols, _ptr(out))
+    return out
+
+
+def dequant_f32(p: Packed) -> np.ndarray:
+    out = np.empty((p.rows, p.cols), dtype=np.float32)
+    off = _offsets(p.kind, p.offsets)
+    lib().rzo_dequant_f32(p.kind, _ptr(p.codes), _ptr(p.scales), float(p.tensor_scale), _ptr(off),
+                          p.rows, p.cols, _ptr(out))
+    return out
+
+
+def gemm(x, p: Packed, cols=None):
+    """fp64 product y = x @ w^T over the packed weight, plus the norm sum |x||w|.
+
+    ``cols`` selects weight rows (output columns); None means all.  Returns
+    (y [m, ncols], norm [m, ncols])."""
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    if x.ndim == 1:
+        x = x[None, :]
+    m, k = x.shape
+    if k != p.cols:
+        raise ValueError("inner dimensions differ")
+    off = _offsets(p.kind, p.offsets)
+    if cols is None:
+        idx = None
+        ncols = p.rows
+    else:
+        idx = np.ascontiguousarray(np.asarray(cols, dtype=np.int64))
+        ncols = idx.size
+    y = np.zeros((m, ncols), dtype=np.float64)
+    nrm = np.zeros((m, ncols), dtype=np.float64)
+    lib().rzo_gemm(_ptr(x), m, k, p.kind, _ptr(p.codes), _ptr(p.scales), float(p.tensor_scale),
+                   _ptr(off), p.rows, None if idx is None else _ptr(idx), ncols, _ptr(y), _ptr(nrm))
+    return y, nrm

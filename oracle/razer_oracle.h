@@ -1,0 +1,92 @@
+/*
+ * razer_oracle.h -- CPU oracle for RaZeR-NVFP4 (test infrastructure only).
+ *
+ * A plain, slow, single-threaded C statement of what the RaZeR-NVFP4 layer
+ * computes: the two-level block-scaled FP4 encoder with redundant-zero
+ * remapping, its decoder, and the W4A16 product.  It exists so that tests,
+ * the smoke check and the bench's CPU-baseline leg have something obviously
+ * correct to compare the GPU library against.  Nothing in the product path
+ * may load it, and it shares no code, header, table or constant with the GPU
+ * library (the two are written independently from the pages).
+ *
+ * Sources (page title, then the part of it used):
+ *   [notes]   "RaZeR: Pushing the Limits of NVFP4 Quantization with Redundant
+ *             Zero Remapping" (papernotes.org notes)
+ *   [summary] "Technical Summary: RaZeR - Pushing the Limits of NVFP4
+ *             Quantization with Redundant Zero Remapping" (gist.science)
+ *
+ * Pins (tests/test_oracle_pins.py): FP4 set, special-value rule, E4M3/E3M3
+ * tables and rounding (torch float8_e4m3fn), FP4 rounding (closed form with
+ * numpy rint), block argmin (exact rational brute force), error never above
+ * plain NVFP4, product (numpy matmul).  Parity unpinned: the fp32 operation
+ * order of the scale steps is a convention the pages do not fix; it is pinned
+ * only up to fp32 rounding (scale codes equal the exact-rational nearest code
+ * except within 2^-20 of a midpoint) and otherwise by GPU/CPU agreement.
+ *
+ * All pointers are host pointers.  Tensors are row-major [rows, cols]; blocks
+ * are 16 consecutive elements of a row (cols must be a multiple of 16).
+ * Packed layout: codes[r*cols/2 + i] = code(r,2i) | code(r,2i+1) << 4;
+ * scales[r*cols/16 + b] = metadata bits | scale code.
+ */
+#ifndef RAZER_ORACLE_H
+#define RAZER_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { RZO_WEIGHT = 0, RZO_ACT = 1 };
+
+/* FP4-E2M1 value of a 4-bit code (bit 3 = sign); code 8 is -0.0. */
+double rzo_fp4_value(int code);
+/* Index 0..7 of the FP4 magnitude nearest to a >= 0; ties go to the even index. */
+int rzo_fp4_round_mag(double a);
+/* Value of a block-scale code: E3M3 (kind = weight, code 0..63) or E4M3 (act, 0..126). */
+double rzo_scale_value(int kind, int code);
+/* Nearest block-scale code to v >= 0; ties go to the even code; saturates at the maximum. */
+int rzo_scale_round(int kind, float v);
+/* Largest block-scale value: 30 (E3M3) or 448 (E4M3). */
+double rzo_scale_max(int kind);
+/* Special value selected by the metadata: (neg ? -1 : 1) * (6 + off_half/2). */
+double rzo_special_value(int neg, int off_half);
+
+/* Block remap on already-scaled values y[0..n): rounds each value to the FP4
+ * grid, then (if remap) tries every candidate in cand[0..ncand) and keeps the
+ * one with the lowest block squared error, ties to the lowest index.  Writes
+ * one 4-bit code per element and the selected candidate index. */
+void rzo_encode_block_scaled(const float* y, int n, const double* cand, int ncand,
+                             int remap, uint8_t* codes, int* sel);
+
+/* Full-tensor encode.  x: fp32 [rows, cols] (fp16/bf16 inputs are widened
+ * exactly by the caller).  off_half: weight -> 2 entries, act -> 1 entry, each
+ * in [-7, 7] (special value magnitude 6 + off/2).  remap = 0 gives the plain
+ * NVFP4 baseline with the same scale format.  Returns 0, or -1 on bad args. */
+int rzo_quantize(int kind, const float* x, int64_t rows, int64_t cols,
+                 const int8_t* off_half, int remap, uint8_t* codes, uint8_t* scales,
+                 float* tensor_scale);
+
+/* Decoded value (no scaling) of element code `code` in a block with scale byte `sbyte`. */
+double rzo_decode_value(int kind, int code, int sbyte, const int8_t* off_half);
+/* Block scale value held in scale byte `sbyte` (metadata bits stripped). */
+double rzo_block_scale(int kind, int sbyte);
+
+/* Dequantize: out64 exact (val*sb*st in fp64); out32 = fl32(fl32(val*sb)*st). */
+void rzo_dequant_f64(int kind, const uint8_t* codes, const uint8_t* scales, float tensor_scale,
+                     const int8_t* off_half, int64_t rows, int64_t cols, double* out);
+void rzo_dequant_f32(int kind, const uint8_t* codes, const uint8_t* scales, float tensor_scale,
+                     const int8_t* off_half, int64_t rows, int64_t cols, float* out);
+
+/* W4A16 product y[i, j] = sum_k x[i, k] * w[col_j, k] accumulated in fp64,
+ * and norm[i, j] = sum_k |x[i, k]| * |w[col_j, k]|, for the weight rows listed
+ * in cols_idx (NULL = all n rows, in order).  x: fp32 [m, k]; weight packed
+ * [n, k].  y and norm: [m, ncols]. */
+void rzo_gemm(const float* x, int64_t m, int64_t k, int kind, const uint8_t* codes,
+              const uint8_t* scales, float tensor_scale, const int8_t* off_half, int64_t n,
+              const int64_t* cols_idx, int64_t ncols, double* y, double* norm);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,406 @@
+"""Pins for the CPU oracle: checks against what the pages and mathematics fix.
+
+Each test checks the oracle against something other than itself: values the
+pages state, a library routine (torch's float8_e4m3fn cast, numpy's rint and
+matmul), exact rational brute force on small blocks, or invariants the method
+guarantees.  Page names: "RaZeR notes" is the papernotes.org page "RaZeR:
+Pushing the Limits of NVFP4 Quantization with Redundant Zero Remapping";
+"RaZeR summary" is the gist.science technical summary of the same paper.
+"""
+import json
+import math
+import os
+from fractions import Fraction as F
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+FP4_SET = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+# ---- format pins -------------------------------------------------------------
+
+def test_fp4_value_set_matches_pages():
+    # RaZeR notes, Key design 2; RaZeR summary §1: the 15 distinct FP4 values
+    # are +/-{0, 0.5, 1, 1.5, 2, 3, 4, 6}, sign-magnitude with a duplicate zero.
+    vals = [oracle.fp4_value(c) for c in range(16)]
+    assert sorted({abs(v) for v in vals}) == FP4_SET
+    assert len({v for v in vals}) == 15  # +0 and -0 compare equal
+    for c in range(8):
+        assert vals[c] == FP4_SET[c] and vals[c + 8] == -FP4_SET[c]
+    # the redundant code is 0b1000, the negative zero
+    assert vals[8] == 0.0 and math.copysign(1.0, vals[8]) == -1.0
+
+
+def test_special_value_decode_rule():
+    # RaZeR notes, Key design 3: offset register in [-3.5, 3.5], step 0.5, added
+    # to 6.0, sign attached; Key design 2 / RaZeR summary §2.2: special values
+    # are multiples of 0.5 and come as +/- pairs.
+    seen = set()
+    for off in range(-7, 8):
+        pos = oracle.special_value(0, off)
+        neg = oracle.special_value(1, off)
+        offset = off * 0.5
+        assert -3.5 <= offset <= 3.5
+        assert pos == 6.0 + offset and neg == -pos
+        assert (2 * pos) == int(2 * pos)  # multiple of 0.5
+        assert 2.5 <= pos <= 9.5
+        seen.add(pos)
+    assert len(seen) == 15
+    # default pair +/-5 sits in the middle of the 4..6 gap (RaZeR notes, Key design 2)
+    assert oracle.special_value(0, -2) == 5.0
+    # the second pair of the worked example, +/-8
+    assert oracle.special_value(0, 4) == 8.0
+
+
+def test_decode_value_uses_metadata_bits():
+    # RaZeR notes, complete example + Key design 1: weights carry 2 metadata
+    # bits (4 choices), activations 1 bit (2 choices).  Bit 7 = sign, bit 6 = pair.
+    offs = (-2, 4)
+    assert oracle.decode_value(oracle.WEIGHT, 8, 0x00 | 5, offs) == 5.0
+    assert oracle.decode_value(oracle.WEIGHT, 8, 0x80 | 5, offs) == -5.0
+    assert oracle.decode_value(oracle.WEIGHT, 8, 0x40 | 5, offs) == 8.0
+    assert oracle.decode_value(oracle.WEIGHT, 8, 0xC0 | 5, offs) == -8.0
+    assert oracle.decode_value(oracle.ACT, 8, 0x00 | 0x40, (-2,)) == 5.0
+    assert oracle.decode_value(oracle.ACT, 8, 0x80 | 0x40, (-2,)) == -5.0
+    for c in range(16):
+        if c != 8:
+            assert oracle.decode_value(oracle.WEIGHT, c, 0xC0, offs) == oracle.fp4_value(c)
+    # metadata bits never change the block scale
+    assert oracle.block_scale(oracle.WEIGHT, 0xC0 | 0x21) == oracle.block_scale(oracle.WEIGHT, 0x21)
+    assert oracle.block_scale(oracle.ACT, 0x80 | 0x61) == oracle.block_scale(oracle.ACT, 0x61)
+
+
+def _torch_e4m3(code: int) -> float:
+    return float(torch.tensor([code], dtype=torch.uint8).view(torch.float8_e4m3fn).float()[0])
+
+
+def test_e4m3_table_matches_library():
+    # RaZeR notes, Background: the activation block scale is FP8-E4M3.
+    for c in range(127):
+        assert oracle.scale_value(oracle.ACT, c) == _torch_e4m3(c), c
+    assert oracle.scale_max(oracle.ACT) == 448.0
+
+
+def test_e3m3_is_e4m3_with_top_exponent_bit_freed():
+    # RaZeR notes, Key design 1: weights trim the scale to 6-bit E3M3.  Reading:
+    # 3 exponent bits, bias 3, 3 mantissa bits, subnormals; every E3M3 value is
+    # 16x the E4M3 value of the same 6-bit code.
+    vals = [oracle.scale_value(oracle.WEIGHT, c) for c in range(64)]
+    for c in range(64):
+        assert vals[c] == 16.0 * _torch_e4m3(c)
+    assert vals == sorted(vals) and len(set(vals)) == 64
+    assert vals[-1] == 30.0 and vals[1] == 2.0 ** -5 and vals[8] == 0.25
+    assert oracle.scale_max(oracle.WEIGHT) == 30.0
+
+
+def _scale_probe_values():
+    rng = np.random.default_rng(7)
+    v = [0.0, 1e-30, 2.0 ** -10, 2.0 ** -9, 2.0 ** -6, 0.001, 1.0, 448.0, 447.0, 30.0, 29.0]
+    v += list(rng.uniform(0, 448, 3000)) + list(np.exp(rng.uniform(-12, 6, 3000)))
+    # exact midpoints between neighbouring E4M3 values, and one fp32 ulp either side
+    for c in range(126):
+        a, b = _torch_e4m3(c), _torch_e4m3(c + 1)
+        m = np.float32((a + b) / 2)
+        v += [float(m), float(np.nextafter(m, np.float32(0))), float(np.nextafter(m, np.float32(1e9)))]
+    return [float(np.float32(x)) for x in v if 0 <= x <= 448.0]
+
+
+def test_scale_rounding_matches_library_e4m3():
+    # round-to-nearest-even onto the E4M3 grid, as torch's float8_e4m3fn cast does
+    vals = _scale_probe_values()
+    ref = torch.tensor(vals, dtype=torch.float32).to(torch.float8_e4m3fn).float().tolist()
+    for v, r in zip(vals, ref):
+        c = oracle.scale_round(oracle.ACT, v)
+        assert oracle.scale_value(oracle.ACT, c) == r, v
+
+
+def test_scale_rounding_matches_library_e3m3():
+    vals = [v for v in _scale_probe_values() if v <= 30.0]
+    vals += [16.0 * v for v in _scale_probe_values() if 16.0 * v <= 30.0]
+    vals = [float(np.float32(v)) for v in vals]
+    ref = (torch.tensor(vals, dtype=torch.float32) / 16).to(torch.float8_e4m3fn).float() * 16
+    for v, r in zip(vals, ref.tolist()):
+        c = oracle.scale_round(oracle.WEIGHT, v)
+        assert oracle.scale_value(oracle.WEIGHT, c) == r, v
+        assert c < 64
+
+
+def _fp4_rne_closed_form(a: float) -> float:
+    """E2M1 round-to-nearest-even from the float layout: below 1 the step is
+    0.5; in [2^e, 2^(e+1)) one mantissa bit is kept; the result saturates at 6."""
+    if a < 1.0:
+        r = float(np.rint(2.0 * a)) / 2.0
+    else:
+        e = math.floor(math.log2(a))
+        r = float(np.rint(a / 2.0 ** e * 2.0)) / 2.0 * 2.0 ** e
+    return min(r, 6.0)
+
+
+def test_fp4_rounding_matches_closed_form():
+    rng = np.random.default_rng(3)
+    probes = list(rng.uniform(0, 8, 20000)) + list(rng.uniform(0, 0.3, 2000))
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    for m in mids:
+        m32 = np.float32(m)
+        probes += [m, float(np.nextafter(m32, np.float32(0))), float(np.nextafter(m32, np.float32(9)))]
+    probes += [0.0, 6.0, 6.5, 7.0, 100.0, 1e30]
+    for a in probes:
+        a = float(np.float32(a))
+        got = FP4_SET[oracle.fp4_round_mag(a)]
+        assert got == _fp4_rne_closed_form(a), a
+    # ties go to the even mantissa (RNE): the seven midpoints
+    assert [FP4_SET[oracle.fp4_round_mag(m)] for m in mids] == [0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0]
+
+
+# ---- the worked example ------------------------------------------------------
+
+def test_worked_example_from_pages():
+    g = json.load(open(os.path.join(HERE, "golden", "worked_example.json")))
+    codes, sel = oracle.encode_block_scaled(g["block_scaled"], g["candidates"])
+    assert sel == g["expected_sel"]
+    assert codes.tolist() == g["expected_codes"]
+    dec = [oracle.decode_value(oracle.WEIGHT, int(c), 0, g["offsets_half"]) for c in codes]
+    assert dec == g["expected_decoded"]
+    # without remapping the 5.2 values fall to 6 (plain NVFP4)
+    codes0, sel0 = oracle.encode_block_scaled(g["block_scaled"], g["candidates"], remap=False)
+    assert sel0 == 0 and codes0[0] == 7
+    t = g["tie_case"]
+    _, sel_t = oracle.encode_block_scaled(t["block_scaled"], g["candidates"])
+    assert sel_t == t["expected_sel"]
+
+
+# ---- exact brute force of the block-MSE argmin --------------------------------
+
+def _brute_force_block(y, cand):
+    """Exact rational brute force of the block equation: every element goes to
+    the nearest point of the 15-value FP4 codebook plus the candidate (FP4
+    neighbours tie to the even magnitude; the candidate must be strictly
+    nearer), squared error summed exactly, argmin with lowest index."""
+    yq = [F(float(np.float32(v))) for v in y]
+    table = []
+    for code in range(16):
+        if code == 8:
+            continue
+        mag = F(FP4_SET[code & 7])
+        table.append((code, -mag if code & 8 else mag, code & 7))
+
+    def fp4_nearest(v):
+        best = None
+        for code, val, idx in table:
+            d = abs(v - val)
+            if best is None or d < best[0] or (d == best[0] and idx % 2 == 0 and best[2] % 2 == 1):
+                best = (d, code, idx, val)
+        d, code, idx, val = best
+        return (0 if val == 0 else code), val, d
+
+    base = [fp4_nearest(v) for v in yq]
+    best_sse, best_c = None, 0
+    for ci, cv in enumerate(cand):
+        cvf = F(cv)
+        sse = F(0)
+        for v, (code, val, d) in zip(yq, base):
+            q = cvf if abs(v - cvf) < d else val
+            sse += (q - v) ** 2
+        if best_sse is None or sse < best_sse:
+            best_sse, best_c = sse, ci
+    cvf = F(cand[best_c])
+    codes = [8 if abs(v - cvf) < d else code for v, (code, val, d) in zip(yq, base)]
+    return codes, best_c
+
+
+def _adversarial_values():
+    pts = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 4.5, 5.5, 2.25, 2.75, 3.25, 3.75, 4.25, 4.75,
+           5.25, 5.75, 6.25, 6.5, 7.0, 7.5, 8.0, 8.5, 9.0, 0.0, 6.0, 4.0, 3.0]
+    out = []
+    for p in pts:
+        p32 = np.float32(p)
+        out += [p, float(np.nextafter(p32, np.float32(0))), float(np.nextafter(p32, np.float32(99)))]
+    return out + [-v for v in out]
+
+
+CANDIDATE_SETS = [
+    [5.0, -5.0, 8.0, -8.0],      # default weight pairs (+/-5, +/-8)
+    [5.0, -5.0, 3.5, -3.5],      # a second pair that is actually selected
+    [5.0, -5.0, 5.5, -5.5],      # overlapping mapping intervals
+    [2.5, -2.5, 9.5, -9.5],      # extreme offsets
+    [5.0, -5.0],                 # activations
+    [4.5, -4.5, 7.0, -7.0],
+]
+
+
+@pytest.mark.parametrize("cand", CANDIDATE_SETS)
+def test_block_argmin_matches_exact_brute_force(cand):
+    rng = np.random.default_rng(11)
+    adv = _adversarial_values()
+    for trial in range(300):
+        n = int(rng.integers(1, 17))
+        kind = trial % 3
+        if kind == 0:
+            y = rng.uniform(-6.5, 6.5, n)
+        elif kind == 1:
+            y = rng.choice(adv, n)
+        else:  # mostly near the large end, where the special values act
+            y = rng.choice([-1, 1], n) * rng.uniform(3.5, 6.2, n)
+        y = np.asarray(y, dtype=np.float32)
+        codes, sel = oracle.encode_block_scaled(y, cand)
+        bcodes, bsel = _brute_force_block(y, cand)
+        assert sel == bsel, (y.tolist(), cand)
+        assert codes.tolist() == bcodes, (y.tolist(), cand)
+
+
+def test_no_candidate_in_grid_ever_maps():
+    # special case: a candidate equal to an FP4 value never wins an element
+    # (ties keep the regular value), so the block equals plain NVFP4 with sel 0
+    rng = np.random.default_rng(5)
+    for cand in ([6.0, -6.0, 4.0, -4.0], [3.0, -3.0], [6.0, -6.0]):
+        for _ in range(200):
+            y = rng.uniform(-7, 7, 16).astype(np.float32)
+            c1, s1 = oracle.encode_block_scaled(y, cand)
+            c0, _ = oracle.encode_block_scaled(y, cand, remap=False)
+            assert s1 == 0 and c1.tolist() == c0.tolist()
+            assert 8 not in c0.tolist()  # plain NVFP4 never writes -0
+
+
+# ---- tensor-level pins --------------------------------------------------------
+
+def _exact_block_sse(x_blk, xhat_blk):
+    return sum((F(float(a)) - F(float(b))) ** 2 for a, b in zip(x_blk, xhat_blk))
+
+
+@pytest.mark.parametrize("kind,offs", [(oracle.WEIGHT, (-2, 4)), (oracle.WEIGHT, (-2, -5)),
+                                       (oracle.ACT, (-2,))])
+def test_block_error_never_worse_than_nvfp4(kind, offs):
+    # RaZeR adds one value to each block's codebook: with the same scales the
+    # block squared error can only drop (Q is a subset of Q U {v}).
+    rng = np.random.default_rng(21)
+    x = (rng.standard_t(5, (24, 256)) * 0.02).astype(np.float32)
+    if kind == oracle.ACT:
+        x[:, 7] *= 40
+    p1 = oracle.quantize(kind, x, offs)
+    p0 = oracle.quantize(kind, x, offs, remap=False)
+    s1 = p1.scales & (0x3F if kind == oracle.WEIGHT else 0x7F)
+    assert (s1 == p0.scales).all()  # same block scales
+    d1, d0 = oracle.dequant_f64(p1), oracle.dequant_f64(p0)
+    xb, b1, b0 = x.reshape(-1, 16), d1.reshape(-1, 16), d0.reshape(-1, 16)
+    strict = 0
+    for i in range(xb.shape[0]):
+        e1, e0 = _exact_block_sse(xb[i], b1[i]), _exact_block_sse(xb[i], b0[i])
+        assert e1 <= e0
+        strict += e1 < e0
+    assert strict > 0
+
+
+def test_full_tensor_blocks_match_brute_force():
+    # Each block, scaled by the oracle's own block/tensor scale, must be the
+    # exact brute-force argmin; the scale code must be the nearest E3M3 code of
+    # S_MAX * amax_block / amax_tensor unless that exact ratio lies within
+    # 2^-20 (relative) of a rounding midpoint (fp32 op-order convention).
+    rng = np.random.default_rng(8)
+    x = rng.normal(0, 0.02, (16, 128)).astype(np.float32)
+    x.reshape(-1)[rng.choice(x.size, 6, replace=False)] *= 10
+    offs = (-2, -5)
+    p = oracle.quantize_weight(x, offs)
+    st = float(p.tensor_scale)
+    amax = F(float(np.abs(x).max()))
+    assert st == float(np.float32(np.abs(x).max() / np.float32(180.0)))
+    cand = [5.0, -5.0, 3.5, -3.5]
+    grid = [F(oracle.scale_value(oracle.WEIGHT, c)) for c in range(64)]
+    codes = p.unpacked_codes().reshape(-1, 16)
+    for b in range(x.size // 16):
+        xb = x.reshape(-1, 16)[b]
+        sbyte = int(p.scales[b])
+        scode = sbyte & 63
+        exact = 30 * F(float(np.abs(xb).max())) / amax
+        dists = [abs(exact - g) for g in grid]
+        near = min(range(64), key=lambda c: (dists[c], c % 2))
+        if scode != near:
+            mids = [(grid[c] + grid[c + 1]) / 2 for c in range(63)]
+            assert min(abs(exact - m) for m in mids) <= exact * F(1, 2 ** 20)
+        sb = np.float32(oracle.scale_value(oracle.WEIGHT, scode))
+        rcp = np.float32(1.0) / (sb * np.float32(st))
+        y = (xb * rcp).astype(np.float32)
+        bc, bs = _brute_force_block(y, cand)
+        assert codes[b].tolist() == bc
+        meta = ((bs & 1) << 7) | ((bs >> 1) << 6)
+        assert sbyte == meta | scode
+
+
+def test_tensor_max_is_reconstructed():
+    # The block holding the tensor maximum uses the top scale code and maps its
+    # max to FP4 6, so it decodes back to amax up to fp32 rounding.
+    rng = np.random.default_rng(2)
+    for kind, offs in ((oracle.WEIGHT, (-2, 4)), (oracle.ACT, (-2,))):
+        x = rng.normal(0, 1, (8, 64)).astype(np.float32)
+        p = oracle.quantize(kind, x, offs)
+        d = oracle.dequant_f64(p)
+        i = np.unravel_index(np.abs(x).argmax(), x.shape)
+        assert abs(d[i] - x[i]) <= abs(x[i]) * 2.0 ** -22
+        blk = (i[0] * 64 + i[1]) // 16
+        top = 0x3F if kind == oracle.WEIGHT else 0x7E
+        mask = 0x3F if kind == oracle.WEIGHT else 0x7F
+        assert (int(p.scales[blk]) & mask) == top
+
+
+def test_dequant_f32_is_single_rounding_of_exact():
+    rng = np.random.default_rng(4)
+    x = (rng.standard_t(4, (16, 64)) * 0.015).astype(np.float32)
+    p = oracle.quantize_weight(x)
+    assert (oracle.dequant_f32(p) == oracle.dequant_f64(p).astype(np.float32)).all()
+
+
+def test_nonfinite_and_zero_inputs():
+    x = np.zeros((4, 32), dtype=np.float32)
+    p = oracle.quantize_weight(x)
+    assert p.tensor_scale == 0 and not p.codes.any() and not p.scales.any()
+    for bad in (np.nan, np.inf, -np.inf):
+        x = np.ones((4, 32), dtype=np.float32)
+        x[2, 5] = bad
+        p = oracle.quantize_act(x)
+        assert np.isnan(p.tensor_scale) and not p.codes.any() and not p.scales.any()
+
+
+def test_activation_encoding_uses_one_bit():
+    rng = np.random.default_rng(9)
+    x = rng.normal(0, 1, (32, 64)).astype(np.float32)
+    x[:, 3] *= 50
+    p = oracle.quantize_act(x)
+    sel = p.scales >> 7
+    codes = p.unpacked_codes()
+    assert set(np.unique(sel)) <= {0, 1}
+    assert (sel == 1).any() and (sel == 0).any()
+    # blocks that selected -5 hold no remapped element with a positive value
+    d = oracle.dequant_f64(p)
+    blocks = codes.reshape(-1, 16)
+    for b in np.nonzero((sel == 1) & (blocks == 8).any(axis=1))[0]:
+        vals = d.reshape(-1, 16)[b][blocks[b] == 8]
+        assert (vals < 0).all()
+
+
+def test_gemm_matches_library_matmul():
+    rng = np.random.default_rng(12)
+    w = (rng.normal(0, 0.02, (48, 96))).astype(np.float32)
+    x = rng.normal(0, 1, (5, 96)).astype(np.float32)
+    p = oracle.quantize_weight(w)
+    d = oracle.dequant_f64(p)
+    y, nrm = oracle.gemm(x, p)
+    ref = x.astype(np.float64) @ d.T
+    nref = np.abs(x.astype(np.float64)) @ np.abs(d).T
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-12)
+    assert np.allclose(nrm, nref, rtol=1e-12, atol=0)
+    cols = [47, 0, 13]
+    ys, ns = oracle.gemm(x, p, cols)
+    assert np.array_equal(ys, y[:, cols]) and np.array_equal(ns, nrm[:, cols])
+
+
+def test_weight_selection_exercises_every_candidate():
+    # with a second pair at +/-3.5 all four selections occur on Gaussian blocks
+    rng = np.random.default_rng(13)
+    x = rng.normal(0, 0.02, (64, 256)).astype(np.float32)
+    p = oracle.quantize_weight(x, (-2, -5))
+    sel = ((p.scales >> 7) & 1) | (((p.scales >> 6) & 1) << 1)
+    assert set(np.unique(sel)) == {0, 1, 2, 3}
