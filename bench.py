@@ -1,0 +1,338 @@
+#!/usr/bin/env python3
+"""Benchmark of the RaZeR-NVFP4 W4A16 layer on one MI355X.
+
+Headline (the JSON line's ``value``): batch-1 decode throughput of the
+Llama-3-8B-shaped linear layers -- qkv [6144,4096], gate [14336,4096],
+up [14336,4096], down [4096,14336] -- with fp16 activations and RaZeR-W4
+weights (0.02 * Student-t(5)), over L distinct layer copies (default 8, 906 MB
+of packed weights, larger than the 256 MB Infinity Cache).  One step = one
+token through the L layers = 4L razer_gemv launches, replayed from a HIP graph.
+``value`` is algorithmic GB/s (packed weights + x + y + tensor scale, each
+counted once) over the timed steps.
+
+Also measured in the same run (the ``rows`` object): the weight and activation
+encoders (Gelem/s, GB/s, special-value-search overhead), the small-batch GEMM
+sweep (M = 1..32, GB/s) and the M=2048 prefill GEMM (TFLOP/s), each on its own
+synthetic workload; ``roofline`` for the GEMV kernel; ``cpu_baseline`` = the CPU
+oracle on one layer.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L]
+                       [--no-rows] [--no-cpu-baseline] [--only NAME]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA
+METRIC = "RaZeR W4A16 GEMV/GEMM GB/s & TFLOP/s (% roofline); quantizer Gelem/s"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def packed_bytes(n, k):
+    return n * k // 2 + n * k // 16 + 4
+
+
+def gemv_bytes(n, k, xb=2, yb=2):
+    return packed_bytes(n, k) + k * xb + n * yb
+
+
+def clone_packed(rz, p):
+    q = rz.PackedTensor(p.kind, p.rows, p.cols, p.offsets, p.codes.device, p.flags)
+    q.codes.copy_(p.codes)
+    q.scales.copy_(p.scales)
+    q.tensor_scale.copy_(p.tensor_scale)
+    return q
+
+
+class GraphTimer:
+    """Capture fn() (a batch of launches on the current stream) in a HIP graph
+    and time replays with events on that stream."""
+
+    def __init__(self, torch, fn, warmup=2):
+        self.torch = torch
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for _ in range(warmup):
+                fn()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        self.g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.g):
+            fn()
+        torch.cuda.synchronize()
+
+    def time(self, iters, warmup=1):
+        t = self.torch
+        for _ in range(warmup):
+            self.g.replay()
+        t.cuda.synchronize()
+        st = t.cuda.current_stream()
+        e0, e1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(iters):
+            self.g.replay()
+        e1.record(st)
+        e1.synchronize()
+        return e0.elapsed_time(e1) / iters  # ms per replay
+
+
+def source_hash(*names):
+    h = hashlib.sha1()
+    for n in names:
+        h.update(open(os.path.join(ROOT, "nvfp4_razer_w4a16_amd", "csrc", n), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_key, src_hash):
+    """HBM traffic measured by rocprofv3 counters for the current kernel source,
+    or None when the counters are missing or were taken on another version."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        d = json.load(open(path))[kernel_key]
+    except Exception:
+        return None
+    if d.get("source_hash") != src_hash:
+        return None
+    return d.get("bytes_per_launch")
+
+
+# ---- headline: decode GEMV -----------------------------------------------------
+
+def setup_decode(torch, rz, synth, layers):
+    dev = torch.device("cuda:0")
+    names = ["qkv", "gate", "up", "down"]
+    base = {}
+    for name in names:
+        w = torch.from_numpy(synth.llama3_8b_decode_weight(name)).to(dev)
+        base[name] = rz.razer_quantize_weight(w, (-2, 4))
+        del w
+    torch.cuda.synchronize()
+    mats = [{n: (base[n] if li == 0 else clone_packed(rz, base[n])) for n in names}
+            for li in range(layers)]
+    xs = {4096: synth.llama3_8b_decode_x(4096).to(dev).reshape(-1),
+          14336: synth.llama3_8b_decode_x(14336).to(dev).reshape(-1)}
+    ys = {n: torch.empty(base[n].rows, dtype=torch.float16, device=dev) for n in names}
+    launches = [(xs[m.cols], m, ys[n]) for layer in mats for n, m in layer.items()]
+    step_bytes = sum(gemv_bytes(m.rows, m.cols) for _, m, _ in launches)
+    return launches, step_bytes, base
+
+
+def run_launches(rz, launches):
+    for x, w, y in launches:
+        rz.razer_gemv(x, w, out=y)
+
+
+# ---- other rows --------------------------------------------------------------------
+
+def bench_rows(torch, rz, synth, args, decode_base):
+    dev = torch.device("cuda:0")
+    rows = {}
+
+    # weight encoder on the decode layer's weights (offline path, 4 candidates)
+    ws = {}
+    for name in ("gate", "down"):
+        w = torch.from_numpy(synth.llama3_8b_decode_weight(name)).to(dev)
+        out = rz.PackedTensor(rz.RAZER_WEIGHT, w.shape[0], w.shape[1], (-2, 4), dev)
+        out0 = rz.PackedTensor(rz.RAZER_WEIGHT, w.shape[0], w.shape[1], (-2, 4), dev,
+                               rz.RAZER_FLAG_NO_REMAP)
+        ws[name] = (w, out, out0)
+    n_el = sum(w.numel() for w, _, _ in ws.values())
+    t = GraphTimer(torch, lambda: [rz.razer_quantize_weight(w, out=o) for w, o, _ in ws.values()])
+    ms = t.time(20)
+    t0 = GraphTimer(torch, lambda: [rz.razer_quantize_weight(w, out=o0) for w, _, o0 in ws.values()])
+    ms0 = t0.time(20)
+    rows["quantize_weight"] = {
+        "workload": "gate [14336,4096] + down [4096,14336] fp32, 0.02*t(5), offsets (-2,4)",
+        "gelem_per_s": n_el / ms / 1e6, "ms": ms,
+        "gbs_1read": n_el * (4 + 0.5625) / ms / 1e6,
+        "frac_hbm_1read": n_el * (4 + 0.5625) / ms / 1e6 / HBM_PEAK_GBS,
+        "no_remap_ms": ms0, "search_overhead_pct": 100.0 * (ms - ms0) / ms0}
+    del ws, t, t0
+    torch.cuda.empty_cache()
+
+    # activation encoder X[4096, 8192] bf16 (online path, 2 candidates)
+    x = synth.act_quant_x().to(dev)
+    out = rz.PackedTensor(rz.RAZER_ACT, 4096, 8192, (-2,), dev)
+    out0 = rz.PackedTensor(rz.RAZER_ACT, 4096, 8192, (-2,), dev, rz.RAZER_FLAG_NO_REMAP)
+    wsp = torch.empty(rz.razer_workspace_bytes(rz.RAZER_OP_QUANTIZE_ACT, 4096, 0, 8192),
+                      dtype=torch.uint8, device=dev)
+    t = GraphTimer(torch, lambda: rz.razer_quantize_act(x, out=out, workspace=wsp))
+    ms = t.time(50)
+    t0 = GraphTimer(torch, lambda: rz.razer_quantize_act(x, out=out0, workspace=wsp))
+    ms0 = t0.time(50)
+    n_el = x.numel()
+    rows["quantize_act"] = {
+        "workload": "X [4096,8192] bf16 N(0,1), 16 channels x50, 1% tokens x5",
+        "gelem_per_s": n_el / ms / 1e6, "ms": ms,
+        "gbs_1read": n_el * (2 + 0.5625) / ms / 1e6,
+        "frac_hbm_1read": n_el * (2 + 0.5625) / ms / 1e6 / HBM_PEAK_GBS,
+        "no_remap_ms": ms0, "search_overhead_pct": 100.0 * (ms - ms0) / ms0}
+    del x, t, t0
+    torch.cuda.empty_cache()
+
+    # small-batch GEMM sweep
+    sweep = {}
+    for (n, k) in synth.SMALL_BATCH_SHAPES:
+        w = torch.from_numpy(synth.small_batch_weight(n, k)).to(dev)
+        base = rz.razer_quantize_weight(w, (-2, 4))
+        del w
+        copies = max(1, int(640e6 // packed_bytes(n, k)))  # > 2x the Infinity Cache
+        mats = [base] + [clone_packed(rz, base) for _ in range(copies - 1)]
+        for m in synth.SMALL_BATCH_M:
+            x = synth.small_batch_x(m, k).to(dev)
+            y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            t = GraphTimer(torch, lambda: [rz.razer_gemm(x, mm, out=y) for mm in mats])
+            ms = t.time(5) / len(mats)
+            byts = packed_bytes(n, k) + m * k * 2 + m * n * 2
+            sweep[f"{n}x{k}_m{m}"] = {"us": ms * 1e3, "gbs": byts / ms / 1e6,
+                                      "frac_hbm": byts / ms / 1e6 / HBM_PEAK_GBS,
+                                      "tflops": 2.0 * m * n * k / ms / 1e9}
+            del t
+        del mats, base
+        torch.cuda.empty_cache()
+    rows["gemm_small_batch"] = sweep
+
+    # prefill GEMM M=2048, N=28672, K=8192 (+ its offline weight encode)
+    w = torch.from_numpy(synth.prefill_weight()).to(dev)
+    wp = rz.PackedTensor(rz.RAZER_WEIGHT, 28672, 8192, (-2, 4), dev)
+    t = GraphTimer(torch, lambda: rz.razer_quantize_weight(w, out=wp))
+    ms_q = t.time(5)
+    del t, w
+    torch.cuda.empty_cache()
+    x = synth.prefill_x().to(dev)
+    y = torch.empty((2048, 28672), dtype=torch.bfloat16, device=dev)
+    t = GraphTimer(torch, lambda: rz.razer_gemm(x, wp, out=y))
+    ms = t.time(10)
+    flops = 2.0 * 2048 * 28672 * 8192
+    rows["gemm_prefill"] = {
+        "workload": "x [2048,8192] bf16 x W [28672,8192] RaZeR-W4 (0.015*t(4)) -> bf16",
+        "ms": ms, "tflops": flops / ms / 1e9, "frac_mfma": flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS}
+    n_el = 28672 * 8192
+    rows["quantize_weight_prefill"] = {
+        "workload": "W [28672,8192] fp32, 4 candidates", "ms": ms_q, "gelem_per_s": n_el / ms_q / 1e6,
+        "gbs_1read": n_el * (4 + 0.5625) / ms_q / 1e6,
+        "frac_hbm_1read": n_el * (4 + 0.5625) / ms_q / 1e6 / HBM_PEAK_GBS}
+    out = torch.empty((28672, 8192), dtype=torch.bfloat16, device=dev)
+    t = GraphTimer(torch, lambda: rz.razer_dequant(wp, out=out))
+    ms_d = t.time(10)
+    byts = packed_bytes(28672, 8192) + n_el * 2
+    rows["dequant"] = {"workload": "W [28672,8192] -> bf16", "ms": ms_d, "gbs": byts / ms_d / 1e6,
+                       "frac_hbm": byts / ms_d / 1e6 / HBM_PEAK_GBS}
+    del t, x, y, wp, out
+    torch.cuda.empty_cache()
+    return rows
+
+
+# ---- CPU oracle baseline ------------------------------------------------------------
+
+def cpu_baseline(synth):
+    import numpy as np
+    import oracle
+
+    names = ["qkv", "gate", "up", "down"]
+    packs = {}
+    for n in names:
+        packs[n] = oracle.quantize_weight(synth.llama3_8b_decode_weight(n), (-2, 4))
+    xs = {4096: synth.llama3_8b_decode_x(4096).float().numpy(),
+          14336: synth.llama3_8b_decode_x(14336).float().numpy()}
+    byts = 0
+    t0 = time.perf_counter()
+    for n in names:
+        p = packs[n]
+        oracle.gemm(xs[p.cols], p)
+        byts += gemv_bytes(p.rows, p.cols)
+    dt = time.perf_counter() - t0
+    return {"value": byts / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "one layer (qkv, gate, up, down GEMVs, 201M weights) of the decode workload, "
+                      "weights encoded by the oracle (encode not timed), fp64 accumulation, "
+                      f"{dt:.1f} s single-threaded",
+            "seconds": dt, "host_cpus": os.cpu_count()}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--layers", type=int, default=8)
+    ap.add_argument("--no-rows", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import nvfp4_razer_w4a16_amd as rz
+    from nvfp4_razer_w4a16_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    rz.lib()
+    log(f"device: {torch.cuda.get_device_name(0)}")
+
+    log("decode: generating and encoding weights ...")
+    launches, step_bytes, base = setup_decode(torch, rz, synth, args.layers)
+    timer = GraphTimer(torch, lambda: run_launches(rz, launches), warmup=1)
+    for _ in range(args.warmup):
+        timer.g.replay()
+    torch.cuda.synchronize()
+    ms_step = timer.time(args.steps, warmup=0)
+    value = step_bytes / ms_step / 1e6  # GB/s
+    log(f"decode: {ms_step * 1e3:.1f} us/step, {value:.0f} GB/s")
+
+    # live per-kernel figure for the GEMV kernel: the same launches, timed as one
+    # graph on the launch stream; average duration per launch = elapsed / launches
+    n_launch = len(launches)
+    avg_us = ms_step * 1e3 / n_launch
+    bytes_per_launch = step_bytes / n_launch
+    achieved = bytes_per_launch / (avg_us * 1e-6) / 1e9
+    src = source_hash("rz_gemv.hip", "rz_device.h")
+    traffic = load_traffic("gemv_decode", src)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "gemv_kernel (razer_gemv)", "avg_launch_us": round(avg_us, 3),
+                "algorithmic_bytes_per_launch": bytes_per_launch}
+
+    rows = None
+    if not args.no_rows:
+        log("rows: encoders, small-batch sweep, prefill ...")
+        rows = bench_rows(torch, rz, synth, args, base)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline: oracle on one layer ...")
+        cpu = cpu_baseline(synth)
+        cpu["value"] = round(cpu["value"], 4)
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp16",
+        "data": "synthetic (seeded Philox; Student-t(5)*0.02 weights, N(0,1) fp16 x with 8 channels x20)",
+        "config": {"workload": f"llama3-8b decode GEMV: qkv 6144x4096, gate 14336x4096, "
+                               f"up 14336x4096, down 4096x14336; M=1; {args.layers} layer copies; "
+                               "RaZeR-W4 weights, fp16 x and y",
+                   "layers": args.layers, "m": 1, "launches_per_step": n_launch,
+                   "bytes_per_step": step_bytes},
+        "roofline": roofline, "cpu_baseline": cpu, "rows": rows,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,161 @@
+/*
+ * librazer.h -- C ABI of librazer, the RaZeR-NVFP4 W4A16 layer for AMD MI355X
+ * (CDNA4, gfx950).
+ *
+ * Sources cited below (page title, then section):
+ *   [notes]   "RaZeR: Pushing the Limits of NVFP4 Quantization with Redundant
+ *             Zero Remapping" (papernotes.org notes)
+ *   [summary] "Technical Summary: RaZeR - Pushing the Limits of NVFP4
+ *             Quantization with Redundant Zero Remapping" (gist.science)
+ *
+ * THE FORMAT ([notes] Background, Overall framework, Key design 1-3;
+ * [summary] §2.1-2.2).  A tensor X[rows, cols] (row-major, cols % 16 == 0) is
+ * cut into 16-element blocks along each row.  It carries one FP32 tensor
+ * scale st and, per block, one scale byte and 16 four-bit element codes:
+ *
+ *   st       = amax(|X|) / (6 * S_MAX)                       (fp32)
+ *   sb_code  = round_nearest_even(S_MAX * amax_block / amax(|X|))
+ *              onto E3M3 (weights: 3 exp bits, bias 3, max 30) or
+ *              E4M3 (activations: OCP E4M3FN, max 448)
+ *   y_j      = x_j * (1 / (sb * st))                         (fp32)
+ *   code_j   = FP4-E2M1 of y_j: sign bit 3, magnitude index 0..7 of
+ *              {0, 0.5, 1, 1.5, 2, 3, 4, 6}, nearest-even, saturating at 6;
+ *              zero is always written as +0 (0b0000)
+ *   The redundant -0 code 0b1000 is remapped to a per-block special value
+ *   SV = sign * (6 + off/2).  Each block keeps the candidate with the lowest
+ *   block squared error ([notes] Key design 2, block MSE equation), ties to
+ *   the lowest candidate index; an element takes SV only if SV is strictly
+ *   nearer than its FP4 rounding.
+ *     weights:     4 candidates +M0, -M0, +M1, -M1 (two +/- pairs),
+ *                  scale byte = sign << 7 | pair << 6 | E3M3 code (6 bits)
+ *     activations: 2 candidates +M0, -M0,
+ *                  scale byte = sign << 7 | E4M3 code (7 bits)
+ *   with M_i = 6 + sv_off_half[i] / 2 ([notes] Key design 3: 4-bit offset
+ *   registers holding [-3.5, 3.5] in steps of 0.5).
+ *
+ * MEMORY LAYOUT of a packed tensor (all device memory, caller-owned):
+ *   codes[r * cols/2 + i]   = code(r, 2i) | code(r, 2i+1) << 4   (u8)
+ *   scales[r * cols/16 + b] = scale byte of block b of row r     (u8)
+ *   tensor_scale[0]         = st                                 (fp32)
+ * A weight W[N, K] is stored like a PyTorch Linear weight (row n holds the K
+ * inputs of output n); products compute y[M, N] = x[M, K] * W^T.
+ *
+ * CONVENTIONS for every call:
+ *   - Pointers marked "device" point to GPU memory on the current HIP device.
+ *     The caller allocates and frees every buffer, including workspaces; the
+ *     library never allocates, frees or synchronises, and keeps no mutable
+ *     global state.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *     work is enqueued on it, asynchronously, in stream order.
+ *   - Host-side argument checks are synchronous: on RAZER_E_INVALID or
+ *     RAZER_E_UNSUPPORTED nothing is enqueued and nothing is written.
+ *     RAZER_E_HIP reports a failed kernel launch.
+ *   - Data errors are reported through data, not status: a non-finite input
+ *     element makes the encoder write tensor_scale = NaN and all codes and
+ *     scale bytes 0; a product whose weight has a NaN tensor scale outputs NaN.
+ *   - Device pointers must be 16-byte aligned (x, w, y, codes) and 4-byte
+ *     aligned (scales, tensor_scale, workspace).
+ *   - Calls on different streams may run concurrently if they write disjoint
+ *     buffers (including workspaces).
+ */
+#ifndef LIBRAZER_H
+#define LIBRAZER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum razer_status {
+  RAZER_OK = 0,
+  RAZER_E_INVALID = 1,     /* bad argument: null pointer, shape, alignment, offsets, workspace */
+  RAZER_E_UNSUPPORTED = 2, /* valid but not implemented (dtype/kind/shape combination) */
+  RAZER_E_HIP = 3          /* the HIP runtime refused a launch */
+} razer_status;
+
+typedef enum razer_dtype { RAZER_F32 = 0, RAZER_F16 = 1, RAZER_BF16 = 2 } razer_dtype;
+
+/* Which scale format and candidate set a packed tensor uses ([notes] Key
+ * design 1: weights free 2 scale bits, activations 1). */
+typedef enum razer_kind { RAZER_WEIGHT = 0, RAZER_ACT = 1 } razer_kind;
+
+/* flags of razer_packed */
+enum {
+  /* Encode as plain NVFP4 (no special value; sel = 0 everywhere) with the same
+   * scale format: the comparator of the pages' main table, used to measure
+   * what the special-value search costs ([notes] Key design 2 states the
+   * activation search adds under 2% to quantizer time). */
+  RAZER_FLAG_NO_REMAP = 1u
+};
+
+typedef struct razer_packed {
+  int32_t kind;          /* razer_kind */
+  uint32_t flags;        /* RAZER_FLAG_* (read by the encoder only) */
+  int64_t rows;          /* >= 0 */
+  int64_t cols;          /* >= 0, multiple of 16 */
+  int8_t sv_off_half[2]; /* special-value offsets in units of 0.5, each in [-7, 7];
+                            weights use both, activations use [0] only */
+  int8_t reserved[6];
+  uint8_t* codes;        /* device, rows*cols/2 bytes */
+  uint8_t* scales;       /* device, rows*cols/16 bytes */
+  float* tensor_scale;   /* device, 1 float */
+} razer_packed;
+
+/* Operation ids for razer_workspace_bytes. */
+enum {
+  RAZER_OP_QUANTIZE_WEIGHT = 0,
+  RAZER_OP_QUANTIZE_ACT = 1,
+  RAZER_OP_GEMV = 2,
+  RAZER_OP_GEMM = 3
+};
+
+/* Offline weight encoder: 4-candidate block-MSE search ([notes] Key design 2:
+ * weights are searched offline over two +/- pairs; [summary] §2.2).
+ * w: device [out->rows, out->cols] in w_dt (F32, F16 or BF16).  out: describes
+ * the destination; kind must be RAZER_WEIGHT; codes/scales/tensor_scale are
+ * written.  ws: device workspace of at least
+ * razer_workspace_bytes(RAZER_OP_QUANTIZE_WEIGHT, rows, 0, cols) bytes. */
+razer_status razer_quantize_weight(const void* w, razer_dtype w_dt, const razer_packed* out,
+                                   void* ws, size_t ws_bytes, void* stream);
+
+/* Online activation encoder: 2 candidates +/-M0 with the E4M3 block scale
+ * ([notes] Key design 1 and 2; [summary] §2.2).  x: device [rows, cols] in
+ * F16 or BF16 (F32 also accepted).  out->kind must be RAZER_ACT. */
+razer_status razer_quantize_act(const void* x, razer_dtype x_dt, const razer_packed* out,
+                                void* ws, size_t ws_bytes, void* stream);
+
+/* Decode a packed tensor ([notes] Key design 3 decoder): out[r, c] =
+ * value(code) * sb * st, with value(0b1000) = (bit7 ? -1 : 1) * (6 + off/2).
+ * F32 output is fl32(fl32(value * sb) * st); F16/BF16 output is that fp32
+ * value rounded to nearest even.  out: device [rows, cols] in out_dt. */
+razer_status razer_dequant(const razer_packed* t, void* out, razer_dtype out_dt, void* stream);
+
+/* Batch-1 W4A16 product y[1, N] = x[1, K] * W^T with W decoded in registers
+ * ([notes] Key design 3: weight-only GEMV kernels; [summary] §2.3).
+ * x: device [K] in F16 or BF16.  w: packed weight [N, K].  y: device [N] in
+ * F32, F16 or BF16.  Accumulation is fp32.  ws: at least
+ * razer_workspace_bytes(RAZER_OP_GEMV, 1, N, K) bytes (may be 0 -> ws NULL). */
+razer_status razer_gemv(const void* x, razer_dtype x_dt, const razer_packed* w, void* y,
+                        razer_dtype y_dt, void* ws, size_t ws_bytes, void* stream);
+
+/* Batched W4A16 product y[M, N] = x[M, K] * W^T ([notes] Key design 3;
+ * [summary] §2.3: weight-only GEMM kernels for small and large batches).
+ * x: device [m, K] row-major in F16 or BF16.  y: device [m, N] in F32, F16 or
+ * BF16.  m >= 1; m == 1 runs the GEMV path.  ws: at least
+ * razer_workspace_bytes(RAZER_OP_GEMM, m, N, K) bytes. */
+razer_status razer_gemm(const void* x, razer_dtype x_dt, int64_t m, const razer_packed* w, void* y,
+                        razer_dtype y_dt, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes an operation needs for the given sizes (m rows of x, n
+ * weight rows / output features, k reduction length).  0 means none. */
+size_t razer_workspace_bytes(int op, int64_t m, int64_t n, int64_t k);
+
+/* Static, human-readable name of a status code. */
+const char* razer_status_string(razer_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LIBRAZER_H */

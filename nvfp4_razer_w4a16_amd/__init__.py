@@ -1,1 +1,215 @@
-"""RaZeR-NVFP4 W4A16 for AMD MI355X (gfx950): Python binding of librazer."""
+"""RaZeR-NVFP4 W4A16 on AMD MI355X (gfx950): Python binding of librazer.
+
+Thin ctypes marshalling over the C ABI in ``include/librazer.h``; every step of
+the computation runs in librazer's HIP kernels.  PyTorch supplies device memory
+(outputs and workspaces are torch tensors) and the current HIP stream.  If
+``librazer.so`` has not been built, every call raises ``RuntimeError``: there is
+no fallback path.
+
+Functions carry the C names: ``razer_quantize_weight``, ``razer_quantize_act``,
+``razer_dequant``, ``razer_gemv``, ``razer_gemm``, ``razer_workspace_bytes``,
+``razer_status_string``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librazer.so")
+
+RAZER_OK, RAZER_E_INVALID, RAZER_E_UNSUPPORTED, RAZER_E_HIP = 0, 1, 2, 3
+RAZER_F32, RAZER_F16, RAZER_BF16 = 0, 1, 2
+RAZER_WEIGHT, RAZER_ACT = 0, 1
+RAZER_FLAG_NO_REMAP = 1
+RAZER_OP_QUANTIZE_WEIGHT, RAZER_OP_QUANTIZE_ACT, RAZER_OP_GEMV, RAZER_OP_GEMM = 0, 1, 2, 3
+
+EXPORTED = ("razer_quantize_weight", "razer_quantize_act", "razer_dequant", "razer_gemv",
+            "razer_gemm", "razer_workspace_bytes", "razer_status_string")
+
+DEFAULT_WEIGHT_OFFSETS = (-2, 4)  # special values +/-5 and +/-8
+DEFAULT_ACT_OFFSETS = (-2,)       # special values +/-5
+
+_DT = {torch.float32: RAZER_F32, torch.float16: RAZER_F16, torch.bfloat16: RAZER_BF16}
+
+
+class razer_packed(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("flags", ctypes.c_uint32), ("rows", ctypes.c_int64),
+                ("cols", ctypes.c_int64), ("sv_off_half", ctypes.c_int8 * 2),
+                ("reserved", ctypes.c_int8 * 6), ("codes", ctypes.c_void_p),
+                ("scales", ctypes.c_void_p), ("tensor_scale", ctypes.c_void_p)]
+
+
+class RazerError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {razer_status_string(status)}")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded librazer.so.  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "(or python nvfp4_razer_w4a16_amd/build.py)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz, i32, i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int64
+        P = ctypes.POINTER(razer_packed)
+        for name in ("razer_quantize_weight", "razer_quantize_act"):
+            f = getattr(L, name)
+            f.restype, f.argtypes = i32, [vp, i32, P, vp, sz, vp]
+        L.razer_dequant.restype, L.razer_dequant.argtypes = i32, [P, vp, i32, vp]
+        L.razer_gemv.restype, L.razer_gemv.argtypes = i32, [vp, i32, P, vp, i32, vp, sz, vp]
+        L.razer_gemm.restype, L.razer_gemm.argtypes = i32, [vp, i32, i64, P, vp, i32, vp, sz, vp]
+        L.razer_workspace_bytes.restype = sz
+        L.razer_workspace_bytes.argtypes = [i32, i64, i64, i64]
+        L.razer_status_string.restype, L.razer_status_string.argtypes = ctypes.c_char_p, [i32]
+        _lib = L
+    return _lib
+
+
+def razer_status_string(status: int) -> str:
+    return lib().razer_status_string(int(status)).decode()
+
+
+def razer_workspace_bytes(op: int, m: int, n: int, k: int) -> int:
+    return int(lib().razer_workspace_bytes(op, m, n, k))
+
+
+def _check(status: int, what: str):
+    if status != RAZER_OK:
+        raise RazerError(status, what)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt not in _DT:
+        raise TypeError(f"unsupported dtype {dt}")
+    return _DT[dt]
+
+
+class PackedTensor:
+    """A RaZeR-packed tensor in device memory (torch tensors own the bytes).
+
+    codes: uint8 [rows, cols // 2]; scales: uint8 [rows, cols // 16];
+    tensor_scale: float32 [1]; kind: RAZER_WEIGHT or RAZER_ACT; offsets:
+    special-value offsets in units of 0.5."""
+
+    def __init__(self, kind: int, rows: int, cols: int, offsets, device, flags: int = 0):
+        if cols % 16:
+            raise ValueError("cols must be a multiple of 16")
+        self.kind, self.rows, self.cols, self.flags = kind, rows, cols, flags
+        self.offsets = tuple(int(o) for o in offsets)
+        self.codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=device)
+        self.scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=device)
+        self.tensor_scale = torch.empty(1, dtype=torch.float32, device=device)
+
+    @property
+    def shape(self):
+        return (self.rows, self.cols)
+
+    def struct(self) -> razer_packed:
+        s = razer_packed()
+        s.kind, s.flags, s.rows, s.cols = self.kind, self.flags, self.rows, self.cols
+        off = list(self.offsets) + [self.offsets[0]] * (2 - len(self.offsets))
+        s.sv_off_half[0], s.sv_off_half[1] = off[0], off[1]
+        s.codes, s.scales = self.codes.data_ptr(), self.scales.data_ptr()
+        s.tensor_scale = self.tensor_scale.data_ptr()
+        return s
+
+    def nbytes(self) -> int:
+        return self.codes.numel() + self.scales.numel() + 4
+
+
+def _workspace(op, m, n, k, device, workspace):
+    need = razer_workspace_bytes(op, m, n, k)
+    if need == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def _quantize(fn, op, kind, x, offsets, remap, out, workspace, stream):
+    if x.dim() != 2:
+        raise ValueError("expected a 2-D tensor")
+    x = x.contiguous()
+    rows, cols = x.shape
+    if out is None:
+        out = PackedTensor(kind, rows, cols, offsets, x.device, 0 if remap else RAZER_FLAG_NO_REMAP)
+    s = out.struct()
+    ws, wsb = _workspace(op, rows, 0, cols, x.device, workspace)
+    _check(fn(ctypes.c_void_p(x.data_ptr()), _dtype_code(x.dtype), ctypes.byref(s),
+              ctypes.c_void_p(ws.data_ptr() if ws is not None else 0), wsb,
+              ctypes.c_void_p(_stream(stream))), fn.__name__)
+    return out
+
+
+def razer_quantize_weight(w: torch.Tensor, offsets=DEFAULT_WEIGHT_OFFSETS, remap: bool = True,
+                          out: PackedTensor | None = None, workspace=None, stream=None):
+    """Offline RaZeR weight encoding of w [N, K] (fp32/fp16/bf16, on the GPU)."""
+    return _quantize(lib().razer_quantize_weight, RAZER_OP_QUANTIZE_WEIGHT, RAZER_WEIGHT, w,
+                     offsets, remap, out, workspace, stream)
+
+
+def razer_quantize_act(x: torch.Tensor, offsets=DEFAULT_ACT_OFFSETS, remap: bool = True,
+                       out: PackedTensor | None = None, workspace=None, stream=None):
+    """Online RaZeR activation encoding of x [rows, cols] (fp16/bf16, on the GPU)."""
+    return _quantize(lib().razer_quantize_act, RAZER_OP_QUANTIZE_ACT, RAZER_ACT, x, offsets,
+                     remap, out, workspace, stream)
+
+
+def razer_dequant(t: PackedTensor, dtype: torch.dtype = torch.float32, out=None, stream=None):
+    if out is None:
+        out = torch.empty((t.rows, t.cols), dtype=dtype, device=t.codes.device)
+    s = t.struct()
+    _check(lib().razer_dequant(ctypes.byref(s), ctypes.c_void_p(out.data_ptr()),
+                               _dtype_code(out.dtype), ctypes.c_void_p(_stream(stream))),
+           "razer_dequant")
+    return out
+
+
+def razer_gemv(x: torch.Tensor, w: PackedTensor, out_dtype: torch.dtype | None = None, out=None,
+               workspace=None, stream=None):
+    """y[N] = x[K] . W^T for a packed weight W [N, K]."""
+    x = x.contiguous()
+    if x.numel() != w.cols:
+        raise ValueError("x must hold K elements")
+    if out is None:
+        out = torch.empty(w.rows, dtype=out_dtype or x.dtype, device=x.device)
+    ws, wsb = _workspace(RAZER_OP_GEMV, 1, w.rows, w.cols, x.device, workspace)
+    s = w.struct()
+    _check(lib().razer_gemv(ctypes.c_void_p(x.data_ptr()), _dtype_code(x.dtype), ctypes.byref(s),
+                            ctypes.c_void_p(out.data_ptr()), _dtype_code(out.dtype),
+                            ctypes.c_void_p(ws.data_ptr() if ws is not None else 0), wsb,
+                            ctypes.c_void_p(_stream(stream))), "razer_gemv")
+    return out
+
+
+def razer_gemm(x: torch.Tensor, w: PackedTensor, out_dtype: torch.dtype | None = None, out=None,
+               workspace=None, stream=None):
+    """y[M, N] = x[M, K] . W^T for a packed weight W [N, K]."""
+    x = x.contiguous()
+    if x.dim() != 2 or x.shape[1] != w.cols:
+        raise ValueError("x must be [M, K]")
+    m = x.shape[0]
+    if out is None:
+        out = torch.empty((m, w.rows), dtype=out_dtype or x.dtype, device=x.device)
+    ws, wsb = _workspace(RAZER_OP_GEMM, m, w.rows, w.cols, x.device, workspace)
+    s = w.struct()
+    _check(lib().razer_gemm(ctypes.c_void_p(x.data_ptr()), _dtype_code(x.dtype), m, ctypes.byref(s),
+                            ctypes.c_void_p(out.data_ptr()), _dtype_code(out.dtype),
+                            ctypes.c_void_p(ws.data_ptr() if ws is not None else 0), wsb,
+                            ctypes.c_void_p(_stream(stream))), "razer_gemm")
+    return out

@@ -1,0 +1,166 @@
+// rz_api.cpp -- the extern "C" entry points of librazer (see include/librazer.h).
+//
+// Host-side argument checks happen here, synchronously, before anything is
+// enqueued; then the launchers in the kernel translation units are called on
+// the caller's stream.  No allocation, no synchronisation, no exceptions cross
+// the ABI.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <stdint.h>
+
+#include "../../include/librazer.h"
+#include "rz_launch.h"
+
+namespace rz {
+
+int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  const int slot = dev & 63;
+  int v = cache[slot].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int cu = 0;
+  if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0)
+    cu = 256;
+  cache[slot].store(cu, std::memory_order_relaxed);
+  return cu;
+}
+
+}  // namespace rz
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+bool dtype_ok(int dt) { return dt == RAZER_F32 || dt == RAZER_F16 || dt == RAZER_BF16; }
+
+// Shape and offset checks shared by every call that reads or writes a packed tensor.
+razer_status check_packed(const razer_packed* p, bool need_data) {
+  if (!p) return RAZER_E_INVALID;
+  if (p->kind != RAZER_WEIGHT && p->kind != RAZER_ACT) return RAZER_E_INVALID;
+  if (p->rows < 0 || p->cols < 0 || p->cols % 16 != 0) return RAZER_E_INVALID;
+  if (p->cols > 0 && p->rows > INT64_MAX / 2 / p->cols) return RAZER_E_INVALID;
+  const int npairs = p->kind == RAZER_WEIGHT ? 2 : 1;
+  for (int i = 0; i < npairs; i++)
+    if (p->sv_off_half[i] < -7 || p->sv_off_half[i] > 7) return RAZER_E_INVALID;
+  if (!p->tensor_scale || !aligned(p->tensor_scale, 4)) return RAZER_E_INVALID;
+  if (need_data && p->rows * p->cols > 0) {
+    if (!p->codes || !p->scales) return RAZER_E_INVALID;
+    if (!aligned(p->codes, 16) || !aligned(p->scales, 4)) return RAZER_E_INVALID;
+  }
+  return RAZER_OK;
+}
+
+rz::PackedView view_of(const razer_packed* p) {
+  rz::PackedView v;
+  v.kind = p->kind;
+  v.flags = p->flags;
+  v.rows = p->rows;
+  v.cols = p->cols;
+  v.off_half[0] = p->sv_off_half[0];
+  v.off_half[1] = p->kind == RAZER_WEIGHT ? p->sv_off_half[1] : p->sv_off_half[0];
+  v.codes = p->codes;
+  v.scales = p->scales;
+  v.tensor_scale = p->tensor_scale;
+  return v;
+}
+
+razer_status status_of(hipError_t e) { return e == hipSuccess ? RAZER_OK : RAZER_E_HIP; }
+
+razer_status quantize_common(const void* x, razer_dtype dt, const razer_packed* out, void* ws,
+                             size_t ws_bytes, void* stream, int kind) {
+  razer_status s = check_packed(out, true);
+  if (s != RAZER_OK) return s;
+  if (out->kind != kind || !dtype_ok(dt)) return RAZER_E_INVALID;
+  const int64_t n = out->rows * out->cols;
+  if (n > 0 && (!x || !aligned(x, 16))) return RAZER_E_INVALID;
+  const size_t need = rz::quantize_ws_bytes();
+  if (!ws || ws_bytes < need || !aligned(ws, 4)) return RAZER_E_INVALID;
+  return status_of(rz::launch_quantize(x, dt, view_of(out), ws, (hipStream_t)stream));
+}
+
+constexpr int64_t kGemvMaxK = 65536;  // x is staged whole in LDS
+
+}  // namespace
+
+extern "C" {
+
+razer_status razer_quantize_weight(const void* w, razer_dtype w_dt, const razer_packed* out,
+                                   void* ws, size_t ws_bytes, void* stream) {
+  return quantize_common(w, w_dt, out, ws, ws_bytes, stream, RAZER_WEIGHT);
+}
+
+razer_status razer_quantize_act(const void* x, razer_dtype x_dt, const razer_packed* out,
+                                void* ws, size_t ws_bytes, void* stream) {
+  return quantize_common(x, x_dt, out, ws, ws_bytes, stream, RAZER_ACT);
+}
+
+razer_status razer_dequant(const razer_packed* t, void* out, razer_dtype out_dt, void* stream) {
+  razer_status s = check_packed(t, true);
+  if (s != RAZER_OK) return s;
+  if (!dtype_ok(out_dt)) return RAZER_E_INVALID;
+  if (t->rows * t->cols == 0) return RAZER_OK;
+  if (!out || !aligned(out, 16)) return RAZER_E_INVALID;
+  return status_of(rz::launch_dequant(view_of(t), out, out_dt, (hipStream_t)stream));
+}
+
+razer_status razer_gemv(const void* x, razer_dtype x_dt, const razer_packed* w, void* y,
+                        razer_dtype y_dt, void* ws, size_t ws_bytes, void* stream) {
+  razer_status s = check_packed(w, true);
+  if (s != RAZER_OK) return s;
+  if (!dtype_ok(x_dt) || !dtype_ok(y_dt)) return RAZER_E_INVALID;
+  if (x_dt == RAZER_F32) return RAZER_E_UNSUPPORTED;
+  if (w->cols > kGemvMaxK) return RAZER_E_UNSUPPORTED;
+  if (w->rows == 0) return RAZER_OK;
+  if (!y || !aligned(y, 16)) return RAZER_E_INVALID;
+  if (w->cols > 0 && (!x || !aligned(x, 16))) return RAZER_E_INVALID;
+  const size_t need = rz::gemv_ws_bytes(w->rows, w->cols);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 4))) return RAZER_E_INVALID;
+  return status_of(rz::launch_gemv(x, x_dt, view_of(w), y, y_dt, ws, ws_bytes, (hipStream_t)stream));
+}
+
+razer_status razer_gemm(const void* x, razer_dtype x_dt, int64_t m, const razer_packed* w, void* y,
+                        razer_dtype y_dt, void* ws, size_t ws_bytes, void* stream) {
+  razer_status s = check_packed(w, true);
+  if (s != RAZER_OK) return s;
+  if (!dtype_ok(x_dt) || !dtype_ok(y_dt) || m < 0) return RAZER_E_INVALID;
+  if (x_dt == RAZER_F32) return RAZER_E_UNSUPPORTED;
+  if (m == 0 || w->rows == 0) return RAZER_OK;
+  if (m == 1) return razer_gemv(x, x_dt, w, y, y_dt, ws, ws_bytes, stream);
+  if (!y || !aligned(y, 16)) return RAZER_E_INVALID;
+  if (w->cols > 0 && (!x || !aligned(x, 16))) return RAZER_E_INVALID;
+  if (m > INT64_MAX / 2 / (w->rows > w->cols ? w->rows : (w->cols ? w->cols : 1)))
+    return RAZER_E_INVALID;
+  const size_t need = rz::gemm_ws_bytes(m, w->rows, w->cols);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 4))) return RAZER_E_INVALID;
+  return status_of(
+      rz::launch_gemm(x, x_dt, m, view_of(w), y, y_dt, ws, ws_bytes, (hipStream_t)stream));
+}
+
+size_t razer_workspace_bytes(int op, int64_t m, int64_t n, int64_t k) {
+  switch (op) {
+    case RAZER_OP_QUANTIZE_WEIGHT:
+    case RAZER_OP_QUANTIZE_ACT:
+      return rz::quantize_ws_bytes();
+    case RAZER_OP_GEMV:
+      return rz::gemv_ws_bytes(n, k);
+    case RAZER_OP_GEMM:
+      return m <= 1 ? rz::gemv_ws_bytes(n, k) : rz::gemm_ws_bytes(m, n, k);
+    default:
+      return 0;
+  }
+}
+
+const char* razer_status_string(razer_status s) {
+  switch (s) {
+    case RAZER_OK: return "RAZER_OK";
+    case RAZER_E_INVALID: return "RAZER_E_INVALID: invalid argument";
+    case RAZER_E_UNSUPPORTED: return "RAZER_E_UNSUPPORTED: unsupported combination";
+    case RAZER_E_HIP: return "RAZER_E_HIP: kernel launch failed";
+    default: return "unknown razer_status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,49 @@
+// rz_launch.h -- internal launcher interface between the C ABI layer and the
+// kernel translation units.  Host-only declarations; no torch types.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace rz {
+
+struct PackedView {
+  int kind;          // 0 weight (E3M3, 4 candidates), 1 activation (E4M3, 2 candidates)
+  uint32_t flags;    // bit 0: plain NVFP4 (no special value)
+  int64_t rows, cols;
+  int off_half[2];   // special-value offsets in units of 0.5
+  uint8_t* codes;
+  uint8_t* scales;
+  float* tensor_scale;
+};
+
+// Special-value candidate magnitudes M = 6 + off/2 and the open interval
+// (lo, hi) of |y| values that move to M instead of their FP4 rounding.
+struct Candidate {
+  float mag;       // M
+  float lo, hi;    // lo < |y| < hi moves to M; lo = hi = 0 when M is an FP4 value
+  int mag_x2;      // 2 * M (integer)
+};
+Candidate make_candidate(int off_half);
+
+// Quantizer: partial tensor-amax pass + block encode pass.
+constexpr int kAmaxMaxPartials = 1024;
+size_t quantize_ws_bytes();
+hipError_t launch_quantize(const void* x, int dtype, const PackedView& out, void* ws,
+                           hipStream_t stream);
+
+hipError_t launch_dequant(const PackedView& t, void* out, int out_dtype, hipStream_t stream);
+
+size_t gemv_ws_bytes(int64_t n, int64_t k);
+hipError_t launch_gemv(const void* x, int x_dtype, const PackedView& w, void* y, int y_dtype,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+size_t gemm_ws_bytes(int64_t m, int64_t n, int64_t k);
+hipError_t launch_gemm(const void* x, int x_dtype, int64_t m, const PackedView& w, void* y,
+                       int y_dtype, void* ws, size_t ws_bytes, hipStream_t stream);
+
+// Device properties used for launch sizing (cached per device).
+int device_cu_count();
+
+}  // namespace rz

@@ -1,0 +1,327 @@
+// rz_quantize.hip -- RaZeR encoder for gfx950: tensor amax pass + block encode.
+//
+// Method: "RaZeR: Pushing the Limits of NVFP4 Quantization with Redundant Zero
+// Remapping" (papernotes.org notes), Overall framework and Key designs 1-2;
+// "Technical Summary: RaZeR ..." (gist.science), §2.1-2.2.
+//
+// Pass 1 (amax_partial_kernel): each workgroup reduces |x| over a grid-stride
+// slice with 128-bit loads and writes one partial maximum (as fp32 bits; NaN
+// and Inf sort above every finite value) to the workspace.  No atomics, so
+// the workspace needs no clearing and the pass can be graph-captured.
+// Pass 2 (encode_kernel): every workgroup folds the partials into the tensor
+// amax, then encodes 16-element blocks, one block per thread:
+//   st = amax / (6 * S_MAX); sb = nearest-even(S_MAX * amax_b / amax) on the
+//   E3M3 / E4M3 grid; y = x * (1 / (sb * st)); FP4 nearest-even codes; the
+//   special value whose block squared error is lowest replaces the redundant
+//   -0 code.  All fp32 steps are single IEEE operations in a fixed order
+//   (this file is compiled with -ffp-contract=off), so the bytes are
+//   reproducible on any IEEE machine.
+//
+// Exact candidate comparison: moving element y (|y| = a) from its FP4 rounding
+// q to the special value M changes the block squared error by
+// (M - q)(M + q - 2a).  With M2 = 2M, Q2 = 2q (integers) and A = a * 2^22 (an
+// integer for every a > 2, which every moved element has), that change times
+// 2^23 is the integer (M2 - Q2) * ((M2 + Q2) * 2^21 - 2A).  Summing these in
+// int64 gives every candidate's error change exactly, so the argmin (ties to
+// the lowest candidate index) never depends on rounding or summation order.
+#include "rz_device.h"
+#include "rz_launch.h"
+
+#include <math.h>
+
+namespace rz {
+
+Candidate make_candidate(int off_half) {
+  static const double kGrid[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+  const double M = 6.0 + off_half / 2.0;
+  Candidate c;
+  c.mag = (float)M;
+  c.mag_x2 = 12 + off_half;
+  bool on_grid = false;
+  double below = 0.0, above = INFINITY;
+  for (double g : kGrid) {
+    if (g == M) on_grid = true;
+    if (g < M && g > below) below = g;
+    if (g > M && g < above) above = g;
+  }
+  if (on_grid) {
+    c.lo = c.hi = 0.0f;  // an FP4 value never wins (a tie keeps the FP4 code)
+  } else {
+    c.lo = (float)((below + M) / 2.0);  // exact: quarter-integers
+    c.hi = std::isinf(above) ? INFINITY : (float)((M + above) / 2.0);
+  }
+  return c;
+}
+
+size_t quantize_ws_bytes() { return kAmaxMaxPartials * sizeof(uint32_t); }
+
+struct EncodeParams {
+  float lo[2], hi[2];
+  int mag_x2[2];
+  int remap;
+};
+
+// ---- pass 1: partial tensor amax ---------------------------------------------
+// |x| as fp32 bit patterns: unsigned order equals magnitude order, and NaN/Inf
+// (>= 0x7F800000) sort above every finite value.
+template <typename T> __device__ __forceinline__ uint32_t absbits_max(uint4 v);
+
+template <> __device__ __forceinline__ uint32_t absbits_max<float>(uint4 v) {
+  return max(max(v.x & 0x7FFFFFFFu, v.y & 0x7FFFFFFFu), max(v.z & 0x7FFFFFFFu, v.w & 0x7FFFFFFFu));
+}
+template <> __device__ __forceinline__ uint32_t absbits_max<__bf16>(uint4 v) {
+  uint32_t m = 0;
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; i++) m = max(m, max(w[i] & 0x7FFF0000u, (w[i] << 16) & 0x7FFF0000u));
+  return m;
+}
+// fp16: reduce 15-bit magnitudes (monotone in value), widened to fp32 later.
+template <> __device__ __forceinline__ uint32_t absbits_max<_Float16>(uint4 v) {
+  uint32_t m = 0;
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; i++) m = max(m, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+  return m;
+}
+
+template <typename T> __device__ __forceinline__ uint32_t absbits_finish(uint32_t m) { return m; }
+template <> __device__ __forceinline__ uint32_t absbits_finish<_Float16>(uint32_t m) {
+  return f2u((float)__builtin_bit_cast(_Float16, (uint16_t)m));
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void amax_partial_kernel(const uint4* __restrict__ x, int64_t nvec,
+                                                           uint32_t* __restrict__ partial) {
+  uint32_t m = 0;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  for (; i + 3 * stride < nvec; i += 4 * stride) {
+    uint4 a = load_nt16(x + i);
+    uint4 b = load_nt16(x + i + stride);
+    uint4 c = load_nt16(x + i + 2 * stride);
+    uint4 d = load_nt16(x + i + 3 * stride);
+    m = max(m, max(max(absbits_max<T>(a), absbits_max<T>(b)), max(absbits_max<T>(c), absbits_max<T>(d))));
+  }
+  for (; i < nvec; i += stride) m = max(m, absbits_max<T>(x[i]));
+  m = wave_max_u32(absbits_finish<T>(m));
+  __shared__ uint32_t sm[4];
+  if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) partial[blockIdx.x] = max(max(sm[0], sm[1]), max(sm[2], sm[3]));
+}
+
+// ---- pass 2: block encode ----------------------------------------------------
+template <typename T> __device__ __forceinline__ void load_block(const T* p, float (&v)[16]);
+
+template <> __device__ __forceinline__ void load_block<float>(const float* p, float (&v)[16]) {
+  const float4* q = (const float4*)p;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    float4 t = q[i];
+    v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
+  }
+}
+template <> __device__ __forceinline__ void load_block<__bf16>(const __bf16* p, float (&v)[16]) {
+  const uint4* q = (const uint4*)p;
+#pragma unroll
+  for (int i = 0; i < 2; i++) {
+    uint4 t = q[i];
+    uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      v[8 * i + 2 * j] = u2f(w[j] << 16);
+      v[8 * i + 2 * j + 1] = u2f(w[j] & 0xFFFF0000u);
+    }
+  }
+}
+template <> __device__ __forceinline__ void load_block<_Float16>(const _Float16* p, float (&v)[16]) {
+  const uint4* q = (const uint4*)p;
+#pragma unroll
+  for (int i = 0; i < 2; i++) {
+    uint4 t = q[i];
+    uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      v[8 * i + 2 * j] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[j] & 0xFFFFu));
+      v[8 * i + 2 * j + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[j] >> 16));
+    }
+  }
+}
+
+// Nearest-even block-scale code for v >= 0, saturating at the format maximum.
+// Normal range: keep 3 mantissa bits of the fp32 value with a round-to-even
+// carry; subnormal range: round v / quantum to an integer (v_rndne_f32).  The
+// subnormal result 8 is exactly the smallest normal code, so both ranges join.
+template <int KIND> __device__ __forceinline__ uint32_t round_scale(float v) {
+  constexpr float kMax = KIND == kWeight ? 30.0f : 448.0f;
+  constexpr float kNormMin = KIND == kWeight ? 0.25f : 0.015625f;
+  constexpr float kSubInv = KIND == kWeight ? 32.0f : 512.0f;
+  constexpr int kBias = KIND == kWeight ? 3 : 7;
+  constexpr uint32_t kMaxCode = KIND == kWeight ? 63u : 126u;
+  if (v >= kMax) return kMaxCode;
+  if (v < kNormMin) return (uint32_t)__builtin_rintf(v * kSubInv);
+  uint32_t b = f2u(v);
+  b = (b + 0x7FFFFu + ((b >> 20) & 1u)) & 0xFFF00000u;
+  uint32_t code = ((uint32_t)((int)(b >> 23) - 127 + kBias) << 3) | ((b >> 20) & 7u);
+  return min(code, kMaxCode);
+}
+
+template <int KIND> __device__ __forceinline__ float scale_of_code(uint32_t code) {
+  return scale_of_byte<KIND>(code);
+}
+
+template <int KIND>
+__device__ __forceinline__ void encode_block(const float (&xf)[16], float amax, float st,
+                                             const EncodeParams& prm, uint2& cw, uint32_t& sbyte) {
+  constexpr float kSMax = KIND == kWeight ? 30.0f : 448.0f;
+  constexpr int kPairs = KIND == kWeight ? 2 : 1;
+  cw = make_uint2(0u, 0u);
+  sbyte = 0u;
+  float amax_b = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 16; j++) amax_b = fmaxf(amax_b, fabsf(xf[j]));
+  const float r = amax_b / amax;
+  const float sb_real = r * kSMax;
+  const uint32_t scode = round_scale<KIND>(sb_real);
+  if (scode == 0u) return;  // block underflows to zero
+  const float sb = scale_of_code<KIND>(scode);
+  const float d = sb * st;
+  const float rcp = 1.0f / d;
+  if (!(rcp < INFINITY)) return;  // scale product underflowed: zero block
+
+  float a[16];
+  uint32_t m0[16];
+  uint32_t neg = 0u;
+  long long acc[2 * kPairs];
+#pragma unroll
+  for (int c = 0; c < 2 * kPairs; c++) acc[c] = 0;
+#pragma unroll
+  for (int j = 0; j < 16; j++) {
+    const float y = xf[j] * rcp;
+    const uint32_t nj = f2u(y) >> 31;
+    neg |= nj << j;
+    const float aj = fabsf(y);
+    a[j] = aj;
+    // FP4 nearest-even magnitude index: count the decision points passed.
+    // A tie at 0.25, 1.25, 2.5, 5 stays below, at 0.75, 1.75, 3.5 goes up.
+    m0[j] = (uint32_t)(aj > 0.25f) + (uint32_t)(aj >= 0.75f) + (uint32_t)(aj > 1.25f) +
+            (uint32_t)(aj >= 1.75f) + (uint32_t)(aj > 2.5f) + (uint32_t)(aj >= 3.5f) +
+            (uint32_t)(aj > 5.0f);
+    if (prm.remap) {
+      const int q2 = (int)fp4_mag_x2(m0[j]);
+      const int a2 = 2 * (int)(aj * 4194304.0f);  // 2 * a * 2^22 (exact when it matters)
+#pragma unroll
+      for (int p = 0; p < kPairs; p++) {
+        const bool in = aj > prm.lo[p] && aj < prm.hi[p];
+        const int dd = prm.mag_x2[p] - q2;
+        const int ee = ((prm.mag_x2[p] + q2) << 21) - a2;
+        const int dpos = (in && !nj) ? dd : 0;
+        const int dneg = (in && nj) ? dd : 0;
+        acc[2 * p] += (long long)dpos * (long long)ee;
+        acc[2 * p + 1] += (long long)dneg * (long long)ee;
+      }
+    }
+  }
+  uint32_t sel = 0u;
+  if (prm.remap) {
+    long long best = acc[0];
+#pragma unroll
+    for (int c = 1; c < 2 * kPairs; c++)
+      if (acc[c] < best) {
+        best = acc[c];
+        sel = (uint32_t)c;
+      }
+  }
+  const int p = (int)(sel >> 1);
+  const uint32_t sneg = sel & 1u;
+  const float lo = prm.lo[p], hi = prm.hi[p];
+  uint32_t w[2] = {0u, 0u};
+#pragma unroll
+  for (int j = 0; j < 16; j++) {
+    const uint32_t nj = (neg >> j) & 1u;
+    const bool hit = prm.remap && a[j] > lo && a[j] < hi && nj == sneg;
+    const uint32_t nib = hit ? 8u : (m0[j] == 0u ? 0u : ((nj << 3) | m0[j]));
+    w[j >> 3] |= nib << (4 * (j & 7));
+  }
+  cw = make_uint2(w[0], w[1]);
+  sbyte = (KIND == kWeight) ? (((sel & 1u) << 7) | ((sel >> 1) << 6) | scode) : ((sel << 7) | scode);
+}
+
+template <int KIND, typename T>
+__global__ __launch_bounds__(256) void encode_kernel(const T* __restrict__ x, int64_t nblk,
+                                                     const uint32_t* __restrict__ partial,
+                                                     int npartial, uint2* __restrict__ codes,
+                                                     uint8_t* __restrict__ scales,
+                                                     float* __restrict__ ts_out, EncodeParams prm) {
+  constexpr float kSMax = KIND == kWeight ? 30.0f : 448.0f;
+  uint32_t m = 0u;
+  for (int i = threadIdx.x; i < npartial; i += 256) m = max(m, partial[i]);
+  m = wave_max_u32(m);
+  __shared__ uint32_t sm[4];
+  if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = max(max(sm[0], sm[1]), max(sm[2], sm[3]));
+  const bool nonfinite = m >= 0x7F800000u;
+  const float amax = u2f(m);
+  const float st = amax / (6.0f * kSMax);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *ts_out = nonfinite ? __builtin_nanf("") : st;
+  const bool all_zero = nonfinite || amax == 0.0f;
+
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x; b < nblk; b += stride) {
+    uint2 cw = make_uint2(0u, 0u);
+    uint32_t sbyte = 0u;
+    if (!all_zero) {
+      float xf[16];
+      load_block<T>(x + 16 * b, xf);
+      encode_block<KIND>(xf, amax, st, prm, cw, sbyte);
+    }
+    codes[b] = cw;
+    scales[b] = (uint8_t)sbyte;
+  }
+}
+
+template <int KIND, typename T>
+static hipError_t run_quantize(const T* x, const PackedView& out, uint32_t* partial,
+                               hipStream_t stream) {
+  const int64_t n = out.rows * out.cols;
+  const int64_t nblk = n / 16;
+  const int64_t nvec = n / (16 / (int64_t)sizeof(T));
+  int64_t g1 = (nvec + 4 * 256 - 1) / (4 * 256);
+  if (g1 < 1) g1 = 1;
+  if (g1 > kAmaxMaxPartials) g1 = kAmaxMaxPartials;
+  hipLaunchKernelGGL(amax_partial_kernel<T>, dim3((unsigned)g1), dim3(256), 0, stream,
+                     (const uint4*)x, nvec, partial);
+  EncodeParams prm;
+  const int npairs = KIND == kWeight ? 2 : 1;
+  for (int p = 0; p < 2; p++) {
+    Candidate c = make_candidate(out.off_half[p < npairs ? p : 0]);
+    prm.lo[p] = c.lo;
+    prm.hi[p] = c.hi;
+    prm.mag_x2[p] = c.mag_x2;
+  }
+  prm.remap = (out.flags & 1u) ? 0 : 1;
+  int64_t g2 = (nblk + 255) / 256;
+  const int64_t cap = (int64_t)device_cu_count() * 8;
+  if (g2 > cap) g2 = cap;
+  if (g2 < 1) g2 = 1;
+  hipLaunchKernelGGL((encode_kernel<KIND, T>), dim3((unsigned)g2), dim3(256), 0, stream, x, nblk,
+                     partial, (int)g1, (uint2*)out.codes, out.scales, out.tensor_scale, prm);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize(const void* x, int dtype, const PackedView& out, void* ws,
+                           hipStream_t stream) {
+  uint32_t* partial = (uint32_t*)ws;
+  if (out.kind == kWeight) {
+    if (dtype == kF32) return run_quantize<kWeight>((const float*)x, out, partial, stream);
+    if (dtype == kF16) return run_quantize<kWeight>((const _Float16*)x, out, partial, stream);
+    return run_quantize<kWeight>((const __bf16*)x, out, partial, stream);
+  }
+  if (dtype == kF32) return run_quantize<kAct>((const float*)x, out, partial, stream);
+  if (dtype == kF16) return run_quantize<kAct>((const _Float16*)x, out, partial, stream);
+  return run_quantize<kAct>((const __bf16*)x, out, partial, stream);
+}
+
+}  // namespace rz

@@ -1,0 +1,123 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/librazer.h declares, and rejects bad arguments on the host before any
+HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import nvfp4_razer_w4a16_amd as rz
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "librazer.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(razer_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_five_calls():
+    names = _declared_functions()
+    for n in ("razer_quantize_weight", "razer_quantize_act", "razer_dequant", "razer_gemv",
+              "razer_gemm"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = rz.lib()
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+    assert set(rz.EXPORTED) <= set(_declared_functions())
+
+
+def test_struct_layout_matches_header():
+    # int32 kind, uint32 flags, int64 rows, int64 cols, int8[2] + 6 reserved, 3 pointers
+    assert ctypes.sizeof(rz.razer_packed) == 4 + 4 + 8 + 8 + 8 + 3 * 8
+    assert rz.razer_packed.codes.offset == 32
+
+
+def test_status_strings():
+    assert rz.razer_status_string(rz.RAZER_OK) == "RAZER_OK"
+    assert "invalid" in rz.razer_status_string(rz.RAZER_E_INVALID)
+    assert "unknown" in rz.razer_status_string(99)
+
+
+def test_workspace_sizes():
+    assert rz.razer_workspace_bytes(rz.RAZER_OP_QUANTIZE_WEIGHT, 0, 256, 1024) >= 4096
+    assert rz.razer_workspace_bytes(rz.RAZER_OP_QUANTIZE_ACT, 4096, 0, 8192) >= 4096
+    assert rz.razer_workspace_bytes(99, 1, 1, 1) == 0
+
+
+def _packed(kind=rz.RAZER_WEIGHT, rows=4, cols=32, off=(-2, 4), codes=0x1000, scales=0x2000,
+            ts=0x3000):
+    s = rz.razer_packed()
+    s.kind, s.flags, s.rows, s.cols = kind, 0, rows, cols
+    s.sv_off_half[0], s.sv_off_half[1] = off
+    s.codes, s.scales, s.tensor_scale = codes, scales, ts
+    return s
+
+
+FAKE_X = ctypes.c_void_p(0x4000)   # never dereferenced: every case fails host checks
+FAKE_WS = ctypes.c_void_p(0x5000)
+
+
+@pytest.mark.parametrize("mutate", [
+    lambda s: setattr(s, "cols", 24),                  # cols % 16 != 0
+    lambda s: setattr(s, "rows", -1),
+    lambda s: s.sv_off_half.__setitem__(0, 8),         # offset outside [-7, 7]
+    lambda s: s.sv_off_half.__setitem__(1, -8),
+    lambda s: setattr(s, "codes", None),
+    lambda s: setattr(s, "scales", None),
+    lambda s: setattr(s, "tensor_scale", None),
+    lambda s: setattr(s, "codes", 0x1008),             # misaligned codes
+    lambda s: setattr(s, "kind", rz.RAZER_ACT),        # wrong kind for the weight encoder
+    lambda s: setattr(s, "kind", 7),
+])
+def test_quantize_weight_rejects_bad_packed(mutate):
+    s = _packed()
+    mutate(s)
+    st = rz.lib().razer_quantize_weight(FAKE_X, rz.RAZER_F32, ctypes.byref(s), FAKE_WS, 4096, None)
+    assert st == rz.RAZER_E_INVALID
+
+
+def test_quantize_rejects_bad_buffers():
+    L = rz.lib()
+    s = _packed()
+    assert L.razer_quantize_weight(None, rz.RAZER_F32, ctypes.byref(s), FAKE_WS, 4096, None) == rz.RAZER_E_INVALID
+    assert L.razer_quantize_weight(ctypes.c_void_p(0x4004), rz.RAZER_F32, ctypes.byref(s), FAKE_WS, 4096, None) == rz.RAZER_E_INVALID
+    assert L.razer_quantize_weight(FAKE_X, rz.RAZER_F32, ctypes.byref(s), FAKE_WS, 16, None) == rz.RAZER_E_INVALID
+    assert L.razer_quantize_weight(FAKE_X, rz.RAZER_F32, ctypes.byref(s), None, 4096, None) == rz.RAZER_E_INVALID
+    assert L.razer_quantize_weight(FAKE_X, 9, ctypes.byref(s), FAKE_WS, 4096, None) == rz.RAZER_E_INVALID
+    assert L.razer_quantize_weight(FAKE_X, rz.RAZER_F32, None, FAKE_WS, 4096, None) == rz.RAZER_E_INVALID
+    a = _packed(kind=rz.RAZER_ACT, off=(-2, 99))  # act kind ignores the second offset ...
+    a.sv_off_half[0] = -9                          # ... but checks the first
+    assert L.razer_quantize_act(FAKE_X, rz.RAZER_BF16, ctypes.byref(a), FAKE_WS, 4096, None) == rz.RAZER_E_INVALID
+
+
+def test_products_reject_bad_arguments():
+    L = rz.lib()
+    s = _packed()
+    y = ctypes.c_void_p(0x6000)
+    assert L.razer_gemv(FAKE_X, rz.RAZER_F32, ctypes.byref(s), y, rz.RAZER_F32, None, 0, None) == rz.RAZER_E_UNSUPPORTED
+    assert L.razer_gemv(FAKE_X, 7, ctypes.byref(s), y, rz.RAZER_F32, None, 0, None) == rz.RAZER_E_INVALID
+    assert L.razer_gemv(FAKE_X, rz.RAZER_F16, ctypes.byref(s), None, rz.RAZER_F32, None, 0, None) == rz.RAZER_E_INVALID
+    assert L.razer_gemv(ctypes.c_void_p(0x4002), rz.RAZER_F16, ctypes.byref(s), y, rz.RAZER_F32, None, 0, None) == rz.RAZER_E_INVALID
+    big = _packed(cols=65536 + 16)
+    assert L.razer_gemv(FAKE_X, rz.RAZER_F16, ctypes.byref(big), y, rz.RAZER_F32, None, 0, None) == rz.RAZER_E_UNSUPPORTED
+    assert L.razer_gemm(FAKE_X, rz.RAZER_BF16, -1, ctypes.byref(s), y, rz.RAZER_F32, None, 0, None) == rz.RAZER_E_INVALID
+    assert L.razer_gemm(FAKE_X, rz.RAZER_BF16, 0, ctypes.byref(s), y, rz.RAZER_F32, None, 0, None) == rz.RAZER_OK
+    assert L.razer_gemm(FAKE_X, rz.RAZER_F32, 4, ctypes.byref(s), y, rz.RAZER_F32, None, 0, None) == rz.RAZER_E_UNSUPPORTED
+    assert L.razer_gemm(FAKE_X, rz.RAZER_BF16, 4, ctypes.byref(s), ctypes.c_void_p(0x6004), rz.RAZER_F32, None, 0, None) == rz.RAZER_E_INVALID
+    bad = _packed(cols=20)
+    assert L.razer_dequant(ctypes.byref(bad), y, rz.RAZER_F32, None) == rz.RAZER_E_INVALID
+    assert L.razer_dequant(ctypes.byref(s), y, 5, None) == rz.RAZER_E_INVALID
+    assert L.razer_dequant(ctypes.byref(s), None, rz.RAZER_F32, None) == rz.RAZER_E_INVALID
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(rz, "_lib", None)
+    monkeypatch.setattr(rz, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        rz.lib()

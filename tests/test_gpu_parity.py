@@ -1,0 +1,406 @@
+"""GPU parity: librazer (HIP, through the C ABI) against the CPU oracle.
+
+Encodings (codes, scale bytes, tensor scale) and dequantized values must match
+bit for bit.  Products must satisfy |y - y_ref| <= 2e-3 * sum_k |x| |w| per
+output, with y_ref the oracle's fp64 product over the oracle's own packed
+weights.  Inputs come from the seeded generators in nvfp4_razer_w4a16_amd.synth;
+no expected value comes from the GPU path.
+"""
+import functools
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_razer_w4a16_amd as rz
+import oracle
+from nvfp4_razer_w4a16_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3  # relative to sum |x||w| per output
+
+# Rounding the finished fp32 value to a 16-bit output adds up to half an ulp
+# of that format on top of the product tolerance (bf16: 8 significant bits,
+# fp16: 11).  With small K, |y| comes close to sum |x||w| and this term alone
+# can exceed 2e-3 * sum |x||w|.
+OUT_MANT_BITS = {None: None, "float32": None, "float16": 11, "bfloat16": 8}
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+# ---- helpers -----------------------------------------------------------------
+
+def gpu_encode(kind, x_cpu: torch.Tensor, offsets, remap=True):
+    x = x_cpu.cuda()
+    if kind == oracle.WEIGHT:
+        p = rz.razer_quantize_weight(x, offsets, remap)
+    else:
+        p = rz.razer_quantize_act(x, offsets, remap)
+    torch.cuda.synchronize()
+    return p
+
+
+def as_f32(x_cpu: torch.Tensor) -> np.ndarray:
+    return x_cpu.float().numpy()
+
+
+def assert_same_encoding(p: rz.PackedTensor, ref: oracle.Packed, x=None, what=""):
+    codes = p.codes.cpu().numpy().reshape(-1)
+    scales = p.scales.cpu().numpy().reshape(-1)
+    ts = p.tensor_scale.cpu().numpy().view(np.uint32)[0]
+    ts_ref = np.array([ref.tensor_scale], dtype=np.float32).view(np.uint32)[0]
+    assert ts == ts_ref, f"{what}: tensor scale {ts:#x} vs {ts_ref:#x}"
+    bad_s = np.nonzero(scales != ref.scales)[0]
+    bad_c = np.nonzero(codes != ref.codes)[0]
+    if bad_s.size or bad_c.size:
+        blk = int(bad_s[0]) if bad_s.size else int(bad_c[0]) // 8
+        msg = (f"{what}: {bad_s.size} scale bytes and {bad_c.size} code bytes differ; first block {blk}: "
+               f"gpu scale {scales[blk]:#04x} codes {codes[8*blk:8*blk+8].tolist()} / "
+               f"ref scale {ref.scales[blk]:#04x} codes {ref.codes[8*blk:8*blk+8].tolist()}")
+        if x is not None:
+            msg += f"; block input {np.asarray(x).reshape(-1)[16*blk:16*blk+16].tolist()}"
+        raise AssertionError(msg)
+
+
+def to_device(pk: oracle.Packed) -> rz.PackedTensor:
+    t = rz.PackedTensor(pk.kind, pk.rows, pk.cols, pk.offsets, "cuda")
+    t.codes.copy_(torch.from_numpy(pk.codes.reshape(pk.rows, pk.cols // 2)))
+    t.scales.copy_(torch.from_numpy(pk.scales.reshape(pk.rows, pk.cols // 16)))
+    t.tensor_scale.copy_(torch.tensor([float(pk.tensor_scale)], dtype=torch.float32))
+    return t
+
+
+def assert_product_close(y_gpu: np.ndarray, y_ref: np.ndarray, norm: np.ndarray, what="",
+                         out_dtype=None):
+    y_gpu = np.asarray(y_gpu, dtype=np.float64)
+    err = np.abs(y_gpu - y_ref)
+    bound = TOL * norm
+    bits = OUT_MANT_BITS[str(out_dtype).replace("torch.", "") if out_dtype is not None else None]
+    if bits is not None:
+        mag = np.maximum(np.abs(y_ref), np.abs(y_gpu))
+        with np.errstate(divide="ignore"):
+            e = np.floor(np.log2(np.where(mag > 0, mag, 1.0)))
+        bound = bound + np.where(mag > 0, np.ldexp(0.5, (e - (bits - 1)).astype(np.int64)), 0.0)
+    bad = ~((err <= bound) | ((norm == 0) & (y_gpu == 0)))
+    if bad.any():
+        i = np.unravel_index(np.argmax(np.where(bad, err / np.maximum(bound, 1e-300), 0)), bad.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outputs out of tolerance; worst at "
+                             f"{i}: gpu {y_gpu[i]!r} ref {y_ref[i]!r} norm {norm[i]!r}")
+    return float((err / np.maximum(norm, 1e-300)).max())
+
+
+# ---- cached workloads ----------------------------------------------------------
+
+@functools.lru_cache(maxsize=None)
+def pr1():
+    w, x = synth.pr1_tiny()
+    return torch.from_numpy(w), x
+
+
+@functools.lru_cache(maxsize=None)
+def llama_weight(name):
+    return synth.llama3_8b_decode_weight(name)
+
+
+@functools.lru_cache(maxsize=None)
+def llama_ref(name):
+    return oracle.quantize_weight(llama_weight(name))
+
+
+# ---- encoder parity ------------------------------------------------------------
+
+@pytest.mark.parametrize("offsets", [(-2, 4), (-2, -5), (-7, 7), (0, -1)])
+def test_quantize_weight_pr1(offsets):
+    _need_gpu()
+    w, _ = pr1()
+    ref = oracle.quantize_weight(w.numpy(), offsets)
+    p = gpu_encode(oracle.WEIGHT, w, offsets)
+    assert_same_encoding(p, ref, w.numpy(), f"pr1 offsets {offsets}")
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+def test_quantize_weight_16bit_inputs(dtype):
+    _need_gpu()
+    w, _ = pr1()
+    w16 = w.to(dtype)
+    ref = oracle.quantize_weight(as_f32(w16), (-2, -5))
+    p = gpu_encode(oracle.WEIGHT, w16, (-2, -5))
+    assert_same_encoding(p, ref, as_f32(w16), f"weights in {dtype}")
+
+
+def test_quantize_no_remap_is_plain_nvfp4():
+    _need_gpu()
+    w, _ = pr1()
+    ref = oracle.quantize_weight(w.numpy(), (-2, 4), remap=False)
+    p = gpu_encode(oracle.WEIGHT, w, (-2, 4), remap=False)
+    assert_same_encoding(p, ref, w.numpy(), "no remap")
+    assert not (p.scales.cpu() & 0xC0).any()
+
+
+def _edge_tensors():
+    rng = np.random.default_rng(101)
+    cases = {}
+    cases["one_block"] = rng.normal(0, 1, (1, 16)).astype(np.float32)
+    cases["ragged_rows_cols"] = rng.normal(0, 0.02, (7, 48)).astype(np.float32)
+    cases["zeros"] = np.zeros((4, 64), np.float32)
+    t = rng.normal(0, 1, (8, 64)).astype(np.float32)
+    t[3, 17] = np.nan
+    cases["nan"] = t
+    t = rng.normal(0, 1, (8, 64)).astype(np.float32)
+    t[0, 0] = -np.inf
+    cases["inf"] = t
+    cases["tiny_subnormal"] = (rng.normal(0, 1, (4, 64)) * 1e-40).astype(np.float32)
+    cases["huge"] = (rng.normal(0, 1, (4, 64)) * 1e37).astype(np.float32)
+    t = rng.normal(0, 1, (16, 64)).astype(np.float32)
+    t[2, :16] *= 1e-6      # block underflows to scale code 0
+    t[5, 16:32] *= 1e-3    # subnormal scale codes
+    t[9, 32:48] = 0.0      # all-zero block
+    t[11, 0] = 1e4         # one dominant element
+    cases["mixed_blocks"] = t
+    # values placed on exact decision points after scaling (block max 6 * D)
+    t = np.zeros((4, 64), np.float32)
+    pts = np.array([6, 5, 4.5, 5.5, 4.75, 5.25, 2.25, 2.75, 3.25, 3.75, 0.25, 0.75, 1.25, 1.75,
+                    2.5, 3.5], np.float32)
+    for r in range(4):
+        t[r] = np.tile(pts * (1 if r % 2 else -1), 4)
+    cases["decision_points"] = t
+    cases["all_equal"] = np.full((2, 32), 0.37, np.float32)
+    return cases
+
+
+EDGE = _edge_tensors()
+
+
+@pytest.mark.parametrize("name", sorted(EDGE))
+@pytest.mark.parametrize("kind,offsets", [(oracle.WEIGHT, (-2, -5)), (oracle.ACT, (-2,))])
+def test_quantize_edge_cases(name, kind, offsets):
+    _need_gpu()
+    x = EDGE[name]
+    ref = oracle.quantize(kind, x, offsets)
+    p = gpu_encode(kind, torch.from_numpy(x), offsets)
+    assert_same_encoding(p, ref, x, f"edge {name} kind {kind}")
+
+
+def test_quantize_empty_tensor():
+    _need_gpu()
+    x = torch.zeros((0, 32), device="cuda")
+    p = rz.razer_quantize_weight(x)
+    torch.cuda.synchronize()
+    assert float(p.tensor_scale.cpu()[0]) == 0.0
+
+
+def test_quantize_weight_every_second_pair_offset():
+    _need_gpu()
+    rng = np.random.default_rng(55)
+    w = rng.standard_t(5, (32, 256)).astype(np.float32) * 0.02
+    wt = torch.from_numpy(w)
+    for off in range(-7, 8):
+        ref = oracle.quantize_weight(w, (-2, off))
+        p = gpu_encode(oracle.WEIGHT, wt, (-2, off))
+        assert_same_encoding(p, ref, w, f"second pair offset {off}")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_quantize_act_parity(dtype):
+    _need_gpu()
+    x = synth.act_quant_x(256, 8192).to(dtype)
+    ref = oracle.quantize_act(as_f32(x))
+    p = gpu_encode(oracle.ACT, x, (-2,))
+    assert_same_encoding(p, ref, as_f32(x), f"act {dtype}")
+
+
+def test_quantize_act_full_size():
+    """Activation quantizer at its full size, X[4096, 8192] bf16."""
+    _need_gpu()
+    x = synth.act_quant_x()
+    log("act full: oracle ...")
+    ref = oracle.quantize_act(as_f32(x))
+    log("act full: gpu ...")
+    p = gpu_encode(oracle.ACT, x, (-2,))
+    assert_same_encoding(p, ref, None, "act full size")
+    sel = (p.scales.cpu().numpy() >> 7)
+    log(f"act full: blocks selecting -5: {sel.mean():.3f}")
+
+
+def test_quantize_weight_prefill_full_size():
+    """Weight quantizer at its full size, W[28672, 8192] fp32 ~ 0.015 t(4)."""
+    _need_gpu()
+    log("prefill W: generating ...")
+    w = synth.prefill_weight()
+    log("prefill W: oracle ...")
+    ref = oracle.quantize_weight(w)
+    log("prefill W: gpu ...")
+    p = gpu_encode(oracle.WEIGHT, torch.from_numpy(w), (-2, 4))
+    assert_same_encoding(p, ref, None, "prefill weight full size")
+    del p
+    torch.cuda.empty_cache()
+
+
+def test_quantize_deterministic_across_calls():
+    _need_gpu()
+    w, _ = pr1()
+    a = gpu_encode(oracle.WEIGHT, w, (-2, -5))
+    b = gpu_encode(oracle.WEIGHT, w, (-2, -5))
+    assert torch.equal(a.codes, b.codes) and torch.equal(a.scales, b.scales)
+
+
+# ---- decoder parity ------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("kind", [oracle.WEIGHT, oracle.ACT])
+def test_dequant_parity(dtype, kind):
+    _need_gpu()
+    rng = np.random.default_rng(17)
+    x = (rng.standard_t(4, (64, 272)) * 0.02).astype(np.float32)
+    x[:, 5] *= 30
+    offs = (-2, -5) if kind == oracle.WEIGHT else (-2,)
+    ref = oracle.quantize(kind, x, offs)
+    t = to_device(ref)
+    out = rz.razer_dequant(t, dtype).cpu()
+    want = torch.from_numpy(oracle.dequant_f32(ref)).to(dtype)  # RNE of the fp32 value
+    assert torch.equal(out.view(torch.int16 if dtype != torch.float32 else torch.int32),
+                       want.view(torch.int16 if dtype != torch.float32 else torch.int32))
+
+
+# ---- product parity --------------------------------------------------------------
+
+@pytest.mark.parametrize("out_dtype", [torch.float16, torch.float32])
+def test_gemv_pr1(out_dtype):
+    _need_gpu()
+    w, x = pr1()
+    ref = oracle.quantize_weight(w.numpy())
+    y_ref, nrm = oracle.gemm(as_f32(x), ref)
+    y = rz.razer_gemv(x.cuda().reshape(-1), to_device(ref), out_dtype).cpu().double().numpy()
+    assert_product_close(y[None, :], y_ref, nrm, "gemv pr1", out_dtype)
+
+
+@pytest.mark.parametrize("name", ["qkv", "gate", "up", "down"])
+def test_gemv_llama3_8b_decode(name):
+    _need_gpu()
+    w = llama_weight(name)
+    ref = llama_ref(name)
+    x = synth.llama3_8b_decode_x(w.shape[1])
+    log(f"gemv {name}: oracle product ...")
+    y_ref, nrm = oracle.gemm(as_f32(x), ref)
+    t = to_device(ref)
+    y16 = rz.razer_gemv(x.cuda().reshape(-1), t, torch.float16).cpu().double().numpy()
+    y32 = rz.razer_gemv(x.cuda().reshape(-1), t, torch.float32).cpu().double().numpy()
+    e32 = assert_product_close(y32[None, :], y_ref, nrm, f"gemv {name} f32")
+    e16 = assert_product_close(y16[None, :], y_ref, nrm, f"gemv {name} f16", torch.float16)
+    log(f"gemv {name}: max err/norm f32 {e32:.2e} f16 {e16:.2e}")
+    # the GPU encoder yields the same bytes for this weight
+    p = gpu_encode(oracle.WEIGHT, torch.from_numpy(w), (-2, 4))
+    assert_same_encoding(p, ref, None, f"llama {name} weight")
+
+
+@pytest.mark.parametrize("n,k,xdt", [(7, 48, torch.float16), (33, 16, torch.bfloat16),
+                                     (257, 1040, torch.float16), (64, 96, torch.bfloat16),
+                                     (5, 65536, torch.float16)])
+def test_gemv_ragged_shapes(n, k, xdt):
+    _need_gpu()
+    rng = np.random.default_rng(n * 7 + k)
+    w = (rng.standard_t(5, (n, k)) * 0.02).astype(np.float32)
+    x = torch.from_numpy(rng.normal(0, 1, k).astype(np.float32)).to(xdt)
+    ref = oracle.quantize_weight(w, (-2, -5))
+    y_ref, nrm = oracle.gemm(as_f32(x)[None, :], ref)
+    y = rz.razer_gemv(x.cuda(), to_device(ref), torch.float32).cpu().double().numpy()
+    assert_product_close(y[None, :], y_ref, nrm, f"gemv {n}x{k}")
+
+
+def test_gemv_nan_tensor_scale_gives_nan():
+    _need_gpu()
+    x = EDGE["nan"]
+    ref = oracle.quantize_weight(x, (-2, 4))
+    t = to_device(ref)
+    y = rz.razer_gemv(torch.ones(64, dtype=torch.float16, device="cuda"), t, torch.float32).cpu()
+    assert torch.isnan(y).all()
+
+
+@functools.lru_cache(maxsize=None)
+def small_batch_ref(n, k):
+    w = synth.small_batch_weight(n, k)
+    ref = oracle.quantize_weight(w, (-2, 4))
+    return ref
+
+
+@pytest.mark.parametrize("m", [2, 4, 8, 16, 32])
+def test_gemm_small_batch_4096(m):
+    _need_gpu()
+    ref = small_batch_ref(4096, 4096)
+    x32 = synth.small_batch_x(32, 4096)
+    y_ref, nrm = _small_batch_oracle_4096()
+    t = to_device(ref)
+    x = synth.small_batch_x(m, 4096).cuda()
+    y = rz.razer_gemm(x, t, torch.float32).cpu().double().numpy()
+    assert torch.equal(x.cpu(), x32[:m])
+    e = assert_product_close(y, y_ref[:m], nrm[:m], f"gemm m={m} 4096x4096")
+    log(f"gemm m={m} 4096: max err/norm {e:.2e}")
+
+
+@functools.lru_cache(maxsize=None)
+def _small_batch_oracle_4096():
+    log("gemm 4096: oracle product for M=32 ...")
+    return oracle.gemm(as_f32(synth.small_batch_x(32, 4096)), small_batch_ref(4096, 4096))
+
+
+@pytest.mark.parametrize("m", [2, 8, 32])
+def test_gemm_small_batch_70b_sampled(m):
+    _need_gpu()
+    log("gemm 70b: reference encode ...")
+    ref = small_batch_ref(28672, 8192)
+    t = to_device(ref)
+    x = synth.small_batch_x(m, 8192)
+    y = rz.razer_gemm(x.cuda(), t, torch.bfloat16).cpu().double().numpy()
+    cols = np.random.default_rng(m).choice(28672, 256, replace=False)
+    y_ref, nrm = oracle.gemm(as_f32(x), ref, cols)
+    assert_product_close(y[:, cols], y_ref, nrm, f"gemm m={m} 28672x8192 (256 sampled columns)",
+                         torch.bfloat16)
+
+
+def test_gemm_prefill_sampled():
+    """Prefill product M=2048, N=28672, K=8192 (bf16), checked on sampled columns."""
+    _need_gpu()
+    log("prefill: generating W ...")
+    w = synth.prefill_weight()
+    log("prefill: oracle encode ...")
+    ref = oracle.quantize_weight(w, (-2, 4))
+    del w
+    t = to_device(ref)
+    x = synth.prefill_x()
+    log("prefill: gpu gemm ...")
+    y = rz.razer_gemm(x.cuda(), t, torch.bfloat16)
+    torch.cuda.synchronize()
+    cols = np.random.default_rng(2048).choice(28672, 24, replace=False)
+    yc = y[:, torch.from_numpy(cols).cuda()].cpu().double().numpy()
+    log("prefill: oracle product on 24 columns ...")
+    y_ref, nrm = oracle.gemm(as_f32(x), ref, cols)
+    e = assert_product_close(yc, y_ref, nrm, "prefill gemm (24 sampled columns x 2048 rows)",
+                             torch.bfloat16)
+    log(f"prefill: max err/norm {e:.2e}")
+    # every output is finite
+    assert torch.isfinite(y).all()
+
+
+@pytest.mark.parametrize("m,n,k,xdt", [(3, 100, 48, torch.bfloat16), (130, 257, 80, torch.float16),
+                                       (2, 16, 16, torch.bfloat16), (129, 129, 4096, torch.bfloat16),
+                                       (33, 64, 32, torch.float16)])
+def test_gemm_ragged_shapes(m, n, k, xdt):
+    _need_gpu()
+    rng = np.random.default_rng(m * 1000 + n + k)
+    w = (rng.standard_t(4, (n, k)) * 0.015).astype(np.float32)
+    x = torch.from_numpy(rng.normal(0, 1, (m, k)).astype(np.float32)).to(xdt)
+    ref = oracle.quantize_weight(w, (-2, -5))
+    y_ref, nrm = oracle.gemm(as_f32(x), ref)
+    for odt in (torch.float32, torch.bfloat16):
+        y = rz.razer_gemm(x.cuda(), to_device(ref), odt).cpu().double().numpy()
+        assert_product_close(y, y_ref, nrm, f"gemm {m}x{n}x{k} out {odt}", odt)
