@@ -393,7 +393,8 @@ def test_gemm_prefill_sampled():
 
 @pytest.mark.parametrize("m,n,k,xdt", [(3, 100, 48, torch.bfloat16), (130, 257, 80, torch.float16),
                                        (2, 16, 16, torch.bfloat16), (129, 129, 4096, torch.bfloat16),
-                                       (33, 64, 32, torch.float16)])
+                                       (33, 64, 32, torch.float16), (257, 300, 128, torch.bfloat16),
+                                       (512, 256, 192, torch.float16), (300, 520, 4096, torch.bfloat16)])
 def test_gemm_ragged_shapes(m, n, k, xdt):
     _need_gpu()
     rng = np.random.default_rng(m * 1000 + n + k)
