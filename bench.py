@@ -192,7 +192,9 @@ def bench_rows(torch, rz, synth, args, decode_base):
         for m in synth.SMALL_BATCH_M:
             x = synth.small_batch_x(m, k).to(dev)
             y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
-            t = GraphTimer(torch, lambda: [rz.razer_gemm(x, mm, out=y) for mm in mats])
+            wsb = max(1, rz.razer_workspace_bytes(rz.RAZER_OP_GEMM, m, n, k))
+            wsp = torch.empty(wsb, dtype=torch.uint8, device=dev)
+            t = GraphTimer(torch, lambda: [rz.razer_gemm(x, mm, out=y, workspace=wsp) for mm in mats])
             ms = t.time(5) / len(mats)
             byts = packed_bytes(n, k) + m * k * 2 + m * n * 2
             sweep[f"{n}x{k}_m{m}"] = {"us": ms * 1e3, "gbs": byts / ms / 1e6,

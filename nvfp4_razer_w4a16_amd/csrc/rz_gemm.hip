@@ -173,11 +173,8 @@ template <> __device__ __forceinline__ uint32_t bits16<_Float16>(float v) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v);
 }
 
-// Two codes (byte SEL of w) -> one packed 16-bit pair of value * sb, with the
-// remapped code replaced by svb2 (SV * sb in both halves).  The remapped code
-// converts to -0; it is detected on the unscaled pair (the int16 minimum:
-// max_i16(p, 0x8001) ^ p is 1 there and 0 elsewhere, negated into a 0xFFFF
-// mask) so no later rounding step can touch the sign of that zero.
+// The remapped code converts to -0, the int16 minimum of a packed pair; it is
+// detected on the unscaled pair, so no rounding step can lose that sign.
 __device__ __forceinline__ uint32_t remapped_mask(uint32_t p) {
   const short2_t q = __builtin_elementwise_max(__builtin_bit_cast(short2_t, p),
                                                (short2_t){(short)0x8001, (short)0x8001});
@@ -185,42 +182,77 @@ __device__ __forceinline__ uint32_t remapped_mask(uint32_t p) {
   return __builtin_bit_cast(uint32_t, (ushort2_t){0, 0} - one);
 }
 
-// fp16: FP4 -> f16 pair directly, then an exact packed multiply by sb (value *
-// sb has at most 9 significant bits).
-template <typename XT, int SEL>
-__device__ __forceinline__ uint32_t decode_pair_impl(uint32_t w, float sb, uint32_t svb2) {
-  if constexpr (__is_same(XT, _Float16)) {
-    const half2_t h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL);
-    const uint32_t mask = remapped_mask(__builtin_bit_cast(uint32_t, h));
-    const _Float16 s16 = (_Float16)sb;  // exact: sb has 4 significant bits, in fp16 range
-    const uint32_t v = __builtin_bit_cast(uint32_t, h * (half2_t){s16, s16});
-    return (mask & svb2) | (~mask & v);
-  } else {
-    // bf16: FP4 -> fp32 pair, scaled with fma(f, sb, -0) so a -0 stays -0,
-    // then rounded to bf16 (exact unless an SV has 5 significant bits).
-    const float2_t f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
-    const uint32_t p = pack2<XT>(__builtin_fmaf(f[0], sb, -0.0f), __builtin_fmaf(f[1], sb, -0.0f));
-    const uint32_t mask = remapped_mask(p);
-    return (mask & svb2) | (~mask & p);
-  }
+// Replace the -0 halves of p by sv (both halves of svd hold sv ^ 0x8000, i.e.
+// sv - 0x8000 mod 2^16): d = max_i16(p, 0x8001) ^ p is 1 exactly at -0, and p + d * svd puts
+// 0x8000 + sv - 0x8000 = sv there (v_pk_max_i16, v_xor, v_pk_mad_u16).
+__device__ __forceinline__ uint32_t insert_special(uint32_t p, uint32_t svd) {
+  const short2_t q = __builtin_elementwise_max(__builtin_bit_cast(short2_t, p),
+                                               (short2_t){(short)0x8001, (short)0x8001});
+  const ushort2_t d = __builtin_bit_cast(ushort2_t, __builtin_bit_cast(uint32_t, q) ^ p);
+  return __builtin_bit_cast(uint32_t, d * __builtin_bit_cast(ushort2_t, svd) +
+                                          __builtin_bit_cast(ushort2_t, p));
 }
 
-template <typename XT, int KIND>
-__device__ __forceinline__ void decode_row64(const uint4 (&c)[2], uint32_t sw, float m0, float m1,
-                                             uint4 (&out)[8]) {
+// One dword (8 codes, all in one block) -> 4 packed 16-bit pairs, each stage
+// applied to the four pairs before the next so independent work can fill the
+// conversion and packed-integer latencies.
+template <typename XT>
+__device__ __forceinline__ uint4 decode_dword(uint32_t w, float sb, uint32_t svd) {
+  uint32_t p[4];
+  if constexpr (__is_same(XT, _Float16)) {
+    half2_t h[4];
+    h[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
+    h[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
+    h[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
+    h[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
+    uint32_t mask[4];
 #pragma unroll
-  for (int blk = 0; blk < 4; blk++) {
-    const uint32_t byte = (sw >> (8 * blk)) & 0xFFu;
-    const float sb = scale_of_byte<KIND>(byte);
-    const uint32_t svb = bits16<XT>(special_of_byte<KIND>(byte, m0, m1) * sb);
-    const uint32_t svb2 = svb | (svb << 16);
-    const uint4 cw = c[blk >> 1];
-    const uint32_t w0 = (blk & 1) ? cw.z : cw.x;
-    const uint32_t w1 = (blk & 1) ? cw.w : cw.y;
-    out[2 * blk] = make_uint4(decode_pair_impl<XT, 0>(w0, sb, svb2), decode_pair_impl<XT, 1>(w0, sb, svb2),
-                              decode_pair_impl<XT, 2>(w0, sb, svb2), decode_pair_impl<XT, 3>(w0, sb, svb2));
-    out[2 * blk + 1] = make_uint4(decode_pair_impl<XT, 0>(w1, sb, svb2), decode_pair_impl<XT, 1>(w1, sb, svb2),
-                                  decode_pair_impl<XT, 2>(w1, sb, svb2), decode_pair_impl<XT, 3>(w1, sb, svb2));
+    for (int i = 0; i < 4; i++) mask[i] = remapped_mask(__builtin_bit_cast(uint32_t, h[i]));
+    const _Float16 s16 = (_Float16)sb;
+#pragma unroll
+    for (int i = 0; i < 4; i++) p[i] = __builtin_bit_cast(uint32_t, h[i] * (half2_t){s16, s16});
+    // mask is taken before scaling; the scaled -0 may lose its sign
+    const uint32_t svb2 = svd ^ 0x80008000u;  // back to SV*sb bits in both halves
+#pragma unroll
+    for (int i = 0; i < 4; i++) p[i] = (mask[i] & svb2) | (~mask[i] & p[i]);
+  } else {
+    float2_t f[4];
+    f[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    f[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    f[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    f[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+      p[i] = insert_special(pack2<XT>(__builtin_fmaf(f[i][0], sb, -0.0f), __builtin_fmaf(f[i][1], sb, -0.0f)), svd);
+  }
+  return make_uint4(p[0], p[1], p[2], p[3]);
+}
+
+// One pair (byte `sel` of w) of the decode above; `sel` folds to a constant
+// once the caller's loop is unrolled.
+template <typename XT>
+__device__ __forceinline__ uint32_t decode_one_pair(uint32_t w, int sel, float sb, uint32_t svd) {
+  if constexpr (__is_same(XT, _Float16)) {
+    half2_t h;
+    switch (sel) {
+      case 0: h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0); break;
+      case 1: h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1); break;
+      case 2: h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2); break;
+      default: h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3); break;
+    }
+    const uint32_t mask = remapped_mask(__builtin_bit_cast(uint32_t, h));
+    const _Float16 s16 = (_Float16)sb;
+    const uint32_t v = __builtin_bit_cast(uint32_t, h * (half2_t){s16, s16});
+    return (mask & (svd ^ 0x80008000u)) | (~mask & v);
+  } else {
+    float2_t f;
+    switch (sel) {
+      case 0: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0); break;
+      case 1: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1); break;
+      case 2: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2); break;
+      default: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3); break;
+    }
+    return insert_special(pack2<XT>(__builtin_fmaf(f[0], sb, -0.0f), __builtin_fmaf(f[1], sb, -0.0f)), svd);
   }
 }
 
@@ -235,47 +267,61 @@ __global__ __launch_bounds__(256) void gemm_tile256_kernel(const XT* __restrict_
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   XT* As = (XT*)smem;                    // [2][kTM * kTS]
   XT* Bs = As + 2 * kTM * kTS;           // [2][kTN * kTS]
+  float2* lut = (float2*)(Bs + 2 * kTN * kTS);  // scale byte -> (sb, SV*sb bits x2)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t ntn = (n + kTN - 1) / kTN;
   const int64_t m_base = (int64_t)(blockIdx.x / ntn) * kTM;
   const int64_t n_base = (int64_t)(blockIdx.x % ntn) * kTN;
   const int ktiles = (int)(k / kTK);
+  {
+    const uint32_t b = (uint32_t)tid;
+    const float sb = scale_of_byte<KIND>(b);
+    const uint32_t svd = bits16<XT>(special_of_byte<KIND>(b, m0, m1) * sb) ^ 0x8000u;
+    lut[b] = make_float2(sb, __builtin_bit_cast(float, svd | (svd << 16)));
+  }
 
-  uint4 areg[8];
-  uint4 creg[2];
-  uint32_t sreg;
+  // Two register sets: the tile two K steps ahead is in flight while the
+  // next tile is decoded into LDS under the current tile's MFMAs.
+  struct Stage {
+    uint4 a[8];
+    uint4 c[2];
+    uint32_t s;
+  };
+  Stage st0, st1;
   const int64_t gn = n_base + tid;
-  auto gload = [&](int kt) {
+  auto gload = [&](int kt, Stage& r) {
     const int64_t k0 = (int64_t)kt * kTK;
 #pragma unroll
     for (int i = 0; i < 8; i++) {
       const int idx = i * 256 + tid;
       const int64_t gr = m_base + (idx >> 3);
-      areg[i] = gr < m ? *(const uint4*)(x + gr * k + k0 + (idx & 7) * 8) : make_uint4(0, 0, 0, 0);
+      r.a[i] = gr < m ? *(const uint4*)(x + gr * k + k0 + (idx & 7) * 8) : make_uint4(0, 0, 0, 0);
     }
     if (gn < n) {
       const uint4* cp = (const uint4*)(codes + gn * (k / 2) + k0 / 2);
-      creg[0] = cp[0];
-      creg[1] = cp[1];
-      sreg = *(const uint32_t*)(scales + gn * (k / 16) + k0 / 16);
+      r.c[0] = cp[0];
+      r.c[1] = cp[1];
+      r.s = *(const uint32_t*)(scales + gn * (k / 16) + k0 / 16);
     } else {
-      creg[0] = creg[1] = make_uint4(0, 0, 0, 0);
-      sreg = 0;
+      r.c[0] = r.c[1] = make_uint4(0, 0, 0, 0);
+      r.s = 0;
     }
   };
-  auto lstore = [&](int buf) {
+  // part `blk` (0..3) of writing stage r into LDS buffer buf: two x vectors
+  // and the decode of 16-element block blk of this thread's weight row.
+  auto lstore_part = [&](const Stage& r, int buf, int blk, float2 f) {
     XT* a = As + buf * kTM * kTS;
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
+    for (int i = 2 * blk; i < 2 * blk + 2; i++) {
       const int idx = i * 256 + tid;
-      *(uint4*)(a + (idx >> 3) * kTS + (idx & 7) * 8) = areg[i];
+      *(uint4*)(a + (idx >> 3) * kTS + (idx & 7) * 8) = r.a[i];
     }
-    uint4 dec[8];
-    decode_row64<XT, KIND>(creg, sreg, m0, m1, dec);
-    uint4* b = (uint4*)(Bs + buf * kTN * kTS + tid * kTS);
-#pragma unroll
-    for (int i = 0; i < 8; i++) b[i] = dec[i];
+    const uint32_t svd = __builtin_bit_cast(uint32_t, f.y);
+    const uint4 cw = r.c[blk >> 1];
+    uint4* b = (uint4*)(Bs + buf * kTN * kTS + tid * kTS) + 2 * blk;
+    b[0] = decode_dword<XT>((blk & 1) ? cw.z : cw.x, f.x, svd);
+    b[1] = decode_dword<XT>((blk & 1) ? cw.w : cw.y, f.x, svd);
   };
 
   floatx16 acc[4][4];
@@ -286,33 +332,70 @@ __global__ __launch_bounds__(256) void gemm_tile256_kernel(const XT* __restrict_
 #pragma unroll
       for (int e = 0; e < 16; e++) acc[i][j][e] = 0.0f;
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < ktiles; kt++) {
+  // One K step, branch free so the scheduler can interleave the next tile's
+  // decode (VALU) and LDS writes with this tile's MFMAs: the prefetch index
+  // is clamped to the last tile and the final step's decode lands in the
+  // buffer that is never read again.
+  auto step = [&](int kt, Stage& cur_stage, Stage& next_stage) {
     const int cur = kt & 1;
-    if (kt + 1 < ktiles) gload(kt + 1);
+    gload(kt + 2 < ktiles ? kt + 2 : ktiles - 1, next_stage);
+    float2 f[4];
+#pragma unroll
+    for (int blk = 0; blk < 4; blk++) f[blk] = lut[(cur_stage.s >> (8 * blk)) & 0xFFu];
     const XT* a = As + cur * kTM * kTS;
     const XT* b = Bs + cur * kTN * kTS;
 #pragma unroll
-    for (int kk = 0; kk < kTK; kk += 16) {
+    for (int kk = 0; kk < 4; kk++) {
       V av[4], bv[4];
 #pragma unroll
       for (int i = 0; i < 4; i++)
-        av[i] = *(const V*)(a + (wm * 128 + i * 32 + (lane & 31)) * kTS + kk + 8 * (lane >> 5));
+        av[i] = *(const V*)(a + (wm * 128 + i * 32 + (lane & 31)) * kTS + 16 * kk + 8 * (lane >> 5));
 #pragma unroll
       for (int j = 0; j < 4; j++)
-        bv[j] = *(const V*)(b + (wn * 128 + j * 32 + (lane & 31)) * kTS + kk + 8 * (lane >> 5));
+        bv[j] = *(const V*)(b + (wn * 128 + j * 32 + (lane & 31)) * kTS + 16 * kk + 8 * (lane >> 5));
+      // the next tile's x vectors for this sub-step go straight to LDS
+      XT* an = As + (cur ^ 1) * kTM * kTS;
 #pragma unroll
-      for (int i = 0; i < 4; i++)
+      for (int i = 2 * kk; i < 2 * kk + 2; i++) {
+        const int idx = i * 256 + tid;
+        *(uint4*)(an + (idx >> 3) * kTS + (idx & 7) * 8) = cur_stage.a[i];
+      }
+      const uint4 cw = cur_stage.c[kk >> 1];
+      const uint32_t w0 = (kk & 1) ? cw.z : cw.x, w1 = (kk & 1) ? cw.w : cw.y;
+      const uint32_t svd = __builtin_bit_cast(uint32_t, f[kk].y);
+      uint32_t dec[8];
+      // two MFMAs, then one decoded pair: the pair's VALU work issues while the
+      // matrix unit runs (fences keep the compiler from regrouping them)
 #pragma unroll
-        for (int j = 0; j < 4; j++) acc[i][j] = Mfma32<XT>::run(av[i], bv[j], acc[i][j]);
+      for (int g = 0; g < 8; g++) {
+        const int i = g >> 1, j = 2 * (g & 1);
+        acc[i][j] = Mfma32<XT>::run(av[i], bv[j], acc[i][j]);
+        acc[i][j + 1] = Mfma32<XT>::run(av[i], bv[j + 1], acc[i][j + 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        dec[g] = decode_one_pair<XT>(g < 4 ? w0 : w1, g & 3, f[kk].x, svd);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      uint4* bn = (uint4*)(Bs + (cur ^ 1) * kTN * kTS + tid * kTS) + 2 * kk;
+      bn[0] = make_uint4(dec[0], dec[1], dec[2], dec[3]);
+      bn[1] = make_uint4(dec[4], dec[5], dec[6], dec[7]);
     }
-    if (kt + 1 < ktiles) lstore(cur ^ 1);
     __syncthreads();
-  }
+  };
 
-  const float st = *ts;
+  gload(0, st0);
+  gload(ktiles > 1 ? 1 : 0, st1);
+  __syncthreads();  // lut ready
+#pragma unroll
+  for (int blk = 0; blk < 4; blk++) lstore_part(st0, 0, blk, lut[(st0.s >> (8 * blk)) & 0xFFu]);
+  __syncthreads();
+  int kt = 0;
+  for (; kt + 1 < ktiles; kt += 2) {
+    step(kt, st1, st0);
+    step(kt + 1, st0, st1);
+  }
+  if (kt < ktiles) step(kt, st1, st0);
+
+  const float scale = *ts;
 #pragma unroll
   for (int i = 0; i < 4; i++)
 #pragma unroll
@@ -321,22 +404,227 @@ __global__ __launch_bounds__(256) void gemm_tile256_kernel(const XT* __restrict_
 #pragma unroll
       for (int e = 0; e < 16; e++) {
         const int64_t gr = m_base + wm * 128 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        if (gr < m && gc < n) y[gr * n + gc] = from_f32<OT>(acc[i][j][e] * st);
+        if (gr < m && gc < n) y[gr * n + gc] = from_f32<OT>(acc[i][j][e] * scale);
       }
     }
 }
 
-size_t gemm_ws_bytes(int64_t, int64_t, int64_t) { return 0; }
+// ---- small M (2..32): weight-streaming MFMA with split K -------------------------
+//
+// HBM-bound.  A wave owns 64 weight rows (4 groups of 16) for a K range; a
+// workgroup's 4 waves split that range 4 ways and fold their partial tiles in
+// LDS; a global split of K across workgroups (chosen so >= ~2k waves run)
+// writes fp32 partials that skinny_reduce_kernel sums, scales by st and
+// converts.  MFMA 16x16x32 (A = x rows, B = decoded weights): lane (c, q) =
+// (l % 16, l / 16) loads 16 code bytes of weight row c covering 32
+// consecutive k, k0 + 32q .. k0 + 32q + 31, and MFMA j (j = 0..3) of the
+// 128-k window uses dword j of it, i.e. k0 + 32q + 8j .. +7, with the x
+// fragment taken from the same k range (the MFMA sums over k, so any k order
+// shared by A and B is valid).  Each dword lies in one 16-element block, so
+// one scale byte serves it.
+typedef __bf16 bf16x8s_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8s_t __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+template <typename XT> struct Mfma16;
+template <> struct Mfma16<__bf16> {
+  typedef bf16x8s_t V;
+  static __device__ __forceinline__ floatx4 run(V a, V b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct Mfma16<_Float16> {
+  typedef f16x8s_t V;
+  static __device__ __forceinline__ floatx4 run(V a, V b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+constexpr int kSkGroups = 4;      // 16-row weight groups per wave
+constexpr int kSkRows = 16 * kSkGroups;
+
+struct SkinnyPlan {
+  int64_t wg_cols;   // workgroups along N (64 rows each)
+  int split;         // global K split
+  int64_t win_per_wave;  // 128-k windows per wave
+};
+
+static SkinnyPlan skinny_plan(int64_t n, int64_t k) {
+  SkinnyPlan p;
+  p.wg_cols = (n + kSkRows - 1) / kSkRows;
+  const int64_t windows = (k + 127) / 128;
+  const int64_t target_wgs = 4LL * device_cu_count();  // ~16 waves per CU
+  int split = 1;
+  // double the split while the grid is still small and every wave keeps >= 2
+  // windows to pipeline
+  while (split < 64 && p.wg_cols * split * 2 <= target_wgs && windows >= 4LL * split * 4) split *= 2;
+  p.split = split;
+  p.win_per_wave = (windows + 4LL * split - 1) / (4LL * split);
+  return p;
+}
+
+template <typename XT, int KIND, int MT>
+__global__ __launch_bounds__(256) void gemm_skinny_kernel(const XT* __restrict__ x, int m,
+                                                          const uint8_t* __restrict__ codes,
+                                                          const uint8_t* __restrict__ scales,
+                                                          int64_t n, int64_t k, float m0, float m1,
+                                                          int64_t win_per_wave,
+                                                          float* __restrict__ partial) {
+  typedef typename Mfma16<XT>::V V;
+  __shared__ floatx4 red[3][kSkGroups * MT][64];
+  __shared__ float2 lut[256];  // scale byte -> (sb, SV * sb bits ^ 0x8000 in both halves)
+  {
+    const uint32_t b = threadIdx.x;
+    const float sb = scale_of_byte<KIND>(b);
+    const uint32_t svd = bits16<XT>(special_of_byte<KIND>(b, m0, m1) * sb) ^ 0x8000u;
+    lut[b] = make_float2(sb, __builtin_bit_cast(float, svd | (svd << 16)));
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 15, q = lane >> 4;
+  const int64_t wg_cols = (n + kSkRows - 1) / kSkRows;
+  const int64_t col_wg = blockIdx.x % wg_cols;
+  const int split_id = (int)(blockIdx.x / wg_cols);
+  const int64_t nwin = (k + 127) / 128;
+  const int64_t w_begin = ((int64_t)split_id * 4 + wave) * win_per_wave;
+  const int64_t w_end = w_begin + win_per_wave < nwin ? w_begin + win_per_wave : nwin;
+  const int64_t row_base = col_wg * kSkRows;
+
+  floatx4 acc[kSkGroups][MT];
+#pragma unroll
+  for (int g = 0; g < kSkGroups; g++)
+#pragma unroll
+    for (int t = 0; t < MT; t++) acc[g][t] = (floatx4){0.f, 0.f, 0.f, 0.f};
+
+  struct Win {
+    uint4 cw[kSkGroups];
+    uint32_t sw[kSkGroups];
+    V xa[MT][4];
+  };
+  auto load_win = [&](int64_t w, Win& r) {
+    const int64_t kq = w * 128 + 32 * q;  // this lane's 32-k slice
+    const bool kvalid = kq < k;
+#pragma unroll
+    for (int g = 0; g < kSkGroups; g++) {
+      const int64_t row = row_base + 16 * g + c;
+      if (row < n && kvalid) {
+        r.cw[g] = load_nt16(codes + row * (k / 2) + kq / 2);
+        r.sw[g] = *(const uint16_t*)(scales + row * (k / 16) + kq / 16);
+      } else {
+        r.cw[g] = make_uint4(0, 0, 0, 0);
+        r.sw[g] = 0;
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < MT; t++) {
+      const int row = 16 * t + c;
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (row < m && kvalid) v = *(const uint4*)(x + (int64_t)row * k + kq + 8 * j);
+        r.xa[t][j] = __builtin_bit_cast(V, v);
+      }
+    }
+  };
+  auto compute_win = [&](const Win& r) {
+#pragma unroll
+    for (int g = 0; g < kSkGroups; g++) {
+      const float2 f0 = lut[r.sw[g] & 0xFFu], f1 = lut[(r.sw[g] >> 8) & 0xFFu];
+      const uint32_t d[4] = {r.cw[g].x, r.cw[g].y, r.cw[g].z, r.cw[g].w};
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const float2 f = j < 2 ? f0 : f1;
+        const uint4 bv = decode_dword<XT>(d[j], f.x, __builtin_bit_cast(uint32_t, f.y));
+        const V b = __builtin_bit_cast(V, bv);
+#pragma unroll
+        for (int t = 0; t < MT; t++) acc[g][t] = Mfma16<XT>::run(r.xa[t][j], b, acc[g][t]);
+      }
+    }
+  };
+  // two register sets, loads for the next window in flight during each decode
+  Win r0, r1;
+  if (w_begin < w_end) load_win(w_begin, r0);
+  for (int64_t w = w_begin; w < w_end; w += 2) {
+    if (w + 1 < w_end) load_win(w + 1, r1);
+    compute_win(r0);
+    if (w + 2 < w_end) load_win(w + 2, r0);
+    if (w + 1 < w_end) compute_win(r1);
+  }
+
+  // fold the 4 waves' K slices
+  if (wave > 0) {
+#pragma unroll
+    for (int g = 0; g < kSkGroups; g++)
+#pragma unroll
+      for (int t = 0; t < MT; t++) red[wave - 1][g * MT + t][lane] = acc[g][t];
+  }
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int g = 0; g < kSkGroups; g++)
+#pragma unroll
+      for (int t = 0; t < MT; t++) {
+        floatx4 v = acc[g][t];
+#pragma unroll
+        for (int o = 0; o < 3; o++) v += red[o][g * MT + t][lane];
+        // C layout: lane (c, q) holds rows 4q .. 4q+3 of column c
+        const int64_t col = row_base + 16 * g + c;
+        if (col < n) {
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            const int row = 16 * t + 4 * q + i;
+            if (row < m) partial[((int64_t)split_id * m + row) * n + col] = v[i];
+          }
+        }
+      }
+  }
+}
+
+template <typename OT>
+__global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restrict__ partial,
+                                                            int split, int64_t mn,
+                                                            const float* __restrict__ ts,
+                                                            OT* __restrict__ y) {
+  const float st = *ts;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < mn; i += (int64_t)gridDim.x * 256) {
+    float v = 0.0f;
+    for (int s = 0; s < split; s++) v += partial[(int64_t)s * mn + i];
+    y[i] = from_f32<OT>(v * st);
+  }
+}
+
+size_t gemm_ws_bytes(int64_t m, int64_t n, int64_t k) {
+  if (m < 2 || m > 32 || k % 32 != 0) return 0;
+  const SkinnyPlan p = skinny_plan(n, k);
+  return (size_t)p.split * (size_t)m * (size_t)n * sizeof(float);
+}
 
 template <typename XT, int KIND, typename OT>
-static hipError_t run_gemm(const XT* x, int64_t m, const PackedView& w, OT* y,
+static hipError_t run_gemm(const XT* x, int64_t m, const PackedView& w, OT* y, void* ws,
                            hipStream_t stream) {
   const int64_t n = w.rows, k = w.cols;
   const float m0 = 6.0f + 0.5f * (float)w.off_half[0];
   const float m1 = 6.0f + 0.5f * (float)w.off_half[KIND == kWeight ? 1 : 0];
+  if (m >= 2 && m <= 32 && k % 32 == 0 && ws != nullptr) {
+    const SkinnyPlan p = skinny_plan(n, k);
+    float* partial = (float*)ws;
+    const int64_t grid = p.wg_cols * p.split;
+    if (m <= 16)
+      hipLaunchKernelGGL((gemm_skinny_kernel<XT, KIND, 1>), dim3((unsigned)grid), dim3(256), 0, stream,
+                         x, (int)m, w.codes, w.scales, n, k, m0, m1, p.win_per_wave, partial);
+    else
+      hipLaunchKernelGGL((gemm_skinny_kernel<XT, KIND, 2>), dim3((unsigned)grid), dim3(256), 0, stream,
+                         x, (int)m, w.codes, w.scales, n, k, m0, m1, p.win_per_wave, partial);
+    const int64_t mn = m * n;
+    int64_t g2 = (mn + 255) / 256;
+    if (g2 > 4LL * device_cu_count()) g2 = 4LL * device_cu_count();
+    hipLaunchKernelGGL((skinny_reduce_kernel<OT>), dim3((unsigned)g2), dim3(256), 0, stream, partial,
+                       p.split, mn, w.tensor_scale, y);
+    return hipGetLastError();
+  }
   if (m >= kTM && k % kTK == 0) {
     auto kern = gemm_tile256_kernel<XT, KIND, OT>;
-    const size_t lds = (size_t)2 * (kTM + kTN) * kTS * sizeof(XT);
+    const size_t lds = (size_t)2 * (kTM + kTN) * kTS * sizeof(XT) + 256 * sizeof(float2);
     hipError_t e = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
@@ -353,20 +641,20 @@ static hipError_t run_gemm(const XT* x, int64_t m, const PackedView& w, OT* y,
 
 template <typename XT, int KIND>
 static hipError_t gemm_out_dispatch(const XT* x, int64_t m, const PackedView& w, void* y,
-                                    int y_dtype, hipStream_t stream) {
-  if (y_dtype == kF32) return run_gemm<XT, KIND>(x, m, w, (float*)y, stream);
-  if (y_dtype == kF16) return run_gemm<XT, KIND>(x, m, w, (_Float16*)y, stream);
-  return run_gemm<XT, KIND>(x, m, w, (__bf16*)y, stream);
+                                    int y_dtype, void* ws, hipStream_t stream) {
+  if (y_dtype == kF32) return run_gemm<XT, KIND>(x, m, w, (float*)y, ws, stream);
+  if (y_dtype == kF16) return run_gemm<XT, KIND>(x, m, w, (_Float16*)y, ws, stream);
+  return run_gemm<XT, KIND>(x, m, w, (__bf16*)y, ws, stream);
 }
 
 hipError_t launch_gemm(const void* x, int x_dtype, int64_t m, const PackedView& w, void* y,
-                       int y_dtype, void*, size_t, hipStream_t stream) {
+                       int y_dtype, void* ws, size_t, hipStream_t stream) {
   if (x_dtype == kF16) {
-    if (w.kind == kWeight) return gemm_out_dispatch<_Float16, kWeight>((const _Float16*)x, m, w, y, y_dtype, stream);
-    return gemm_out_dispatch<_Float16, kAct>((const _Float16*)x, m, w, y, y_dtype, stream);
+    if (w.kind == kWeight) return gemm_out_dispatch<_Float16, kWeight>((const _Float16*)x, m, w, y, y_dtype, ws, stream);
+    return gemm_out_dispatch<_Float16, kAct>((const _Float16*)x, m, w, y, y_dtype, ws, stream);
   }
-  if (w.kind == kWeight) return gemm_out_dispatch<__bf16, kWeight>((const __bf16*)x, m, w, y, y_dtype, stream);
-  return gemm_out_dispatch<__bf16, kAct>((const __bf16*)x, m, w, y, y_dtype, stream);
+  if (w.kind == kWeight) return gemm_out_dispatch<__bf16, kWeight>((const __bf16*)x, m, w, y, y_dtype, ws, stream);
+  return gemm_out_dispatch<__bf16, kAct>((const __bf16*)x, m, w, y, y_dtype, ws, stream);
 }
 
 }  // namespace rz
