@@ -81,7 +81,7 @@ razer_status quantize_common(const void* x, razer_dtype dt, const razer_packed* 
   return status_of(rz::launch_quantize(x, dt, view_of(out), ws, (hipStream_t)stream));
 }
 
-constexpr int64_t kGemvMaxK = 65536;  // x is staged whole in LDS
+constexpr int64_t kGemvMaxK = 65536;  // each lane holds at most 8 x 32 or 16 x 16 elements of x
 
 }  // namespace
 

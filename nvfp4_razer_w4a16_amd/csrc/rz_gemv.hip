@@ -7,23 +7,25 @@
 // small matrices are not over-split; "Technical Summary: RaZeR ..."
 // (gist.science), §2.3.  The pages' kernel (group-128 FP16 scales on another
 // GPU) is prior art only; this one is written for CDNA4:
-//   - a wavefront owns R weight rows; lane l takes chunks (32 or 16 elements)
-//     l, l+64, ..., so every 16-byte code load is one coalesced 1 KiB wave
-//     access, and all R * CPL chunk loads of a pass are issued before any is
-//     consumed (and before x is staged), keeping enough bytes in flight to
-//     cover HBM latency;
-//   - x is staged once per workgroup in LDS (zero padded), with a 256-entry
-//     table of (sb, sb * SV / 2) indexed by the scale byte;
+//   - streaming: a wavefront keeps its slice of x in registers for the whole
+//     launch and walks a run of weight rows, with the code loads of the next D
+//     rows in flight while it decodes the current one, so the decode work of
+//     every wave overlaps the HBM stream instead of waiting behind it;
+//   - lane l of a wave takes chunks (32 or 16 elements) l, l+64, ... of the
+//     wave's K slice, so every 16-byte code load is one coalesced 1 KiB wave
+//     access; for long rows the K range is split over KS waves of a workgroup
+//     and their row sums are added in LDS;
 //   - codes become fp16/bf16 pairs with the gfx950 packed FP4 conversion and
 //     are contracted with x by v_dot2 (fp32 accumulate).  The remapped code
-//     0b1000 converts to -0 (0x8000), the only pair half below -0.25 when read
-//     as int16, so a packed int16 max against -0.25 followed by an xor with
-//     the converted pair leaves exactly 0.25 at remapped positions and 0
-//     elsewhere; a second v_dot2 of that one-hot with x gives sum(x) / 4 over
-//     the remapped positions, and the block sum is
-//     dot * sb + onehot_dot * (sb * SV * 4);
-//   - each row's 64 lane partials are summed across the wave and scaled once
-//     by the tensor scale.
+//     0b1000 converts to -0 (0x8000), the smallest pair half when read as
+//     int16; a packed int16 max against -0.25 replaces exactly those halves by
+//     -0.25 (every other converted value is +0 or has magnitude >= 0.5).  With
+//     d0 = x . q and d1 = x . max(q, -0.25) the block sum is
+//     d0 + SV * S = d0 * (1 + 4 SV) - 4 SV * d1, where S sums x over the
+//     remapped positions; a 256-entry LDS table holds the two coefficients
+//     (times the block scale) for every scale byte;
+//   - each row's 64 lane partials are summed with DPP and scaled once by the
+//     tensor scale.
 #include "rz_device.h"
 #include "rz_launch.h"
 
@@ -53,40 +55,70 @@ template <> struct Pair<__bf16> {
   }
 };
 
-// 0.25 where the converted half is the remapped -0, 0 elsewhere.  Every other
-// converted half (+0, +/-0.5 .. +/-6) is >= -0.5 > -0.25 - as int16 patterns
-// it compares above the -0.25 pattern, which compares above 0x8000.
+// The converted pair with remapped halves (-0) replaced by -0.25.
 template <typename XT>
-__device__ __forceinline__ typename Pair<XT>::T remapped_onehot(typename Pair<XT>::T p) {
+__device__ __forceinline__ typename Pair<XT>::T mark_remapped(typename Pair<XT>::T p) {
   const short2_t q = __builtin_elementwise_max(__builtin_bit_cast(short2_t, p),
                                                (short2_t){Pair<XT>::kQuarterNeg, Pair<XT>::kQuarterNeg});
-  return __builtin_bit_cast(typename Pair<XT>::T,
-                            __builtin_bit_cast(uint32_t, q) ^ __builtin_bit_cast(uint32_t, p));
+  return __builtin_bit_cast(typename Pair<XT>::T, q);
 }
 
-// Contract 8 codes (one dword; byte j holds elements 2j, 2j+1, low nibble
-// first) with 4 x pairs: d += FP4 dot, s += one-hot dot.
-template <typename XT, int SEL>
-__device__ __forceinline__ void dot2_step(uint32_t w, typename Pair<XT>::T xv, float& d, float& s) {
-  const typename Pair<XT>::T p = Pair<XT>::template cvt<SEL>(w);
-  d = Pair<XT>::dot(p, xv, d);
-  s = Pair<XT>::dot(remapped_onehot<XT>(p), xv, s);
-}
-
-// One 16-element block (codes w0: elements 0..7, w1: 8..15).
+// One 16-element block (codes w0: elements 0..7, w1: 8..15; byte j of a word
+// holds elements 2j, 2j+1, low nibble first) against 8 x pairs: d0 = x . q and
+// d1 = x . max(q, -0.25).  All conversions come first so that no dot reads a
+// register written by the instruction just before it.
 template <typename XT>
 __device__ __forceinline__ void block_dot(uint32_t w0, uint32_t w1, const typename Pair<XT>::T* xp,
-                                          float& d, float& s) {
-  d = 0.0f;
-  s = 0.0f;
-  dot2_step<XT, 0>(w0, xp[0], d, s);
-  dot2_step<XT, 1>(w0, xp[1], d, s);
-  dot2_step<XT, 2>(w0, xp[2], d, s);
-  dot2_step<XT, 3>(w0, xp[3], d, s);
-  dot2_step<XT, 0>(w1, xp[4], d, s);
-  dot2_step<XT, 1>(w1, xp[5], d, s);
-  dot2_step<XT, 2>(w1, xp[6], d, s);
-  dot2_step<XT, 3>(w1, xp[7], d, s);
+                                          float& d0, float& d1) {
+  typedef typename Pair<XT>::T P;
+  P p[8], m[8];
+  p[0] = Pair<XT>::template cvt<0>(w0);
+  p[1] = Pair<XT>::template cvt<1>(w0);
+  p[2] = Pair<XT>::template cvt<2>(w0);
+  p[3] = Pair<XT>::template cvt<3>(w0);
+  p[4] = Pair<XT>::template cvt<0>(w1);
+  p[5] = Pair<XT>::template cvt<1>(w1);
+  p[6] = Pair<XT>::template cvt<2>(w1);
+  p[7] = Pair<XT>::template cvt<3>(w1);
+#pragma unroll
+  for (int j = 0; j < 8; j++) m[j] = mark_remapped<XT>(p[j]);
+  d0 = 0.0f;
+  d1 = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; j++) {
+    d0 = Pair<XT>::dot(p[j], xp[j], d0);
+    d1 = Pair<XT>::dot(m[j], xp[j], d1);
+  }
+}
+
+// Lane sums of four values at once.  v_permlane32_swap exchanges lanes 32..63
+// of its first operand with lanes 0..31 of its second, v_permlane16_swap the
+// odd 16-lane rows of the first with the even rows of the second (gfx950), so
+// two swap+add steps leave, in 16-lane row rho, the sum over lanes l, l+16,
+// l+32, l+48 of value {0, 2, 1, 3}[rho]; DPP then sums each row.  Every lane
+// of row rho ends with the total of value quad_row(rho).
+__device__ __forceinline__ float swap_sum32(float a, float b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return a + b;
+}
+__device__ __forceinline__ float swap_sum16(float a, float b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return a + b;
+}
+template <int CTRL> __device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float quad_sum(const float* a) {
+  float v = swap_sum16(swap_sum32(a[0], a[1]), swap_sum32(a[2], a[3]));
+  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp<0x141>(v);  // row_half_mirror
+  v += dpp<0x140>(v);  // row_mirror
+  return v;
+}
+__device__ __forceinline__ int quad_row(int lane) {
+  const int rho = lane >> 4;
+  return ((rho & 1) << 1) | (rho >> 1);
 }
 
 struct GemvArgs {
@@ -96,7 +128,9 @@ struct GemvArgs {
   const float* ts;
   void* y;
   int64_t n, k, nchunk;
-  int npass, kind, ydt;
+  int rpw;   // rows per workgroup
+  int rpwv;  // rows per row group (multiple of 4)
+  int kind, ydt;
   float m0, m1;
 };
 
@@ -106,57 +140,103 @@ __device__ __forceinline__ void store_out(void* y, int64_t i, float v, int ydt) 
   else ((__bf16*)y)[i] = (__bf16)v;
 }
 
+// Raw buffer loads: a read past num_records returns zero and moves no data,
+// which covers the ragged tail of K and the rows past the end of a run
+// without branches around the loads.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr int kRsrcWord3 = 0x00020000;      // gfx950 raw buffer, 32-bit data format
+constexpr int kOob = 0x40000000;             // past any num_records, also when added twice
+constexpr int kNt = 2;                       // non-temporal: weights are read once
+
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, kRsrcWord3);
+}
+
 template <int UNIT> struct Chunk;
 template <> struct Chunk<2> {  // 32 elements: 16 code bytes, 2 scale bytes
-  uint4 c;
+  u32x4_t c;
   uint32_t s;
-  __device__ __forceinline__ void load(const uint8_t* crow, const uint8_t* srow, int64_t i) {
-    c = load_nt16(crow + 16 * i);
-    s = *(const uint16_t*)(srow + 2 * i);
+  __device__ __forceinline__ void load(Rsrc cr, Rsrc sr, int coff, int soff) {
+    c = __builtin_amdgcn_raw_buffer_load_b128(cr, coff, 0, kNt);
+    s = __builtin_amdgcn_raw_buffer_load_b16(sr, soff, 0, 0);
   }
-  __device__ __forceinline__ void zero() { c = make_uint4(0, 0, 0, 0); s = 0; }
-  __device__ __forceinline__ uint32_t w(int j) const { return j == 0 ? c.x : j == 1 ? c.y : j == 2 ? c.z : c.w; }
+  __device__ __forceinline__ uint32_t w(int j) const { return c[j]; }
 };
 template <> struct Chunk<1> {  // 16 elements: 8 code bytes, 1 scale byte
-  uint2 c;
+  u32x2_t c;
   uint32_t s;
-  __device__ __forceinline__ void load(const uint8_t* crow, const uint8_t* srow, int64_t i) {
-    c = load_nt8(crow + 8 * i);
-    s = srow[i];
+  __device__ __forceinline__ void load(Rsrc cr, Rsrc sr, int coff, int soff) {
+    c = __builtin_amdgcn_raw_buffer_load_b64(cr, coff, 0, kNt);
+    s = __builtin_amdgcn_raw_buffer_load_b8(sr, soff, 0, 0);
   }
-  __device__ __forceinline__ void zero() { c = make_uint2(0, 0); s = 0; }
-  __device__ __forceinline__ uint32_t w(int j) const { return j == 0 ? c.x : c.y; }
+  __device__ __forceinline__ uint32_t w(int j) const { return c[j]; }
 };
 
-// R rows per wave, CPL chunks per lane per pass, UNIT blocks per chunk.
-template <typename XT, int UNIT, int R, int CPL>
+constexpr int kGemvMaxRpw = 64;  // rows per workgroup (bounds the LDS partials)
+
+// Workgroup = 4 waves = KS K-slices x (4 / KS) row groups.  Row group rg owns
+// the rows [rg * rpwv, (rg + 1) * rpwv) of the workgroup's run (rpwv a
+// multiple of 4) and walks them four at a time; within a row, wave (ks, rg)
+// takes chunks (i * KS + ks) * 64 + lane for i < CPL.  The loads of the next
+// NQ - 1 row quads are in flight while a quad is decoded.
+template <typename XT, int UNIT, int CPL, int KS, int NQ>
 __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   typedef typename Pair<XT>::T P;
-  constexpr int kPairsPerChunk = 8 * UNIT;
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  float2* lut = (float2*)smem;
-  P* xs = (P*)(smem + 256 * sizeof(float2));
+  constexpr int kPairs = 8 * UNIT;  // x pairs per chunk
+  __shared__ float2 lut[256];
+  __shared__ float part[KS > 1 ? KS * kGemvMaxRpw : 1];
 
   const int lane = threadIdx.x & 63;
-  const int64_t row0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * R;
-  const int64_t rcb = a.k / 2, rsb = a.k / 16;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ks = wave % KS, rg = wave / KS;
+  const int64_t base = (int64_t)blockIdx.x * a.rpw;
+  const int rows_wg = (int)min((int64_t)a.rpw, a.n - base);
+  const int r0 = rg * a.rpwv;                                  // first row of this wave in the run
+  const int nrw = max(0, min(a.rpwv, rows_wg - r0));           // rows of this wave
+  const int nq = (nrw + 3) >> 2;
+  const int rcb = (int)(a.k / 2), rsb = (int)(a.k / 16);
+  const Rsrc crs = make_rsrc(a.codes + base * rcb, (int64_t)rows_wg * rcb);
+  const Rsrc srs = make_rsrc(a.scales + base * rsb, (int64_t)rows_wg * rsb);
+  const Rsrc xrs = make_rsrc(a.x, a.k * 2);
 
-  Chunk<UNIT> ch[R][CPL];
-  auto load_pass = [&](int p) {
+  // Chunks of this wave: ni of them hold any valid lane (wave-uniform); a
+  // lane past K reads nothing (offset kOob) and holds zero x.
+  int ni = 0;
+  int coff[CPL], soff[CPL];
 #pragma unroll
-    for (int r = 0; r < R; r++) {
-      const int64_t row = row0 + r;
-      const uint8_t* crow = a.codes + row * rcb;
-      const uint8_t* srow = a.scales + row * rsb;
+  for (int i = 0; i < CPL; i++) {
+    const int c0 = (i * KS + ks) * 64;
+    if (c0 < a.nchunk) ni = i + 1;
+    const int c = c0 + lane;
+    const bool ok = c < a.nchunk;
+    coff[i] = ok ? c * 8 * UNIT : kOob;
+    soff[i] = ok ? c * UNIT : kOob;
+  }
+
+  // x slice in registers, requested before any weight bytes.
+  P xv[CPL][kPairs];
 #pragma unroll
-      for (int i = 0; i < CPL; i++) {
-        const int64_t c = ((int64_t)p * CPL + i) * 64 + lane;
-        if (row < a.n && c < a.nchunk) ch[r][i].load(crow, srow, c);
-        else ch[r][i].zero();
-      }
+  for (int i = 0; i < CPL; i++) {
+#pragma unroll
+    for (int q = 0; q < kPairs / 4; q++) {
+      const int off = coff[i] == kOob ? kOob : coff[i] * 4 + 16 * q;  // x: 4 bytes per code byte
+      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0);
+      ((u32x4_t*)xv[i])[q] = v;
+    }
+  }
+
+  Chunk<UNIT> buf[NQ][4][CPL];
+  auto load_quad = [&](Chunk<UNIT> (*b)[CPL], int q) {
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const int j = 4 * q + r;
+      const int cb = j < nrw ? (r0 + j) * rcb : kOob, sbase = j < nrw ? (r0 + j) * rsb : kOob;
+#pragma unroll
+      for (int i = 0; i < CPL; i++) b[r][i].load(crs, srs, cb + coff[i], sbase + soff[i]);
     }
   };
-  load_pass(0);  // weight bytes in flight while x is staged
+#pragma unroll
+  for (int s = 0; s < NQ - 1; s++) load_quad(buf[s], s);
 
   {
     const uint32_t i = threadIdx.x;
@@ -168,93 +248,111 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
       sb = scale_of_byte<kAct>(i);
       sv = special_of_byte<kAct>(i, a.m0, a.m1);
     }
-    lut[i] = make_float2(sb, sb * sv * 4.0f);
+    lut[i] = make_float2(sb * (1.0f + 4.0f * sv), -4.0f * sb * sv);
   }
-  const int64_t xvec = a.k / 8;                                           // 16-byte x vectors
-  const int64_t xpad = (int64_t)a.npass * CPL * 64 * kPairsPerChunk / 4;  // padded, in vectors
-  const uint4* xg = (const uint4*)a.x;
-  for (int64_t i = threadIdx.x; i < xpad; i += 256)
-    ((uint4*)xs)[i] = i < xvec ? xg[i] : make_uint4(0, 0, 0, 0);
   __syncthreads();
+  const float st = *a.ts;
+  const int my_row = quad_row(lane);  // the row of the quad this lane's sum belongs to
 
-  float acc[R];
+  for (int q0 = 0; q0 < nq; q0 += NQ) {
 #pragma unroll
-  for (int r = 0; r < R; r++) acc[r] = 0.0f;
-  for (int p = 0; p < a.npass; p++) {
-    if (p > 0) load_pass(p);
+    for (int s = 0; s < NQ; s++) {
+      const int q = q0 + s;
+      load_quad(buf[(s + NQ - 1) % NQ], q + NQ - 1);
+      if (q < nq) {
+        float acc[4];
 #pragma unroll
-    for (int i = 0; i < CPL; i++) {
-      const int64_t c = ((int64_t)p * CPL + i) * 64 + lane;
-      P xv[kPairsPerChunk];
+        for (int r = 0; r < 4; r++) {
+          acc[r] = 0.0f;
 #pragma unroll
-      for (int q = 0; q < kPairsPerChunk / 4; q++)
-        ((uint4*)xv)[q] = ((const uint4*)(xs + c * kPairsPerChunk))[q];
+          for (int i = 0; i < CPL; i++) {
+            if (i < ni) {
+              const Chunk<UNIT>& ch = buf[s][r][i];
 #pragma unroll
-      for (int r = 0; r < R; r++) {
-#pragma unroll
-        for (int u = 0; u < UNIT; u++) {
-          float d, s;
-          block_dot<XT>(ch[r][i].w(2 * u), ch[r][i].w(2 * u + 1), xv + 8 * u, d, s);
-          const float2 f = lut[(ch[r][i].s >> (8 * u)) & 0xFFu];
-          acc[r] = fmaf(d, f.x, acc[r]);
-          acc[r] = fmaf(s, f.y, acc[r]);
+              for (int u = 0; u < UNIT; u++) {
+                float d0, d1;
+                block_dot<XT>(ch.w(2 * u), ch.w(2 * u + 1), xv[i] + 8 * u, d0, d1);
+                const float2 f = lut[(ch.s >> (8 * u)) & 0xFFu];
+                acc[r] = fmaf(d0, f.x, acc[r]);
+                acc[r] = fmaf(d1, f.y, acc[r]);
+              }
+            }
+          }
+        }
+        const float v = quad_sum(acc);
+        const int j = 4 * q + my_row;
+        if ((lane & 15) == 0 && j < nrw) {
+          if (KS == 1) store_out(a.y, base + r0 + j, v * st, a.ydt);
+          else part[ks * kGemvMaxRpw + r0 + j] = v;
         }
       }
     }
   }
-
-  const float st = *a.ts;
+  if (KS > 1) {
+    __syncthreads();
+    for (int r = threadIdx.x; r < rows_wg; r += 256) {
+      float v = 0.0f;
 #pragma unroll
-  for (int r = 0; r < R; r++) {
-    const float v = wave_sum_f32(acc[r]);
-    if (lane == r && row0 + r < a.n) store_out(a.y, row0 + r, v * st, a.ydt);
+      for (int q = 0; q < KS; q++) v += part[q * kGemvMaxRpw + r];
+      store_out(a.y, base + r, v * st, a.ydt);
+    }
   }
 }
 
 size_t gemv_ws_bytes(int64_t, int64_t) { return 0; }
 
-template <typename XT, int UNIT, int R, int CPL>
-static hipError_t launch_cfg(const GemvArgs& a, hipStream_t stream) {
-  constexpr int kPairsPerChunk = 8 * UNIT;
-  const size_t lds = 256 * sizeof(float2) + (size_t)a.npass * CPL * 64 * kPairsPerChunk * 4;
-  auto kern = gemv_kernel<XT, UNIT, R, CPL>;
-  if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
-  const int64_t waves = (a.n + R - 1) / R;
-  const int64_t grid = (waves + 3) / 4;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds, stream, a);
+struct GemvPlan {
+  int ks, cpl, nq, rpwv, rpw;
+  int64_t grid;
+};
+
+template <typename XT, int UNIT, int CPL, int KS, int NQ>
+static hipError_t launch_cfg(GemvArgs a, const GemvPlan& p, hipStream_t stream) {
+  a.rpw = p.rpw;
+  a.rpwv = p.rpwv;
+  hipLaunchKernelGGL((gemv_kernel<XT, UNIT, CPL, KS, NQ>), dim3((unsigned)p.grid), dim3(256), 0,
+                     stream, a);
   return hipGetLastError();
 }
 
-// Launch sizing (the CDNA counterpart of the pages' SM-launch trimming): pick
-// chunks per lane so one pass covers K where possible, then the largest row
-// group R that still leaves >= 6 waves per SIMD for latency hiding.
+// Launch sizing (the CDNA counterpart of the pages' SM-launch trimming).  K is
+// split over KS waves when a lane would otherwise hold more than two chunks of
+// x; each row group then gets a run of whole row quads, sized so that about
+// wg_per_cu workgroups land on each CU, and never more workgroups than the
+// rows need.
+static GemvPlan plan_gemv(int64_t n, int64_t nchunk, int cus, int wg_per_cu) {
+  GemvPlan p;
+  p.ks = nchunk <= 64 ? 1 : nchunk <= 128 ? 2 : 4;
+  const int64_t per_lane = (nchunk + 64LL * p.ks - 1) / (64LL * p.ks);
+  p.cpl = per_lane <= 1 ? 1 : per_lane <= 2 ? 2 : per_lane <= 4 ? 4 : per_lane <= 8 ? 8 : 16;
+  p.nq = 1;
+  const int rw = 4 / p.ks;
+  const int64_t groups = (int64_t)cus * wg_per_cu * rw;
+  int64_t rpwv = (n + groups - 1) / groups;
+  rpwv = (rpwv + 3) / 4 * 4;
+  if (rpwv * rw > kGemvMaxRpw) rpwv = kGemvMaxRpw / rw;
+  p.rpwv = (int)rpwv;
+  p.rpw = (int)(rpwv * rw);
+  p.grid = (n + p.rpw - 1) / p.rpw;
+  return p;
+}
+
 template <typename XT, int UNIT>
-static hipError_t dispatch(GemvArgs a, hipStream_t stream) {
-  const int64_t per_lane = (a.nchunk + 63) / 64;
-  const int cpl = per_lane <= 1 ? 1 : per_lane <= 2 ? 2 : per_lane <= 4 ? 4 : per_lane <= 7 ? 7 : 8;
-  a.npass = (int)((a.nchunk + 64LL * cpl - 1) / (64LL * cpl));
-  if (a.npass < 1) a.npass = 1;
-  const int64_t simds = 4LL * device_cu_count();
-  int r = 1;
-  if (cpl <= 4) {
-    if (a.n / 4 >= 6 * simds) r = 4;
-    else if (a.n / 2 >= 6 * simds) r = 2;
+static hipError_t dispatch(const GemvArgs& a, const GemvPlan& p, hipStream_t stream) {
+#define RZ_CASE(C_, K_, Q_) \
+  if (p.cpl == C_ && p.ks == K_ && p.nq == Q_) return launch_cfg<XT, UNIT, C_, K_, Q_>(a, p, stream);
+  RZ_CASE(1, 1, 1) RZ_CASE(1, 2, 1) RZ_CASE(1, 4, 1) RZ_CASE(2, 4, 1) RZ_CASE(4, 4, 1)
+  RZ_CASE(8, 4, 1)
+  if constexpr (UNIT == 1) {
+    RZ_CASE(16, 4, 1)  // 16-element chunks with K up to 65536
   }
-#define RZ_CASE(R_, C_) \
-  if (r == R_ && cpl == C_) return launch_cfg<XT, UNIT, R_, C_>(a, stream);
-  RZ_CASE(1, 1) RZ_CASE(1, 2) RZ_CASE(1, 4) RZ_CASE(1, 7) RZ_CASE(1, 8)
-  RZ_CASE(2, 1) RZ_CASE(2, 2) RZ_CASE(2, 4)
-  RZ_CASE(4, 1) RZ_CASE(4, 2) RZ_CASE(4, 4)
 #undef RZ_CASE
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemv(const void* x, int x_dtype, const PackedView& w, void* y, int y_dtype,
                        void*, size_t, hipStream_t stream) {
+  if (w.rows <= 0) return hipSuccess;
   GemvArgs a;
   a.x = x;
   a.codes = w.codes;
@@ -267,11 +365,13 @@ hipError_t launch_gemv(const void* x, int x_dtype, const PackedView& w, void* y,
   a.ydt = y_dtype;
   a.m0 = 6.0f + 0.5f * (float)w.off_half[0];
   a.m1 = 6.0f + 0.5f * (float)w.off_half[w.kind == kWeight ? 1 : 0];
-  a.npass = 1;
+  a.rpw = 4;
+  a.rpwv = 4;
   const bool unit2 = a.k % 32 == 0;
   a.nchunk = a.k / (unit2 ? 32 : 16);
-  if (x_dtype == kF16) return unit2 ? dispatch<_Float16, 2>(a, stream) : dispatch<_Float16, 1>(a, stream);
-  return unit2 ? dispatch<__bf16, 2>(a, stream) : dispatch<__bf16, 1>(a, stream);
+  const GemvPlan p = plan_gemv(a.n, a.nchunk, device_cu_count(), 8);
+  if (x_dtype == kF16) return unit2 ? dispatch<_Float16, 2>(a, p, stream) : dispatch<_Float16, 1>(a, p, stream);
+  return unit2 ? dispatch<__bf16, 2>(a, p, stream) : dispatch<__bf16, 1>(a, p, stream);
 }
 
 }  // namespace rz

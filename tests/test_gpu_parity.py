@@ -305,7 +305,8 @@ def test_gemv_llama3_8b_decode(name):
 
 @pytest.mark.parametrize("n,k,xdt", [(7, 48, torch.float16), (33, 16, torch.bfloat16),
                                      (257, 1040, torch.float16), (64, 96, torch.bfloat16),
-                                     (5, 65536, torch.float16)])
+                                     (5, 65536, torch.float16), (3, 40976, torch.bfloat16),
+                                     (9001, 2080, torch.float16)])
 def test_gemv_ragged_shapes(n, k, xdt):
     _need_gpu()
     rng = np.random.default_rng(n * 7 + k)
