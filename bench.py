@@ -17,7 +17,15 @@ synthetic workload; ``roofline`` for the GEMV kernel; ``cpu_baseline`` = the CPU
 oracle on one layer.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L]
-                       [--no-rows] [--no-cpu-baseline] [--only NAME]
+                       [--no-rows] [--no-cpu-baseline] [--eager]
+       python bench.py --copy-calibration
+       python bench.py --traffic-summary FETCH.csv WRITE.csv CAL_FETCH.csv CAL_WRITE.csv
+
+--eager replays the decode launches without a graph (for counter passes);
+--copy-calibration runs a plain elementwise copy (negation) of 512 MiB, the reference for
+scaling the FETCH_SIZE / WRITE_SIZE counters; --traffic-summary turns the four
+rocprofv3 counter CSVs (decode GEMV fetch, write; copy fetch, write) into
+profiles/traffic.json, stamped with the hash of the GEMV source.
 """
 import argparse
 import hashlib
@@ -92,6 +100,59 @@ def source_hash(*names):
     for n in names:
         h.update(open(os.path.join(ROOT, "nvfp4_razer_w4a16_amd", "csrc", n), "rb").read())
     return h.hexdigest()[:16]
+
+
+COPY_BYTES = 512 << 20  # the calibration copy reads and writes this many bytes
+
+
+def copy_calibration():
+    import torch
+
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):  # one elementwise kernel: reads and writes COPY_BYTES each
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    log(f"copy calibration: 5 elementwise copies of {COPY_BYTES} bytes")
+
+
+def _counter_per_dispatch(path, name_part):
+    """Mean over dispatches of a kernel (name contains name_part) of the counter
+    summed over its instances, from a rocprofv3 counter_collection CSV."""
+    import csv
+    from collections import defaultdict
+
+    per = defaultdict(float)
+    for r in csv.DictReader(open(path)):
+        if name_part in r["Kernel_Name"]:
+            per[r["Dispatch_Id"]] += float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no dispatch of {name_part!r} in {path}")
+    return sum(per.values()) / len(per), len(per)
+
+
+def traffic_summary(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv):
+    """FETCH_SIZE / WRITE_SIZE are KiB per dispatch; each is scaled by what the
+    same counter reads for the calibration copy (COPY_BYTES read, COPY_BYTES
+    written), so the factor absorbs any per-channel sampling of the counter."""
+    f_k, nf = _counter_per_dispatch(fetch_csv, "gemv_kernel")
+    w_k, nw = _counter_per_dispatch(write_csv, "gemv_kernel")
+    cf, _ = _counter_per_dispatch(cal_fetch_csv, "elementwise")
+    cw, _ = _counter_per_dispatch(cal_write_csv, "elementwise")
+    f_scale = COPY_BYTES / (cf * 1024.0)
+    w_scale = COPY_BYTES / (cw * 1024.0)
+    fetch = f_k * 1024.0 * f_scale
+    write = w_k * 1024.0 * w_scale
+    src = source_hash("rz_gemv.hip", "rz_device.h")
+    out = {"gemv_decode": {
+        "source_hash": src, "bytes_per_launch": round(fetch + write),
+        "fetch_bytes_per_launch": round(fetch), "write_bytes_per_launch": round(write),
+        "fetch_kib_raw": f_k, "write_kib_raw": w_k, "dispatches": [nf, nw],
+        "copy_fetch_kib_raw": cf, "copy_write_kib_raw": cw,
+        "fetch_scale": f_scale, "write_scale": w_scale}}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    json.dump(out, open(path, "w"), indent=1)
+    print(json.dumps(out))
 
 
 def load_traffic(kernel_key, src_hash):
@@ -270,7 +331,13 @@ def main():
     ap.add_argument("--layers", type=int, default=8)
     ap.add_argument("--no-rows", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--traffic-summary", nargs=4, metavar="CSV")
     args = ap.parse_args()
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
@@ -286,9 +353,18 @@ def main():
         sys.exit(1)
     rz.lib()
     log(f"device: {torch.cuda.get_device_name(0)}")
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     log("decode: generating and encoding weights ...")
     launches, step_bytes, base = setup_decode(torch, rz, synth, args.layers)
+    if args.eager:  # counter passes: plain launches, nothing timed
+        for _ in range(args.warmup + args.steps):
+            run_launches(rz, launches)
+        torch.cuda.synchronize()
+        log(f"decode: {args.warmup + args.steps} eager steps of {len(launches)} launches")
+        return
     timer = GraphTimer(torch, lambda: run_launches(rz, launches), warmup=1)
     for _ in range(args.warmup):
         timer.g.replay()
