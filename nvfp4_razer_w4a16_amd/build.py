@@ -29,6 +29,7 @@ SOURCES = {
     "rz_dequant.hip": EXACT,
     "rz_gemv.hip": [],
     "rz_gemm.hip": [],
+    "rz_smallm.hip": [],
     "rz_api.cpp": [],
 }
 

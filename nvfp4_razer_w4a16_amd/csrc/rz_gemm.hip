@@ -593,7 +593,17 @@ __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restr
   }
 }
 
+// Two rows go to the MFMA small-batch kernel (no workspace) where it covers the
+// shape, three or four rows too on weights up to 64M elements (on larger ones
+// its 8-byte code loads per lane make it request-bound and the skinny kernel is
+// faster); above that the skinny split-K kernel takes up to 32 rows.
+static bool use_smallm(int64_t m, int64_t n, int64_t k) {
+  if (m < 2 || m > 4 || !smallm_supported(m, n, k)) return false;
+  return m == 2 || n * k <= (64LL << 20);
+}
+
 size_t gemm_ws_bytes(int64_t m, int64_t n, int64_t k) {
+  if (use_smallm(m, n, k)) return 0;
   if (m < 2 || m > 32 || k % 32 != 0) return 0;
   const SkinnyPlan p = skinny_plan(n, k);
   return (size_t)p.split * (size_t)m * (size_t)n * sizeof(float);
@@ -649,6 +659,7 @@ static hipError_t gemm_out_dispatch(const XT* x, int64_t m, const PackedView& w,
 
 hipError_t launch_gemm(const void* x, int x_dtype, int64_t m, const PackedView& w, void* y,
                        int y_dtype, void* ws, size_t, hipStream_t stream) {
+  if (use_smallm(m, w.rows, w.cols)) return launch_smallm(x, x_dtype, m, w, y, y_dtype, stream);
   if (x_dtype == kF16) {
     if (w.kind == kWeight) return gemm_out_dispatch<_Float16, kWeight>((const _Float16*)x, m, w, y, y_dtype, ws, stream);
     return gemm_out_dispatch<_Float16, kAct>((const _Float16*)x, m, w, y, y_dtype, ws, stream);

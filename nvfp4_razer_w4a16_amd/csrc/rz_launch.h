@@ -39,6 +39,12 @@ size_t gemv_ws_bytes(int64_t n, int64_t k);
 hipError_t launch_gemv(const void* x, int x_dtype, const PackedView& w, void* y, int y_dtype,
                        void* ws, size_t ws_bytes, hipStream_t stream);
 
+// MFMA kernel for 1..4 activation rows (K a multiple of 256 / M rounded up to
+// 1, 2, 4); returns hipErrorNotSupported for shapes it does not cover.
+bool smallm_supported(int64_t m, int64_t n, int64_t k);
+hipError_t launch_smallm(const void* x, int x_dtype, int64_t m, const PackedView& w, void* y,
+                         int y_dtype, hipStream_t stream);
+
 size_t gemm_ws_bytes(int64_t m, int64_t n, int64_t k);
 hipError_t launch_gemm(const void* x, int x_dtype, int64_t m, const PackedView& w, void* y,
                        int y_dtype, void* ws, size_t ws_bytes, hipStream_t stream);

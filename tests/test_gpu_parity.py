@@ -334,7 +334,7 @@ def small_batch_ref(n, k):
     return ref
 
 
-@pytest.mark.parametrize("m", [2, 4, 8, 16, 32])
+@pytest.mark.parametrize("m", [2, 3, 4, 8, 16, 32])
 def test_gemm_small_batch_4096(m):
     _need_gpu()
     ref = small_batch_ref(4096, 4096)
@@ -354,7 +354,7 @@ def _small_batch_oracle_4096():
     return oracle.gemm(as_f32(synth.small_batch_x(32, 4096)), small_batch_ref(4096, 4096))
 
 
-@pytest.mark.parametrize("m", [2, 8, 32])
+@pytest.mark.parametrize("m", [2, 4, 8, 32])
 def test_gemm_small_batch_70b_sampled(m):
     _need_gpu()
     log("gemm 70b: reference encode ...")
@@ -395,7 +395,10 @@ def test_gemm_prefill_sampled():
 @pytest.mark.parametrize("m,n,k,xdt", [(3, 100, 48, torch.bfloat16), (130, 257, 80, torch.float16),
                                        (2, 16, 16, torch.bfloat16), (129, 129, 4096, torch.bfloat16),
                                        (33, 64, 32, torch.float16), (257, 300, 128, torch.bfloat16),
-                                       (512, 256, 192, torch.float16), (300, 520, 4096, torch.bfloat16)])
+                                       (512, 256, 192, torch.float16), (300, 520, 4096, torch.bfloat16),
+                                       (3, 33, 320, torch.float16), (2, 50, 384, torch.bfloat16),
+                                       (4, 1000, 4096, torch.float16), (2, 17, 256, torch.float16),
+                                       (3, 64, 960, torch.bfloat16), (2, 40, 320, torch.bfloat16)])
 def test_gemm_ragged_shapes(m, n, k, xdt):
     _need_gpu()
     rng = np.random.default_rng(m * 1000 + n + k)
