@@ -190,26 +190,34 @@ __device__ __forceinline__ void encode_block(const float (&xf)[16], float amax, 
   const float rcp = 1.0f / d;
   if (!(rcp < INFINITY)) return;  // scale product underflowed: zero block
 
-  float a[16];
-  uint32_t m0[16];
-  uint32_t neg = 0u;
-  long long acc[2 * kPairs];
+  // FP4 codes with the gfx950 conversion: nearest on the E2M1 grid, ties to
+  // the even code (0.25, 1.25, 2.5, 5 go down; 0.75, 1.75, 3.5 go up),
+  // saturating at 6, sign in bit 3.  A negative value that rounds to zero
+  // comes out as 0b1000 and is cleared to +0.
+  float y[16];
 #pragma unroll
-  for (int c = 0; c < 2 * kPairs; c++) acc[c] = 0;
+  for (int j = 0; j < 16; j++) y[j] = xf[j] * rcp;
+  uint32_t w[2] = {0u, 0u};
 #pragma unroll
-  for (int j = 0; j < 16; j++) {
-    const float y = xf[j] * rcp;
-    const uint32_t nj = f2u(y) >> 31;
-    neg |= nj << j;
-    const float aj = fabsf(y);
-    a[j] = aj;
-    // FP4 nearest-even magnitude index: count the decision points passed.
-    // A tie at 0.25, 1.25, 2.5, 5 stays below, at 0.75, 1.75, 3.5 goes up.
-    m0[j] = (uint32_t)(aj > 0.25f) + (uint32_t)(aj >= 0.75f) + (uint32_t)(aj > 1.25f) +
-            (uint32_t)(aj >= 1.75f) + (uint32_t)(aj > 2.5f) + (uint32_t)(aj >= 3.5f) +
-            (uint32_t)(aj > 5.0f);
-    if (prm.remap) {
-      const int q2 = (int)fp4_mag_x2(m0[j]);
+  for (int h = 0; h < 2; h++) {
+    w[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[h], y[8 * h + 0], y[8 * h + 1], 1.0f, 0);
+    w[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[h], y[8 * h + 2], y[8 * h + 3], 1.0f, 1);
+    w[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[h], y[8 * h + 4], y[8 * h + 5], 1.0f, 2);
+    w[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[h], y[8 * h + 6], y[8 * h + 7], 1.0f, 3);
+    const uint32_t nz = (w[h] & 0x77777777u) + 0x77777777u;  // bit 3: magnitude != 0
+    w[h] &= ~(~nz & 0x88888888u);                            // -0 -> +0
+  }
+  uint32_t sel = 0u;
+  if (prm.remap) {
+    long long acc[2 * kPairs];
+#pragma unroll
+    for (int c = 0; c < 2 * kPairs; c++) acc[c] = 0;
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+      const uint32_t c = (w[j >> 3] >> (4 * (j & 7))) & 15u;
+      const uint32_t nj = c >> 3;  // moved elements have |y| > 2, so the code keeps the sign
+      const float aj = fabsf(y[j]);
+      const int q2 = (int)fp4_mag_x2(c & 7u);
       const int a2 = 2 * (int)(aj * 4194304.0f);  // 2 * a * 2^22 (exact when it matters)
 #pragma unroll
       for (int p = 0; p < kPairs; p++) {
@@ -222,9 +230,6 @@ __device__ __forceinline__ void encode_block(const float (&xf)[16], float amax, 
         acc[2 * p + 1] += (long long)dneg * (long long)ee;
       }
     }
-  }
-  uint32_t sel = 0u;
-  if (prm.remap) {
     long long best = acc[0];
 #pragma unroll
     for (int c = 1; c < 2 * kPairs; c++)
@@ -232,17 +237,17 @@ __device__ __forceinline__ void encode_block(const float (&xf)[16], float amax, 
         best = acc[c];
         sel = (uint32_t)c;
       }
-  }
-  const int p = (int)(sel >> 1);
-  const uint32_t sneg = sel & 1u;
-  const float lo = prm.lo[p], hi = prm.hi[p];
-  uint32_t w[2] = {0u, 0u};
+    const int p = (int)(sel >> 1);
+    const uint32_t sneg = sel & 1u;
+    const float lo = prm.lo[p], hi = prm.hi[p];
 #pragma unroll
-  for (int j = 0; j < 16; j++) {
-    const uint32_t nj = (neg >> j) & 1u;
-    const bool hit = prm.remap && a[j] > lo && a[j] < hi && nj == sneg;
-    const uint32_t nib = hit ? 8u : (m0[j] == 0u ? 0u : ((nj << 3) | m0[j]));
-    w[j >> 3] |= nib << (4 * (j & 7));
+    for (int j = 0; j < 16; j++) {
+      const uint32_t sh = 4 * (j & 7);
+      const uint32_t c = (w[j >> 3] >> sh) & 15u;
+      const float aj = fabsf(y[j]);
+      const bool hit = aj > lo && aj < hi && (c >> 3) == sneg;
+      w[j >> 3] ^= hit ? ((c ^ 8u) << sh) : 0u;  // the special value's code
+    }
   }
   cw = make_uint2(w[0], w[1]);
   sbyte = (KIND == kWeight) ? (((sel & 1u) << 7) | ((sel >> 1) << 6) | scode) : ((sel << 7) | scode);
