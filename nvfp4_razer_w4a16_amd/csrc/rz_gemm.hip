@@ -344,15 +344,21 @@ __global__ __launch_bounds__(256) void gemm_tile256_kernel(const XT* __restrict_
     for (int blk = 0; blk < 4; blk++) f[blk] = lut[(cur_stage.s >> (8 * blk)) & 0xFFu];
     const XT* a = As + cur * kTM * kTS;
     const XT* b = Bs + cur * kTN * kTS;
-#pragma unroll
-    for (int kk = 0; kk < 4; kk++) {
-      V av[4], bv[4];
+    // fragments of sub-step kk + 1 are read from LDS while sub-step kk's MFMAs
+    // run, so only the first sub-step after the barrier waits for LDS
+    V av[2][4], bv[2][4];
+    auto frags = [&](int kk, V* ar, V* br) {
 #pragma unroll
       for (int i = 0; i < 4; i++)
-        av[i] = *(const V*)(a + (wm * 128 + i * 32 + (lane & 31)) * kTS + 16 * kk + 8 * (lane >> 5));
+        ar[i] = *(const V*)(a + (wm * 128 + i * 32 + (lane & 31)) * kTS + 16 * kk + 8 * (lane >> 5));
 #pragma unroll
       for (int j = 0; j < 4; j++)
-        bv[j] = *(const V*)(b + (wn * 128 + j * 32 + (lane & 31)) * kTS + 16 * kk + 8 * (lane >> 5));
+        br[j] = *(const V*)(b + (wn * 128 + j * 32 + (lane & 31)) * kTS + 16 * kk + 8 * (lane >> 5));
+    };
+    frags(0, av[0], bv[0]);
+#pragma unroll
+    for (int kk = 0; kk < 4; kk++) {
+      if (kk < 3) frags(kk + 1, av[(kk + 1) & 1], bv[(kk + 1) & 1]);
       // the next tile's x vectors for this sub-step go straight to LDS
       XT* an = As + (cur ^ 1) * kTM * kTS;
 #pragma unroll
@@ -364,17 +370,46 @@ __global__ __launch_bounds__(256) void gemm_tile256_kernel(const XT* __restrict_
       const uint32_t w0 = (kk & 1) ? cw.z : cw.x, w1 = (kk & 1) ? cw.w : cw.y;
       const uint32_t svd = __builtin_bit_cast(uint32_t, f[kk].y);
       uint32_t dec[8];
-      // two MFMAs, then one decoded pair: the pair's VALU work issues while the
-      // matrix unit runs (fences keep the compiler from regrouping them)
+#ifndef RZ_GEMM_SCHED
+#define RZ_GEMM_SCHED 2
+#endif
+#if RZ_GEMM_SCHED == 0
+      // two MFMAs, then one decoded pair behind scheduling fences
 #pragma unroll
       for (int g = 0; g < 8; g++) {
         const int i = g >> 1, j = 2 * (g & 1);
-        acc[i][j] = Mfma32<XT>::run(av[i], bv[j], acc[i][j]);
-        acc[i][j + 1] = Mfma32<XT>::run(av[i], bv[j + 1], acc[i][j + 1]);
+        acc[i][j] = Mfma32<XT>::run(av[kk & 1][i], bv[kk & 1][j], acc[i][j]);
+        acc[i][j + 1] = Mfma32<XT>::run(av[kk & 1][i], bv[kk & 1][j + 1], acc[i][j + 1]);
         __builtin_amdgcn_sched_barrier(0);
         dec[g] = decode_one_pair<XT>(g < 4 ? w0 : w1, g & 3, f[kk].x, svd);
         __builtin_amdgcn_sched_barrier(0);
       }
+#else
+      // the eight pair decodes are independent chains; the scheduler is asked
+      // to alternate one MFMA with a few VALU instructions drawn from them, so
+      // the decode latency is hidden by the chains' interleaving and the
+      // matrix unit never waits for a whole chain
+#pragma unroll
+      for (int g = 0; g < 8; g++) dec[g] = decode_one_pair<XT>(g < 4 ? w0 : w1, g & 3, f[kk].x, svd);
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) acc[i][j] = Mfma32<XT>::run(av[kk & 1][i], bv[kk & 1][j], acc[i][j]);
+#if RZ_GEMM_SCHED == 2
+#pragma unroll
+      for (int g = 0; g < 16; g++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // up to five VALU
+      }
+#elif RZ_GEMM_SCHED == 3
+#pragma unroll
+      for (int g = 0; g < 16; g++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // up to five VALU
+      }
+#endif
+#endif
       uint4* bn = (uint4*)(Bs + (cur ^ 1) * kTN * kTS + tid * kTS) + 2 * kk;
       bn[0] = make_uint4(dec[0], dec[1], dec[2], dec[3]);
       bn[1] = make_uint4(dec[4], dec[5], dec[6], dec[7]);
@@ -593,13 +628,10 @@ __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restr
   }
 }
 
-// Two rows go to the MFMA small-batch kernel (no workspace) where it covers the
-// shape, three or four rows too on weights up to 64M elements (on larger ones
-// its 8-byte code loads per lane make it request-bound and the skinny kernel is
-// faster); above that the skinny split-K kernel takes up to 32 rows.
+// Two to four rows go to the MFMA small-batch kernel (no workspace) where it
+// covers the shape; above that the skinny split-K kernel takes up to 32 rows.
 static bool use_smallm(int64_t m, int64_t n, int64_t k) {
-  if (m < 2 || m > 4 || !smallm_supported(m, n, k)) return false;
-  return m == 2 || n * k <= (64LL << 20);
+  return m >= 2 && m <= 4 && smallm_supported(m, n, k);
 }
 
 size_t gemm_ws_bytes(int64_t m, int64_t n, int64_t k) {

@@ -33,9 +33,9 @@
 // scale bytes a lane needs (weight row c, the four slots of its D rows) are
 // one aligned dword of the scale row.
 //
-// Work split: a workgroup of KS waves owns T 16-row tiles; wave w covers a
-// contiguous range of K groups for all T tiles, with the next group's loads in
-// flight while one is multiplied; the KS partial sums meet in LDS.
+// Work split: a workgroup of KS waves owns one 16-row tile; wave w covers a
+// contiguous range of 256-element K units with the loads of the next two units
+// in flight while one is multiplied; the KS partial sums meet in LDS.
 #include "rz_device.h"
 #include "rz_launch.h"
 
@@ -136,6 +136,16 @@ struct GroupBuf {
 
 constexpr int kSection = 256 * 2 + 16;  // LDS bytes per K group: M x (256 / M) halves + zeros
 
+// Weights reach the MFMA layout through LDS: a wave loads a unit of its tile
+// (16 rows x 128 code bytes = 256 K elements, plus the 16 scale bytes of each
+// row) with fully coalesced 16-byte loads -- each instruction covers whole
+// 128-byte row segments -- writes it to a padded per-wave stage (row stride
+// 144 bytes, so the MFMA-layout reads of 8 rows hit distinct banks) and reads
+// each lane's slice back.  Loading the MFMA layout straight from memory would
+// cover only 64 bytes of a row per instruction and double the L2 requests.
+constexpr int kUnitRow = 128 + 16;              // staged code bytes per row
+constexpr int kStageBytes = 16 * kUnitRow + 16 * 16;  // codes + scales of one unit
+
 template <typename XT, int M, int T, int KS>
 __global__ __launch_bounds__(64 * KS) void smallm_kernel(SmArgs a) {
   typedef typename Ops<XT>::V V;
@@ -144,21 +154,25 @@ __global__ __launch_bounds__(64 * KS) void smallm_kernel(SmArgs a) {
   constexpr int EPG = 256 / M;     // elements per K group
   constexpr int BPL = S / 4;       // blocks of a K group in one lane's slice
   constexpr int CB = 32 / M;       // code bytes of one lane per tile and group
+  static_assert(T == 1, "one 16-row tile per workgroup");
   __shared__ float2 lut[256];
   __shared__ float red[KS][T][64];
+  __shared__ __attribute__((aligned(16))) uint8_t stage[KS][2][kStageBytes];
   extern __shared__ __attribute__((aligned(16))) uint8_t xs[];  // KS * gpw sections
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, q = lane >> 4;
-  const int64_t row0 = (int64_t)blockIdx.x * (16 * T);
-  const int rows_wg = (int)min((int64_t)(16 * T), a.n - row0);
+  const int64_t row0 = (int64_t)blockIdx.x * 16;
+  const int rows_wg = (int)min((int64_t)16, a.n - row0);
   const int rcb = (int)(a.k / 2), rsb = (int)(a.k / 16);
   const Rsrc crs = make_rsrc(a.codes + row0 * rcb, (int64_t)rows_wg * rcb);
   const Rsrc srs = make_rsrc(a.scales + row0 * rsb, (int64_t)rows_wg * rsb);
   const Rsrc xrs = make_rsrc(a.x, (int64_t)a.m * a.k * 2);
-  const int ngroups = (int)(a.k / EPG);
-  const int g0 = wave * a.gpw, g1 = min(ngroups, g0 + a.gpw);
+  const int nunits = (int)(a.k / 256);
+  const int upw = a.gpw / M;  // units per wave
+  const int u0 = wave * upw, u1 = min(nunits, u0 + upw);
+  const int g0 = u0 * M, g1 = u1 * M;  // K groups of this wave
   uint8_t* xw = xs + wave * a.gpw * kSection;  // this wave's sections
 
   // x of this wave's groups: 32 chunks of 16 bytes per section (vector-major)
@@ -176,14 +190,28 @@ __global__ __launch_bounds__(64 * KS) void smallm_kernel(SmArgs a) {
     xv[j] = __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0);
   }
 
-  // Per-lane offsets, fixed for the launch; the group enters as soffset.
-  int cvo[T], svo[T];
-#pragma unroll
-  for (int t = 0; t < T; t++) {
-    const bool ok = 16 * t + c < rows_wg;
-    cvo[t] = ok ? (16 * t + c) * rcb + q * CB : kOob;
-    svo[t] = ok ? (16 * t + c) * rsb + (4 * q) % S : kOob;
-  }
+  // Coalesced unit loads: codes, lane i -> row (i >> 3) (+8 for the second
+  // load), bytes 16 * (i & 7); scales, lane i -> row i >> 2, bytes 4 * (i & 3).
+  const int lr = lane >> 3, lb = (lane & 7) * 16;
+  const int cvo0 = lr < rows_wg ? lr * rcb + lb : kOob;
+  const int cvo1 = lr + 8 < rows_wg ? (lr + 8) * rcb + lb : kOob;
+  const int svo = (lane >> 2) < rows_wg ? (lane >> 2) * rsb + (lane & 3) * 4 : kOob;
+  struct UnitRegs {
+    u32x4_t c0, c1;
+    uint32_t s;
+  };
+  auto load_unit = [&](UnitRegs& r, int u) {
+    const bool ok = u < u1;
+    const int cso = ok ? u * 128 : kOob, sso = ok ? u * 16 : kOob;
+    r.c0 = __builtin_amdgcn_raw_buffer_load_b128(crs, cvo0, cso, kNt);
+    r.c1 = __builtin_amdgcn_raw_buffer_load_b128(crs, cvo1, cso, kNt);
+    r.s = __builtin_amdgcn_raw_buffer_load_b32(srs, svo, sso, 0);
+  };
+  auto store_unit = [&](const UnitRegs& r, uint8_t* st) {
+    *(u32x4_t*)(st + lr * kUnitRow + lb) = r.c0;
+    *(u32x4_t*)(st + (lr + 8) * kUnitRow + lb) = r.c1;
+    *(uint32_t*)(st + 16 * kUnitRow + lane * 4) = r.s;
+  };
   int xo[G];  // LDS byte offset of this lane's A fragment inside a section
   {
     const int mv = c / S, s = c % S;  // this lane's A row: vector mv, block slot s
@@ -191,18 +219,10 @@ __global__ __launch_bounds__(64 * KS) void smallm_kernel(SmArgs a) {
     for (int i = 0; i < G; i++)
       xo[i] = (s == q * BPL + i / 2) ? (mv * EPG + 16 * s + 8 * (i % 2)) * 2 : 256 * 2;
   }
-  auto load_group = [&](GroupBuf<M, T>& b, int g) {
-    const bool ok = g < g1;
-    const int cso = ok ? g * (EPG / 2) : kOob, sso = ok ? g * S : kOob;
-#pragma unroll
-    for (int t = 0; t < T; t++) {
-      b.c[t].load(crs, cvo[t], cso);
-      b.s[t] = __builtin_amdgcn_raw_buffer_load_b32(srs, svo[t], sso, 0);
-    }
-  };
 
-  GroupBuf<M, T> b0, b1;
-  load_group(b0, g0);
+  UnitRegs ra, rb;
+  load_unit(ra, u0);
+  load_unit(rb, u0 + 1);
 #pragma unroll
   for (int j = 0; j < kStage; j++) {
     const int ch = lane + 64 * j;
@@ -229,49 +249,60 @@ __global__ __launch_bounds__(64 * KS) void smallm_kernel(SmArgs a) {
   __syncthreads();
 
   float acc[T];
-#pragma unroll
-  for (int t = 0; t < T; t++) acc[t] = 0.0f;
+  acc[0] = 0.0f;
 
-  auto compute_group = [&](const GroupBuf<M, T>& b, int g) {
-    const uint8_t* sec = xw + (g - g0) * kSection;
-    f32x4_t d0[T], d1[T];
-#pragma unroll
-    for (int t = 0; t < T; t++) {
-      d0[t] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-      d1[t] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  // One K group (gi-th of the unit staged at st): lane (q, c) reads row c's
+  // slice and the scale dword of its D rows, then G MFMA pairs and the epilogue.
+  auto compute_group = [&](const uint8_t* st, int gi, const uint8_t* sec) {
+    const uint8_t* crow = st + c * kUnitRow + gi * (128 / M) + q * CB;
+    uint32_t cw[8 / M];
+    if constexpr (M == 1) {
+      const u32x4_t lo = *(const u32x4_t*)crow, hi = *(const u32x4_t*)(crow + 16);
+      cw[0] = lo[0]; cw[1] = lo[1]; cw[2] = lo[2]; cw[3] = lo[3];
+      cw[4] = hi[0]; cw[5] = hi[1]; cw[6] = hi[2]; cw[7] = hi[3];
+    } else if constexpr (M == 2) {
+      const u32x4_t v = *(const u32x4_t*)crow;
+      cw[0] = v[0]; cw[1] = v[1]; cw[2] = v[2]; cw[3] = v[3];
+    } else {
+      const u32x2_t v = *(const u32x2_t*)crow;
+      cw[0] = v[0]; cw[1] = v[1];
     }
+    const uint32_t sw = *(const uint32_t*)(st + 16 * kUnitRow + c * 16 + gi * S + (4 * q) % S);
+    f32x4_t d0 = (f32x4_t){0.f, 0.f, 0.f, 0.f}, d1 = d0;
 #pragma unroll
     for (int i = 0; i < G; i++) {
       const V xa = *(const V*)(sec + xo[i]);
-#pragma unroll
-      for (int t = 0; t < T; t++) {
-        const uint32_t w = b.c[t].w(i);
-        const u32x4_t p = {Ops<XT>::template cvt<0>(w), Ops<XT>::template cvt<1>(w),
-                           Ops<XT>::template cvt<2>(w), Ops<XT>::template cvt<3>(w)};
-        const u32x4_t pm = {mark_remapped(p[0], Ops<XT>::kQuarterNeg2),
-                            mark_remapped(p[1], Ops<XT>::kQuarterNeg2),
-                            mark_remapped(p[2], Ops<XT>::kQuarterNeg2),
-                            mark_remapped(p[3], Ops<XT>::kQuarterNeg2)};
-        d0[t] = Ops<XT>::mfma(xa, __builtin_bit_cast(V, p), d0[t]);
-        d1[t] = Ops<XT>::mfma(xa, __builtin_bit_cast(V, pm), d1[t]);
-      }
+      const uint32_t w = cw[i];
+      const u32x4_t p = {Ops<XT>::template cvt<0>(w), Ops<XT>::template cvt<1>(w),
+                         Ops<XT>::template cvt<2>(w), Ops<XT>::template cvt<3>(w)};
+      const u32x4_t pm = {mark_remapped(p[0], Ops<XT>::kQuarterNeg2),
+                          mark_remapped(p[1], Ops<XT>::kQuarterNeg2),
+                          mark_remapped(p[2], Ops<XT>::kQuarterNeg2),
+                          mark_remapped(p[3], Ops<XT>::kQuarterNeg2)};
+      d0 = Ops<XT>::mfma(xa, __builtin_bit_cast(V, p), d0);
+      d1 = Ops<XT>::mfma(xa, __builtin_bit_cast(V, pm), d1);
     }
 #pragma unroll
-    for (int t = 0; t < T; t++) {
-#pragma unroll
-      for (int e = 0; e < 4; e++) {
-        const float2 f = lut[(b.s[t] >> (8 * e)) & 0xFFu];
-        acc[t] = fmaf(d0[t][e], f.x, acc[t]);
-        acc[t] = fmaf(d1[t][e], f.y, acc[t]);
-      }
+    for (int e = 0; e < 4; e++) {
+      const float2 f = lut[(sw >> (8 * e)) & 0xFFu];
+      acc[0] = fmaf(d0[e], f.x, acc[0]);
+      acc[0] = fmaf(d1[e], f.y, acc[0]);
     }
   };
 
-  for (int g = g0; g < g1; g += 2) {
-    load_group(b1, g + 1);
-    compute_group(b0, g);
-    load_group(b0, g + 2);
-    if (g + 1 < g1) compute_group(b1, g + 1);
+  for (int u = u0; u < u1; u += 2) {
+    uint8_t* sa = stage[wave][0];
+    store_unit(ra, sa);
+    load_unit(ra, u + 2);
+#pragma unroll
+    for (int gi = 0; gi < M; gi++) compute_group(sa, gi, xw + ((u - u0) * M + gi) * kSection);
+    if (u + 1 < u1) {
+      uint8_t* sb = stage[wave][1];
+      store_unit(rb, sb);
+      load_unit(rb, u + 3);
+#pragma unroll
+      for (int gi = 0; gi < M; gi++) compute_group(sb, gi, xw + ((u + 1 - u0) * M + gi) * kSection);
+    }
   }
 
 #pragma unroll
@@ -301,19 +332,22 @@ struct SmPlan {
   int64_t grid;
 };
 
-// Launch sizing: one 16-row tile per workgroup of KS waves, KS the smallest
-// power of two that puts about 8 waves on each CU, doubled while every wave
-// still keeps >= 8 K groups and the grid stays under ~32 waves per CU.
+// Launch sizing: one 16-row tile per workgroup of KS <= 8 waves, KS the
+// smallest power of two that puts about 8 waves on each CU, doubled while
+// every wave still keeps >= 8 K units and the grid stays under ~16 (one row)
+// or ~32 (two to four rows) waves per CU.
 SmPlan plan_smallm(int64_t m, int64_t n, int64_t k, int cus) {
   SmPlan p;
   p.mt = m <= 1 ? 1 : m <= 2 ? 2 : 4;
-  const int64_t ngroups = k / (256 / p.mt);
+  const int64_t nunits = k / 256;
   const int64_t tiles = (n + 15) / 16;
   p.t = 1;
   p.ks = 1;
-  while (p.ks < 16 && tiles * p.ks < 8LL * cus && ngroups / (2 * p.ks) >= 2) p.ks *= 2;
-  while (p.ks < 16 && ngroups / p.ks >= 8 && tiles * p.ks < 32LL * cus) p.ks *= 2;
-  p.gpw = (int)((ngroups + p.ks - 1) / p.ks);
+  while (p.ks < 8 && tiles * p.ks < 8LL * cus && nunits / (2 * p.ks) >= 2) p.ks *= 2;
+  const int64_t cap = (p.mt == 1 ? 16LL : 32LL) * cus;  // wider batches carry more LDS/epilogue work per byte
+  while (p.ks < 8 && nunits / p.ks >= 8 && tiles * p.ks < cap) p.ks *= 2;
+  const int64_t upw = (nunits + p.ks - 1) / p.ks;
+  p.gpw = (int)(upw * p.mt);  // K groups per wave (whole units)
   p.grid = tiles;
   return p;
 }
@@ -322,7 +356,7 @@ template <typename XT, int M, int T, int KS>
 hipError_t launch_cfg(const SmArgs& a, hipStream_t stream, int64_t grid) {
   auto kern = smallm_kernel<XT, M, T, KS>;
   const size_t lds = (size_t)KS * a.gpw * kSection;
-  if (lds + 2048 + KS * T * 256 > 65536) {
+  if (lds + 2048 + KS * T * 256 + KS * 2 * kStageBytes > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
@@ -337,7 +371,6 @@ hipError_t dispatch_ks(const SmArgs& a, const SmPlan& p, hipStream_t stream) {
     case 2: return launch_cfg<XT, M, T, 2>(a, stream, p.grid);
     case 4: return launch_cfg<XT, M, T, 4>(a, stream, p.grid);
     case 8: return launch_cfg<XT, M, T, 8>(a, stream, p.grid);
-    case 16: return launch_cfg<XT, M, T, 16>(a, stream, p.grid);
   }
   return hipErrorInvalidValue;
 }
@@ -355,12 +388,11 @@ hipError_t dispatch(const SmArgs& a, const SmPlan& p, hipStream_t stream) {
 bool smallm_supported(int64_t m, int64_t n, int64_t k) {
   // K must fill whole groups of the widest variant (256 elements for M = 1,
   // 64 for M = 4); row and x offsets must fit the 32-bit buffer offsets.
-  if (m < 1 || m > 4 || n < 1 || k < 256) return false;
+  if (m < 1 || m > 4 || n < 1 || k < 256 || k % 256 != 0) return false;
   const int mt = m <= 1 ? 1 : m <= 2 ? 2 : 4;
-  if (k % (256 / mt) != 0) return false;
   if (32LL * k / 2 >= (1LL << 30)) return false;
-  // x of all K groups staged in LDS: at most 120 KiB per workgroup
-  return (k / (256 / mt) + 16) * kSection <= 120 * 1024;
+  // x of all K groups staged in LDS next to the weight stages of up to 8 waves
+  return (k / (256 / mt) + 8) * kSection <= 100 * 1024;
 }
 
 hipError_t launch_smallm(const void* x, int x_dtype, int64_t m, const PackedView& w, void* y,
