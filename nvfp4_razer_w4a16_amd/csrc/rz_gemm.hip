@@ -615,6 +615,199 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const XT* __restrict__
   }
 }
 
+// ---- batches of 5..32 rows: weight-streaming MFMA, x unit shared in LDS ---------
+//
+// HBM-bound like the small-batch kernel, but x is dense: for every 256-element
+// K unit the workgroup stages x[M, 256] once in LDS (row stride 528 bytes, so
+// the 16-byte fragment reads of 16 rows hit distinct banks) and its four
+// waves each stream TW 16-row weight tiles through a padded per-wave stage
+// (coalesced 16-byte loads covering whole 128-byte row segments).  Lane
+// (q, c) decodes 64 elements of weight row c -- value * sb with the remapped
+// code replaced by SV * sb (decode_dword) -- into the B operands of 8
+// v_mfma_f32_16x16x32 MFMAs (K slot 8q + t of MFMA i = element 64q + 8i + t
+// of the unit), and reads the matching x fragments as A.  The next unit's
+// loads are in flight during each unit; a global K split, when the rows are
+// too few to fill the GPU, goes through fp32 partials and skinny_reduce_kernel.
+constexpr int kBxRow = 256 + 8;                    // staged x halves per row
+constexpr int kBStage = 16 * 144 + 16 * 16;        // one 16-row tile unit: codes + scales
+
+template <typename XT, int KIND, int MT, int TW>
+__global__ __launch_bounds__(256) void gemm_batch_kernel(const XT* __restrict__ x, int m,
+                                                         const uint8_t* __restrict__ codes,
+                                                         const uint8_t* __restrict__ scales,
+                                                         const float* __restrict__ ts, int64_t n,
+                                                         int64_t k, float m0, float m1, int wg_rows,
+                                                         int upw, float* __restrict__ partial,
+                                                         void* __restrict__ y, int ydt) {
+  typedef typename Mfma16<XT>::V V;
+  typedef __amdgpu_buffer_rsrc_t Rsrc;
+  constexpr int kOob = 0x40000000;
+  __shared__ float2 lut[256];  // scale byte -> (sb, SV * sb bits ^ 0x8000 in both halves)
+  __shared__ __attribute__((aligned(16))) XT xs[2][MT * 16][kBxRow];
+  __shared__ __attribute__((aligned(16))) uint8_t stage[4][2][TW][kBStage];
+  {
+    const uint32_t b = threadIdx.x;
+    const float sb = scale_of_byte<KIND>(b);
+    const uint32_t svd = bits16<XT>(special_of_byte<KIND>(b, m0, m1) * sb) ^ 0x8000u;
+    lut[b] = make_float2(sb, __builtin_bit_cast(float, svd | (svd << 16)));
+  }
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = lane & 15, q = lane >> 4;
+  const int sid = blockIdx.x / wg_rows;                       // K split index
+  const int64_t row0 = (int64_t)(blockIdx.x % wg_rows) * (64 * TW) + wave * (16 * TW);
+  const int nunits = (int)(k / 256);
+  const int u0 = sid * upw, u1 = min(nunits, u0 + upw);
+  const int rcb = (int)(k / 2), rsb = (int)(k / 16);
+  const int rows_w = (int)max((int64_t)0, min((int64_t)(16 * TW), n - row0));
+  const Rsrc crs = __builtin_amdgcn_make_buffer_rsrc((void*)(codes + (row0 < n ? row0 : 0) * rcb), (short)0,
+                                                     rows_w * rcb, 0x00020000);
+  const Rsrc srs = __builtin_amdgcn_make_buffer_rsrc((void*)(scales + (row0 < n ? row0 : 0) * rsb), (short)0,
+                                                     rows_w * rsb, 0x00020000);
+  const Rsrc xrs = __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, (int)((int64_t)m * k * 2), 0x00020000);
+
+  // per-unit loads: x chunks (MT * 16 rows x 32 chunks of 16 bytes, 2 * MT per
+  // thread), this wave's codes (lane i: row i >> 3 (+8), bytes 16 * (i & 7))
+  // and scales (lane i: row i >> 2, bytes 4 * (i & 3)) for each of its tiles
+  struct Regs {
+    u32x4_t xv[2 * MT];
+    u32x4_t c0[TW], c1[TW];
+    uint32_t s[TW];
+  };
+  int xvo[2 * MT];
+#pragma unroll
+  for (int j = 0; j < 2 * MT; j++) {
+    const int ch = tid + 256 * j, r = ch >> 5, cc = ch & 31;
+    xvo[j] = r < m ? (int)(((int64_t)r * k + cc * 8) * 2) : kOob;
+  }
+  const int lr = lane >> 3, lb = (lane & 7) * 16;
+  int cvo0[TW], cvo1[TW], svo[TW];
+#pragma unroll
+  for (int t = 0; t < TW; t++) {
+    cvo0[t] = 16 * t + lr < rows_w ? (16 * t + lr) * rcb + lb : kOob;
+    cvo1[t] = 16 * t + lr + 8 < rows_w ? (16 * t + lr + 8) * rcb + lb : kOob;
+    svo[t] = 16 * t + (lane >> 2) < rows_w ? (16 * t + (lane >> 2)) * rsb + (lane & 3) * 4 : kOob;
+  }
+  auto load_unit = [&](Regs& r, int u) {
+    const bool ok = u < u1;
+    const int xso = ok ? u * 512 : kOob, cso = ok ? u * 128 : kOob, sso = ok ? u * 16 : kOob;
+#pragma unroll
+    for (int j = 0; j < 2 * MT; j++) r.xv[j] = __builtin_amdgcn_raw_buffer_load_b128(xrs, xvo[j], xso, 0);
+#pragma unroll
+    for (int t = 0; t < TW; t++) {
+      r.c0[t] = __builtin_amdgcn_raw_buffer_load_b128(crs, cvo0[t], cso, 2);
+      r.c1[t] = __builtin_amdgcn_raw_buffer_load_b128(crs, cvo1[t], cso, 2);
+      r.s[t] = __builtin_amdgcn_raw_buffer_load_b32(srs, svo[t], sso, 0);
+    }
+  };
+  auto store_unit = [&](const Regs& r, int buf) {
+#pragma unroll
+    for (int j = 0; j < 2 * MT; j++) {
+      const int ch = tid + 256 * j;
+      *(u32x4_t*)(&xs[buf][ch >> 5][(ch & 31) * 8]) = r.xv[j];
+    }
+#pragma unroll
+    for (int t = 0; t < TW; t++) {
+      uint8_t* st = stage[wave][buf][t];
+      *(u32x4_t*)(st + lr * 144 + lb) = r.c0[t];
+      *(u32x4_t*)(st + (lr + 8) * 144 + lb) = r.c1[t];
+      *(uint32_t*)(st + 16 * 144 + lane * 4) = r.s[t];
+    }
+  };
+
+  floatx4 acc[TW][MT];
+#pragma unroll
+  for (int t = 0; t < TW; t++)
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) acc[t][mt] = (floatx4){0.f, 0.f, 0.f, 0.f};
+
+  auto compute_unit = [&](int buf) {
+#pragma unroll
+    for (int t = 0; t < TW; t++) {
+      const uint8_t* st = stage[wave][buf][t];
+      const u32x4_t lo = *(const u32x4_t*)(st + c * 144 + 32 * q);
+      const u32x4_t hi = *(const u32x4_t*)(st + c * 144 + 32 * q + 16);
+      const uint32_t sw = *(const uint32_t*)(st + 16 * 144 + c * 16 + 4 * q);
+      const uint32_t cw[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      float2 f[4];
+#pragma unroll
+      for (int b = 0; b < 4; b++) f[b] = lut[(sw >> (8 * b)) & 0xFFu];
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const uint4 bv = decode_dword<XT>(cw[i], f[i >> 1].x, __builtin_bit_cast(uint32_t, f[i >> 1].y));
+        const V bb = __builtin_bit_cast(V, bv);
+#pragma unroll
+        for (int mt = 0; mt < MT; mt++) {
+          const V xa = *(const V*)(&xs[buf][mt * 16 + c][64 * q + 8 * i]);
+          acc[t][mt] = Mfma16<XT>::run(xa, bb, acc[t][mt]);
+        }
+      }
+    }
+  };
+
+  Regs rg;
+  load_unit(rg, u0);
+  __syncthreads();  // lut
+  store_unit(rg, 0);
+  load_unit(rg, u0 + 1);
+  __syncthreads();
+  for (int u = u0; u < u1; u++) {
+    const int buf = (u - u0) & 1;
+    compute_unit(buf);
+    store_unit(rg, buf ^ 1);
+    load_unit(rg, u + 2);
+    __syncthreads();
+  }
+
+  // D layout: lane (q, c) holds rows 4q .. 4q+3 (x rows mt * 16 + ...) of column
+  // c (weight row row0 + 16 t + c)
+  const float st = *ts;
+#pragma unroll
+  for (int t = 0; t < TW; t++) {
+    const int64_t col = row0 + 16 * t + c;
+    if (col >= n) continue;
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const int xr = mt * 16 + 4 * q + e;
+        if (xr >= m) continue;
+        const float v = acc[t][mt][e];
+        if (partial) {
+          partial[((int64_t)sid * m + xr) * n + col] = v;
+        } else {
+          const int64_t o = (int64_t)xr * n + col;
+          if (ydt == kF32) ((float*)y)[o] = v * st;
+          else if (ydt == kF16) ((_Float16*)y)[o] = (_Float16)(v * st);
+          else ((__bf16*)y)[o] = (__bf16)(v * st);
+        }
+      }
+  }
+}
+
+struct BatchPlan {
+  int tw, split, upw;
+  int64_t wg_rows;
+};
+
+// One or two 16-row tiles per wave (two when the rows are plentiful, to share
+// each staged x unit over 128 rows); a global K split while the grid is under
+// ~1.5 workgroups per CU and every split keeps >= 4 units.
+static BatchPlan batch_plan(int64_t n, int64_t k) {
+  BatchPlan p;
+  const int64_t tiles = (n + 15) / 16;
+  const int64_t cus = device_cu_count();
+  p.tw = tiles >= 16 * cus ? 2 : 1;
+  p.wg_rows = (tiles + 4 * p.tw - 1) / (4 * p.tw);
+  const int64_t nunits = k / 256;
+  p.split = 1;
+  while (p.wg_rows * p.split * 2 <= 3 * cus && nunits / (2 * p.split) >= 4) p.split *= 2;
+  p.upw = (int)((nunits + p.split - 1) / p.split);
+  return p;
+}
+
+static bool use_batch(int64_t m, int64_t k) { return m >= 5 && m <= 32 && k >= 256 && k % 256 == 0 && k < (1LL << 24); }
+
 template <typename OT>
 __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restrict__ partial,
                                                             int split, int64_t mn,
@@ -636,6 +829,10 @@ static bool use_smallm(int64_t m, int64_t n, int64_t k) {
 
 size_t gemm_ws_bytes(int64_t m, int64_t n, int64_t k) {
   if (use_smallm(m, n, k)) return 0;
+  if (use_batch(m, k)) {
+    const BatchPlan p = batch_plan(n, k);
+    return p.split > 1 ? (size_t)p.split * (size_t)m * (size_t)n * sizeof(float) : 0;
+  }
   if (m < 2 || m > 32 || k % 32 != 0) return 0;
   const SkinnyPlan p = skinny_plan(n, k);
   return (size_t)p.split * (size_t)m * (size_t)n * sizeof(float);
@@ -647,6 +844,31 @@ static hipError_t run_gemm(const XT* x, int64_t m, const PackedView& w, OT* y, v
   const int64_t n = w.rows, k = w.cols;
   const float m0 = 6.0f + 0.5f * (float)w.off_half[0];
   const float m1 = 6.0f + 0.5f * (float)w.off_half[KIND == kWeight ? 1 : 0];
+  if (use_batch(m, k)) {
+    const BatchPlan p = batch_plan(n, k);
+    float* partial = p.split > 1 ? (float*)ws : nullptr;
+    if (p.split > 1 && !partial) return hipErrorInvalidValue;
+    const int ydt = sizeof(OT) == 4 ? kF32 : __is_same(OT, _Float16) ? kF16 : kBF16;
+    const int64_t grid = p.wg_rows * p.split;
+#define RZ_BATCH(MT_, TW_)                                                                                \
+  hipLaunchKernelGGL((gemm_batch_kernel<XT, KIND, MT_, TW_>), dim3((unsigned)grid), dim3(256), 0, stream, x, \
+                     (int)m, w.codes, w.scales, w.tensor_scale, n, k, m0, m1, (int)p.wg_rows, p.upw,        \
+                     partial, (void*)y, ydt)
+    if (m <= 16) {
+      if (p.tw == 2) RZ_BATCH(1, 2); else RZ_BATCH(1, 1);
+    } else {
+      if (p.tw == 2) RZ_BATCH(2, 2); else RZ_BATCH(2, 1);
+    }
+#undef RZ_BATCH
+    if (p.split > 1) {
+      const int64_t mn = m * n;
+      int64_t g2 = (mn + 255) / 256;
+      if (g2 > 4LL * device_cu_count()) g2 = 4LL * device_cu_count();
+      hipLaunchKernelGGL((skinny_reduce_kernel<OT>), dim3((unsigned)g2), dim3(256), 0, stream, partial,
+                         p.split, mn, w.tensor_scale, y);
+    }
+    return hipGetLastError();
+  }
   if (m >= 2 && m <= 32 && k % 32 == 0 && ws != nullptr) {
     const SkinnyPlan p = skinny_plan(n, k);
     float* partial = (float*)ws;

@@ -398,7 +398,9 @@ def test_gemm_prefill_sampled():
                                        (512, 256, 192, torch.float16), (300, 520, 4096, torch.bfloat16),
                                        (3, 33, 320, torch.float16), (2, 50, 384, torch.bfloat16),
                                        (4, 1000, 4096, torch.float16), (2, 17, 256, torch.float16),
-                                       (3, 64, 960, torch.bfloat16), (2, 40, 320, torch.bfloat16)])
+                                       (3, 64, 960, torch.bfloat16), (2, 40, 320, torch.bfloat16),
+                                       (5, 100, 512, torch.bfloat16), (17, 77, 768, torch.float16),
+                                       (32, 4100, 1024, torch.bfloat16), (9, 16, 256, torch.float16)])
 def test_gemm_ragged_shapes(m, n, k, xdt):
     _need_gpu()
     rng = np.random.default_rng(m * 1000 + n + k)
