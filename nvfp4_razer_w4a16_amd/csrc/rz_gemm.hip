@@ -289,24 +289,38 @@ __global__ __launch_bounds__(256) void gemm_tile256_kernel(const XT* __restrict_
     uint32_t s;
   };
   Stage st0, st1;
-  const int64_t gn = n_base + tid;
+  // Raw buffer loads (descriptors cover this workgroup's rows only): rows past
+  // m or n read zero without a branch, so the wait counters stay exact.
+  typedef __amdgpu_buffer_rsrc_t Rsrc;
+  constexpr int kOob = 0x40000000;
+  const int rows_m = (int)min((int64_t)kTM, m - m_base), rows_n = (int)min((int64_t)kTN, n - n_base);
+  const Rsrc xr = __builtin_amdgcn_make_buffer_rsrc((void*)(x + m_base * k), (short)0,
+                                                    (int)(rows_m * k * (int64_t)sizeof(XT)), 0x00020000);
+  const Rsrc cr = __builtin_amdgcn_make_buffer_rsrc((void*)(codes + n_base * (k / 2)), (short)0,
+                                                    (int)(rows_n * (k / 2)), 0x00020000);
+  const Rsrc sr = __builtin_amdgcn_make_buffer_rsrc((void*)(scales + n_base * (k / 16)), (short)0,
+                                                    (int)(rows_n * (k / 16)), 0x00020000);
+  int xo[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const int idx = i * 256 + tid;
+    xo[i] = (idx >> 3) < rows_m ? (int)(((int64_t)(idx >> 3) * k + (idx & 7) * 8) * (int64_t)sizeof(XT)) : kOob;
+  }
+  const int co = tid < rows_n ? (int)((int64_t)tid * (k / 2)) : kOob;
+  const int so = tid < rows_n ? (int)((int64_t)tid * (k / 16)) : kOob;
   auto gload = [&](int kt, Stage& r) {
-    const int64_t k0 = (int64_t)kt * kTK;
+    const int k0 = kt * kTK;
 #pragma unroll
     for (int i = 0; i < 8; i++) {
-      const int idx = i * 256 + tid;
-      const int64_t gr = m_base + (idx >> 3);
-      r.a[i] = gr < m ? *(const uint4*)(x + gr * k + k0 + (idx & 7) * 8) : make_uint4(0, 0, 0, 0);
+      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(xr, xo[i], k0 * (int)sizeof(XT), 0);
+      r.a[i] = make_uint4(v[0], v[1], v[2], v[3]);
     }
-    if (gn < n) {
-      const uint4* cp = (const uint4*)(codes + gn * (k / 2) + k0 / 2);
-      r.c[0] = cp[0];
-      r.c[1] = cp[1];
-      r.s = *(const uint32_t*)(scales + gn * (k / 16) + k0 / 16);
-    } else {
-      r.c[0] = r.c[1] = make_uint4(0, 0, 0, 0);
-      r.s = 0;
-    }
+    // codes are read by every row tile of the grid: keep them cacheable
+    const u32x4_t c0 = __builtin_amdgcn_raw_buffer_load_b128(cr, co, k0 / 2, 0);
+    const u32x4_t c1 = __builtin_amdgcn_raw_buffer_load_b128(cr, co + 16, k0 / 2, 0);
+    r.c[0] = make_uint4(c0[0], c0[1], c0[2], c0[3]);
+    r.c[1] = make_uint4(c1[0], c1[1], c1[2], c1[3]);
+    r.s = __builtin_amdgcn_raw_buffer_load_b32(sr, so, k0 / 16, 0);
   };
   // part `blk` (0..3) of writing stage r into LDS buffer buf: two x vectors
   // and the decode of 16-element block blk of this thread's weight row.
@@ -407,6 +421,25 @@ __global__ __launch_bounds__(256) void gemm_tile256_kernel(const XT* __restrict_
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
         __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // up to five VALU
+      }
+#elif RZ_GEMM_SCHED == 4
+#pragma unroll
+      for (int g = 0; g < 16; g++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+      }
+#elif RZ_GEMM_SCHED == 5
+#pragma unroll
+      for (int g = 0; g < 8; g++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
+      }
+#elif RZ_GEMM_SCHED == 6
+#pragma unroll
+      for (int g = 0; g < 16; g++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // one LDS write
       }
 #endif
 #endif
@@ -790,23 +823,25 @@ struct BatchPlan {
   int64_t wg_rows;
 };
 
-// One or two 16-row tiles per wave (two when the rows are plentiful, to share
-// each staged x unit over 128 rows); a global K split while the grid is under
-// ~1.5 workgroups per CU and every split keeps >= 4 units.
-static BatchPlan batch_plan(int64_t n, int64_t k) {
+// One 16-row tile per wave; a global K split while the grid stays under a
+// row-count dependent target (more rows carry more MFMA and x work per weight
+// byte, so need fewer workgroups to cover HBM latency) and every split keeps
+// >= 2 units.
+static BatchPlan batch_plan(int64_t m, int64_t n, int64_t k) {
   BatchPlan p;
   const int64_t tiles = (n + 15) / 16;
   const int64_t cus = device_cu_count();
-  p.tw = tiles >= 16 * cus ? 2 : 1;
+  p.tw = 1;
   p.wg_rows = (tiles + 4 * p.tw - 1) / (4 * p.tw);
   const int64_t nunits = k / 256;
+  const int64_t target = m <= 8 ? 8 * cus : m <= 16 ? 4 * cus : 3 * cus / 2;
   p.split = 1;
-  while (p.wg_rows * p.split * 2 <= 3 * cus && nunits / (2 * p.split) >= 4) p.split *= 2;
+  while (p.wg_rows * p.split * 2 <= target && nunits / (2 * p.split) >= 2) p.split *= 2;
   p.upw = (int)((nunits + p.split - 1) / p.split);
   return p;
 }
 
-static bool use_batch(int64_t m, int64_t k) { return m >= 5 && m <= 32 && k >= 256 && k % 256 == 0 && k < (1LL << 24); }
+static bool use_batch(int64_t m, int64_t k) { return m >= 3 && m <= 32 && k >= 256 && k % 256 == 0 && k < (1LL << 24); }
 
 template <typename OT>
 __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restrict__ partial,
@@ -821,16 +856,19 @@ __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restr
   }
 }
 
-// Two to four rows go to the MFMA small-batch kernel (no workspace) where it
-// covers the shape; above that the skinny split-K kernel takes up to 32 rows.
+// Two rows go to the MFMA small-batch kernel (no workspace) where it covers the
+// shape, three and four rows too on weights under 128M elements (above that the
+// batch kernel streams them faster); the batch kernel takes up to 32 rows, the
+// skinny split-K kernel the shapes neither covers.
 static bool use_smallm(int64_t m, int64_t n, int64_t k) {
-  return m >= 2 && m <= 4 && smallm_supported(m, n, k);
+  if (m < 2 || m > 4 || !smallm_supported(m, n, k)) return false;
+  return m == 2 || n * k < (128LL << 20);
 }
 
 size_t gemm_ws_bytes(int64_t m, int64_t n, int64_t k) {
   if (use_smallm(m, n, k)) return 0;
   if (use_batch(m, k)) {
-    const BatchPlan p = batch_plan(n, k);
+    const BatchPlan p = batch_plan(m, n, k);
     return p.split > 1 ? (size_t)p.split * (size_t)m * (size_t)n * sizeof(float) : 0;
   }
   if (m < 2 || m > 32 || k % 32 != 0) return 0;
@@ -845,7 +883,7 @@ static hipError_t run_gemm(const XT* x, int64_t m, const PackedView& w, OT* y, v
   const float m0 = 6.0f + 0.5f * (float)w.off_half[0];
   const float m1 = 6.0f + 0.5f * (float)w.off_half[KIND == kWeight ? 1 : 0];
   if (use_batch(m, k)) {
-    const BatchPlan p = batch_plan(n, k);
+    const BatchPlan p = batch_plan(m, n, k);
     float* partial = p.split > 1 ? (float*)ws : nullptr;
     if (p.split > 1 && !partial) return hipErrorInvalidValue;
     const int ydt = sizeof(OT) == 4 ? kF32 : __is_same(OT, _Float16) ? kF16 : kBF16;
@@ -886,7 +924,7 @@ static hipError_t run_gemm(const XT* x, int64_t m, const PackedView& w, OT* y, v
                        p.split, mn, w.tensor_scale, y);
     return hipGetLastError();
   }
-  if (m >= kTM && k % kTK == 0) {
+  if (m >= kTM && k % kTK == 0 && (int64_t)kTM * k * (int64_t)sizeof(XT) < (1LL << 30)) {
     auto kern = gemm_tile256_kernel<XT, KIND, OT>;
     const size_t lds = (size_t)2 * (kTM + kTN) * kTS * sizeof(XT) + 256 * sizeof(float2);
     hipError_t e = hipFuncSetAttribute((const void*)kern,
