@@ -103,6 +103,9 @@ def source_hash(*names):
 
 
 COPY_BYTES = 512 << 20  # the calibration copy reads and writes this many bytes
+# razer_gemv runs gemv_kernel for more than 4096 rows and smallm_kernel up to 4096
+DECODE_KERNELS = ("gemv_kernel", "smallm_kernel")
+DECODE_SOURCES = ("rz_gemv.hip", "rz_smallm.hip", "rz_device.h")
 
 
 def copy_calibration():
@@ -116,18 +119,19 @@ def copy_calibration():
     log(f"copy calibration: 5 elementwise copies of {COPY_BYTES} bytes")
 
 
-def _counter_per_dispatch(path, name_part):
-    """Mean over dispatches of a kernel (name contains name_part) of the counter
-    summed over its instances, from a rocprofv3 counter_collection CSV."""
+def _counter_per_dispatch(path, name_parts):
+    """Mean over dispatches of the kernels whose names contain one of name_parts
+    of the counter summed over its instances, from a rocprofv3
+    counter_collection CSV."""
     import csv
     from collections import defaultdict
 
     per = defaultdict(float)
     for r in csv.DictReader(open(path)):
-        if name_part in r["Kernel_Name"]:
+        if any(p in r["Kernel_Name"] for p in name_parts):
             per[r["Dispatch_Id"]] += float(r["Counter_Value"])
     if not per:
-        raise SystemExit(f"no dispatch of {name_part!r} in {path}")
+        raise SystemExit(f"no dispatch of {name_parts!r} in {path}")
     return sum(per.values()) / len(per), len(per)
 
 
@@ -135,15 +139,15 @@ def traffic_summary(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv):
     """FETCH_SIZE / WRITE_SIZE are KiB per dispatch; each is scaled by what the
     same counter reads for the calibration copy (COPY_BYTES read, COPY_BYTES
     written), so the factor absorbs any per-channel sampling of the counter."""
-    f_k, nf = _counter_per_dispatch(fetch_csv, "gemv_kernel")
-    w_k, nw = _counter_per_dispatch(write_csv, "gemv_kernel")
-    cf, _ = _counter_per_dispatch(cal_fetch_csv, "elementwise")
-    cw, _ = _counter_per_dispatch(cal_write_csv, "elementwise")
+    f_k, nf = _counter_per_dispatch(fetch_csv, DECODE_KERNELS)
+    w_k, nw = _counter_per_dispatch(write_csv, DECODE_KERNELS)
+    cf, _ = _counter_per_dispatch(cal_fetch_csv, ("elementwise",))
+    cw, _ = _counter_per_dispatch(cal_write_csv, ("elementwise",))
     f_scale = COPY_BYTES / (cf * 1024.0)
     w_scale = COPY_BYTES / (cw * 1024.0)
     fetch = f_k * 1024.0 * f_scale
     write = w_k * 1024.0 * w_scale
-    src = source_hash("rz_gemv.hip", "rz_device.h")
+    src = source_hash(*DECODE_SOURCES)
     out = {"gemv_decode": {
         "source_hash": src, "bytes_per_launch": round(fetch + write),
         "fetch_bytes_per_launch": round(fetch), "write_bytes_per_launch": round(write),
@@ -379,11 +383,12 @@ def main():
     avg_us = ms_step * 1e3 / n_launch
     bytes_per_launch = step_bytes / n_launch
     achieved = bytes_per_launch / (avg_us * 1e-6) / 1e9
-    src = source_hash("rz_gemv.hip", "rz_device.h")
+    src = source_hash(*DECODE_SOURCES)
     traffic = load_traffic("gemv_decode", src)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "gemv_kernel (razer_gemv)", "avg_launch_us": round(avg_us, 3),
+                "kernel": "razer_gemv: gemv_kernel (qkv, gate, up) + smallm_kernel (down)",
+                "avg_launch_us": round(avg_us, 3),
                 "algorithmic_bytes_per_launch": bytes_per_launch}
 
     rows = None
