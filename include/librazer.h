@@ -134,7 +134,8 @@ razer_status razer_dequant(const razer_packed* t, void* out, razer_dtype out_dt,
 
 /* Batch-1 W4A16 product y[1, N] = x[1, K] * W^T with W decoded in registers
  * ([notes] Key design 3: weight-only GEMV kernels; [summary] §2.3).
- * x: device [K] in F16 or BF16.  w: packed weight [N, K].  y: device [N] in
+ * x: device [K] in F16 or BF16.  w: packed tensor [N, K] of either kind
+ * (weights, or an activation encoding used as the right operand).  y: device [N] in
  * F32, F16 or BF16.  Accumulation is fp32.  ws: at least
  * razer_workspace_bytes(RAZER_OP_GEMV, 1, N, K) bytes (may be 0 -> ws NULL). */
 razer_status razer_gemv(const void* x, razer_dtype x_dt, const razer_packed* w, void* y,
@@ -142,8 +143,8 @@ razer_status razer_gemv(const void* x, razer_dtype x_dt, const razer_packed* w, 
 
 /* Batched W4A16 product y[M, N] = x[M, K] * W^T ([notes] Key design 3;
  * [summary] §2.3: weight-only GEMM kernels for small and large batches).
- * x: device [m, K] row-major in F16 or BF16.  y: device [m, N] in F32, F16 or
- * BF16.  m >= 1; m == 1 runs the GEMV path.  ws: at least
+ * x: device [m, K] row-major in F16 or BF16.  w: packed tensor [N, K] of either
+ * kind.  y: device [m, N] in F32, F16 or BF16.  m >= 1; m == 1 runs the GEMV path.  ws: at least
  * razer_workspace_bytes(RAZER_OP_GEMM, m, N, K) bytes. */
 razer_status razer_gemm(const void* x, razer_dtype x_dt, int64_t m, const razer_packed* w, void* y,
                         razer_dtype y_dt, void* ws, size_t ws_bytes, void* stream);

@@ -154,17 +154,16 @@ __global__ __launch_bounds__(64 * KS) void smallm_kernel(SmArgs a) {
   constexpr int EPG = 256 / M;     // elements per K group
   constexpr int BPL = S / 4;       // blocks of a K group in one lane's slice
   constexpr int CB = 32 / M;       // code bytes of one lane per tile and group
-  static_assert(T == 1, "one 16-row tile per workgroup");
   __shared__ float2 lut[256];
   __shared__ float red[KS][T][64];
-  __shared__ __attribute__((aligned(16))) uint8_t stage[KS][2][kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t stage[KS][2][T][kStageBytes];
   extern __shared__ __attribute__((aligned(16))) uint8_t xs[];  // KS * gpw sections
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, q = lane >> 4;
-  const int64_t row0 = (int64_t)blockIdx.x * 16;
-  const int rows_wg = (int)min((int64_t)16, a.n - row0);
+  const int64_t row0 = (int64_t)blockIdx.x * (16 * T);
+  const int rows_wg = (int)min((int64_t)(16 * T), a.n - row0);
   const int rcb = (int)(a.k / 2), rsb = (int)(a.k / 16);
   const Rsrc crs = make_rsrc(a.codes + row0 * rcb, (int64_t)rows_wg * rcb);
   const Rsrc srs = make_rsrc(a.scales + row0 * rsb, (int64_t)rows_wg * rsb);
@@ -193,24 +192,34 @@ __global__ __launch_bounds__(64 * KS) void smallm_kernel(SmArgs a) {
   // Coalesced unit loads: codes, lane i -> row (i >> 3) (+8 for the second
   // load), bytes 16 * (i & 7); scales, lane i -> row i >> 2, bytes 4 * (i & 3).
   const int lr = lane >> 3, lb = (lane & 7) * 16;
-  const int cvo0 = lr < rows_wg ? lr * rcb + lb : kOob;
-  const int cvo1 = lr + 8 < rows_wg ? (lr + 8) * rcb + lb : kOob;
-  const int svo = (lane >> 2) < rows_wg ? (lane >> 2) * rsb + (lane & 3) * 4 : kOob;
+  int cvo0[T], cvo1[T], svo[T];
+#pragma unroll
+  for (int t = 0; t < T; t++) {
+    cvo0[t] = 16 * t + lr < rows_wg ? (16 * t + lr) * rcb + lb : kOob;
+    cvo1[t] = 16 * t + lr + 8 < rows_wg ? (16 * t + lr + 8) * rcb + lb : kOob;
+    svo[t] = 16 * t + (lane >> 2) < rows_wg ? (16 * t + (lane >> 2)) * rsb + (lane & 3) * 4 : kOob;
+  }
   struct UnitRegs {
-    u32x4_t c0, c1;
-    uint32_t s;
+    u32x4_t c0[T], c1[T];
+    uint32_t s[T];
   };
   auto load_unit = [&](UnitRegs& r, int u) {
     const bool ok = u < u1;
     const int cso = ok ? u * 128 : kOob, sso = ok ? u * 16 : kOob;
-    r.c0 = __builtin_amdgcn_raw_buffer_load_b128(crs, cvo0, cso, kNt);
-    r.c1 = __builtin_amdgcn_raw_buffer_load_b128(crs, cvo1, cso, kNt);
-    r.s = __builtin_amdgcn_raw_buffer_load_b32(srs, svo, sso, 0);
+#pragma unroll
+    for (int t = 0; t < T; t++) {
+      r.c0[t] = __builtin_amdgcn_raw_buffer_load_b128(crs, cvo0[t], cso, kNt);
+      r.c1[t] = __builtin_amdgcn_raw_buffer_load_b128(crs, cvo1[t], cso, kNt);
+      r.s[t] = __builtin_amdgcn_raw_buffer_load_b32(srs, svo[t], sso, 0);
+    }
   };
-  auto store_unit = [&](const UnitRegs& r, uint8_t* st) {
-    *(u32x4_t*)(st + lr * kUnitRow + lb) = r.c0;
-    *(u32x4_t*)(st + (lr + 8) * kUnitRow + lb) = r.c1;
-    *(uint32_t*)(st + 16 * kUnitRow + lane * 4) = r.s;
+  auto store_unit = [&](const UnitRegs& r, uint8_t (*st)[kStageBytes]) {
+#pragma unroll
+    for (int t = 0; t < T; t++) {
+      *(u32x4_t*)(st[t] + lr * kUnitRow + lb) = r.c0[t];
+      *(u32x4_t*)(st[t] + (lr + 8) * kUnitRow + lb) = r.c1[t];
+      *(uint32_t*)(st[t] + 16 * kUnitRow + lane * 4) = r.s[t];
+    }
   };
   int xo[G];  // LDS byte offset of this lane's A fragment inside a section
   {
@@ -249,59 +258,72 @@ __global__ __launch_bounds__(64 * KS) void smallm_kernel(SmArgs a) {
   __syncthreads();
 
   float acc[T];
-  acc[0] = 0.0f;
+#pragma unroll
+  for (int t = 0; t < T; t++) acc[t] = 0.0f;
 
   // One K group (gi-th of the unit staged at st): lane (q, c) reads row c's
-  // slice and the scale dword of its D rows, then G MFMA pairs and the epilogue.
-  auto compute_group = [&](const uint8_t* st, int gi, const uint8_t* sec) {
-    const uint8_t* crow = st + c * kUnitRow + gi * (128 / M) + q * CB;
-    uint32_t cw[8 / M];
-    if constexpr (M == 1) {
-      const u32x4_t lo = *(const u32x4_t*)crow, hi = *(const u32x4_t*)(crow + 16);
-      cw[0] = lo[0]; cw[1] = lo[1]; cw[2] = lo[2]; cw[3] = lo[3];
-      cw[4] = hi[0]; cw[5] = hi[1]; cw[6] = hi[2]; cw[7] = hi[3];
-    } else if constexpr (M == 2) {
-      const u32x4_t v = *(const u32x4_t*)crow;
-      cw[0] = v[0]; cw[1] = v[1]; cw[2] = v[2]; cw[3] = v[3];
-    } else {
-      const u32x2_t v = *(const u32x2_t*)crow;
-      cw[0] = v[0]; cw[1] = v[1];
+  // slice of every tile and the scale dword of its D rows, then G MFMA pairs
+  // per tile sharing one A fragment, and the epilogue.
+  auto compute_group = [&](uint8_t (*st)[kStageBytes], int gi, const uint8_t* sec) {
+    uint32_t cw[T][8 / M], sw[T];
+#pragma unroll
+    for (int t = 0; t < T; t++) {
+      const uint8_t* crow = st[t] + c * kUnitRow + gi * (128 / M) + q * CB;
+      if constexpr (M == 1) {
+        const u32x4_t lo = *(const u32x4_t*)crow, hi = *(const u32x4_t*)(crow + 16);
+        cw[t][0] = lo[0]; cw[t][1] = lo[1]; cw[t][2] = lo[2]; cw[t][3] = lo[3];
+        cw[t][4] = hi[0]; cw[t][5] = hi[1]; cw[t][6] = hi[2]; cw[t][7] = hi[3];
+      } else if constexpr (M == 2) {
+        const u32x4_t v = *(const u32x4_t*)crow;
+        cw[t][0] = v[0]; cw[t][1] = v[1]; cw[t][2] = v[2]; cw[t][3] = v[3];
+      } else {
+        const u32x2_t v = *(const u32x2_t*)crow;
+        cw[t][0] = v[0]; cw[t][1] = v[1];
+      }
+      sw[t] = *(const uint32_t*)(st[t] + 16 * kUnitRow + c * 16 + gi * S + (4 * q) % S);
     }
-    const uint32_t sw = *(const uint32_t*)(st + 16 * kUnitRow + c * 16 + gi * S + (4 * q) % S);
-    f32x4_t d0 = (f32x4_t){0.f, 0.f, 0.f, 0.f}, d1 = d0;
+    f32x4_t d0[T], d1[T];
+#pragma unroll
+    for (int t = 0; t < T; t++) {
+      d0[t] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+      d1[t] = d0[t];
+    }
 #pragma unroll
     for (int i = 0; i < G; i++) {
       const V xa = *(const V*)(sec + xo[i]);
-      const uint32_t w = cw[i];
-      const u32x4_t p = {Ops<XT>::template cvt<0>(w), Ops<XT>::template cvt<1>(w),
-                         Ops<XT>::template cvt<2>(w), Ops<XT>::template cvt<3>(w)};
-      const u32x4_t pm = {mark_remapped(p[0], Ops<XT>::kQuarterNeg2),
-                          mark_remapped(p[1], Ops<XT>::kQuarterNeg2),
-                          mark_remapped(p[2], Ops<XT>::kQuarterNeg2),
-                          mark_remapped(p[3], Ops<XT>::kQuarterNeg2)};
-      d0 = Ops<XT>::mfma(xa, __builtin_bit_cast(V, p), d0);
-      d1 = Ops<XT>::mfma(xa, __builtin_bit_cast(V, pm), d1);
+#pragma unroll
+      for (int t = 0; t < T; t++) {
+        const uint32_t w = cw[t][i];
+        const u32x4_t p = {Ops<XT>::template cvt<0>(w), Ops<XT>::template cvt<1>(w),
+                           Ops<XT>::template cvt<2>(w), Ops<XT>::template cvt<3>(w)};
+        const u32x4_t pm = {mark_remapped(p[0], Ops<XT>::kQuarterNeg2),
+                            mark_remapped(p[1], Ops<XT>::kQuarterNeg2),
+                            mark_remapped(p[2], Ops<XT>::kQuarterNeg2),
+                            mark_remapped(p[3], Ops<XT>::kQuarterNeg2)};
+        d0[t] = Ops<XT>::mfma(xa, __builtin_bit_cast(V, p), d0[t]);
+        d1[t] = Ops<XT>::mfma(xa, __builtin_bit_cast(V, pm), d1[t]);
+      }
     }
 #pragma unroll
-    for (int e = 0; e < 4; e++) {
-      const float2 f = lut[(sw >> (8 * e)) & 0xFFu];
-      acc[0] = fmaf(d0[e], f.x, acc[0]);
-      acc[0] = fmaf(d1[e], f.y, acc[0]);
-    }
+    for (int t = 0; t < T; t++)
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const float2 f = lut[(sw[t] >> (8 * e)) & 0xFFu];
+        acc[t] = fmaf(d0[t][e], f.x, acc[t]);
+        acc[t] = fmaf(d1[t][e], f.y, acc[t]);
+      }
   };
 
   for (int u = u0; u < u1; u += 2) {
-    uint8_t* sa = stage[wave][0];
-    store_unit(ra, sa);
+    store_unit(ra, stage[wave][0]);
     load_unit(ra, u + 2);
 #pragma unroll
-    for (int gi = 0; gi < M; gi++) compute_group(sa, gi, xw + ((u - u0) * M + gi) * kSection);
+    for (int gi = 0; gi < M; gi++) compute_group(stage[wave][0], gi, xw + ((u - u0) * M + gi) * kSection);
     if (u + 1 < u1) {
-      uint8_t* sb = stage[wave][1];
-      store_unit(rb, sb);
+      store_unit(rb, stage[wave][1]);
       load_unit(rb, u + 3);
 #pragma unroll
-      for (int gi = 0; gi < M; gi++) compute_group(sb, gi, xw + ((u + 1 - u0) * M + gi) * kSection);
+      for (int gi = 0; gi < M; gi++) compute_group(stage[wave][1], gi, xw + ((u + 1 - u0) * M + gi) * kSection);
     }
   }
 
@@ -356,7 +378,7 @@ template <typename XT, int M, int T, int KS>
 hipError_t launch_cfg(const SmArgs& a, hipStream_t stream, int64_t grid) {
   auto kern = smallm_kernel<XT, M, T, KS>;
   const size_t lds = (size_t)KS * a.gpw * kSection;
-  if (lds + 2048 + KS * T * 256 + KS * 2 * kStageBytes > 65536) {
+  if (lds + 2048 + KS * T * 256 + KS * 2 * T * kStageBytes > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
@@ -377,7 +399,7 @@ hipError_t dispatch_ks(const SmArgs& a, const SmPlan& p, hipStream_t stream) {
 
 template <typename XT>
 hipError_t dispatch(const SmArgs& a, const SmPlan& p, hipStream_t stream) {
-  if (p.t != 1) return hipErrorInvalidValue;
+  if (p.t != 1) return hipErrorInvalidValue;  // two tiles per workgroup measured slower
   if (p.mt == 1) return dispatch_ks<XT, 1, 1>(a, p, stream);
   if (p.mt == 2) return dispatch_ks<XT, 2, 1>(a, p, stream);
   return dispatch_ks<XT, 4, 1>(a, p, stream);

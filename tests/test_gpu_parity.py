@@ -411,3 +411,24 @@ def test_gemm_ragged_shapes(m, n, k, xdt):
     for odt in (torch.float32, torch.bfloat16):
         y = rz.razer_gemm(x.cuda(), to_device(ref), odt).cpu().double().numpy()
         assert_product_close(y, y_ref, nrm, f"gemm {m}x{n}x{k} out {odt}", odt)
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 200, 1024), (1, 5000, 512), (2, 96, 768), (4, 40, 512),
+                                   (8, 64, 512), (300, 260, 256)])
+def test_products_with_activation_kind_operand(m, n, k):
+    """The products take a packed tensor of either kind: an E4M3 / 1-bit
+    activation encoding used as the right operand goes through every product
+    kernel (GEMV, small batch, batch, prefill) against the oracle."""
+    _need_gpu()
+    rng = np.random.default_rng(n * 31 + k + m)
+    w = rng.normal(0, 1, (n, k)).astype(np.float32)
+    w[:, rng.choice(k, 4, replace=False)] *= 20.0
+    ref = oracle.quantize_act(w, (-2,))
+    x = torch.from_numpy(rng.normal(0, 1, (m, k)).astype(np.float32)).to(torch.bfloat16)
+    y_ref, nrm = oracle.gemm(as_f32(x), ref)
+    t = to_device(ref)
+    if m == 1:
+        y = rz.razer_gemv(x.cuda().reshape(-1), t, torch.float32).cpu().double().numpy()[None, :]
+    else:
+        y = rz.razer_gemm(x.cuda(), t, torch.float32).cpu().double().numpy()
+    assert_product_close(y, y_ref, nrm, f"act-kind operand {m}x{n}x{k}")
