@@ -308,19 +308,20 @@ __global__ __launch_bounds__(256) void gemm_tile256_kernel(const XT* __restrict_
   }
   const int co = tid < rows_n ? (int)((int64_t)tid * (k / 2)) : kOob;
   const int so = tid < rows_n ? (int)((int64_t)tid * (k / 16)) : kOob;
+  // issued in the order the next step consumes them: scale word, codes, x
   auto gload = [&](int kt, Stage& r) {
     const int k0 = kt * kTK;
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(xr, xo[i], k0 * (int)sizeof(XT), 0);
-      r.a[i] = make_uint4(v[0], v[1], v[2], v[3]);
-    }
+    r.s = __builtin_amdgcn_raw_buffer_load_b32(sr, so, k0 / 16, 0);
     // codes are read by every row tile of the grid: keep them cacheable
     const u32x4_t c0 = __builtin_amdgcn_raw_buffer_load_b128(cr, co, k0 / 2, 0);
     const u32x4_t c1 = __builtin_amdgcn_raw_buffer_load_b128(cr, co + 16, k0 / 2, 0);
     r.c[0] = make_uint4(c0[0], c0[1], c0[2], c0[3]);
     r.c[1] = make_uint4(c1[0], c1[1], c1[2], c1[3]);
-    r.s = __builtin_amdgcn_raw_buffer_load_b32(sr, so, k0 / 16, 0);
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(xr, xo[i], k0 * (int)sizeof(XT), 0);
+      r.a[i] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
   };
   // part `blk` (0..3) of writing stage r into LDS buffer buf: two x vectors
   // and the decode of 16-element block blk of this thread's weight row.

@@ -19,11 +19,18 @@
 //
 // Exact candidate comparison: moving element y (|y| = a) from its FP4 rounding
 // q to the special value M changes the block squared error by
-// (M - q)(M + q - 2a).  With M2 = 2M, Q2 = 2q (integers) and A = a * 2^22 (an
-// integer for every a > 2, which every moved element has), that change times
-// 2^23 is the integer (M2 - Q2) * ((M2 + Q2) * 2^21 - 2A).  Summing these in
-// int64 gives every candidate's error change exactly, so the argmin (ties to
-// the lowest candidate index) never depends on rounding or summation order.
+// (M - q)(M + q - 2a).  Only elements inside M's window (closer to M than to
+// either FP4 neighbour) move, and for them q is the grid point just below or
+// just above M.  With a power of two 2^s (s = 21, or 20 when the window starts
+// at 4 or above), V = 2^s (M + q) - 2^(s+1) a is an integer (a > 2 is a
+// multiple of 2^-22, a >= 4 of 2^-21) with |V| < 2^23, one fma computes it
+// exactly, and the change is (2M - 2q) V / 2^(s+1).  The products fit the
+// 24-bit multiplier and 16 of them fit int32, so every candidate's change is
+// summed exactly and the argmin (ties to the lowest candidate index) never
+// depends on rounding or summation order.  The bound on V needs every |y| of
+// the block below kFastCap, which fails only for blocks whose tensor scale is
+// subnormal; those blocks take the same comparison in int64 with
+// A = a * 2^22: (2M - 2q) * ((2M + 2q) * 2^21 - 2A).
 #include "rz_device.h"
 #include "rz_launch.h"
 
@@ -55,11 +62,54 @@ Candidate make_candidate(int off_half) {
 
 size_t quantize_ws_bytes() { return kAmaxMaxPartials * sizeof(uint32_t); }
 
+// Per candidate pair, for the int32 search (see the header comment).
+struct PairFast {
+  float lo, hi;     // window: lo < |y| < hi moves to M (lo = hi = 0: M is an FP4 value)
+  float thr;        // |y| >= thr rounds to the grid point above M (ties to the even code)
+  float klo, khi;   // 2^s (M + q) for q below / above M
+  float ascale;     // -2^(s+1)
+  int ddlo, ddhi;   // 2M - 2q for q below / above M (|.| <= 7)
+  int shift;        // 21 - s: brings the pair's sums to the common scale
+};
+
 struct EncodeParams {
   float lo[2], hi[2];
   int mag_x2[2];
+  PairFast f[2];
   int remap;
 };
+
+constexpr float kFastCap = 10.0f;
+
+static PairFast make_pair_fast(int off_half) {
+  static const double kGrid[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+  const Candidate c = make_candidate(off_half);
+  PairFast f{};
+  if (c.hi == 0.0f) return f;  // M on the FP4 grid: no element ever moves
+  const double M = 6.0 + off_half / 2.0;
+  int i = 0;  // index of the grid point just below M
+  while (i + 1 < 8 && kGrid[i + 1] < M) i++;
+  const double below = kGrid[i];
+  const bool top = i == 7;  // M above 6: every moved element rounds to 6
+  const double above = top ? below : kGrid[i + 1];
+  const int s = c.lo >= 4.0f ? 20 : 21;
+  f.lo = c.lo;
+  f.hi = c.hi;
+  if (top) {
+    f.thr = INFINITY;
+  } else {
+    const float mid = (float)((below + above) / 2.0);
+    // a tie rounds to the even grid index: up when i + 1 is even
+    f.thr = ((i + 1) % 2 == 0) ? mid : nextafterf(mid, INFINITY);
+  }
+  f.klo = (float)std::ldexp(M + below, s);
+  f.khi = (float)std::ldexp(M + above, s);
+  f.ascale = (float)-std::ldexp(1.0, s + 1);
+  f.ddlo = (int)(2.0 * (M - below));
+  f.ddhi = (int)(2.0 * (M - above));
+  f.shift = 21 - s;
+  return f;
+}
 
 // ---- pass 1: partial tensor amax ---------------------------------------------
 // |x| as fp32 bit patterns: unsigned order equals magnitude order, and NaN/Inf
@@ -171,6 +221,80 @@ template <int KIND> __device__ __forceinline__ float scale_of_code(uint32_t code
   return scale_of_byte<KIND>(code);
 }
 
+// d * v + c on the 24-bit multiplier (v_mad_i32_i24 reads the low 24 bits of
+// d and v, sign-extended).  Written out because the compiler otherwise spends a
+// mask or sign-extension on an operand whose range it cannot see.
+__device__ __forceinline__ int mad_i24(int d, int v, int c) {
+  int r;
+  asm("v_mad_i32_i24 %0, %1, %2, %3" : "=v"(r) : "v"(d), "v"(v), "v"(c));
+  return r;
+}
+
+// Fast exact search (int32 sums, see the header comment) and the remap of the
+// chosen candidate's elements to code 0b1000.  Returns the candidate index.
+template <int KIND>
+__device__ __forceinline__ uint32_t search_fast(const float (&y)[16], uint32_t (&w)[2],
+                                                const EncodeParams& prm) {
+  constexpr int kPairs = KIND == kWeight ? 2 : 1;
+  int pos[kPairs], neg[kPairs];  // summed changes of the +M and -M candidates
+  uint32_t bits[kPairs];         // bit j: element j is inside the pair's window
+#pragma unroll
+  for (int p = 0; p < kPairs; p++) pos[p] = neg[p] = 0, bits[p] = 0u;
+#pragma unroll
+  for (int p = 0; p < kPairs; p++) {
+    const PairFast& f = prm.f[p];
+    const int dlo = f.ddlo, dhi = f.ddhi;
+#pragma unroll
+    for (int j = 15; j >= 0; j--) {
+      const float a = fabsf(y[j]);
+      const bool in = a > f.lo && a < f.hi;
+      const bool up = a >= f.thr;
+      const float k = up ? f.khi : f.klo;
+      const int d = in ? (up ? dhi : dlo) : 0;
+      if constexpr (kPairs == 1) {
+        // one sum: sign(y) * V from the fma with sign(y) * 2^s (M + q), so
+        // pos[0] accumulates (+M change) - (-M change)
+        const float ks = __builtin_bit_cast(
+            float, __builtin_bit_cast(uint32_t, k) | (__builtin_bit_cast(uint32_t, y[j]) & 0x80000000u));
+        pos[p] = mad_i24(d, (int)__builtin_fmaf(y[j], f.ascale, ks), pos[p]);
+      } else {
+        const int t = mad_i24(d, (int)__builtin_fmaf(a, f.ascale, k), 0);
+        pos[p] += t;  // all moved elements here; the -M part is taken out below
+        neg[p] += y[j] < 0.0f ? t : 0;
+      }
+      bits[p] = bits[p] + bits[p] + (in ? 1u : 0u);
+    }
+    if constexpr (kPairs == 2) pos[p] -= neg[p];
+  }
+  // candidates +M0, -M0 (, +M1, -M1): lowest change wins, ties to the lower index
+  uint32_t sel = 0u;
+  if constexpr (kPairs == 1) {
+    sel = pos[0] > 0 ? 1u : 0u;  // (+M change) > (-M change)
+  } else {
+    int best = pos[0] * (1 << prm.f[0].shift);
+    const int c1 = neg[0] * (1 << prm.f[0].shift);
+    const int c2 = pos[1] * (1 << prm.f[1].shift);
+    const int c3 = neg[1] * (1 << prm.f[1].shift);
+    if (c1 < best) best = c1, sel = 1u;
+    if (c2 < best) best = c2, sel = 2u;
+    if (c3 < best) best = c3, sel = 3u;
+  }
+  // elements of the chosen pair's window whose sign matches the candidate
+  // (the sign is bit 3 of their nonzero FP4 code) become code 0b1000
+  const uint32_t b = (kPairs == 2 && (sel >> 1)) ? bits[kPairs - 1] : bits[0];
+  const uint32_t keep = (sel & 1u) ? 0u : 0x11111111u;
+#pragma unroll
+  for (int h = 0; h < 2; h++) {
+    uint32_t x = (b >> (8 * h)) & 0xFFu;  // element 8h + i -> bit 4i
+    x = (x | (x << 12)) & 0x000F000Fu;
+    x = (x | (x << 6)) & 0x03030303u;
+    x = (x | (x << 3)) & 0x11111111u;
+    const uint32_t hit = x & ((w[h] >> 3) ^ keep);
+    w[h] = (w[h] & ~(hit * 15u)) | (hit << 3);
+  }
+  return sel;
+}
+
 template <int KIND>
 __device__ __forceinline__ void encode_block(const float (&xf)[16], float amax, float st,
                                              const EncodeParams& prm, uint2& cw, uint32_t& sbyte) {
@@ -208,7 +332,9 @@ __device__ __forceinline__ void encode_block(const float (&xf)[16], float amax, 
     w[h] &= ~(~nz & 0x88888888u);                            // -0 -> +0
   }
   uint32_t sel = 0u;
-  if (prm.remap) {
+  if (prm.remap && amax_b * rcp < kFastCap) {
+    sel = search_fast<KIND>(y, w, prm);
+  } else if (prm.remap) {
     long long acc[2 * kPairs];
 #pragma unroll
     for (int c = 0; c < 2 * kPairs; c++) acc[c] = 0;
@@ -305,6 +431,7 @@ static hipError_t run_quantize(const T* x, const PackedView& out, uint32_t* part
     prm.lo[p] = c.lo;
     prm.hi[p] = c.hi;
     prm.mag_x2[p] = c.mag_x2;
+    prm.f[p] = make_pair_fast(out.off_half[p < npairs ? p : 0]);
   }
   prm.remap = (out.flags & 1u) ? 0 : 1;
   int64_t g2 = (nblk + 255) / 256;
