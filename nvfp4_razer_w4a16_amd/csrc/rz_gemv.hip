@@ -15,6 +15,9 @@
 //     wave's K slice, so every 16-byte code load is one coalesced 1 KiB wave
 //     access; for long rows the K range is split over KS waves of a workgroup
 //     and their row sums are added in LDS;
+//   - the scale bytes of a row quad arrive with one 8- or 4-byte load per lane
+//     (issued before the codes) and reach their lanes through a per-wave LDS
+//     stage, instead of a 1- or 2-byte load per lane and row;
 //   - codes become fp16/bf16 pairs with the gfx950 packed FP4 conversion and
 //     are contracted with x by v_dot2 (fp32 accumulate).  The remapped code
 //     0b1000 converts to -0 (0x8000), the smallest pair half when read as
@@ -152,24 +155,62 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, kRsrcWord3);
 }
 
+// Codes of one chunk (32 or 16 elements) of one row.
 template <int UNIT> struct Chunk;
-template <> struct Chunk<2> {  // 32 elements: 16 code bytes, 2 scale bytes
+template <> struct Chunk<2> {  // 32 elements: 16 code bytes
   u32x4_t c;
-  uint32_t s;
-  __device__ __forceinline__ void load(Rsrc cr, Rsrc sr, int coff, int soff) {
+  __device__ __forceinline__ void load(Rsrc cr, int coff) {
     c = __builtin_amdgcn_raw_buffer_load_b128(cr, coff, 0, kNt);
-    s = __builtin_amdgcn_raw_buffer_load_b16(sr, soff, 0, 0);
   }
   __device__ __forceinline__ uint32_t w(int j) const { return c[j]; }
 };
-template <> struct Chunk<1> {  // 16 elements: 8 code bytes, 1 scale byte
+template <> struct Chunk<1> {  // 16 elements: 8 code bytes
   u32x2_t c;
-  uint32_t s;
-  __device__ __forceinline__ void load(Rsrc cr, Rsrc sr, int coff, int soff) {
+  __device__ __forceinline__ void load(Rsrc cr, int coff) {
     c = __builtin_amdgcn_raw_buffer_load_b64(cr, coff, 0, kNt);
-    s = __builtin_amdgcn_raw_buffer_load_b8(sr, soff, 0, 0);
   }
   __device__ __forceinline__ uint32_t w(int j) const { return c[j]; }
+};
+
+// Scale bytes of a row quad, 4 * UNIT per lane: lane l holds bytes
+// 4 * UNIT * (l % 16) .. of row l / 16's segment (the 64 * UNIT bytes that
+// cover one chunk index of all 64 lanes).  One wide load per lane replaces a
+// 1- or 2-byte load per lane and row; the bytes reach their lanes through a
+// per-wave LDS stage.
+template <int UNIT, bool WIDE> struct ScaleWord;
+template <> struct ScaleWord<2, true> {
+  u32x2_t v;
+  __device__ __forceinline__ void load(Rsrc sr, int off) { v = __builtin_amdgcn_raw_buffer_load_b64(sr, off, 0, 0); }
+  __device__ __forceinline__ void store(uint8_t* p) const { *(u32x2_t*)p = v; }
+};
+template <> struct ScaleWord<1, true> {
+  uint32_t v;
+  __device__ __forceinline__ void load(Rsrc sr, int off) { v = __builtin_amdgcn_raw_buffer_load_b32(sr, off, 0, 0); }
+  __device__ __forceinline__ void store(uint8_t* p) const { *(uint32_t*)p = v; }
+};
+// Scale rows whose stride breaks the wide loads' alignment: the same bytes
+// with 2- or 1-byte loads.
+template <> struct ScaleWord<2, false> {
+  uint32_t h[4];
+  __device__ __forceinline__ void load(Rsrc sr, int off) {
+#pragma unroll
+    for (int j = 0; j < 4; j++) h[j] = __builtin_amdgcn_raw_buffer_load_b16(sr, off, 2 * j, 0);
+  }
+  __device__ __forceinline__ void store(uint8_t* p) const {
+#pragma unroll
+    for (int j = 0; j < 4; j++) *(uint16_t*)(p + 2 * j) = (uint16_t)h[j];
+  }
+};
+template <> struct ScaleWord<1, false> {
+  uint32_t b[4];
+  __device__ __forceinline__ void load(Rsrc sr, int off) {
+#pragma unroll
+    for (int j = 0; j < 4; j++) b[j] = __builtin_amdgcn_raw_buffer_load_b8(sr, off, j, 0);
+  }
+  __device__ __forceinline__ void store(uint8_t* p) const {
+#pragma unroll
+    for (int j = 0; j < 4; j++) p[j] = (uint8_t)b[j];
+  }
 };
 
 constexpr int kGemvMaxRpw = 64;  // rows per workgroup (bounds the LDS partials)
@@ -179,12 +220,14 @@ constexpr int kGemvMaxRpw = 64;  // rows per workgroup (bounds the LDS partials)
 // multiple of 4) and walks them four at a time; within a row, wave (ks, rg)
 // takes chunks (i * KS + ks) * 64 + lane for i < CPL.  The loads of the next
 // NQ - 1 row quads are in flight while a quad is decoded.
-template <typename XT, int UNIT, int CPL, int KS, int NQ>
+template <typename XT, int UNIT, int CPL, int KS, int NQ, bool SW>
 __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   typedef typename Pair<XT>::T P;
   constexpr int kPairs = 8 * UNIT;  // x pairs per chunk
+  constexpr int kSeg = 64 * UNIT;  // scale bytes of one chunk index, one row
   __shared__ float2 lut[256];
   __shared__ float part[KS > 1 ? KS * kGemvMaxRpw : 1];
+  __shared__ __attribute__((aligned(16))) uint8_t sstage[4][CPL][4][kSeg];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -202,15 +245,16 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   // Chunks of this wave: ni of them hold any valid lane (wave-uniform); a
   // lane past K reads nothing (offset kOob) and holds zero x.
   int ni = 0;
-  int coff[CPL], soff[CPL];
+  int coff[CPL], sgo[CPL];
 #pragma unroll
   for (int i = 0; i < CPL; i++) {
     const int c0 = (i * KS + ks) * 64;
     if (c0 < a.nchunk) ni = i + 1;
     const int c = c0 + lane;
-    const bool ok = c < a.nchunk;
-    coff[i] = ok ? c * 8 * UNIT : kOob;
-    soff[i] = ok ? c * UNIT : kOob;
+    coff[i] = c < a.nchunk ? c * 8 * UNIT : kOob;
+    // scale segment i, lane's 4 * UNIT bytes; past the row's end reads zero
+    const int sb0 = (c0 + 4 * (lane & 15)) * UNIT;
+    sgo[i] = c0 + 4 * (lane & 15) < a.nchunk ? sb0 : kOob;
   }
 
   // x slice in registers, requested before any weight bytes.
@@ -226,17 +270,24 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   }
 
   Chunk<UNIT> buf[NQ][4][CPL];
-  auto load_quad = [&](Chunk<UNIT> (*b)[CPL], int q) {
+  ScaleWord<UNIT, SW> sbuf[NQ][CPL];
+  // scale bytes first: the table lookups wait on them, the dots on the codes
+  auto load_quad = [&](int slot, int q) {
+    const int js = 4 * q + (lane >> 4);
+    const int sbase = js < nrw ? (r0 + js) * rsb : kOob;
+#pragma unroll
+    for (int i = 0; i < CPL; i++) sbuf[slot][i].load(srs, sbase + sgo[i]);
 #pragma unroll
     for (int r = 0; r < 4; r++) {
       const int j = 4 * q + r;
-      const int cb = j < nrw ? (r0 + j) * rcb : kOob, sbase = j < nrw ? (r0 + j) * rsb : kOob;
+      const int cb = j < nrw ? (r0 + j) * rcb : kOob;
 #pragma unroll
-      for (int i = 0; i < CPL; i++) b[r][i].load(crs, srs, cb + coff[i], sbase + soff[i]);
+      for (int i = 0; i < CPL; i++) buf[slot][r][i].load(crs, cb + coff[i]);
     }
   };
+  // the first NQ quads are requested before the table is built
 #pragma unroll
-  for (int s = 0; s < NQ - 1; s++) load_quad(buf[s], s);
+  for (int s = 0; s < NQ; s++) load_quad(s, s);
 
   {
     const uint32_t i = threadIdx.x;
@@ -253,13 +304,16 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   __syncthreads();
   const float st = *a.ts;
   const int my_row = quad_row(lane);  // the row of the quad this lane's sum belongs to
+  uint8_t (*stg)[4][kSeg] = sstage[wave];
 
   for (int q0 = 0; q0 < nq; q0 += NQ) {
 #pragma unroll
     for (int s = 0; s < NQ; s++) {
       const int q = q0 + s;
-      load_quad(buf[(s + NQ - 1) % NQ], q + NQ - 1);
       if (q < nq) {
+        // this quad's scale bytes to their lanes (one wave: no barrier)
+#pragma unroll
+        for (int i = 0; i < CPL; i++) sbuf[s][i].store(stg[i][lane >> 4] + 4 * UNIT * (lane & 15));
         float acc[4];
 #pragma unroll
         for (int r = 0; r < 4; r++) {
@@ -268,17 +322,20 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
           for (int i = 0; i < CPL; i++) {
             if (i < ni) {
               const Chunk<UNIT>& ch = buf[s][r][i];
+              const uint32_t sw = UNIT == 2 ? (uint32_t)*(const uint16_t*)(stg[i][r] + 2 * lane)
+                                            : (uint32_t)stg[i][r][lane];
 #pragma unroll
               for (int u = 0; u < UNIT; u++) {
                 float d0, d1;
                 block_dot<XT>(ch.w(2 * u), ch.w(2 * u + 1), xv[i] + 8 * u, d0, d1);
-                const float2 f = lut[(ch.s >> (8 * u)) & 0xFFu];
+                const float2 f = lut[(sw >> (8 * u)) & 0xFFu];
                 acc[r] = fmaf(d0, f.x, acc[r]);
                 acc[r] = fmaf(d1, f.y, acc[r]);
               }
             }
           }
         }
+        load_quad(s, q + NQ);  // refill the slot
         const float v = quad_sum(acc);
         const int j = 4 * q + my_row;
         if ((lane & 15) == 0 && j < nrw) {
@@ -310,8 +367,13 @@ template <typename XT, int UNIT, int CPL, int KS, int NQ>
 static hipError_t launch_cfg(GemvArgs a, const GemvPlan& p, hipStream_t stream) {
   a.rpw = p.rpw;
   a.rpwv = p.rpwv;
-  hipLaunchKernelGGL((gemv_kernel<XT, UNIT, CPL, KS, NQ>), dim3((unsigned)p.grid), dim3(256), 0,
-                     stream, a);
+  // wide scale loads need the scale row stride (K / 16 bytes) to keep 4 * UNIT alignment
+  if ((a.k / 16) % (4 * UNIT) == 0)
+    hipLaunchKernelGGL((gemv_kernel<XT, UNIT, CPL, KS, NQ, true>), dim3((unsigned)p.grid), dim3(256), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL((gemv_kernel<XT, UNIT, CPL, KS, NQ, false>), dim3((unsigned)p.grid), dim3(256), 0,
+                       stream, a);
   return hipGetLastError();
 }
 
