@@ -851,8 +851,31 @@ __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restr
                                                             OT* __restrict__ y) {
   const float st = *ts;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < mn; i += (int64_t)gridDim.x * 256) {
+    // the split partials are independent loads: issue eight at a time
     float v = 0.0f;
-    for (int s = 0; s < split; s++) v += partial[(int64_t)s * mn + i];
+    int s = 0;
+    for (; s + 8 <= split; s += 8) {
+      float p[8];
+#pragma unroll
+      for (int j = 0; j < 8; j++) p[j] = partial[(int64_t)(s + j) * mn + i];
+#pragma unroll
+      for (int j = 0; j < 8; j++) v += p[j];
+    }
+    if (s + 4 <= split) {
+      float p[4];
+#pragma unroll
+      for (int j = 0; j < 4; j++) p[j] = partial[(int64_t)(s + j) * mn + i];
+#pragma unroll
+      for (int j = 0; j < 4; j++) v += p[j];
+      s += 4;
+    }
+    if (s + 2 <= split) {
+      const float p0 = partial[(int64_t)s * mn + i], p1 = partial[(int64_t)(s + 1) * mn + i];
+      v += p0;
+      v += p1;
+      s += 2;
+    }
+    if (s < split) v += partial[(int64_t)s * mn + i];
     y[i] = from_f32<OT>(v * st);
   }
 }
