@@ -1,4 +1,4 @@
-// rz_dequant.hip -- RaZeR decoder for gfx950 (streaming, one block per thread).
+// rz_dequant.hip -- RaZeR decoder for gfx950 (streaming, eight elements per lane and step).
 //
 // "RaZeR: Pushing the Limits of NVFP4 Quantization with Redundant Zero
 // Remapping" (papernotes.org notes), Key design 3 and the complete example:
@@ -17,50 +17,83 @@ template <> __device__ __forceinline__ float to_out<float>(float v) { return v; 
 template <> __device__ __forceinline__ _Float16 to_out<_Float16>(float v) { return (_Float16)v; }
 template <> __device__ __forceinline__ __bf16 to_out<__bf16>(float v) { return (__bf16)v; }
 
+// Eight elements (one code dword, half a block) per lane and step, so each
+// wave's loads and stores are contiguous: 256 code bytes in, 1 KiB (16-bit)
+// or 2 KiB (fp32) out.  The gfx950 packed FP4 conversion gives the exact
+// values, with -0 for the remapped code; that -0 is detected on the converted
+// value before any scaling, so an underflowing product can never pass for it.
+template <typename OT> struct Out8;
+template <> struct Out8<float> {
+  static __device__ __forceinline__ void store(float* o, const float (&v)[8]) {
+    ((float4*)o)[0] = make_float4(v[0], v[1], v[2], v[3]);
+    ((float4*)o)[1] = make_float4(v[4], v[5], v[6], v[7]);
+  }
+};
+template <typename OT> struct Out8 {
+  static __device__ __forceinline__ void store(OT* o, const float (&v)[8]) {
+    OT h[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++) h[j] = to_out<OT>(v[j]);
+    *(uint4*)o = *(const uint4*)h;
+  }
+};
+
+constexpr int kDqUnroll = 4;  // code dwords in flight per lane
+
 template <int KIND, typename OT>
-__global__ __launch_bounds__(256) void dequant_kernel(const uint2* __restrict__ codes,
+__global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict__ codes,
                                                       const uint8_t* __restrict__ scales,
-                                                      const float* __restrict__ ts, int64_t nblk,
+                                                      const float* __restrict__ ts, int64_t ndw,
                                                       float m0, float m1, OT* __restrict__ out) {
   const float st = *ts;
   const int64_t stride = (int64_t)gridDim.x * 256;
-  for (int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x; b < nblk; b += stride) {
-    const uint2 cw = codes[b];
-    const uint32_t sbyte = scales[b];
-    const float sb = scale_of_byte<KIND>(sbyte);
-    const float sv = special_of_byte<KIND>(sbyte, m0, m1) * sb;
-    OT v[16];
+  for (int64_t d0 = (int64_t)blockIdx.x * 256 + threadIdx.x; d0 < ndw; d0 += kDqUnroll * stride) {
+    uint32_t w[kDqUnroll], sbyte[kDqUnroll];
 #pragma unroll
-    for (int j = 0; j < 16; j++) {
-      const uint32_t nib = ((j < 8 ? cw.x : cw.y) >> (4 * (j & 7))) & 15u;
-      // |FP4| * 2 from the magnitude field, then halve: exact small integers.
-      const float mag = (float)fp4_mag_x2(nib & 7u) * 0.5f;
-      float val = (nib & 8u) ? -mag : mag;
-      val = (nib == 8u) ? sv : val * sb;
-      v[j] = to_out<OT>(val * st);
+    for (int u = 0; u < kDqUnroll; u++) {
+      const int64_t d = d0 + u * stride;
+      w[u] = d < ndw ? codes[d] : 0u;
+      sbyte[u] = d < ndw ? scales[d >> 1] : 0u;
     }
-    OT* o = out + 16 * b;
-    if (sizeof(OT) == 4) {
 #pragma unroll
-      for (int i = 0; i < 4; i++) ((uint4*)o)[i] = ((uint4*)v)[i];
-    } else {
+    for (int u = 0; u < kDqUnroll; u++) {
+      const int64_t d = d0 + u * stride;
+      if (d >= ndw) break;
+      const float sb = scale_of_byte<KIND>(sbyte[u]);
+      const float svt = (special_of_byte<KIND>(sbyte[u], m0, m1) * sb) * st;
+      float v[8];
 #pragma unroll
-      for (int i = 0; i < 2; i++) ((uint4*)o)[i] = ((uint4*)v)[i];
+      for (int p = 0; p < 4; p++) {
+        float2_t f;
+        switch (p) {
+          case 0: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[u], 1.0f, 0); break;
+          case 1: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[u], 1.0f, 1); break;
+          case 2: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[u], 1.0f, 2); break;
+          default: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[u], 1.0f, 3); break;
+        }
+        // The halves pass through an empty asm before the -0 tests: without
+        // it this compiler folds the two tests of one conversion into one.
+        float f0 = f[0], f1 = f[1];
+        asm volatile("" : "+v"(f0), "+v"(f1));
+        v[2 * p] = __builtin_bit_cast(uint32_t, f0) == 0x80000000u ? svt : (f0 * sb) * st;
+        v[2 * p + 1] = __builtin_bit_cast(uint32_t, f1) == 0x80000000u ? svt : (f1 * sb) * st;
+      }
+      Out8<OT>::store(out + 8 * d, v);
     }
   }
 }
 
 template <int KIND, typename OT>
 static void run(const PackedView& t, OT* out, hipStream_t stream) {
-  const int64_t nblk = t.rows * t.cols / 16;
-  int64_t g = (nblk + 255) / 256;
+  const int64_t ndw = t.rows * t.cols / 8;
+  int64_t g = (ndw + 255) / 256;
   const int64_t cap = (int64_t)device_cu_count() * 16;
   if (g > cap) g = cap;
   if (g < 1) g = 1;
   const float m0 = 6.0f + 0.5f * (float)t.off_half[0];
   const float m1 = 6.0f + 0.5f * (float)t.off_half[KIND == kWeight ? 1 : 0];
   hipLaunchKernelGGL((dequant_kernel<KIND, OT>), dim3((unsigned)g), dim3(256), 0, stream,
-                     (const uint2*)t.codes, t.scales, t.tensor_scale, nblk, m0, m1, out);
+                     (const uint32_t*)t.codes, t.scales, t.tensor_scale, ndw, m0, m1, out);
 }
 
 hipError_t launch_dequant(const PackedView& t, void* out, int out_dtype, hipStream_t stream) {
