@@ -415,9 +415,9 @@ static hipError_t dispatch(const GemvArgs& a, const GemvPlan& p, hipStream_t str
 hipError_t launch_gemv(const void* x, int x_dtype, const PackedView& w, void* y, int y_dtype,
                        void*, size_t, hipStream_t stream) {
   if (w.rows <= 0) return hipSuccess;
-  // Up to 4096 rows the MFMA small-batch kernel is faster at M = 1 too (its
-  // K split keeps enough waves busy on few rows); above, this kernel is.
-  if (w.rows <= 4096 && smallm_supported(1, w.rows, w.cols))
+  // Long rows (K above 8192) on up to 4096 rows go to the MFMA small-batch
+  // kernel, whose K split keeps enough waves busy; measured faster there only.
+  if (w.rows <= 4096 && w.cols > 8192 && smallm_supported(1, w.rows, w.cols))
     return launch_smallm(x, x_dtype, 1, w, y, y_dtype, stream);
   GemvArgs a;
   a.x = x;
