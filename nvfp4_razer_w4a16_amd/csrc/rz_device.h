@@ -51,6 +51,17 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
   return v;
 }
 
+// Order one wave's LDS writes before its later LDS reads of data written by
+// other lanes of the same wave (and those reads before the next writes).  The
+// LDS executes one wave's operations in issue order, so only the compiler has
+// to be kept from reordering them; it reasons per lane and would otherwise
+// move a read above a write it sees as independent.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // ---- block scale decode ------------------------------------------------------
 // E3M3 (weights): 3 exponent bits, bias 3, 3 mantissa bits, subnormals, max 30.
 // E4M3 (activations): OCP E4M3FN, bias 7, max 448.  The metadata bits of the

@@ -314,6 +314,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
         // this quad's scale bytes to their lanes (one wave: no barrier)
 #pragma unroll
         for (int i = 0; i < CPL; i++) sbuf[s][i].store(stg[i][lane >> 4] + 4 * UNIT * (lane & 15));
+        wave_lds_sync();
         float acc[4];
 #pragma unroll
         for (int r = 0; r < 4; r++) {
@@ -335,6 +336,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
             }
           }
         }
+        wave_lds_sync();       // stage reads done before the next quad's writes
         load_quad(s, q + NQ);  // refill the slot
         const float v = quad_sum(acc);
         const int j = 4 * q + my_row;

@@ -9,7 +9,8 @@
 // and Inf sort above every finite value) to the workspace.  No atomics, so
 // the workspace needs no clearing and the pass can be graph-captured.
 // Pass 2 (encode_kernel): every workgroup folds the partials into the tensor
-// amax, then encodes 16-element blocks, one block per thread:
+// amax, then encodes 16-element blocks, one block per lane (64 consecutive
+// blocks per wave and step, read with contiguous loads through LDS):
 //   st = amax / (6 * S_MAX); sb = nearest-even(S_MAX * amax_b / amax) on the
 //   E3M3 / E4M3 grid; y = x * (1 / (sb * st)); FP4 nearest-even codes; the
 //   special value whose block squared error is lowest replaces the redundant
@@ -162,43 +163,6 @@ __global__ __launch_bounds__(256) void amax_partial_kernel(const uint4* __restri
 }
 
 // ---- pass 2: block encode ----------------------------------------------------
-template <typename T> __device__ __forceinline__ void load_block(const T* p, float (&v)[16]);
-
-template <> __device__ __forceinline__ void load_block<float>(const float* p, float (&v)[16]) {
-  const float4* q = (const float4*)p;
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    float4 t = q[i];
-    v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
-  }
-}
-template <> __device__ __forceinline__ void load_block<__bf16>(const __bf16* p, float (&v)[16]) {
-  const uint4* q = (const uint4*)p;
-#pragma unroll
-  for (int i = 0; i < 2; i++) {
-    uint4 t = q[i];
-    uint32_t w[4] = {t.x, t.y, t.z, t.w};
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      v[8 * i + 2 * j] = u2f(w[j] << 16);
-      v[8 * i + 2 * j + 1] = u2f(w[j] & 0xFFFF0000u);
-    }
-  }
-}
-template <> __device__ __forceinline__ void load_block<_Float16>(const _Float16* p, float (&v)[16]) {
-  const uint4* q = (const uint4*)p;
-#pragma unroll
-  for (int i = 0; i < 2; i++) {
-    uint4 t = q[i];
-    uint32_t w[4] = {t.x, t.y, t.z, t.w};
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      v[8 * i + 2 * j] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[j] & 0xFFFFu));
-      v[8 * i + 2 * j + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[j] >> 16));
-    }
-  }
-}
-
 // Nearest-even block-scale code for v >= 0, saturating at the format maximum.
 // Normal range: keep 3 mantissa bits of the fp32 value with a round-to-even
 // carry; subnormal range: round v / quantum to an integer (v_rndne_f32).  The
@@ -233,7 +197,7 @@ __device__ __forceinline__ int mad_i24(int d, int v, int c) {
 // Fast exact search (int32 sums, see the header comment) and the remap of the
 // chosen candidate's elements to code 0b1000.  Returns the candidate index.
 template <int KIND>
-__device__ __forceinline__ uint32_t search_fast(const float (&y)[16], uint32_t (&w)[2],
+__device__ __forceinline__ uint32_t search_fast(const float (&y)[16], float ymax, uint32_t (&w)[2],
                                                 const EncodeParams& prm) {
   constexpr int kPairs = KIND == kWeight ? 2 : 1;
   int pos[kPairs], neg[kPairs];  // summed changes of the +M and -M candidates
@@ -244,6 +208,11 @@ __device__ __forceinline__ uint32_t search_fast(const float (&y)[16], uint32_t (
   for (int p = 0; p < kPairs; p++) {
     const PairFast& f = prm.f[p];
     const int dlo = f.ddlo, dhi = f.ddhi;
+    // ymax = max |y| of the block exactly (rounding is monotone): at or below
+    // the window no element moves, and a wave whose lanes all are skips the
+    // pair (the usual case for a pair above 6, reachable only from blocks
+    // whose scale rounded down to a subnormal code)
+    if (!(ymax > f.lo && f.hi > f.lo)) continue;
 #pragma unroll
     for (int j = 15; j >= 0; j--) {
       const float a = fabsf(y[j]);
@@ -332,8 +301,9 @@ __device__ __forceinline__ void encode_block(const float (&xf)[16], float amax, 
     w[h] &= ~(~nz & 0x88888888u);                            // -0 -> +0
   }
   uint32_t sel = 0u;
-  if (prm.remap && amax_b * rcp < kFastCap) {
-    sel = search_fast<KIND>(y, w, prm);
+  const float ymax = amax_b * rcp;
+  if (prm.remap && ymax < kFastCap) {
+    sel = search_fast<KIND>(y, ymax, w, prm);
   } else if (prm.remap) {
     long long acc[2 * kPairs];
 #pragma unroll
@@ -379,6 +349,39 @@ __device__ __forceinline__ void encode_block(const float (&xf)[16], float amax, 
   sbyte = (KIND == kWeight) ? (((sel & 1u) << 7) | ((sel >> 1) << 6) | scode) : ((sel << 7) | scode);
 }
 
+// Block values from the 16 input elements' bytes (fp32: 4 x 16 B, 16-bit: 2 x 16 B).
+template <typename T> __device__ __forceinline__ void unpack_block(const u32x4_t* q, float (&v)[16]);
+template <> __device__ __forceinline__ void unpack_block<float>(const u32x4_t* q, float (&v)[16]) {
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) v[4 * i + j] = u2f(q[i][j]);
+}
+template <> __device__ __forceinline__ void unpack_block<__bf16>(const u32x4_t* q, float (&v)[16]) {
+#pragma unroll
+  for (int i = 0; i < 2; i++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      v[8 * i + 2 * j] = u2f(q[i][j] << 16);
+      v[8 * i + 2 * j + 1] = u2f(q[i][j] & 0xFFFF0000u);
+    }
+}
+template <> __device__ __forceinline__ void unpack_block<_Float16>(const u32x4_t* q, float (&v)[16]) {
+#pragma unroll
+  for (int i = 0; i < 2; i++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      v[8 * i + 2 * j] = (float)__builtin_bit_cast(_Float16, (uint16_t)(q[i][j] & 0xFFFFu));
+      v[8 * i + 2 * j + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(q[i][j] >> 16));
+    }
+}
+
+// Each wave takes 64 consecutive blocks per step: its 16-byte loads cover the
+// blocks' bytes contiguously (1 KiB per instruction; a block per lane would
+// spread every instruction over 2-4 KiB), go to a per-wave LDS stage and come
+// back as one block per lane.  The next step's loads are in flight while a
+// step is encoded; the buffer descriptor is rebased per step, so a read past
+// the tensor returns zero and any tensor size works with 32-bit offsets.
 template <int KIND, typename T>
 __global__ __launch_bounds__(256) void encode_kernel(const T* __restrict__ x, int64_t nblk,
                                                      const uint32_t* __restrict__ partial,
@@ -386,6 +389,9 @@ __global__ __launch_bounds__(256) void encode_kernel(const T* __restrict__ x, in
                                                      uint8_t* __restrict__ scales,
                                                      float* __restrict__ ts_out, EncodeParams prm) {
   constexpr float kSMax = KIND == kWeight ? 30.0f : 448.0f;
+  constexpr int kBB = 16 * (int)sizeof(T);  // input bytes per block
+  constexpr int kNI = kBB * 64 / 1024;      // 16-byte loads per lane and step
+  __shared__ __attribute__((aligned(16))) uint8_t stage[4][64 * kBB];
   uint32_t m = 0u;
   for (int i = threadIdx.x; i < npartial; i += 256) m = max(m, partial[i]);
   m = wave_max_u32(m);
@@ -399,17 +405,51 @@ __global__ __launch_bounds__(256) void encode_kernel(const T* __restrict__ x, in
   if (blockIdx.x == 0 && threadIdx.x == 0) *ts_out = nonfinite ? __builtin_nanf("") : st;
   const bool all_zero = nonfinite || amax == 0.0f;
 
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  for (int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x; b < nblk; b += stride) {
-    uint2 cw = make_uint2(0u, 0u);
-    uint32_t sbyte = 0u;
-    if (!all_zero) {
-      float xf[16];
-      load_block<T>(x + 16 * b, xf);
-      encode_block<KIND>(xf, amax, st, prm, cw, sbyte);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t step = (int64_t)gridDim.x * 4 * 64;  // blocks per grid step
+  int64_t bb = ((int64_t)blockIdx.x * 4 + wave) * 64;
+  if (all_zero) {
+    for (; bb < nblk; bb += step)
+      if (bb + lane < nblk) {
+        codes[bb + lane] = make_uint2(0u, 0u);
+        scales[bb + lane] = 0;
+      }
+    return;
+  }
+  const uint8_t* xb = (const uint8_t*)x;
+  const int64_t total = nblk * kBB;
+  auto load = [&](int64_t b0, u32x4_t (&v)[kNI]) {
+    const int64_t rem = total - b0 * kBB;
+    const int nrec = rem <= 0 ? 0 : (int)min(rem, (int64_t)64 * kBB);
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(xb + (rem <= 0 ? 0 : b0 * kBB)), (short)0, nrec, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < kNI; i++) v[i] = __builtin_amdgcn_raw_buffer_load_b128(r, (i * 64 + lane) * 16, 0, 2);
+  };
+  u32x4_t cur[kNI], nxt[kNI];
+  load(bb, cur);
+  uint8_t* stg = stage[wave];
+  for (; bb < nblk; bb += step) {
+    load(bb + step, nxt);
+#pragma unroll
+    for (int i = 0; i < kNI; i++) *(u32x4_t*)(stg + (i * 64 + lane) * 16) = cur[i];
+    wave_lds_sync();
+    u32x4_t q[kBB / 16];
+#pragma unroll
+    for (int i = 0; i < kBB / 16; i++) q[i] = *(const u32x4_t*)(stg + lane * kBB + 16 * i);
+    wave_lds_sync();
+    float xf[16];
+    unpack_block<T>(q, xf);
+    uint2 cw;
+    uint32_t sbyte;
+    encode_block<KIND>(xf, amax, st, prm, cw, sbyte);
+    if (bb + lane < nblk) {
+      codes[bb + lane] = cw;
+      scales[bb + lane] = (uint8_t)sbyte;
     }
-    codes[b] = cw;
-    scales[b] = (uint8_t)sbyte;
+#pragma unroll
+    for (int i = 0; i < kNI; i++) cur[i] = nxt[i];
   }
 }
 

@@ -316,14 +316,18 @@ __global__ __launch_bounds__(64 * KS) void smallm_kernel(SmArgs a) {
 
   for (int u = u0; u < u1; u += 2) {
     store_unit(ra, stage[wave][0]);
+    wave_lds_sync();
     load_unit(ra, u + 2);
 #pragma unroll
     for (int gi = 0; gi < M; gi++) compute_group(stage[wave][0], gi, xw + ((u - u0) * M + gi) * kSection);
+    wave_lds_sync();
     if (u + 1 < u1) {
       store_unit(rb, stage[wave][1]);
+      wave_lds_sync();
       load_unit(rb, u + 3);
 #pragma unroll
       for (int gi = 0; gi < M; gi++) compute_group(stage[wave][1], gi, xw + ((u + 1 - u0) * M + gi) * kSection);
+      wave_lds_sync();
     }
   }
 
