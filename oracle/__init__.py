@@ -185,6 +185,36 @@ def quantize_act(x, offsets=(-2,), remap: bool = True) -> Packed:
     return quantize(ACT, x, offsets, remap)
 
 
+SECOND_PAIR_OFFSETS = tuple(range(-7, 8))  # offsets tried for the second weight pair
+
+
+def weight_offset_sse(w, off0: int = -2) -> np.ndarray:
+    """Total squared reconstruction error of a weight tensor for every
+    second-pair offset.
+
+    "RaZeR: Pushing the Limits of NVFP4 Quantization with Redundant Zero
+    Remapping" (papernotes.org notes), Loss function / training strategy: the
+    extra weight pair is chosen offline by a grid search (one pair per model,
+    e.g. +/-5 with +/-8 for Llama).  Data-free reading: for each offset o in
+    -7..7 the tensor is encoded with offsets (off0, o) and dequantized in fp64;
+    entry o + 7 is sum((w - dequant)^2) in fp64.  A non-finite tensor gives NaN
+    everywhere."""
+    w = np.ascontiguousarray(np.asarray(w, dtype=np.float32))
+    w64 = w.astype(np.float64)
+    out = np.empty(len(SECOND_PAIR_OFFSETS), dtype=np.float64)
+    for i, o in enumerate(SECOND_PAIR_OFFSETS):
+        d = dequant_f64(quantize_weight(w, (off0, o)))
+        out[i] = np.sum((w64 - d) ** 2)
+    return out
+
+
+def best_second_offset(w, off0: int = -2):
+    """(offset with the lowest total error, the 15 errors); ties go to the
+    lowest offset."""
+    sse = weight_offset_sse(w, off0)
+    return SECOND_PAIR_OFFSETS[int(np.argmin(sse))], sse
+
+
 def dequant_f64(p: Packed) -> np.ndarray:
     out = np.empty((p.rows, p.cols), dtype=np.float64)
     off = _offsets(p.kind, p.offsets)

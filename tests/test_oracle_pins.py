@@ -404,3 +404,44 @@ def test_weight_selection_exercises_every_candidate():
     p = oracle.quantize_weight(x, (-2, -5))
     sel = ((p.scales >> 7) & 1) | (((p.scales >> 6) & 1) << 1)
     assert set(np.unique(sel)) == {0, 1, 2, 3}
+
+
+# ---- second-pair offset search (offline weight encoder) ------------------------
+# "RaZeR ..." (papernotes.org notes), Loss function / training strategy: the
+# extra weight pair is found offline by a grid search; the oracle's data-free
+# form sums the squared reconstruction error over the tensor for every offset.
+
+def test_offset_sse_never_above_plain_nvfp4_and_grid_offsets_add_nothing():
+    rng = np.random.default_rng(41)
+    w = (rng.standard_t(5, (32, 256)) * 0.02).astype(np.float32)
+    w[:, 7] *= 12
+    sse = oracle.weight_offset_sse(w, -2)
+    w64 = w.astype(np.float64)
+    plain = np.sum((w64 - oracle.dequant_f64(oracle.quantize_weight(w, (-2, 4), remap=False))) ** 2)
+    assert np.all(sse <= plain * (1 + 1e-12))
+    # M = 3, 4, 6 lie on the FP4 grid, so such a second pair never moves an
+    # element: the error equals the one with the second pair copying the first
+    i = {o: o + 7 for o in oracle.SECOND_PAIR_OFFSETS}
+    for o in (-6, -4, 0):
+        assert sse[i[o]] == sse[i[-2]]
+    # and some offset strictly improves on a pair that adds nothing
+    assert sse.min() < sse[i[-2]]
+
+
+def test_offset_search_finds_planted_special_value():
+    # every block holds 6.0 (its maximum) and 3.5; with amax 6 the block scale
+    # is 30 and the scaled values are 6 and 3.5 up to rounding of 1/(sb*st).
+    # FP4 puts 3.5 on 4 (error 0.5 in scaled units, ~0.5 in real units), so
+    # each planted element costs ~0.25 -- except with M = 3.5 (offset -5),
+    # whose window (3.25, 3.75) takes it to 3.5.
+    w = np.zeros((4, 64), dtype=np.float32)
+    w[:, 0::16] = 6.0
+    w[:, 5::16] = 3.5
+    best, sse = oracle.best_second_offset(w, -2)
+    assert best == -5
+    nplant = w.size // 16
+    for o, e in zip(oracle.SECOND_PAIR_OFFSETS, sse):
+        if o == -5:
+            assert e < 1e-9
+        else:
+            assert abs(e - nplant * 0.25) < 1e-4
