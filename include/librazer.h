@@ -108,7 +108,8 @@ enum {
   RAZER_OP_QUANTIZE_WEIGHT = 0,
   RAZER_OP_QUANTIZE_ACT = 1,
   RAZER_OP_GEMV = 2,
-  RAZER_OP_GEMM = 3
+  RAZER_OP_GEMM = 3,
+  RAZER_OP_OFFSET_SEARCH = 4 /* n = rows, k = cols of the weight */
 };
 
 /* Offline weight encoder: 4-candidate block-MSE search ([notes] Key design 2:
@@ -148,6 +149,22 @@ razer_status razer_gemv(const void* x, razer_dtype x_dt, const razer_packed* w, 
  * razer_workspace_bytes(RAZER_OP_GEMM, m, N, K) bytes. */
 razer_status razer_gemm(const void* x, razer_dtype x_dt, int64_t m, const razer_packed* w, void* y,
                         razer_dtype y_dt, void* ws, size_t ws_bytes, void* stream);
+
+/* Second-pair offset search for the offline weight encoder ([notes] Loss
+ * function / training strategy: the extra weight pair is picked offline by a
+ * grid search).  For each offset o = -7..7 of the second pair, the weight is
+ * encoded exactly as razer_quantize_weight would with offsets (off0_half, o),
+ * and sse[o + 7] receives sum((w - value * sb * st)^2) over the tensor,
+ * accumulated in fp64 (value * sb * st is exact in fp64).  The caller picks
+ * the offset (e.g. the lowest sse, ties to the lowest offset) and passes it to
+ * razer_quantize_weight.  w: device [rows, cols] in w_dt (F32, F16, BF16),
+ * cols % 16 == 0.  sse: device, 15 doubles, 8-byte aligned.  A non-finite
+ * weight gives NaN in all 15; an all-zero or empty weight gives 0.  ws: at
+ * least razer_workspace_bytes(RAZER_OP_OFFSET_SEARCH, 0, rows, cols) bytes,
+ * 8-byte aligned.  Summation order is fixed, so results repeat bit for bit. */
+razer_status razer_weight_offset_sse(const void* w, razer_dtype w_dt, int64_t rows, int64_t cols,
+                                     int off0_half, double* sse, void* ws, size_t ws_bytes,
+                                     void* stream);
 
 /* Workspace bytes an operation needs for the given sizes (m rows of x, n
  * weight rows / output features, k reduction length).  0 means none. */

@@ -7,8 +7,8 @@ the computation runs in librazer's HIP kernels.  PyTorch supplies device memory
 no fallback path.
 
 Functions carry the C names: ``razer_quantize_weight``, ``razer_quantize_act``,
-``razer_dequant``, ``razer_gemv``, ``razer_gemm``, ``razer_workspace_bytes``,
-``razer_status_string``.
+``razer_dequant``, ``razer_gemv``, ``razer_gemm``, ``razer_weight_offset_sse``,
+``razer_workspace_bytes``, ``razer_status_string``.
 """
 from __future__ import annotations
 
@@ -25,9 +25,11 @@ RAZER_F32, RAZER_F16, RAZER_BF16 = 0, 1, 2
 RAZER_WEIGHT, RAZER_ACT = 0, 1
 RAZER_FLAG_NO_REMAP = 1
 RAZER_OP_QUANTIZE_WEIGHT, RAZER_OP_QUANTIZE_ACT, RAZER_OP_GEMV, RAZER_OP_GEMM = 0, 1, 2, 3
+RAZER_OP_OFFSET_SEARCH = 4
+SECOND_PAIR_OFFSETS = tuple(range(-7, 8))  # entry i of razer_weight_offset_sse is offset i - 7
 
 EXPORTED = ("razer_quantize_weight", "razer_quantize_act", "razer_dequant", "razer_gemv",
-            "razer_gemm", "razer_workspace_bytes", "razer_status_string")
+            "razer_gemm", "razer_weight_offset_sse", "razer_workspace_bytes", "razer_status_string")
 
 DEFAULT_WEIGHT_OFFSETS = (-2, 4)  # special values +/-5 and +/-8
 DEFAULT_ACT_OFFSETS = (-2,)       # special values +/-5
@@ -67,6 +69,8 @@ def lib() -> ctypes.CDLL:
         L.razer_dequant.restype, L.razer_dequant.argtypes = i32, [P, vp, i32, vp]
         L.razer_gemv.restype, L.razer_gemv.argtypes = i32, [vp, i32, P, vp, i32, vp, sz, vp]
         L.razer_gemm.restype, L.razer_gemm.argtypes = i32, [vp, i32, i64, P, vp, i32, vp, sz, vp]
+        L.razer_weight_offset_sse.restype = i32
+        L.razer_weight_offset_sse.argtypes = [vp, i32, i64, i64, i32, vp, vp, sz, vp]
         L.razer_workspace_bytes.restype = sz
         L.razer_workspace_bytes.argtypes = [i32, i64, i64, i64]
         L.razer_status_string.restype, L.razer_status_string.argtypes = ctypes.c_char_p, [i32]
@@ -213,3 +217,28 @@ def razer_gemm(x: torch.Tensor, w: PackedTensor, out_dtype: torch.dtype | None =
                             ctypes.c_void_p(ws.data_ptr() if ws is not None else 0), wsb,
                             ctypes.c_void_p(_stream(stream))), "razer_gemm")
     return out
+
+
+def razer_weight_offset_sse(w: torch.Tensor, off0: int = DEFAULT_WEIGHT_OFFSETS[0], out=None,
+                            workspace=None, stream=None) -> torch.Tensor:
+    """Total squared reconstruction error of w [N, K] encoded with offsets
+    (off0, o), for o = -7..7 (device float64 [15], entry o + 7)."""
+    if w.dim() != 2:
+        raise ValueError("expected a 2-D tensor")
+    w = w.contiguous()
+    rows, cols = w.shape
+    if out is None:
+        out = torch.empty(len(SECOND_PAIR_OFFSETS), dtype=torch.float64, device=w.device)
+    ws, wsb = _workspace(RAZER_OP_OFFSET_SEARCH, 0, rows, cols, w.device, workspace)
+    _check(lib().razer_weight_offset_sse(ctypes.c_void_p(w.data_ptr()), _dtype_code(w.dtype), rows, cols,
+                                         int(off0), ctypes.c_void_p(out.data_ptr()),
+                                         ctypes.c_void_p(ws.data_ptr() if ws is not None else 0), wsb,
+                                         ctypes.c_void_p(_stream(stream))), "razer_weight_offset_sse")
+    return out
+
+
+def razer_best_second_offset(w: torch.Tensor, off0: int = DEFAULT_WEIGHT_OFFSETS[0], stream=None):
+    """(offset with the lowest total error -- ties to the lowest offset, the 15
+    errors on the host).  Waits for the result."""
+    sse = razer_weight_offset_sse(w, off0, stream=stream).cpu()
+    return SECOND_PAIR_OFFSETS[int(torch.argmin(sse))], sse

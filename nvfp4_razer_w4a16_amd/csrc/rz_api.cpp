@@ -139,6 +139,20 @@ razer_status razer_gemm(const void* x, razer_dtype x_dt, int64_t m, const razer_
       rz::launch_gemm(x, x_dt, m, view_of(w), y, y_dt, ws, ws_bytes, (hipStream_t)stream));
 }
 
+razer_status razer_weight_offset_sse(const void* w, razer_dtype w_dt, int64_t rows, int64_t cols,
+                                     int off0_half, double* sse, void* ws, size_t ws_bytes,
+                                     void* stream) {
+  if (!dtype_ok(w_dt) || rows < 0 || cols < 0 || cols % 16 != 0) return RAZER_E_INVALID;
+  if (cols > 0 && rows > INT64_MAX / 2 / cols) return RAZER_E_INVALID;
+  if (off0_half < -7 || off0_half > 7) return RAZER_E_INVALID;
+  if (!sse || !aligned(sse, 8)) return RAZER_E_INVALID;
+  const int64_t n = rows * cols;
+  if (n > 0 && (!w || !aligned(w, 16))) return RAZER_E_INVALID;
+  const size_t need = rz::offset_search_ws_bytes(n);
+  if (!ws || ws_bytes < need || !aligned(ws, 8)) return RAZER_E_INVALID;
+  return status_of(rz::launch_offset_search(w, w_dt, rows, cols, off0_half, sse, ws, (hipStream_t)stream));
+}
+
 size_t razer_workspace_bytes(int op, int64_t m, int64_t n, int64_t k) {
   switch (op) {
     case RAZER_OP_QUANTIZE_WEIGHT:
@@ -148,6 +162,8 @@ size_t razer_workspace_bytes(int op, int64_t m, int64_t n, int64_t k) {
       return rz::gemv_ws_bytes(n, k);
     case RAZER_OP_GEMM:
       return m <= 1 ? rz::gemv_ws_bytes(n, k) : rz::gemm_ws_bytes(m, n, k);
+    case RAZER_OP_OFFSET_SEARCH:
+      return (n < 0 || k < 0) ? 0 : rz::offset_search_ws_bytes(n * k);
     default:
       return 0;
   }

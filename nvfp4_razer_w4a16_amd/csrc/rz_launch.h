@@ -33,6 +33,12 @@ size_t quantize_ws_bytes();
 hipError_t launch_quantize(const void* x, int dtype, const PackedView& out, void* ws,
                            hipStream_t stream);
 
+// Second-pair offset search: sse[o + 7] = total fp64 squared error of the
+// weight tensor encoded with offsets (off0, o), o = -7..7.
+size_t offset_search_ws_bytes(int64_t n);
+hipError_t launch_offset_search(const void* x, int dtype, int64_t rows, int64_t cols, int off0,
+                                double* sse, void* ws, hipStream_t stream);
+
 hipError_t launch_dequant(const PackedView& t, void* out, int out_dtype, hipStream_t stream);
 
 size_t gemv_ws_bytes(int64_t n, int64_t k);

@@ -483,6 +483,184 @@ static hipError_t run_quantize(const T* x, const PackedView& out, uint32_t* part
   return hipGetLastError();
 }
 
+// ---- second-pair offset search (offline weight encoder) -------------------------
+// "RaZeR ..." (papernotes.org notes), Loss function / training strategy: the
+// extra weight pair is chosen offline by a grid search.  For every offset o in
+// -7..7 of the second pair, the tensor is encoded exactly as
+// razer_quantize_weight does with offsets (off0, o) -- encode_block below is
+// the same function -- and the squared reconstruction error
+// (x - value * sb * st)^2 is summed in fp64 (value * sb * st is exact in fp64).
+constexpr int kNumOffsets = 15;
+
+struct OffsetSearchParams {
+  EncodeParams base;  // pair 0 as given; pair 1 replaced per offset
+  float lo1[kNumOffsets], hi1[kNumOffsets];
+  int mag1[kNumOffsets];
+  PairFast f1[kNumOffsets];
+  float m0;           // |SV| of pair 0
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void offset_sse_kernel(const T* __restrict__ x, int64_t nblk,
+                                                         const uint32_t* __restrict__ partial,
+                                                         int npartial, OffsetSearchParams prm,
+                                                         double* __restrict__ part_out) {
+  constexpr int kBB = 16 * (int)sizeof(T);
+  constexpr int kNI = kBB * 64 / 1024;
+  __shared__ __attribute__((aligned(16))) uint8_t stage[4][64 * kBB];
+  __shared__ double acc[kNumOffsets][256];
+  uint32_t m = 0u;
+  for (int i = threadIdx.x; i < npartial; i += 256) m = max(m, partial[i]);
+  m = wave_max_u32(m);
+  __shared__ uint32_t sm[4];
+  if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = m;
+  for (int o = 0; o < kNumOffsets; o++) acc[o][threadIdx.x] = 0.0;
+  __syncthreads();
+  m = max(max(sm[0], sm[1]), max(sm[2], sm[3]));
+  const bool nonfinite = m >= 0x7F800000u;
+  const float amax = u2f(m);
+  const float st = amax / (6.0f * 30.0f);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t step = (int64_t)gridDim.x * 4 * 64;
+  int64_t bb = ((int64_t)blockIdx.x * 4 + wave) * 64;
+  if (!nonfinite && amax != 0.0f) {
+    const uint8_t* xb = (const uint8_t*)x;
+    const int64_t total = nblk * kBB;
+    auto load = [&](int64_t b0, u32x4_t (&v)[kNI]) {
+      const int64_t rem = total - b0 * kBB;
+      const int nrec = rem <= 0 ? 0 : (int)min(rem, (int64_t)64 * kBB);
+      const __amdgpu_buffer_rsrc_t r =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(xb + (rem <= 0 ? 0 : b0 * kBB)), (short)0, nrec, 0x00020000);
+#pragma unroll
+      for (int i = 0; i < kNI; i++) v[i] = __builtin_amdgcn_raw_buffer_load_b128(r, (i * 64 + lane) * 16, 0, 2);
+    };
+    const double st64 = (double)st;
+    u32x4_t cur[kNI], nxt[kNI];
+    load(bb, cur);
+    uint8_t* stg = stage[wave];
+    for (; bb < nblk; bb += step) {
+      load(bb + step, nxt);
+#pragma unroll
+      for (int i = 0; i < kNI; i++) *(u32x4_t*)(stg + (i * 64 + lane) * 16) = cur[i];
+      wave_lds_sync();
+      u32x4_t q[kBB / 16];
+#pragma unroll
+      for (int i = 0; i < kBB / 16; i++) q[i] = *(const u32x4_t*)(stg + lane * kBB + 16 * i);
+      wave_lds_sync();
+      float xf[16];
+      unpack_block<T>(q, xf);
+      if (bb + lane < nblk) {
+#pragma unroll 1
+        for (int o = 0; o < kNumOffsets; o++) {
+          EncodeParams e = prm.base;
+          e.lo[1] = prm.lo1[o];
+          e.hi[1] = prm.hi1[o];
+          e.mag_x2[1] = prm.mag1[o];
+          e.f[1] = prm.f1[o];
+          uint2 cw;
+          uint32_t sbyte;
+          encode_block<kWeight>(xf, amax, st, e, cw, sbyte);
+          const double sbst = (double)scale_of_byte<kWeight>(sbyte) * st64;
+          // the special value's sign is bit 7 of the scale byte, not the code's
+          const double svm = (double)((sbyte & 0x40u) ? 0.5f * (float)prm.mag1[o] : prm.m0);
+          const double sv = (sbyte & 0x80u) ? -svm : svm;
+          double err = 0.0;
+#pragma unroll
+          for (int j = 0; j < 16; j++) {
+            const uint32_t c = ((j < 8 ? cw.x : cw.y) >> (4 * (j & 7))) & 15u;
+            const double mag = 0.5 * (double)fp4_mag_x2(c & 7u);
+            const double v = ((c == 8u) ? sv : ((c & 8u) ? -mag : mag)) * sbst;
+            const double d = (double)xf[j] - v;
+            err += d * d;
+          }
+          acc[o][threadIdx.x] += err;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kNI; i++) cur[i] = nxt[i];
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < kNumOffsets) {
+    double sum = 0.0;
+    for (int t = 0; t < 256; t++) sum += acc[threadIdx.x][t];
+    part_out[(int64_t)blockIdx.x * kNumOffsets + threadIdx.x] = nonfinite ? __builtin_nan("") : sum;
+  }
+}
+
+__global__ __launch_bounds__(64) void offset_sse_reduce_kernel(const double* __restrict__ part, int nwg,
+                                                               double* __restrict__ sse) {
+  if (threadIdx.x < kNumOffsets) {
+    double sum = 0.0;
+    for (int g = 0; g < nwg; g++) sum += part[(int64_t)g * kNumOffsets + threadIdx.x];
+    sse[threadIdx.x] = sum;
+  }
+}
+
+static int64_t offset_search_grid(int64_t nblk) {
+  int64_t g = (nblk + 255) / 256;
+  const int64_t cap = (int64_t)device_cu_count() * 4;
+  if (g > cap) g = cap;
+  return g < 1 ? 1 : g;
+}
+
+size_t offset_search_ws_bytes(int64_t n) {
+  return kAmaxMaxPartials * sizeof(uint32_t) +
+         (size_t)offset_search_grid(n / 16) * kNumOffsets * sizeof(double);
+}
+
+template <typename T>
+static hipError_t run_offset_search(const T* x, int64_t n, int off0, double* sse, void* ws,
+                                    hipStream_t stream) {
+  const int64_t nblk = n / 16;
+  uint32_t* partial = (uint32_t*)ws;
+  double* part = (double*)((uint8_t*)ws + kAmaxMaxPartials * sizeof(uint32_t));
+  const int64_t nvec = n / (16 / (int64_t)sizeof(T));
+  int64_t g1 = (nvec + 4 * 256 - 1) / (4 * 256);
+  if (g1 < 1) g1 = 1;
+  if (g1 > kAmaxMaxPartials) g1 = kAmaxMaxPartials;
+  if (nvec > 0)
+    hipLaunchKernelGGL(amax_partial_kernel<T>, dim3((unsigned)g1), dim3(256), 0, stream,
+                       (const uint4*)x, nvec, partial);
+  OffsetSearchParams prm;
+  for (int p = 0; p < 2; p++) {
+    const Candidate c = make_candidate(off0);
+    prm.base.lo[p] = c.lo;
+    prm.base.hi[p] = c.hi;
+    prm.base.mag_x2[p] = c.mag_x2;
+    prm.base.f[p] = make_pair_fast(off0);
+  }
+  prm.base.remap = 1;
+  prm.m0 = 6.0f + 0.5f * (float)off0;
+  for (int o = 0; o < kNumOffsets; o++) {
+    const Candidate c = make_candidate(o - 7);
+    prm.lo1[o] = c.lo;
+    prm.hi1[o] = c.hi;
+    prm.mag1[o] = c.mag_x2;
+    prm.f1[o] = make_pair_fast(o - 7);
+  }
+  const int64_t g2 = offset_search_grid(nblk);
+  if (nvec > 0) {
+    hipLaunchKernelGGL(offset_sse_kernel<T>, dim3((unsigned)g2), dim3(256), 0, stream, x, nblk, partial,
+                       (int)g1, prm, part);
+  } else {
+    hipLaunchKernelGGL(offset_sse_reduce_kernel, dim3(1), dim3(64), 0, stream, (const double*)nullptr, 0, sse);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(offset_sse_reduce_kernel, dim3(1), dim3(64), 0, stream, (const double*)part, (int)g2, sse);
+  return hipGetLastError();
+}
+
+hipError_t launch_offset_search(const void* x, int dtype, int64_t rows, int64_t cols, int off0,
+                                double* sse, void* ws, hipStream_t stream) {
+  const int64_t n = rows * cols;
+  if (dtype == kF32) return run_offset_search((const float*)x, n, off0, sse, ws, stream);
+  if (dtype == kF16) return run_offset_search((const _Float16*)x, n, off0, sse, ws, stream);
+  return run_offset_search((const __bf16*)x, n, off0, sse, ws, stream);
+}
+
 hipError_t launch_quantize(const void* x, int dtype, const PackedView& out, void* ws,
                            hipStream_t stream) {
   uint32_t* partial = (uint32_t*)ws;

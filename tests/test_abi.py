@@ -121,3 +121,30 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(rz, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         rz.lib()
+
+
+@pytest.mark.parametrize("args", [
+    dict(cols=24),                 # cols % 16 != 0
+    dict(rows=-1),
+    dict(off0=8),                  # offset outside [-7, 7]
+    dict(off0=-8),
+    dict(dt=7),                    # unknown dtype
+    dict(sse=None),
+    dict(sse=0x6004),              # misaligned sse
+    dict(w=None),
+    dict(w=0x4008),                # misaligned weight
+    dict(ws=None),
+    dict(wsb=16),                  # workspace too small
+])
+def test_offset_search_rejects_bad_arguments(args):
+    a = dict(w=0x4000, dt=rz.RAZER_F32, rows=4, cols=32, off0=-2, sse=0x6000, ws=0x5000, wsb=1 << 20)
+    a.update(args)
+    st = rz.lib().razer_weight_offset_sse(ctypes.c_void_p(a["w"]), a["dt"], a["rows"], a["cols"], a["off0"],
+                                          ctypes.c_void_p(a["sse"]), ctypes.c_void_p(a["ws"]), a["wsb"], None)
+    assert st == rz.RAZER_E_INVALID
+
+
+def test_offset_search_workspace_covers_partials():
+    # amax partials plus 15 fp64 sums per workgroup
+    assert rz.razer_workspace_bytes(rz.RAZER_OP_OFFSET_SEARCH, 0, 28672, 8192) >= 4096 + 15 * 8
+    assert rz.razer_workspace_bytes(rz.RAZER_OP_OFFSET_SEARCH, 0, 1, 16) >= 4096 + 15 * 8

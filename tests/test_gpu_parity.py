@@ -432,3 +432,84 @@ def test_products_with_activation_kind_operand(m, n, k):
     else:
         y = rz.razer_gemm(x.cuda(), t, torch.float32).cpu().double().numpy()
     assert_product_close(y, y_ref, nrm, f"act-kind operand {m}x{n}x{k}")
+
+
+# ---- second-pair offset search (offline weight encoder) ---------------------------
+
+@functools.lru_cache(maxsize=1)
+def _offset_cases():
+    rng = np.random.default_rng(23)
+    t = (rng.standard_t(5, (64, 256)) * 0.02).astype(np.float32)
+    t[:, 9] *= 15
+    planted = np.zeros((4, 64), np.float32)  # every block: 6.0 and 3.5 (best offset -5)
+    planted[:, 0::16] = 6.0
+    planted[:, 5::16] = 3.5
+    ragged = (rng.standard_normal((3, 48)) * 0.1).astype(np.float32)
+    # blocks ~1/1000 of the tensor maximum get subnormal E3M3 scale codes, so
+    # scaled values reach up to 9 and the second pairs above 6 can move them
+    sub = (rng.standard_normal((8, 64)) * 0.01).astype(np.float32)
+    sub[0, 0] = 30.0
+    nan = t[:2].copy()
+    nan[1, 3] = np.nan
+    return {"student_t": t, "planted": planted, "ragged": ragged, "subnormal_scales": sub,
+            "zeros": np.zeros((2, 32), np.float32), "empty": np.zeros((0, 32), np.float32),
+            "nonfinite": nan}
+
+
+def _check_offset_sse(got, ref, what):
+    assert np.array_equal(np.isnan(got), np.isnan(ref)), what
+    ok = ~np.isnan(ref)
+    np.testing.assert_allclose(got[ok], ref[ok], rtol=1e-9, atol=1e-300, err_msg=what)
+    if ok.all() and ref.size:
+        # the offset the oracle picks is also a minimum of the GPU's sums
+        assert got[int(np.argmin(ref))] <= got.min() * (1 + 1e-9), what
+
+
+@pytest.mark.parametrize("name", sorted(_offset_cases()))
+@pytest.mark.parametrize("off0", [-2, 3])
+def test_offset_sse_matches_oracle(name, off0):
+    _need_gpu()
+    w = _offset_cases()[name]
+    ref = oracle.weight_offset_sse(w, off0)
+    got = rz.razer_weight_offset_sse(torch.from_numpy(w).cuda(), off0).cpu().numpy()
+    _check_offset_sse(got, ref, f"{name} off0={off0}")
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+def test_offset_sse_16bit_inputs(dtype):
+    _need_gpu()
+    w16 = torch.from_numpy(_offset_cases()["student_t"]).to(dtype)
+    ref = oracle.weight_offset_sse(w16.float().numpy(), -2)
+    got = rz.razer_weight_offset_sse(w16.cuda(), -2).cpu().numpy()
+    _check_offset_sse(got, ref, str(dtype))
+
+
+def test_offset_sse_planted_and_best_offset():
+    _need_gpu()
+    best, sse = rz.razer_best_second_offset(torch.from_numpy(_offset_cases()["planted"]).cuda(), -2)
+    assert best == -5
+    assert sse[best + 7] < 1e-9
+
+
+def test_offset_sse_full_size_prefill_weight():
+    """W[28672, 8192] fp32 ~ 0.015 t(4): the default offset's sum against the
+    oracle, the exact equalities that hold at any size, repeatability."""
+    _need_gpu()
+    log("offset search: generating ...")
+    w = synth.prefill_weight()
+    wd = torch.from_numpy(w).cuda()
+    log("offset search: gpu ...")
+    got = rz.razer_weight_offset_sse(wd, -2).cpu().numpy()
+    again = rz.razer_weight_offset_sse(wd, -2).cpu().numpy()
+    assert np.array_equal(got.view(np.uint64), again.view(np.uint64))
+    # a second pair on the FP4 grid (M = 3, 4, 6) moves nothing, exactly like
+    # a second pair equal to the first: same encodings, same summation order
+    for o in (-6, -4, 0):
+        assert got[o + 7] == got[-2 + 7]
+    log("offset search: oracle at offset +4 ...")
+    d = oracle.dequant_f64(oracle.quantize_weight(w, (-2, 4)))
+    ref4 = float(np.sum((w.astype(np.float64) - d) ** 2))
+    del d
+    assert abs(got[4 + 7] - ref4) <= 1e-9 * ref4
+    del wd
+    torch.cuda.empty_cache()
