@@ -275,7 +275,19 @@ def bench_rows(torch, rz, synth, args, decode_base):
     wp = rz.PackedTensor(rz.RAZER_WEIGHT, 28672, 8192, (-2, 4), dev)
     t = GraphTimer(torch, lambda: rz.razer_quantize_weight(w, out=wp))
     ms_q = t.time(5)
-    del t, w
+    # second-pair offset search on the same weight (15 full encodes + fp64 error sums)
+    sse = torch.empty(len(rz.SECOND_PAIR_OFFSETS), dtype=torch.float64, device=dev)
+    wso = torch.empty(rz.razer_workspace_bytes(rz.RAZER_OP_OFFSET_SEARCH, 0, 28672, 8192),
+                      dtype=torch.uint8, device=dev)
+    t = GraphTimer(torch, lambda: rz.razer_weight_offset_sse(w, -2, out=sse, workspace=wso))
+    ms_o = t.time(3)
+    sse_h = sse.cpu()
+    best = rz.SECOND_PAIR_OFFSETS[int(torch.argmin(sse_h))]
+    off_row = {"workload": "W [28672,8192] fp32, second-pair offsets -7..7 with the first pair at -2",
+               "ms": ms_o, "gelem_per_s_per_offset": 15 * 28672 * 8192 / ms_o / 1e6,
+               "best_offset": best,
+               "sse_best_over_default_4": float(sse_h[best + 7] / sse_h[4 + 7])}
+    del t, w, wso
     torch.cuda.empty_cache()
     x = synth.prefill_x().to(dev)
     y = torch.empty((2048, 28672), dtype=torch.bfloat16, device=dev)
@@ -286,6 +298,7 @@ def bench_rows(torch, rz, synth, args, decode_base):
         "workload": "x [2048,8192] bf16 x W [28672,8192] RaZeR-W4 (0.015*t(4)) -> bf16",
         "ms": ms, "tflops": flops / ms / 1e9, "frac_mfma": flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS}
     n_el = 28672 * 8192
+    rows["offset_search_prefill"] = off_row
     rows["quantize_weight_prefill"] = {
         "workload": "W [28672,8192] fp32, 4 candidates", "ms": ms_q, "gelem_per_s": n_el / ms_q / 1e6,
         "gbs_1read": n_el * (4 + 0.5625) / ms_q / 1e6,

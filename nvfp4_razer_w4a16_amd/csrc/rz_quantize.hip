@@ -590,13 +590,21 @@ __global__ __launch_bounds__(256) void offset_sse_kernel(const T* __restrict__ x
   }
 }
 
-__global__ __launch_bounds__(64) void offset_sse_reduce_kernel(const double* __restrict__ part, int nwg,
-                                                               double* __restrict__ sse) {
-  if (threadIdx.x < kNumOffsets) {
-    double sum = 0.0;
-    for (int g = 0; g < nwg; g++) sum += part[(int64_t)g * kNumOffsets + threadIdx.x];
-    sse[threadIdx.x] = sum;
+// One workgroup per offset: strided partial sums, then a fixed-shape LDS tree,
+// so the result does not depend on timing.
+__global__ __launch_bounds__(256) void offset_sse_reduce_kernel(const double* __restrict__ part, int nwg,
+                                                                double* __restrict__ sse) {
+  __shared__ double red[256];
+  const int o = blockIdx.x;
+  double sum = 0.0;
+  for (int g = threadIdx.x; g < nwg; g += 256) sum += part[(int64_t)g * kNumOffsets + o];
+  red[threadIdx.x] = sum;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
   }
+  if (threadIdx.x == 0) sse[o] = red[0];
 }
 
 static int64_t offset_search_grid(int64_t nblk) {
@@ -646,10 +654,10 @@ static hipError_t run_offset_search(const T* x, int64_t n, int off0, double* sse
     hipLaunchKernelGGL(offset_sse_kernel<T>, dim3((unsigned)g2), dim3(256), 0, stream, x, nblk, partial,
                        (int)g1, prm, part);
   } else {
-    hipLaunchKernelGGL(offset_sse_reduce_kernel, dim3(1), dim3(64), 0, stream, (const double*)nullptr, 0, sse);
+    hipLaunchKernelGGL(offset_sse_reduce_kernel, dim3(kNumOffsets), dim3(256), 0, stream, (const double*)nullptr, 0, sse);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(offset_sse_reduce_kernel, dim3(1), dim3(64), 0, stream, (const double*)part, (int)g2, sse);
+  hipLaunchKernelGGL(offset_sse_reduce_kernel, dim3(kNumOffsets), dim3(256), 0, stream, (const double*)part, (int)g2, sse);
   return hipGetLastError();
 }
 
