@@ -254,3 +254,22 @@ def gemm(x, p: Packed, cols=None):
     lib().rzo_gemm(_ptr(x), m, k, p.kind, _ptr(p.codes), _ptr(p.scales), float(p.tensor_scale),
                    _ptr(off), p.rows, None if idx is None else _ptr(idx), ncols, _ptr(y), _ptr(nrm))
     return y, nrm
+
+
+def gemm_w4a4(xp: Packed, wp: Packed, cols=None):
+    """fp64 product of two packed tensors, y = dequant(x) @ dequant(w)^T, plus
+    the norm sum |dequant(x)| |dequant(w)|.
+
+    "RaZeR: Pushing the Limits of NVFP4 Quantization with Redundant Zero
+    Remapping" (papernotes.org notes), Overall framework and Key designs 1-2:
+    in W4A4 the activations carry the online 2-candidate encoding and the
+    weights the offline 4-candidate one; the product is over the decoded
+    values.  ``cols`` selects weight rows (output columns).  Returns
+    (y [m, ncols], norm [m, ncols])."""
+    if xp.cols != wp.cols:
+        raise ValueError("inner dimensions differ")
+    xd = dequant_f64(xp)
+    wd = dequant_f64(wp)
+    if cols is not None:
+        wd = wd[np.asarray(cols, dtype=np.int64)]
+    return xd @ wd.T, np.abs(xd) @ np.abs(wd).T

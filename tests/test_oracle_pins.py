@@ -445,3 +445,28 @@ def test_offset_search_finds_planted_special_value():
             assert e < 1e-9
         else:
             assert abs(e - nplant * 0.25) < 1e-4
+
+
+# ---- W4A4 product ----------------------------------------------------------------
+
+def test_w4a4_product_equals_w4a16_product_of_exact_activations():
+    # With the activation tensor scale a power of two (amax = 2688 * 2^-10 gives
+    # st = 2^-10 exactly) every decoded activation is exact in fp32, so the
+    # W4A4 product must equal the W4A16 product of those fp32 values, whose
+    # oracle sums each output in its own loop.
+    rng = np.random.default_rng(61)
+    x = rng.standard_normal((3, 96)).astype(np.float32)
+    x[0, 0] = 2688.0 * 2.0 ** -10
+    x = np.clip(x, -2.625, 2.625)
+    xp = oracle.quantize_act(x, (-2,))
+    assert xp.tensor_scale == np.float32(2.0 ** -10)
+    wp = oracle.quantize_weight((rng.standard_t(5, (20, 96)) * 0.02).astype(np.float32), (-2, 4))
+    xd = oracle.dequant_f64(xp)
+    assert np.array_equal(xd.astype(np.float32).astype(np.float64), xd)
+    y, nrm = oracle.gemm_w4a4(xp, wp)
+    y16, nrm16 = oracle.gemm(xd.astype(np.float32), wp)
+    np.testing.assert_allclose(y, y16, rtol=1e-12, atol=1e-12 * float(nrm.max()))
+    np.testing.assert_allclose(nrm, nrm16, rtol=1e-12)
+    # and the selected-columns form picks the same outputs
+    ys, _ = oracle.gemm_w4a4(xp, wp, cols=[3, 0, 19])
+    np.testing.assert_array_equal(ys, y[:, [3, 0, 19]])
