@@ -109,7 +109,8 @@ enum {
   RAZER_OP_QUANTIZE_ACT = 1,
   RAZER_OP_GEMV = 2,
   RAZER_OP_GEMM = 3,
-  RAZER_OP_OFFSET_SEARCH = 4 /* n = rows, k = cols of the weight */
+  RAZER_OP_OFFSET_SEARCH = 4, /* n = rows, k = cols of the weight */
+  RAZER_OP_GEMM_W4A4 = 5      /* m = rows of x, n = rows of w, k = cols */
 };
 
 /* Offline weight encoder: 4-candidate block-MSE search ([notes] Key design 2:
@@ -149,6 +150,20 @@ razer_status razer_gemv(const void* x, razer_dtype x_dt, const razer_packed* w, 
  * razer_workspace_bytes(RAZER_OP_GEMM, m, N, K) bytes. */
 razer_status razer_gemm(const void* x, razer_dtype x_dt, int64_t m, const razer_packed* w, void* y,
                         razer_dtype y_dt, void* ws, size_t ws_bytes, void* stream);
+
+/* W4A4 product y[M, N] = dequant(x)[M, K] * dequant(w)^T of two packed
+ * tensors ([notes] Overall framework, Key designs 1-2: activations encoded
+ * online with 2 candidates, weights offline with 4).  On matrix units without
+ * an FP4 path it runs in two passes: x's codes are decoded to value * sb in
+ * fp16 (exact), the W4A16 product runs on them in fp32, and the result is
+ * multiplied by x's tensor scale and rounded once to y_dt.  x: packed [M, K]
+ * (normally RAZER_ACT, either kind accepted); w: packed [N, K] of either kind;
+ * y: device [M, N] in F32, F16 or BF16.  K == 0 is RAZER_E_UNSUPPORTED.
+ * ws: at least razer_workspace_bytes(RAZER_OP_GEMM_W4A4, M, N, K) bytes,
+ * 256-byte aligned.  The accuracy bound is the W4A16 product's plus one fp32
+ * rounding. */
+razer_status razer_gemm_w4a4(const razer_packed* x, const razer_packed* w, void* y, razer_dtype y_dt,
+                             void* ws, size_t ws_bytes, void* stream);
 
 /* Second-pair offset search for the offline weight encoder ([notes] Loss
  * function / training strategy: the extra weight pair is picked offline by a

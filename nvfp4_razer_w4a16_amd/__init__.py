@@ -7,7 +7,7 @@ the computation runs in librazer's HIP kernels.  PyTorch supplies device memory
 no fallback path.
 
 Functions carry the C names: ``razer_quantize_weight``, ``razer_quantize_act``,
-``razer_dequant``, ``razer_gemv``, ``razer_gemm``, ``razer_weight_offset_sse``,
+``razer_dequant``, ``razer_gemv``, ``razer_gemm``, ``razer_gemm_w4a4``, ``razer_weight_offset_sse``,
 ``razer_workspace_bytes``, ``razer_status_string``.
 """
 from __future__ import annotations
@@ -25,11 +25,12 @@ RAZER_F32, RAZER_F16, RAZER_BF16 = 0, 1, 2
 RAZER_WEIGHT, RAZER_ACT = 0, 1
 RAZER_FLAG_NO_REMAP = 1
 RAZER_OP_QUANTIZE_WEIGHT, RAZER_OP_QUANTIZE_ACT, RAZER_OP_GEMV, RAZER_OP_GEMM = 0, 1, 2, 3
-RAZER_OP_OFFSET_SEARCH = 4
+RAZER_OP_OFFSET_SEARCH, RAZER_OP_GEMM_W4A4 = 4, 5
 SECOND_PAIR_OFFSETS = tuple(range(-7, 8))  # entry i of razer_weight_offset_sse is offset i - 7
 
 EXPORTED = ("razer_quantize_weight", "razer_quantize_act", "razer_dequant", "razer_gemv",
-            "razer_gemm", "razer_weight_offset_sse", "razer_workspace_bytes", "razer_status_string")
+            "razer_gemm", "razer_gemm_w4a4", "razer_weight_offset_sse", "razer_workspace_bytes",
+            "razer_status_string")
 
 DEFAULT_WEIGHT_OFFSETS = (-2, 4)  # special values +/-5 and +/-8
 DEFAULT_ACT_OFFSETS = (-2,)       # special values +/-5
@@ -69,6 +70,7 @@ def lib() -> ctypes.CDLL:
         L.razer_dequant.restype, L.razer_dequant.argtypes = i32, [P, vp, i32, vp]
         L.razer_gemv.restype, L.razer_gemv.argtypes = i32, [vp, i32, P, vp, i32, vp, sz, vp]
         L.razer_gemm.restype, L.razer_gemm.argtypes = i32, [vp, i32, i64, P, vp, i32, vp, sz, vp]
+        L.razer_gemm_w4a4.restype, L.razer_gemm_w4a4.argtypes = i32, [P, P, vp, i32, vp, sz, vp]
         L.razer_weight_offset_sse.restype = i32
         L.razer_weight_offset_sse.argtypes = [vp, i32, i64, i64, i32, vp, vp, sz, vp]
         L.razer_workspace_bytes.restype = sz
@@ -242,3 +244,24 @@ def razer_best_second_offset(w: torch.Tensor, off0: int = DEFAULT_WEIGHT_OFFSETS
     errors on the host).  Waits for the result."""
     sse = razer_weight_offset_sse(w, off0, stream=stream).cpu()
     return SECOND_PAIR_OFFSETS[int(torch.argmin(sse))], sse
+
+
+def razer_gemm_w4a4(x: PackedTensor, w: PackedTensor, out_dtype: torch.dtype = torch.bfloat16, out=None,
+                    workspace=None, stream=None):
+    """y[M, N] = dequant(x)[M, K] . dequant(w)^T for packed x [M, K] (normally an
+    activation encoding) and packed w [N, K]."""
+    if x.cols != w.cols:
+        raise ValueError("x and w must have the same K")
+    dev = x.codes.device
+    if out is None:
+        out = torch.empty((x.rows, w.rows), dtype=out_dtype, device=dev)
+    need = razer_workspace_bytes(RAZER_OP_GEMM_W4A4, x.rows, w.rows, w.cols)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    sx, sw = x.struct(), w.struct()
+    _check(lib().razer_gemm_w4a4(ctypes.byref(sx), ctypes.byref(sw), ctypes.c_void_p(out.data_ptr()),
+                                 _dtype_code(out.dtype),
+                                 ctypes.c_void_p(workspace.data_ptr() if workspace is not None else 0), wsb,
+                                 ctypes.c_void_p(_stream(stream))), "razer_gemm_w4a4")
+    return out

@@ -30,6 +30,7 @@ SOURCES = {
     "rz_gemv.hip": [],
     "rz_gemm.hip": [],
     "rz_smallm.hip": [],
+    "rz_w4a4.hip": [],
     "rz_api.cpp": [],
 }
 

@@ -139,6 +139,23 @@ razer_status razer_gemm(const void* x, razer_dtype x_dt, int64_t m, const razer_
       rz::launch_gemm(x, x_dt, m, view_of(w), y, y_dt, ws, ws_bytes, (hipStream_t)stream));
 }
 
+razer_status razer_gemm_w4a4(const razer_packed* x, const razer_packed* w, void* y, razer_dtype y_dt,
+                             void* ws, size_t ws_bytes, void* stream) {
+  razer_status s = check_packed(x, true);
+  if (s != RAZER_OK) return s;
+  s = check_packed(w, true);
+  if (s != RAZER_OK) return s;
+  if (!dtype_ok(y_dt) || x->cols != w->cols) return RAZER_E_INVALID;
+  if (x->rows == 0 || w->rows == 0) return RAZER_OK;
+  if (x->cols == 0) return RAZER_E_UNSUPPORTED;
+  if (w->cols > kGemvMaxK && x->rows == 1) return RAZER_E_UNSUPPORTED;
+  if (!y || !aligned(y, 16)) return RAZER_E_INVALID;
+  if (x->rows > INT64_MAX / 4 / (w->rows > w->cols ? w->rows : w->cols)) return RAZER_E_INVALID;
+  const size_t need = rz::gemm_w4a4_ws_bytes(x->rows, w->rows, w->cols);
+  if (!ws || ws_bytes < need || !aligned(ws, 256)) return RAZER_E_INVALID;
+  return status_of(rz::launch_gemm_w4a4(view_of(x), view_of(w), y, y_dt, ws, ws_bytes, (hipStream_t)stream));
+}
+
 razer_status razer_weight_offset_sse(const void* w, razer_dtype w_dt, int64_t rows, int64_t cols,
                                      int off0_half, double* sse, void* ws, size_t ws_bytes,
                                      void* stream) {
@@ -162,6 +179,8 @@ size_t razer_workspace_bytes(int op, int64_t m, int64_t n, int64_t k) {
       return rz::gemv_ws_bytes(n, k);
     case RAZER_OP_GEMM:
       return m <= 1 ? rz::gemv_ws_bytes(n, k) : rz::gemm_ws_bytes(m, n, k);
+    case RAZER_OP_GEMM_W4A4:
+      return rz::gemm_w4a4_ws_bytes(m, n, k);
     case RAZER_OP_OFFSET_SEARCH:
       return (n < 0 || k < 0) ? 0 : rz::offset_search_ws_bytes(n * k);
     default:

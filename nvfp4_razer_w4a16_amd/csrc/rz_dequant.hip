@@ -45,7 +45,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict
                                                       const uint8_t* __restrict__ scales,
                                                       const float* __restrict__ ts, int64_t ndw,
                                                       float m0, float m1, OT* __restrict__ out) {
-  const float st = *ts;
+  const float st = ts ? *ts : 1.0f;  // no tensor scale: value * sb
   const int64_t stride = (int64_t)gridDim.x * 256;
   for (int64_t d0 = (int64_t)blockIdx.x * 256 + threadIdx.x; d0 < ndw; d0 += kDqUnroll * stride) {
     uint32_t w[kDqUnroll], sbyte[kDqUnroll];
@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict
 }
 
 template <int KIND, typename OT>
-static void run(const PackedView& t, OT* out, hipStream_t stream) {
+static void run(const PackedView& t, OT* out, bool scaled, hipStream_t stream) {
   const int64_t ndw = t.rows * t.cols / 8;
   int64_t g = (ndw + 255) / 256;
   const int64_t cap = (int64_t)device_cu_count() * 16;
@@ -93,20 +93,31 @@ static void run(const PackedView& t, OT* out, hipStream_t stream) {
   const float m0 = 6.0f + 0.5f * (float)t.off_half[0];
   const float m1 = 6.0f + 0.5f * (float)t.off_half[KIND == kWeight ? 1 : 0];
   hipLaunchKernelGGL((dequant_kernel<KIND, OT>), dim3((unsigned)g), dim3(256), 0, stream,
-                     (const uint32_t*)t.codes, t.scales, t.tensor_scale, ndw, m0, m1, out);
+                     (const uint32_t*)t.codes, t.scales, scaled ? t.tensor_scale : nullptr, ndw, m0, m1, out);
+}
+
+static hipError_t dequant_dispatch(const PackedView& t, void* out, int out_dtype, bool scaled,
+                                   hipStream_t stream) {
+  if (t.kind == kWeight) {
+    if (out_dtype == kF32) run<kWeight>(t, (float*)out, scaled, stream);
+    else if (out_dtype == kF16) run<kWeight>(t, (_Float16*)out, scaled, stream);
+    else run<kWeight>(t, (__bf16*)out, scaled, stream);
+  } else {
+    if (out_dtype == kF32) run<kAct>(t, (float*)out, scaled, stream);
+    else if (out_dtype == kF16) run<kAct>(t, (_Float16*)out, scaled, stream);
+    else run<kAct>(t, (__bf16*)out, scaled, stream);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_dequant(const PackedView& t, void* out, int out_dtype, hipStream_t stream) {
-  if (t.kind == kWeight) {
-    if (out_dtype == kF32) run<kWeight>(t, (float*)out, stream);
-    else if (out_dtype == kF16) run<kWeight>(t, (_Float16*)out, stream);
-    else run<kWeight>(t, (__bf16*)out, stream);
-  } else {
-    if (out_dtype == kF32) run<kAct>(t, (float*)out, stream);
-    else if (out_dtype == kF16) run<kAct>(t, (_Float16*)out, stream);
-    else run<kAct>(t, (__bf16*)out, stream);
-  }
-  return hipGetLastError();
+  return dequant_dispatch(t, out, out_dtype, true, stream);
+}
+
+// value * sb without the tensor scale: FP4 or special value (at most 5
+// significant bits) times a 4-bit scale mantissa, exact in fp16.
+hipError_t launch_dequant_unscaled(const PackedView& t, void* out, int out_dtype, hipStream_t stream) {
+  return dequant_dispatch(t, out, out_dtype, false, stream);
 }
 
 }  // namespace rz

@@ -40,6 +40,12 @@ hipError_t launch_offset_search(const void* x, int dtype, int64_t rows, int64_t 
                                 double* sse, void* ws, hipStream_t stream);
 
 hipError_t launch_dequant(const PackedView& t, void* out, int out_dtype, hipStream_t stream);
+hipError_t launch_dequant_unscaled(const PackedView& t, void* out, int out_dtype, hipStream_t stream);
+
+// W4A4 product of two packed tensors (two passes through the W4A16 product).
+size_t gemm_w4a4_ws_bytes(int64_t m, int64_t n, int64_t k);
+hipError_t launch_gemm_w4a4(const PackedView& x, const PackedView& w, void* y, int y_dtype, void* ws,
+                            size_t ws_bytes, hipStream_t stream);
 
 size_t gemv_ws_bytes(int64_t n, int64_t k);
 hipError_t launch_gemv(const void* x, int x_dtype, const PackedView& w, void* y, int y_dtype,

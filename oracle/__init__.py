@@ -269,7 +269,11 @@ def gemm_w4a4(xp: Packed, wp: Packed, cols=None):
     if xp.cols != wp.cols:
         raise ValueError("inner dimensions differ")
     xd = dequant_f64(xp)
+    if cols is not None:  # decode only the selected weight rows (same tensor scale)
+        idx = np.asarray(cols, dtype=np.int64)
+        wp = Packed(wp.kind, idx.size, wp.cols, wp.offsets,
+                    np.ascontiguousarray(wp.codes.reshape(wp.rows, wp.cols // 2)[idx]).reshape(-1),
+                    np.ascontiguousarray(wp.scales.reshape(wp.rows, wp.cols // 16)[idx]).reshape(-1),
+                    wp.tensor_scale)
     wd = dequant_f64(wp)
-    if cols is not None:
-        wd = wd[np.asarray(cols, dtype=np.int64)]
     return xd @ wd.T, np.abs(xd) @ np.abs(wd).T

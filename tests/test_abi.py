@@ -15,7 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _declared_functions():
     text = open(os.path.join(ROOT, "include", "librazer.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(razer_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(razer_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_five_calls():
@@ -148,3 +148,36 @@ def test_offset_search_workspace_covers_partials():
     # amax partials plus 15 fp64 sums per workgroup
     assert rz.razer_workspace_bytes(rz.RAZER_OP_OFFSET_SEARCH, 0, 28672, 8192) >= 4096 + 15 * 8
     assert rz.razer_workspace_bytes(rz.RAZER_OP_OFFSET_SEARCH, 0, 1, 16) >= 4096 + 15 * 8
+
+
+@pytest.mark.parametrize("case", ["cols_differ", "bad_x", "bad_w", "y_null", "y_misaligned", "ws_small",
+                                  "ws_misaligned", "dtype"])
+def test_gemm_w4a4_rejects_bad_arguments(case):
+    x = _packed(kind=rz.RAZER_ACT, rows=2, cols=32, off=(-2, -2))
+    w = _packed(rows=8, cols=32)
+    y, ws, wsb, dt = 0x7000, 0x10000, 1 << 20, rz.RAZER_BF16
+    if case == "cols_differ":
+        w.cols = 48
+    elif case == "bad_x":
+        x.cols = 24
+    elif case == "bad_w":
+        w.sv_off_half[1] = 9
+    elif case == "y_null":
+        y = 0
+    elif case == "y_misaligned":
+        y = 0x7004
+    elif case == "ws_small":
+        wsb = 16
+    elif case == "ws_misaligned":
+        ws = 0x10010
+    elif case == "dtype":
+        dt = 9
+    st = rz.lib().razer_gemm_w4a4(ctypes.byref(x), ctypes.byref(w), ctypes.c_void_p(y), dt,
+                                  ctypes.c_void_p(ws), wsb, None)
+    assert st == rz.RAZER_E_INVALID
+
+
+def test_gemm_w4a4_workspace_holds_both_intermediates():
+    m, n, k = 7, 40, 96
+    assert rz.razer_workspace_bytes(rz.RAZER_OP_GEMM_W4A4, m, n, k) >= m * k * 2 + m * n * 4
+    assert rz.razer_workspace_bytes(rz.RAZER_OP_GEMM_W4A4, 0, n, k) == 0

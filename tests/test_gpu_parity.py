@@ -368,14 +368,18 @@ def test_gemm_small_batch_70b_sampled(m):
                          torch.bfloat16)
 
 
-def test_gemm_prefill_sampled():
-    """Prefill product M=2048, N=28672, K=8192 (bf16), checked on sampled columns."""
-    _need_gpu()
+@functools.lru_cache(maxsize=1)
+def _prefill_weight_packed() -> oracle.Packed:
     log("prefill: generating W ...")
     w = synth.prefill_weight()
     log("prefill: oracle encode ...")
-    ref = oracle.quantize_weight(w, (-2, 4))
-    del w
+    return oracle.quantize_weight(w, (-2, 4))
+
+
+def test_gemm_prefill_sampled():
+    """Prefill product M=2048, N=28672, K=8192 (bf16), checked on sampled columns."""
+    _need_gpu()
+    ref = _prefill_weight_packed()
     t = to_device(ref)
     x = synth.prefill_x()
     log("prefill: gpu gemm ...")
@@ -513,3 +517,55 @@ def test_offset_sse_full_size_prefill_weight():
     assert abs(got[4 + 7] - ref4) <= 1e-9 * ref4
     del wd
     torch.cuda.empty_cache()
+
+
+# ---- W4A4 product ------------------------------------------------------------------
+
+W4A4_CASES = [(1, 512, 1024, torch.float32), (1, 4096, 14336, torch.float16), (3, 100, 48, torch.bfloat16),
+              (8, 4096, 4096, torch.bfloat16), (32, 1000, 512, torch.float32), (256, 512, 1024, torch.bfloat16),
+              (300, 130, 272, torch.float16)]
+
+
+def _w4a4_operands(m, n, k, x_kind=oracle.ACT, x_offsets=(-2,)):
+    rng = np.random.default_rng(m * 7919 + n * 31 + k)
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    x[:, 3] *= 20  # an outlier channel
+    w = (rng.standard_t(5, (n, k)) * 0.02).astype(np.float32)
+    return oracle.quantize(x_kind, x, x_offsets), oracle.quantize_weight(w, (-2, 4))
+
+
+@pytest.mark.parametrize("m,n,k,ydt", W4A4_CASES)
+def test_gemm_w4a4_matches_oracle(m, n, k, ydt):
+    _need_gpu()
+    log(f"w4a4 {m}x{n}x{k} {ydt}")
+    xp, wp = _w4a4_operands(m, n, k)
+    y = rz.razer_gemm_w4a4(to_device(xp), to_device(wp), ydt).cpu().double().numpy()
+    y_ref, nrm = oracle.gemm_w4a4(xp, wp)
+    assert_product_close(y, y_ref, nrm, f"w4a4 {m}x{n}x{k}", ydt)
+
+
+def test_gemm_w4a4_weight_kind_left_operand():
+    # a left operand with the weight encoding and offsets (-7, 7): special
+    # values +/-2.5 and +/-9.5 times E3M3 scales need 9 significant bits
+    _need_gpu()
+    xp, wp = _w4a4_operands(16, 96, 256, oracle.WEIGHT, (-7, 7))
+    y = rz.razer_gemm_w4a4(to_device(xp), to_device(wp), torch.float32).cpu().double().numpy()
+    y_ref, nrm = oracle.gemm_w4a4(xp, wp)
+    assert_product_close(y, y_ref, nrm, "w4a4 weight-kind x", torch.float32)
+
+
+def test_gemm_w4a4_prefill_sampled():
+    """W4A4 at the prefill shape M=2048, N=28672, K=8192, on sampled columns."""
+    _need_gpu()
+    wp = _prefill_weight_packed()
+    log("w4a4 prefill: oracle act encode ...")
+    xp = oracle.quantize_act(synth.prefill_x().float().numpy(), (-2,))
+    log("w4a4 prefill: gpu ...")
+    y = rz.razer_gemm_w4a4(to_device(xp), to_device(wp), torch.bfloat16)
+    torch.cuda.synchronize()
+    cols = np.random.default_rng(4404).choice(28672, 16, replace=False)
+    yc = y[:, torch.from_numpy(cols).cuda()].cpu().double().numpy()
+    log("w4a4 prefill: oracle product on 16 columns ...")
+    y_ref, nrm = oracle.gemm_w4a4(xp, wp, cols)
+    assert_product_close(yc, y_ref, nrm, "w4a4 prefill (16 sampled columns x 2048 rows)", torch.bfloat16)
+    assert torch.isfinite(y).all()
