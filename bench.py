@@ -303,6 +303,17 @@ def bench_rows(torch, rz, synth, args, decode_base):
         "workload": "W [28672,8192] fp32, 4 candidates", "ms": ms_q, "gelem_per_s": n_el / ms_q / 1e6,
         "gbs_1read": n_el * (4 + 0.5625) / ms_q / 1e6,
         "frac_hbm_1read": n_el * (4 + 0.5625) / ms_q / 1e6 / HBM_PEAK_GBS}
+    # W4A4 at the prefill shape: x encoded online (timed separately above), then
+    # the product of the two packed tensors
+    xq = rz.razer_quantize_act(x)
+    w4 = torch.empty(rz.razer_workspace_bytes(rz.RAZER_OP_GEMM_W4A4, 2048, 28672, 8192), dtype=torch.uint8,
+                     device=dev)
+    t = GraphTimer(torch, lambda: rz.razer_gemm_w4a4(xq, wp, out=y, workspace=w4))
+    ms_44 = t.time(10)
+    rows["gemm_w4a4_prefill"] = {
+        "workload": "RaZeR-A4 x [2048,8192] (from bf16 N(0,1)) x RaZeR-W4 W [28672,8192] -> bf16",
+        "ms": ms_44, "tflops": flops / ms_44 / 1e9, "frac_mfma": flops / ms_44 / 1e9 / MFMA_BF16_PEAK_TFLOPS}
+    del t, xq, w4
     out = torch.empty((28672, 8192), dtype=torch.bfloat16, device=dev)
     t = GraphTimer(torch, lambda: rz.razer_dequant(wp, out=out))
     ms_d = t.time(10)
