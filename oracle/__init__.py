@@ -161,7 +161,13 @@ class Packed:
         return out
 
 
-def quantize(kind: int, x, offsets, remap: bool = True) -> Packed:
+MODE_PLAIN, MODE_RAZER, MODE_FOUR_OVER_SIX = 0, 1, 2
+
+
+def quantize(kind: int, x, offsets, remap: bool = True, four_over_six: bool = False) -> Packed:
+    """Encode x (RaZeR, plain NVFP4 when not remap, or the Four Over Six
+    baseline when four_over_six: plain FP4 with a per-block choice of the
+    max -> 6 or max -> 4 scale)."""
     x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
     if x.ndim != 2:
         raise ValueError("x must be 2-D")
@@ -170,19 +176,20 @@ def quantize(kind: int, x, offsets, remap: bool = True) -> Packed:
     codes = np.zeros(rows * cols // 2, dtype=np.uint8)
     scales = np.zeros(rows * cols // 16, dtype=np.uint8)
     ts = np.zeros(1, dtype=np.float32)
-    rc = lib().rzo_quantize(kind, _ptr(x), rows, cols, _ptr(off), int(remap), _ptr(codes),
+    mode = MODE_FOUR_OVER_SIX if four_over_six else (MODE_RAZER if remap else MODE_PLAIN)
+    rc = lib().rzo_quantize(kind, _ptr(x), rows, cols, _ptr(off), mode, _ptr(codes),
                             _ptr(scales), _ptr(ts))
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
     return Packed(kind, rows, cols, offsets, codes, scales, ts[0])
 
 
-def quantize_weight(w, offsets=(-2, 4), remap: bool = True) -> Packed:
-    return quantize(WEIGHT, w, offsets, remap)
+def quantize_weight(w, offsets=(-2, 4), remap: bool = True, four_over_six: bool = False) -> Packed:
+    return quantize(WEIGHT, w, offsets, remap, four_over_six)
 
 
-def quantize_act(x, offsets=(-2,), remap: bool = True) -> Packed:
-    return quantize(ACT, x, offsets, remap)
+def quantize_act(x, offsets=(-2,), remap: bool = True, four_over_six: bool = False) -> Packed:
+    return quantize(ACT, x, offsets, remap, four_over_six)
 
 
 SECOND_PAIR_OFFSETS = tuple(range(-7, 8))  # offsets tried for the second weight pair

@@ -22,6 +22,11 @@
  *   - fp32 op order: r = amax_b / amax_t; sb_real = r * S_MAX; D = sb * st;
  *     R = 1 / D; y = x * R (no fused multiply-add anywhere; build with
  *     -ffp-contract=off)
+ *   - Four Over Six baseline: the same tensor scale; per block the second
+ *     candidate scale is the nearest code to sb_real * 1.5 (max -> 4,
+ *     saturating like any scale code); both candidates are plain FP4 and the
+ *     block keeps the one with the smaller fp64 squared error in real units,
+ *     a tie keeping max -> 6
  */
 #include "razer_oracle.h"
 
@@ -156,9 +161,46 @@ static int valid_offsets(int kind, const int8_t* off) {
   return 1;
 }
 
+/* One block at real block scale sb_real (in units of the tensor scale): the
+ * scale code is the nearest code to sb_real, the elements are divided by the
+ * decoded scale times st and rounded (with the special-value search when
+ * remap).  Returns the scale code; 0 means the block is stored as zero (the
+ * code underflows or the scale product does), and then c16 is all +0. */
+static int encode_at_scale(int kind, const float* xb, float sb_real, float st, const double* cand,
+                           int ncand, int remap, uint8_t* c16, int* sel) {
+  memset(c16, 0, 16);
+  *sel = 0;
+  int scode = rzo_scale_round(kind, sb_real);
+  if (scode == 0) return 0;
+  float sb = (float)rzo_scale_value(kind, scode);
+  float d = sb * st;
+  float rcp = 1.0f / d;
+  if (!isfinite(rcp)) return 0;
+  float y[16];
+  for (int j = 0; j < 16; j++) y[j] = xb[j] * rcp;
+  rzo_encode_block_scaled(y, 16, cand, ncand, remap, c16, sel);
+  return scode;
+}
+
+/* Squared error of a plain-FP4 block (no special value) in real units:
+ * sum over j = 0..15, in that order, of (x_j - value_j * sb * st)^2 in fp64.
+ * value * sb * st is exact in fp64 (3 + 4 + 24 significant bits); the
+ * difference, the square and each partial sum are rounded once each. */
+static double block_sse(int kind, const float* xb, const uint8_t* c16, int scode, float st) {
+  double sb = scode == 0 ? 0.0 : rzo_scale_value(kind, scode);
+  double sse = 0.0;
+  for (int j = 0; j < 16; j++) {
+    double q = rzo_fp4_value(c16[j]) * sb * (double)st;
+    double e = (double)xb[j] - q;
+    sse += e * e;
+  }
+  return sse;
+}
+
 int rzo_quantize(int kind, const float* x, int64_t rows, int64_t cols, const int8_t* off_half,
-                 int remap, uint8_t* codes, uint8_t* scales, float* tensor_scale) {
+                 int mode, uint8_t* codes, uint8_t* scales, float* tensor_scale) {
   if ((kind != RZO_WEIGHT && kind != RZO_ACT) || rows < 0 || cols < 0 || cols % 16 != 0 ||
+      mode < RZO_MODE_PLAIN || mode > RZO_MODE_FOUR_OVER_SIX ||
       !off_half || !valid_offsets(kind, off_half))
     return -1;
   int64_t n = rows * cols, nblk = n / 16;
@@ -217,17 +259,24 @@ int rzo_quantize(int kind, const float* x, int64_t rows, int64_t cols, const int
     }
     float r = amax_b / amax;
     float sb_real = r * smax;
-    int scode = rzo_scale_round(kind, sb_real);
-    if (scode == 0) continue; /* block underflows: all +0, scale byte 0 */
-    float sb = (float)rzo_scale_value(kind, scode);
-    float d = sb * st;
-    float rcp = 1.0f / d;
-    if (!isfinite(rcp)) continue; /* scale product underflows: treated as zero block */
-    float y[16];
-    for (int j = 0; j < 16; j++) y[j] = xb[j] * rcp;
     uint8_t c16[16];
     int sel = 0;
-    rzo_encode_block_scaled(y, 16, cand, ncand, remap, c16, &sel);
+    int scode = encode_at_scale(kind, xb, sb_real, st, cand, ncand, mode == RZO_MODE_RAZER, c16, &sel);
+    if (mode == RZO_MODE_FOUR_OVER_SIX) {
+      /* [Four Over Six] Technical framework / key innovation: a block may
+       * instead be scaled so that its maximum lands on 4 rather than 6 (block
+       * scale 6/4 times larger); the block keeps whichever of the two plain
+       * NVFP4 encodings has the smaller squared error in real units (ties keep
+       * the usual max -> 6 scale). */
+      uint8_t c4[16];
+      int sel4 = 0;
+      int scode4 = encode_at_scale(kind, xb, sb_real * 1.5f, st, cand, ncand, 0, c4, &sel4);
+      if (block_sse(kind, xb, c4, scode4, st) < block_sse(kind, xb, c16, scode, st)) {
+        memcpy(c16, c4, sizeof c16);
+        scode = scode4;
+      }
+    }
+    if (scode == 0) continue; /* zero block: all +0, scale byte 0 */
     for (int j = 0; j < 8; j++) codes[8 * b + j] = (uint8_t)(c16[2 * j] | (c16[2 * j + 1] << 4));
     /* Metadata in the freed scale bits ([notes] Key design 1 and the complete
      * example): bit 7 = sign of the chosen special value; for weights bit 6

@@ -14,6 +14,8 @@
  *             Zero Remapping" (papernotes.org notes)
  *   [summary] "Technical Summary: RaZeR - Pushing the Limits of NVFP4
  *             Quantization with Redundant Zero Remapping" (gist.science)
+ *   [Four Over Six] "Four Over Six: More Accurate NVFP4 Quantization with
+ *             Adaptive Block Scaling" (the baseline encoder only)
  *
  * Pins (tests/test_oracle_pins.py): FP4 set, special-value rule, E4M3/E3M3
  * tables and rounding (torch float8_e4m3fn), FP4 rounding (closed form with
@@ -39,6 +41,12 @@ extern "C" {
 
 enum { RZO_WEIGHT = 0, RZO_ACT = 1 };
 
+/* Encoder modes: plain NVFP4 (same scale format, no special value), RaZeR
+ * (special-value remap), and the Four Over Six baseline (plain FP4; each block
+ * takes the max -> 6 or the max -> 4 block scale, whichever has the smaller
+ * squared error in real units, ties to max -> 6). */
+enum { RZO_MODE_PLAIN = 0, RZO_MODE_RAZER = 1, RZO_MODE_FOUR_OVER_SIX = 2 };
+
 /* FP4-E2M1 value of a 4-bit code (bit 3 = sign); code 8 is -0.0. */
 double rzo_fp4_value(int code);
 /* Index 0..7 of the FP4 magnitude nearest to a >= 0; ties go to the even index. */
@@ -61,10 +69,11 @@ void rzo_encode_block_scaled(const float* y, int n, const double* cand, int ncan
 
 /* Full-tensor encode.  x: fp32 [rows, cols] (fp16/bf16 inputs are widened
  * exactly by the caller).  off_half: weight -> 2 entries, act -> 1 entry, each
- * in [-7, 7] (special value magnitude 6 + off/2).  remap = 0 gives the plain
- * NVFP4 baseline with the same scale format.  Returns 0, or -1 on bad args. */
+ * in [-7, 7] (special value magnitude 6 + off/2).  mode: RZO_MODE_*; the plain
+ * and Four Over Six modes never write the special-value code.  Returns 0, or
+ * -1 on bad args. */
 int rzo_quantize(int kind, const float* x, int64_t rows, int64_t cols,
-                 const int8_t* off_half, int remap, uint8_t* codes, uint8_t* scales,
+                 const int8_t* off_half, int mode, uint8_t* codes, uint8_t* scales,
                  float* tensor_scale);
 
 /* Decoded value (no scaling) of element code `code` in a block with scale byte `sbyte`. */
