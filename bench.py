@@ -200,6 +200,14 @@ def run_launches(rz, launches):
 
 # ---- other rows --------------------------------------------------------------------
 
+def rel_sse(torch, rz, x, packed):
+    """sum (x - dequant(packed))^2 / sum x^2, in fp64 (a quality figure, not timed)."""
+    d = rz.razer_dequant(packed, torch.float32)
+    e = float(torch.sum((x.float() - d).double().square()))
+    del d
+    return e / float(torch.sum(x.double().square()))
+
+
 def bench_rows(torch, rz, synth, args, decode_base):
     dev = torch.device("cuda:0")
     rows = {}
@@ -287,8 +295,28 @@ def bench_rows(torch, rz, synth, args, decode_base):
                "ms": ms_o, "gelem_per_s_per_offset": 15 * 28672 * 8192 / ms_o / 1e6,
                "best_offset": best,
                "sse_best_over_default_4": float(sse_h[best + 7] / sse_h[4 + 7])}
-    del t, w, wso
+    # Four Over Six baseline encoder on the same weight: its encode time and
+    # the relative squared error of each encoder on this weight
+    wf = rz.PackedTensor(rz.RAZER_WEIGHT, 28672, 8192, (-2, 4), dev, rz.RAZER_FLAG_FOUR_OVER_SIX)
+    t = GraphTimer(torch, lambda: rz.razer_quantize_weight(w, out=wf))
+    ms_f = t.time(5)
+    err_w = {"nvfp4": rel_sse(torch, rz, w, rz.razer_quantize_weight(w, (-2, 4), remap=False)),
+             "four_over_six": rel_sse(torch, rz, w, wf),
+             "razer_pairs_-2_4": rel_sse(torch, rz, w, wp),
+             f"razer_pairs_-2_{best}": rel_sse(torch, rz, w, rz.razer_quantize_weight(w, (-2, best)))}
+    del t, w, wso, wf
     torch.cuda.empty_cache()
+    xa = synth.act_quant_x().to(dev)
+    err_a = {"nvfp4": rel_sse(torch, rz, xa, rz.razer_quantize_act(xa, remap=False)),
+             "four_over_six": rel_sse(torch, rz, xa, rz.razer_quantize_act(xa, four_over_six=True)),
+             "razer_pair_-2": rel_sse(torch, rz, xa, rz.razer_quantize_act(xa))}
+    del xa
+    torch.cuda.empty_cache()
+    fos_row = {"workload": "Four Over Six encode of W [28672,8192] fp32; relative squared error "
+                           "sum (x - dequant)^2 / sum x^2 of each encoder on that weight and on "
+                           "X [4096,8192] bf16",
+               "ms": ms_f, "gelem_per_s": 28672 * 8192 / ms_f / 1e6,
+               "rel_sse_weight": err_w, "rel_sse_act": err_a}
     x = synth.prefill_x().to(dev)
     y = torch.empty((2048, 28672), dtype=torch.bfloat16, device=dev)
     t = GraphTimer(torch, lambda: rz.razer_gemm(x, wp, out=y))
@@ -299,6 +327,7 @@ def bench_rows(torch, rz, synth, args, decode_base):
         "ms": ms, "tflops": flops / ms / 1e9, "frac_mfma": flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS}
     n_el = 28672 * 8192
     rows["offset_search_prefill"] = off_row
+    rows["four_over_six_prefill"] = fos_row
     rows["quantize_weight_prefill"] = {
         "workload": "W [28672,8192] fp32, 4 candidates", "ms": ms_q, "gelem_per_s": n_el / ms_q / 1e6,
         "gbs_1read": n_el * (4 + 0.5625) / ms_q / 1e6,

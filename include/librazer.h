@@ -87,7 +87,18 @@ enum {
    * scale format: the comparator of the pages' main table, used to measure
    * what the special-value search costs ([notes] Key design 2 states the
    * activation search adds under 2% to quantizer time). */
-  RAZER_FLAG_NO_REMAP = 1u
+  RAZER_FLAG_NO_REMAP = 1u,
+  /* Encode with the Four Over Six baseline (page "Four Over Six: More Accurate
+   * NVFP4 Quantization with Adaptive Block Scaling", technical framework and
+   * key innovation): plain FP4 (no special value), and each block takes the
+   * block scale whose code is nearest to S_MAX * amax_block / amax_tensor
+   * (max -> 6) or to 1.5 times that (max -> 4, saturating at the format
+   * maximum), whichever gives the smaller squared error against the input in
+   * real units (summed in fp64 in element order; a tie keeps max -> 6).  The
+   * tensor scale and the packed layout are unchanged, so every decoding call
+   * reads such a tensor as plain NVFP4.  Takes precedence over NO_REMAP.
+   * The quantize calls reject any other flag bit with RAZER_E_INVALID. */
+  RAZER_FLAG_FOUR_OVER_SIX = 2u
 };
 
 typedef struct razer_packed {

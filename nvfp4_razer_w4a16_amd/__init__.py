@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_HERE, "librazer.so")
 RAZER_OK, RAZER_E_INVALID, RAZER_E_UNSUPPORTED, RAZER_E_HIP = 0, 1, 2, 3
 RAZER_F32, RAZER_F16, RAZER_BF16 = 0, 1, 2
 RAZER_WEIGHT, RAZER_ACT = 0, 1
-RAZER_FLAG_NO_REMAP = 1
+RAZER_FLAG_NO_REMAP, RAZER_FLAG_FOUR_OVER_SIX = 1, 2
 RAZER_OP_QUANTIZE_WEIGHT, RAZER_OP_QUANTIZE_ACT, RAZER_OP_GEMV, RAZER_OP_GEMM = 0, 1, 2, 3
 RAZER_OP_OFFSET_SEARCH, RAZER_OP_GEMM_W4A4 = 4, 5
 SECOND_PAIR_OFFSETS = tuple(range(-7, 8))  # entry i of razer_weight_offset_sse is offset i - 7
@@ -147,13 +147,19 @@ def _workspace(op, m, n, k, device, workspace):
     return workspace, workspace.numel() * workspace.element_size()
 
 
-def _quantize(fn, op, kind, x, offsets, remap, out, workspace, stream):
+def _encoder_flags(remap: bool, four_over_six: bool) -> int:
+    if four_over_six:
+        return RAZER_FLAG_FOUR_OVER_SIX
+    return 0 if remap else RAZER_FLAG_NO_REMAP
+
+
+def _quantize(fn, op, kind, x, offsets, flags, out, workspace, stream):
     if x.dim() != 2:
         raise ValueError("expected a 2-D tensor")
     x = x.contiguous()
     rows, cols = x.shape
     if out is None:
-        out = PackedTensor(kind, rows, cols, offsets, x.device, 0 if remap else RAZER_FLAG_NO_REMAP)
+        out = PackedTensor(kind, rows, cols, offsets, x.device, flags)
     s = out.struct()
     ws, wsb = _workspace(op, rows, 0, cols, x.device, workspace)
     _check(fn(ctypes.c_void_p(x.data_ptr()), _dtype_code(x.dtype), ctypes.byref(s),
@@ -163,17 +169,22 @@ def _quantize(fn, op, kind, x, offsets, remap, out, workspace, stream):
 
 
 def razer_quantize_weight(w: torch.Tensor, offsets=DEFAULT_WEIGHT_OFFSETS, remap: bool = True,
-                          out: PackedTensor | None = None, workspace=None, stream=None):
-    """Offline RaZeR weight encoding of w [N, K] (fp32/fp16/bf16, on the GPU)."""
+                          out: PackedTensor | None = None, workspace=None, stream=None,
+                          four_over_six: bool = False):
+    """Offline RaZeR weight encoding of w [N, K] (fp32/fp16/bf16, on the GPU).
+    remap=False gives plain NVFP4, four_over_six=True the Four Over Six
+    baseline; a given `out` carries its own flags instead."""
     return _quantize(lib().razer_quantize_weight, RAZER_OP_QUANTIZE_WEIGHT, RAZER_WEIGHT, w,
-                     offsets, remap, out, workspace, stream)
+                     offsets, _encoder_flags(remap, four_over_six), out, workspace, stream)
 
 
 def razer_quantize_act(x: torch.Tensor, offsets=DEFAULT_ACT_OFFSETS, remap: bool = True,
-                       out: PackedTensor | None = None, workspace=None, stream=None):
-    """Online RaZeR activation encoding of x [rows, cols] (fp16/bf16, on the GPU)."""
+                       out: PackedTensor | None = None, workspace=None, stream=None,
+                       four_over_six: bool = False):
+    """Online RaZeR activation encoding of x [rows, cols] (fp16/bf16, on the GPU).
+    remap / four_over_six / out as for razer_quantize_weight."""
     return _quantize(lib().razer_quantize_act, RAZER_OP_QUANTIZE_ACT, RAZER_ACT, x, offsets,
-                     remap, out, workspace, stream)
+                     _encoder_flags(remap, four_over_six), out, workspace, stream)
 
 
 def razer_dequant(t: PackedTensor, dtype: torch.dtype = torch.float32, out=None, stream=None):

@@ -67,12 +67,16 @@ rz::PackedView view_of(const razer_packed* p) {
   return v;
 }
 
+static_assert(RAZER_FLAG_NO_REMAP == rz::kFlagNoRemap && RAZER_FLAG_FOUR_OVER_SIX == rz::kFlagFourOverSix,
+              "encoder flag values");
+
 razer_status status_of(hipError_t e) { return e == hipSuccess ? RAZER_OK : RAZER_E_HIP; }
 
 razer_status quantize_common(const void* x, razer_dtype dt, const razer_packed* out, void* ws,
                              size_t ws_bytes, void* stream, int kind) {
   razer_status s = check_packed(out, true);
   if (s != RAZER_OK) return s;
+  if (out->flags & ~(uint32_t)(RAZER_FLAG_NO_REMAP | RAZER_FLAG_FOUR_OVER_SIX)) return RAZER_E_INVALID;
   if (out->kind != kind || !dtype_ok(dt)) return RAZER_E_INVALID;
   const int64_t n = out->rows * out->cols;
   if (n > 0 && (!x || !aligned(x, 16))) return RAZER_E_INVALID;

@@ -8,9 +8,13 @@
 
 namespace rz {
 
+// Encoder flags (the values of the public RAZER_FLAG_* constants).
+constexpr uint32_t kFlagNoRemap = 1u;       // plain NVFP4: no special value
+constexpr uint32_t kFlagFourOverSix = 2u;   // plain FP4, per-block max -> 6 or max -> 4 scale
+
 struct PackedView {
   int kind;          // 0 weight (E3M3, 4 candidates), 1 activation (E4M3, 2 candidates)
-  uint32_t flags;    // bit 0: plain NVFP4 (no special value)
+  uint32_t flags;    // kFlag* bits
   int64_t rows, cols;
   int off_half[2];   // special-value offsets in units of 0.5
   uint8_t* codes;

@@ -264,6 +264,23 @@ __device__ __forceinline__ uint32_t search_fast(const float (&y)[16], float ymax
   return sel;
 }
 
+// FP4 codes with the gfx950 conversion: nearest on the E2M1 grid, ties to the
+// even code (0.25, 1.25, 2.5, 5 go down; 0.75, 1.75, 3.5 go up), saturating at
+// 6, sign in bit 3.  A negative value that rounds to zero comes out as 0b1000
+// and is cleared to +0.
+__device__ __forceinline__ void fp4_pack16(const float (&y)[16], uint32_t (&w)[2]) {
+#pragma unroll
+  for (int h = 0; h < 2; h++) {
+    w[h] = 0u;
+    w[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[h], y[8 * h + 0], y[8 * h + 1], 1.0f, 0);
+    w[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[h], y[8 * h + 2], y[8 * h + 3], 1.0f, 1);
+    w[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[h], y[8 * h + 4], y[8 * h + 5], 1.0f, 2);
+    w[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[h], y[8 * h + 6], y[8 * h + 7], 1.0f, 3);
+    const uint32_t nz = (w[h] & 0x77777777u) + 0x77777777u;  // bit 3: magnitude != 0
+    w[h] &= ~(~nz & 0x88888888u);                            // -0 -> +0
+  }
+}
+
 template <int KIND>
 __device__ __forceinline__ void encode_block(const float (&xf)[16], float amax, float st,
                                              const EncodeParams& prm, uint2& cw, uint32_t& sbyte) {
@@ -283,23 +300,11 @@ __device__ __forceinline__ void encode_block(const float (&xf)[16], float amax, 
   const float rcp = 1.0f / d;
   if (!(rcp < INFINITY)) return;  // scale product underflowed: zero block
 
-  // FP4 codes with the gfx950 conversion: nearest on the E2M1 grid, ties to
-  // the even code (0.25, 1.25, 2.5, 5 go down; 0.75, 1.75, 3.5 go up),
-  // saturating at 6, sign in bit 3.  A negative value that rounds to zero
-  // comes out as 0b1000 and is cleared to +0.
   float y[16];
 #pragma unroll
   for (int j = 0; j < 16; j++) y[j] = xf[j] * rcp;
-  uint32_t w[2] = {0u, 0u};
-#pragma unroll
-  for (int h = 0; h < 2; h++) {
-    w[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[h], y[8 * h + 0], y[8 * h + 1], 1.0f, 0);
-    w[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[h], y[8 * h + 2], y[8 * h + 3], 1.0f, 1);
-    w[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[h], y[8 * h + 4], y[8 * h + 5], 1.0f, 2);
-    w[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[h], y[8 * h + 6], y[8 * h + 7], 1.0f, 3);
-    const uint32_t nz = (w[h] & 0x77777777u) + 0x77777777u;  // bit 3: magnitude != 0
-    w[h] &= ~(~nz & 0x88888888u);                            // -0 -> +0
-  }
+  uint32_t w[2];
+  fp4_pack16(y, w);
   uint32_t sel = 0u;
   const float ymax = amax_b * rcp;
   if (prm.remap && ymax < kFastCap) {
@@ -349,6 +354,79 @@ __device__ __forceinline__ void encode_block(const float (&xf)[16], float amax, 
   sbyte = (KIND == kWeight) ? (((sel & 1u) << 7) | ((sel >> 1) << 6) | scode) : ((sel << 7) | scode);
 }
 
+// ---- Four Over Six baseline (plain FP4, adaptive block scale) ----------------
+// Page "Four Over Six: More Accurate NVFP4 Quantization with Adaptive Block
+// Scaling", technical framework and key innovation: a block may be scaled so
+// that its maximum maps to 4 instead of 6.  Each block is encoded twice as
+// plain FP4, at the nearest scale code to sb_real (max -> 6) and to
+// 1.5 * sb_real (max -> 4), and keeps the encoding whose squared error in real
+// units is smaller; a tie keeps max -> 6.
+
+// Squared error of a plain-FP4 block: sum over j in order of
+// (x_j - value_j * sb * st)^2 in fp64.  value * sb * st is exact in fp64; the
+// difference, the square and each partial sum round once each, so no
+// contraction into fused multiply-adds.
+__device__ __forceinline__ double plain_block_sse(const float (&xf)[16], const uint32_t (&w)[2],
+                                                  float sb, float st) {
+#pragma clang fp contract(off)
+  const double s = (double)sb * (double)st;
+  double sse = 0.0;
+#pragma unroll
+  for (int j = 0; j < 16; j++) {
+    const uint32_t c = (w[j >> 3] >> (4 * (j & 7))) & 15u;
+    const double v = 0.5 * (double)fp4_mag_x2(c & 7u);
+    const double q = (c & 8u) ? -(v * s) : v * s;
+    const double e = (double)xf[j] - q;
+    sse = sse + e * e;
+  }
+  return sse;
+}
+
+// One plain-FP4 encoding at real block scale sb_real; returns the scale code
+// (0: the block is stored as zero) and the block's squared error.
+template <int KIND>
+__device__ __forceinline__ uint32_t plain_at_scale(const float (&xf)[16], float sb_real, float st,
+                                                   uint32_t (&w)[2], double& sse) {
+  w[0] = 0u;
+  w[1] = 0u;
+  uint32_t scode = round_scale<KIND>(sb_real);
+  float sb = 0.0f;
+  if (scode != 0u) {
+    sb = scale_of_code<KIND>(scode);
+    const float d = sb * st;
+    const float rcp = 1.0f / d;
+    if (rcp < INFINITY) {
+      float y[16];
+#pragma unroll
+      for (int j = 0; j < 16; j++) y[j] = xf[j] * rcp;
+      fp4_pack16(y, w);
+    } else {
+      scode = 0u;
+      sb = 0.0f;
+    }
+  }
+  sse = plain_block_sse(xf, w, sb, st);
+  return scode;
+}
+
+template <int KIND>
+__device__ __forceinline__ void encode_block_fos(const float (&xf)[16], float amax, float st,
+                                                 uint2& cw, uint32_t& sbyte) {
+  constexpr float kSMax = KIND == kWeight ? 30.0f : 448.0f;
+  float amax_b = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 16; j++) amax_b = fmaxf(amax_b, fabsf(xf[j]));
+  const float r = amax_b / amax;
+  const float sb_real = r * kSMax;
+  uint32_t w6[2], w4[2];
+  double e6, e4;
+  const uint32_t c6 = plain_at_scale<KIND>(xf, sb_real, st, w6, e6);
+  const uint32_t c4 = plain_at_scale<KIND>(xf, sb_real * 1.5f, st, w4, e4);
+  const bool four = e4 < e6;
+  cw = four ? make_uint2(w4[0], w4[1]) : make_uint2(w6[0], w6[1]);
+  sbyte = four ? c4 : c6;
+}
+
 // Block values from the 16 input elements' bytes (fp32: 4 x 16 B, 16-bit: 2 x 16 B).
 template <typename T> __device__ __forceinline__ void unpack_block(const u32x4_t* q, float (&v)[16]);
 template <> __device__ __forceinline__ void unpack_block<float>(const u32x4_t* q, float (&v)[16]) {
@@ -382,7 +460,7 @@ template <> __device__ __forceinline__ void unpack_block<_Float16>(const u32x4_t
 // back as one block per lane.  The next step's loads are in flight while a
 // step is encoded; the buffer descriptor is rebased per step, so a read past
 // the tensor returns zero and any tensor size works with 32-bit offsets.
-template <int KIND, typename T>
+template <int KIND, typename T, bool FOS>
 __global__ __launch_bounds__(256) void encode_kernel(const T* __restrict__ x, int64_t nblk,
                                                      const uint32_t* __restrict__ partial,
                                                      int npartial, uint2* __restrict__ codes,
@@ -443,7 +521,10 @@ __global__ __launch_bounds__(256) void encode_kernel(const T* __restrict__ x, in
     unpack_block<T>(q, xf);
     uint2 cw;
     uint32_t sbyte;
-    encode_block<KIND>(xf, amax, st, prm, cw, sbyte);
+    if constexpr (FOS)
+      encode_block_fos<KIND>(xf, amax, st, cw, sbyte);
+    else
+      encode_block<KIND>(xf, amax, st, prm, cw, sbyte);
     if (bb + lane < nblk) {
       codes[bb + lane] = cw;
       scales[bb + lane] = (uint8_t)sbyte;
@@ -473,13 +554,17 @@ static hipError_t run_quantize(const T* x, const PackedView& out, uint32_t* part
     prm.mag_x2[p] = c.mag_x2;
     prm.f[p] = make_pair_fast(out.off_half[p < npairs ? p : 0]);
   }
-  prm.remap = (out.flags & 1u) ? 0 : 1;
+  prm.remap = (out.flags & kFlagNoRemap) ? 0 : 1;
   int64_t g2 = (nblk + 255) / 256;
   const int64_t cap = (int64_t)device_cu_count() * 8;
   if (g2 > cap) g2 = cap;
   if (g2 < 1) g2 = 1;
-  hipLaunchKernelGGL((encode_kernel<KIND, T>), dim3((unsigned)g2), dim3(256), 0, stream, x, nblk,
-                     partial, (int)g1, (uint2*)out.codes, out.scales, out.tensor_scale, prm);
+  if (out.flags & kFlagFourOverSix)
+    hipLaunchKernelGGL((encode_kernel<KIND, T, true>), dim3((unsigned)g2), dim3(256), 0, stream, x,
+                       nblk, partial, (int)g1, (uint2*)out.codes, out.scales, out.tensor_scale, prm);
+  else
+    hipLaunchKernelGGL((encode_kernel<KIND, T, false>), dim3((unsigned)g2), dim3(256), 0, stream, x,
+                       nblk, partial, (int)g1, (uint2*)out.codes, out.scales, out.tensor_scale, prm);
   return hipGetLastError();
 }
 

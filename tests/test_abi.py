@@ -74,6 +74,8 @@ FAKE_WS = ctypes.c_void_p(0x5000)
     lambda s: setattr(s, "codes", 0x1008),             # misaligned codes
     lambda s: setattr(s, "kind", rz.RAZER_ACT),        # wrong kind for the weight encoder
     lambda s: setattr(s, "kind", 7),
+    lambda s: setattr(s, "flags", 4),                  # unknown encoder flag bit
+    lambda s: setattr(s, "flags", 0x80000002),
 ])
 def test_quantize_weight_rejects_bad_packed(mutate):
     s = _packed()

@@ -40,12 +40,12 @@ def log(*a):
 
 # ---- helpers -----------------------------------------------------------------
 
-def gpu_encode(kind, x_cpu: torch.Tensor, offsets, remap=True):
+def gpu_encode(kind, x_cpu: torch.Tensor, offsets, remap=True, four_over_six=False):
     x = x_cpu.cuda()
     if kind == oracle.WEIGHT:
-        p = rz.razer_quantize_weight(x, offsets, remap)
+        p = rz.razer_quantize_weight(x, offsets, remap, four_over_six=four_over_six)
     else:
-        p = rz.razer_quantize_act(x, offsets, remap)
+        p = rz.razer_quantize_act(x, offsets, remap, four_over_six=four_over_six)
     torch.cuda.synchronize()
     return p
 
@@ -252,6 +252,92 @@ def test_quantize_deterministic_across_calls():
     a = gpu_encode(oracle.WEIGHT, w, (-2, -5))
     b = gpu_encode(oracle.WEIGHT, w, (-2, -5))
     assert torch.equal(a.codes, b.codes) and torch.equal(a.scales, b.scales)
+
+
+# ---- Four Over Six baseline encoder ----------------------------------------------
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("kind", [oracle.WEIGHT, oracle.ACT])
+def test_quantize_four_over_six_parity(kind, dtype):
+    _need_gpu()
+    if kind == oracle.WEIGHT:
+        x, offs = pr1()[0].to(dtype), (-2, 4)
+    else:
+        x, offs = synth.act_quant_x(128, 4096).to(dtype), (-2,)
+    ref = oracle.quantize(kind, as_f32(x), offs, four_over_six=True)
+    p = gpu_encode(kind, x, offs, four_over_six=True)
+    assert_same_encoding(p, ref, as_f32(x), f"four over six kind {kind} {dtype}")
+    s = p.scales.cpu().numpy()
+    assert not (s >> (6 if kind == oracle.WEIGHT else 7)).any()  # no metadata bits
+    c = p.codes.cpu().numpy()
+    assert not ((c & 15) == 8).any() and not ((c >> 4) == 8).any()  # never the special code
+
+
+@pytest.mark.parametrize("name", sorted(EDGE))
+@pytest.mark.parametrize("kind,offsets", [(oracle.WEIGHT, (-2, -5)), (oracle.ACT, (-2,))])
+def test_quantize_four_over_six_edge_cases(name, kind, offsets):
+    _need_gpu()
+    x = EDGE[name]
+    ref = oracle.quantize(kind, x, offsets, four_over_six=True)
+    p = gpu_encode(kind, torch.from_numpy(x), offsets, four_over_six=True)
+    assert_same_encoding(p, ref, x, f"four over six edge {name} kind {kind}")
+
+
+def test_quantize_four_over_six_takes_precedence_over_no_remap():
+    _need_gpu()
+    w = pr1()[0]
+    ref = oracle.quantize_weight(w.numpy(), (-2, 4), four_over_six=True)
+    out = rz.PackedTensor(rz.RAZER_WEIGHT, w.shape[0], w.shape[1], (-2, 4), "cuda",
+                          rz.RAZER_FLAG_FOUR_OVER_SIX | rz.RAZER_FLAG_NO_REMAP)
+    rz.razer_quantize_weight(w.cuda(), (-2, 4), out=out)
+    torch.cuda.synchronize()
+    assert_same_encoding(out, ref, w.numpy(), "four over six | no remap")
+
+
+def test_quantize_four_over_six_prefill_weight_sampled():
+    """Four Over Six on the full W[28672, 8192] fp32 weight: every block's
+    encoding depends only on the block and the tensor scale, so the oracle
+    encodes a row sample together with the row holding the tensor maximum
+    (same tensor scale) and the GPU rows must match it byte for byte."""
+    _need_gpu()
+    w = synth.prefill_weight()
+    log("4/6 prefill W: gpu ...")
+    p = gpu_encode(oracle.WEIGHT, torch.from_numpy(w), (-2, 4), four_over_six=True)
+    rmax = int(np.abs(w).max(axis=1).argmax())
+    rows = sorted(set(np.random.default_rng(91).choice(w.shape[0], 96, replace=False).tolist()) | {rmax, 0, w.shape[0] - 1})
+    log("4/6 prefill W: oracle on", len(rows), "rows ...")
+    ref = oracle.quantize_weight(w[rows], (-2, 4), four_over_six=True)
+    k = w.shape[1]
+    codes = p.codes.cpu().numpy().reshape(w.shape[0], k // 2)[rows]
+    scales = p.scales.cpu().numpy().reshape(w.shape[0], k // 16)[rows]
+    ts = p.tensor_scale.cpu().numpy().view(np.uint32)[0]
+    assert ts == np.array([ref.tensor_scale], np.float32).view(np.uint32)[0]
+    np.testing.assert_array_equal(scales.reshape(-1), ref.scales)
+    np.testing.assert_array_equal(codes.reshape(-1), ref.codes)
+    frac4 = float(np.mean(scales != oracle.quantize_weight(w[rows], (-2, 4), remap=False).scales.reshape(scales.shape)))
+    log(f"4/6 prefill W: blocks taking max -> 4: {frac4:.3f}")
+    del p
+    torch.cuda.empty_cache()
+
+
+def test_four_over_six_weights_decode_through_the_products():
+    # The Four Over Six layout is plain NVFP4, so the unchanged decoders
+    # (dequant, GEMV, GEMM) read it exactly as the oracle's decoder does.
+    _need_gpu()
+    rng = np.random.default_rng(93)
+    w = (rng.standard_t(5, (300, 512)) * 0.02).astype(np.float32)
+    x = rng.standard_normal((5, 512)).astype(np.float32)
+    ref = oracle.quantize_weight(w, (-2, 4), four_over_six=True)
+    p = gpu_encode(oracle.WEIGHT, torch.from_numpy(w), (-2, 4), four_over_six=True)
+    assert_same_encoding(p, ref, w, "4/6 weight")
+    d = rz.razer_dequant(p, torch.float32).cpu().numpy()
+    np.testing.assert_array_equal(d, oracle.dequant_f32(ref))
+    xb = torch.from_numpy(x).to(torch.bfloat16)
+    y_ref, nrm = oracle.gemm(as_f32(xb), ref)
+    y = rz.razer_gemm(xb.cuda(), p, out_dtype=torch.float32).cpu().numpy()
+    assert_product_close(y, y_ref, nrm, "4/6 gemm")
+    y1 = rz.razer_gemv(xb[0].cuda(), p, out_dtype=torch.float32).cpu().numpy()
+    assert_product_close(y1[None], y_ref[:1], nrm[:1], "4/6 gemv")
 
 
 # ---- decoder parity ------------------------------------------------------------
