@@ -6,7 +6,9 @@ Llama-3-8B-shaped linear layers -- qkv [6144,4096], gate [14336,4096],
 up [14336,4096], down [4096,14336] -- with fp16 activations and RaZeR-W4
 weights (0.02 * Student-t(5)), over L distinct layer copies (default 8, 906 MB
 of packed weights, larger than the 256 MB Infinity Cache).  One step = one
-token through the L layers = 4L razer_gemv launches, replayed from a HIP graph.
+token through the L layers = 3L launches replayed from a HIP graph: razer_gemv
+for qkv and down, razer_gemv_group for gate and up (the two read the same x);
+--per-matrix times 4L razer_gemv launches instead (also reported as a row).
 ``value`` is algorithmic GB/s (packed weights + x + y + tensor scale, each
 counted once) over the timed steps.
 
@@ -17,7 +19,7 @@ synthetic workload; ``roofline`` for the GEMV kernel; ``cpu_baseline`` = the CPU
 oracle on one layer.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L]
-                       [--no-rows] [--no-cpu-baseline] [--eager]
+                       [--no-rows] [--no-cpu-baseline] [--eager] [--per-matrix]
        python bench.py --copy-calibration
        python bench.py --traffic-summary FETCH.csv WRITE.csv CAL_FETCH.csv CAL_WRITE.csv
 
@@ -175,6 +177,8 @@ def load_traffic(kernel_key, src_hash):
 # ---- headline: decode GEMV -----------------------------------------------------
 
 def setup_decode(torch, rz, synth, layers):
+    """Decode step launches over `layers` copies of the layer's weights: grouped
+    (qkv; gate and up in one launch, they read the same x; down) and per matrix."""
     dev = torch.device("cuda:0")
     names = ["qkv", "gate", "up", "down"]
     base = {}
@@ -188,14 +192,24 @@ def setup_decode(torch, rz, synth, layers):
     xs = {4096: synth.llama3_8b_decode_x(4096).to(dev).reshape(-1),
           14336: synth.llama3_8b_decode_x(14336).to(dev).reshape(-1)}
     ys = {n: torch.empty(base[n].rows, dtype=torch.float16, device=dev) for n in names}
-    launches = [(xs[m.cols], m, ys[n]) for layer in mats for n, m in layer.items()]
-    step_bytes = sum(gemv_bytes(m.rows, m.cols) for _, m, _ in launches)
-    return launches, step_bytes, base
+    out = {}
+    for kind, groups in (("grouped", [("qkv",), ("gate", "up"), ("down",)]),
+                         ("per_matrix", [(n,) for n in names])):
+        launches = [(xs[layer[g[0]].cols], [layer[n] for n in g], [ys[n] for n in g])
+                    for layer in mats for g in groups]
+        # algorithmic bytes: packed weights, x once per launch, y
+        step_bytes = sum(sum(packed_bytes(m.rows, m.cols) + 2 * m.rows for m in ws) + 2 * ws[0].cols
+                         for _, ws, _ in launches)
+        out[kind] = (launches, step_bytes)
+    return out, base
 
 
 def run_launches(rz, launches):
-    for x, w, y in launches:
-        rz.razer_gemv(x, w, out=y)
+    for x, ws, ys in launches:
+        if len(ws) == 1:
+            rz.razer_gemv(x, ws[0], out=ys[0])
+        else:
+            rz.razer_gemv_group(x, ws, outs=ys)
 
 
 # ---- other rows --------------------------------------------------------------------
@@ -387,6 +401,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--layers", type=int, default=8)
     ap.add_argument("--no-rows", action="store_true")
+    ap.add_argument("--per-matrix", action="store_true",
+                    help="one razer_gemv launch per matrix (gate and up not grouped)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -415,7 +431,8 @@ def main():
         return
 
     log("decode: generating and encoding weights ...")
-    launches, step_bytes, base = setup_decode(torch, rz, synth, args.layers)
+    steps, base = setup_decode(torch, rz, synth, args.layers)
+    launches, step_bytes = steps["per_matrix" if args.per_matrix else "grouped"]
     if args.eager:  # counter passes: plain launches, nothing timed
         for _ in range(args.warmup + args.steps):
             run_launches(rz, launches)
@@ -440,14 +457,24 @@ def main():
     traffic = load_traffic("gemv_decode", src)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "razer_gemv: gemv_kernel (qkv, gate, up) + smallm_kernel (down)",
+                "kernel": ("razer_gemv: gemv_kernel (qkv, gate, up) + smallm_kernel (down)" if args.per_matrix
+                           else "razer_gemv (qkv: gemv_kernel; down: smallm_kernel) + razer_gemv_group "
+                                "(gate and up: one gemv_kernel launch)"),
                 "avg_launch_us": round(avg_us, 3),
                 "algorithmic_bytes_per_launch": bytes_per_launch}
 
     rows = None
     if not args.no_rows:
+        # the other launch arrangement of the same step, for comparison
+        other = "grouped" if args.per_matrix else "per_matrix"
+        l2, b2 = steps[other]
+        ms2 = GraphTimer(torch, lambda: run_launches(rz, l2), warmup=1).time(args.steps)
+        decode_other = {"workload": f"the same decode step, {other.replace('_', ' ')} launches",
+                        "launches_per_step": len(l2), "us_per_step": ms2 * 1e3, "gbs": b2 / ms2 / 1e6,
+                        "frac_hbm": b2 / ms2 / 1e6 / HBM_PEAK_GBS}
         log("rows: encoders, small-batch sweep, prefill ...")
-        rows = bench_rows(torch, rz, synth, args, base)
+        rows = {f"decode_{other}": decode_other}
+        rows.update(bench_rows(torch, rz, synth, args, base))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -462,7 +489,8 @@ def main():
         "data": "synthetic (seeded Philox; Student-t(5)*0.02 weights, N(0,1) fp16 x with 8 channels x20)",
         "config": {"workload": f"llama3-8b decode GEMV: qkv 6144x4096, gate 14336x4096, "
                                f"up 14336x4096, down 4096x14336; M=1; {args.layers} layer copies; "
-                               "RaZeR-W4 weights, fp16 x and y",
+                               "RaZeR-W4 weights, fp16 x and y"
+                               + ("" if args.per_matrix else "; gate and up (same x) in one launch"),
                    "layers": args.layers, "m": 1, "launches_per_step": n_launch,
                    "bytes_per_step": step_bytes},
         "roofline": roofline, "cpu_baseline": cpu, "rows": rows,

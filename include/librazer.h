@@ -154,6 +154,25 @@ razer_status razer_dequant(const razer_packed* t, void* out, razer_dtype out_dt,
 razer_status razer_gemv(const void* x, razer_dtype x_dt, const razer_packed* w, void* y,
                         razer_dtype y_dt, void* ws, size_t ws_bytes, void* stream);
 
+/* Largest count accepted by razer_gemv_group. */
+#define RAZER_GEMV_GROUP_MAX 4
+
+/* Several batch-1 products that share one input vector, y_g[1, N_g] = x[1, K] *
+ * W_g^T for g < count, in one launch where the GEMV kernel serves them (the
+ * product of razer_gemv for each weight, [notes] Key design 3; sharing the
+ * launch is the counterpart of the pages' launch sizing for small matrices:
+ * two weights of one input, such as an MLP's gate and up projections, cost
+ * one launch and one ramp instead of two).  x: device [K] in F16 or BF16.
+ * w: host array of count packed-tensor descriptors (either kind, each with its
+ * own tensor scale and offsets) with equal cols K.  y: host array of count
+ * device outputs [N_g] in y_dt (16-byte aligned; may be NULL where N_g == 0).
+ * 1 <= count <= RAZER_GEMV_GROUP_MAX.  Each y_g is bitwise what razer_gemv
+ * writes for W_g.  No workspace.  Errors: RAZER_E_INVALID for a bad count,
+ * unequal K or any argument razer_gemv would reject; RAZER_E_UNSUPPORTED as
+ * for razer_gemv. */
+razer_status razer_gemv_group(const void* x, razer_dtype x_dt, const razer_packed* const* w,
+                              void* const* y, int count, razer_dtype y_dt, void* stream);
+
 /* Batched W4A16 product y[M, N] = x[M, K] * W^T ([notes] Key design 3;
  * [summary] §2.3: weight-only GEMM kernels for small and large batches).
  * x: device [m, K] row-major in F16 or BF16.  w: packed tensor [N, K] of either

@@ -29,7 +29,7 @@ RAZER_OP_OFFSET_SEARCH, RAZER_OP_GEMM_W4A4 = 4, 5
 SECOND_PAIR_OFFSETS = tuple(range(-7, 8))  # entry i of razer_weight_offset_sse is offset i - 7
 
 EXPORTED = ("razer_quantize_weight", "razer_quantize_act", "razer_dequant", "razer_gemv",
-            "razer_gemm", "razer_gemm_w4a4", "razer_weight_offset_sse", "razer_workspace_bytes",
+            "razer_gemv_group", "razer_gemm", "razer_gemm_w4a4", "razer_weight_offset_sse", "razer_workspace_bytes",
             "razer_status_string")
 
 DEFAULT_WEIGHT_OFFSETS = (-2, 4)  # special values +/-5 and +/-8
@@ -69,6 +69,8 @@ def lib() -> ctypes.CDLL:
             f.restype, f.argtypes = i32, [vp, i32, P, vp, sz, vp]
         L.razer_dequant.restype, L.razer_dequant.argtypes = i32, [P, vp, i32, vp]
         L.razer_gemv.restype, L.razer_gemv.argtypes = i32, [vp, i32, P, vp, i32, vp, sz, vp]
+        L.razer_gemv_group.restype = i32
+        L.razer_gemv_group.argtypes = [vp, i32, ctypes.POINTER(P), ctypes.POINTER(vp), i32, i32, vp]
         L.razer_gemm.restype, L.razer_gemm.argtypes = i32, [vp, i32, i64, P, vp, i32, vp, sz, vp]
         L.razer_gemm_w4a4.restype, L.razer_gemm_w4a4.argtypes = i32, [P, P, vp, i32, vp, sz, vp]
         L.razer_weight_offset_sse.restype = i32
@@ -212,6 +214,29 @@ def razer_gemv(x: torch.Tensor, w: PackedTensor, out_dtype: torch.dtype | None =
                             ctypes.c_void_p(ws.data_ptr() if ws is not None else 0), wsb,
                             ctypes.c_void_p(_stream(stream))), "razer_gemv")
     return out
+
+
+RAZER_GEMV_GROUP_MAX = 4
+
+
+def razer_gemv_group(x: torch.Tensor, ws, out_dtype: torch.dtype | None = None, outs=None,
+                     stream=None):
+    """[x[K] . W^T for W in ws] in one launch (weights sharing x, e.g. gate and up)."""
+    x = x.contiguous()
+    ws = list(ws)
+    if not 1 <= len(ws) <= RAZER_GEMV_GROUP_MAX:
+        raise ValueError(f"1..{RAZER_GEMV_GROUP_MAX} weights")
+    if any(w.cols != x.numel() for w in ws):
+        raise ValueError("x must hold K elements for every weight")
+    if outs is None:
+        outs = [torch.empty(w.rows, dtype=out_dtype or x.dtype, device=x.device) for w in ws]
+    structs = [w.struct() for w in ws]
+    ptrs = (ctypes.POINTER(razer_packed) * len(ws))(*[ctypes.pointer(s) for s in structs])
+    ys = (ctypes.c_void_p * len(ws))(*[o.data_ptr() for o in outs])
+    _check(lib().razer_gemv_group(ctypes.c_void_p(x.data_ptr()), _dtype_code(x.dtype), ptrs, ys,
+                                  len(ws), _dtype_code(outs[0].dtype), ctypes.c_void_p(_stream(stream))),
+           "razer_gemv_group")
+    return outs
 
 
 def razer_gemm(x: torch.Tensor, w: PackedTensor, out_dtype: torch.dtype | None = None, out=None,

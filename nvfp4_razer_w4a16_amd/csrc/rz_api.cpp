@@ -125,6 +125,26 @@ razer_status razer_gemv(const void* x, razer_dtype x_dt, const razer_packed* w, 
   return status_of(rz::launch_gemv(x, x_dt, view_of(w), y, y_dt, ws, ws_bytes, (hipStream_t)stream));
 }
 
+razer_status razer_gemv_group(const void* x, razer_dtype x_dt, const razer_packed* const* w,
+                              void* const* y, int count, razer_dtype y_dt, void* stream) {
+  if (count < 1 || count > RAZER_GEMV_GROUP_MAX || !w || !y) return RAZER_E_INVALID;
+  if (!dtype_ok(x_dt) || !dtype_ok(y_dt)) return RAZER_E_INVALID;
+  rz::PackedView v[RAZER_GEMV_GROUP_MAX];
+  void* yy[RAZER_GEMV_GROUP_MAX];
+  for (int g = 0; g < count; g++) {
+    razer_status s = check_packed(w[g], true);
+    if (s != RAZER_OK) return s;
+    if (w[g]->cols != w[0]->cols) return RAZER_E_INVALID;
+    if (w[g]->rows > 0 && (!y[g] || !aligned(y[g], 16))) return RAZER_E_INVALID;
+    v[g] = view_of(w[g]);
+    yy[g] = y[g];
+  }
+  if (x_dt == RAZER_F32) return RAZER_E_UNSUPPORTED;
+  if (w[0]->cols > kGemvMaxK) return RAZER_E_UNSUPPORTED;
+  if (w[0]->cols > 0 && (!x || !aligned(x, 16))) return RAZER_E_INVALID;
+  return status_of(rz::launch_gemv_group(x, x_dt, v, yy, count, y_dt, (hipStream_t)stream));
+}
+
 razer_status razer_gemm(const void* x, razer_dtype x_dt, int64_t m, const razer_packed* w, void* y,
                         razer_dtype y_dt, void* ws, size_t ws_bytes, void* stream) {
   razer_status s = check_packed(w, true);

@@ -124,17 +124,31 @@ __device__ __forceinline__ int quad_row(int lane) {
   return ((rho & 1) << 1) | (rho >> 1);
 }
 
-struct GemvArgs {
-  const void* x;
+// One weight of a launch: its packed buffers, output, rows and decode
+// parameters, and the first workgroup of the launch that works on it.
+struct GemvWeight {
   const uint8_t* codes;
   const uint8_t* scales;
   const float* ts;
   void* y;
-  int64_t n, k, nchunk;
+  int64_t n;
+  int kind;
+  float m0, m1;
+  int wg0;
+};
+
+// A launch covers up to kGemvGroupMax weights that share x and K (for example
+// the gate and up projections of an MLP); workgroups [wg0(g), wg0(g+1)) work
+// on weight g.
+constexpr int kGemvGroupMax = 4;
+struct GemvArgs {
+  const void* x;
+  GemvWeight w[kGemvGroupMax];
+  int count;
+  int64_t k, nchunk;
   int rpw;   // rows per workgroup
   int rpwv;  // rows per row group (multiple of 4)
-  int kind, ydt;
-  float m0, m1;
+  int ydt;
 };
 
 __device__ __forceinline__ void store_out(void* y, int64_t i, float v, int ydt) {
@@ -232,14 +246,19 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ks = wave % KS, rg = wave / KS;
-  const int64_t base = (int64_t)blockIdx.x * a.rpw;
-  const int rows_wg = (int)min((int64_t)a.rpw, a.n - base);
+  // this workgroup's weight (a uniform choice among at most four)
+  GemvWeight w = a.w[0];
+#pragma unroll
+  for (int g = 1; g < kGemvGroupMax; g++)
+    if (g < a.count && (int)blockIdx.x >= a.w[g].wg0) w = a.w[g];
+  const int64_t base = (int64_t)((int)blockIdx.x - w.wg0) * a.rpw;
+  const int rows_wg = (int)min((int64_t)a.rpw, w.n - base);
   const int r0 = rg * a.rpwv;                                  // first row of this wave in the run
   const int nrw = max(0, min(a.rpwv, rows_wg - r0));           // rows of this wave
   const int nq = (nrw + 3) >> 2;
   const int rcb = (int)(a.k / 2), rsb = (int)(a.k / 16);
-  const Rsrc crs = make_rsrc(a.codes + base * rcb, (int64_t)rows_wg * rcb);
-  const Rsrc srs = make_rsrc(a.scales + base * rsb, (int64_t)rows_wg * rsb);
+  const Rsrc crs = make_rsrc(w.codes + base * rcb, (int64_t)rows_wg * rcb);
+  const Rsrc srs = make_rsrc(w.scales + base * rsb, (int64_t)rows_wg * rsb);
   const Rsrc xrs = make_rsrc(a.x, a.k * 2);
 
   // Chunks of this wave: ni of them hold any valid lane (wave-uniform); a
@@ -292,17 +311,17 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   {
     const uint32_t i = threadIdx.x;
     float sb, sv;
-    if (a.kind == kWeight) {
+    if (w.kind == kWeight) {
       sb = scale_of_byte<kWeight>(i);
-      sv = special_of_byte<kWeight>(i, a.m0, a.m1);
+      sv = special_of_byte<kWeight>(i, w.m0, w.m1);
     } else {
       sb = scale_of_byte<kAct>(i);
-      sv = special_of_byte<kAct>(i, a.m0, a.m1);
+      sv = special_of_byte<kAct>(i, w.m0, w.m1);
     }
     lut[i] = make_float2(sb * (1.0f + 4.0f * sv), -4.0f * sb * sv);
   }
   __syncthreads();
-  const float st = *a.ts;
+  const float st = *w.ts;
   const int my_row = quad_row(lane);  // the row of the quad this lane's sum belongs to
   uint8_t (*stg)[4][kSeg] = sstage[wave];
 
@@ -341,7 +360,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
         const float v = quad_sum(acc);
         const int j = 4 * q + my_row;
         if ((lane & 15) == 0 && j < nrw) {
-          if (KS == 1) store_out(a.y, base + r0 + j, v * st, a.ydt);
+          if (KS == 1) store_out(w.y, base + r0 + j, v * st, a.ydt);
           else part[ks * kGemvMaxRpw + r0 + j] = v;
         }
       }
@@ -353,7 +372,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
       float v = 0.0f;
 #pragma unroll
       for (int q = 0; q < KS; q++) v += part[q * kGemvMaxRpw + r];
-      store_out(a.y, base + r, v * st, a.ydt);
+      store_out(w.y, base + r, v * st, a.ydt);
     }
   }
 }
@@ -414,32 +433,60 @@ static hipError_t dispatch(const GemvArgs& a, const GemvPlan& p, hipStream_t str
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_gemv(const void* x, int x_dtype, const PackedView& w, void* y, int y_dtype,
-                       void*, size_t, hipStream_t stream) {
-  if (w.rows <= 0) return hipSuccess;
-  // Long rows (K above 8192) on up to 4096 rows go to the MFMA small-batch
-  // kernel, whose K split keeps enough waves busy; measured faster there only.
-  if (w.rows <= 4096 && w.cols > 8192 && smallm_supported(1, w.rows, w.cols))
-    return launch_smallm(x, x_dtype, 1, w, y, y_dtype, stream);
+// Weights that go to the MFMA small-batch kernel instead: long rows (K above
+// 8192) on up to 4096 rows, where its K split keeps enough waves busy
+// (measured faster there only).
+static bool gemv_to_smallm(const PackedView& w) {
+  return w.rows <= 4096 && w.cols > 8192 && smallm_supported(1, w.rows, w.cols);
+}
+
+hipError_t launch_gemv_group(const void* x, int x_dtype, const PackedView* w, void* const* y,
+                             int count, int y_dtype, hipStream_t stream) {
+  if (count < 1 || count > kGemvGroupMax) return hipErrorInvalidValue;
+  // members for the small-batch kernel, and empty ones, are launched on their own
   GemvArgs a;
   a.x = x;
-  a.codes = w.codes;
-  a.scales = w.scales;
-  a.ts = w.tensor_scale;
-  a.y = y;
-  a.n = w.rows;
-  a.k = w.cols;
-  a.kind = w.kind;
+  a.count = 0;
+  a.k = w[0].cols;
   a.ydt = y_dtype;
-  a.m0 = 6.0f + 0.5f * (float)w.off_half[0];
-  a.m1 = 6.0f + 0.5f * (float)w.off_half[w.kind == kWeight ? 1 : 0];
-  a.rpw = 4;
-  a.rpwv = 4;
+  int64_t n_total = 0;
+  for (int g = 0; g < count; g++) {
+    if (w[g].rows <= 0) continue;
+    if (gemv_to_smallm(w[g])) {
+      const hipError_t e = launch_smallm(x, x_dtype, 1, w[g], y[g], y_dtype, stream);
+      if (e != hipSuccess) return e;
+      continue;
+    }
+    GemvWeight& m = a.w[a.count++];
+    m.codes = w[g].codes;
+    m.scales = w[g].scales;
+    m.ts = w[g].tensor_scale;
+    m.y = y[g];
+    m.n = w[g].rows;
+    m.kind = w[g].kind;
+    m.m0 = 6.0f + 0.5f * (float)w[g].off_half[0];
+    m.m1 = 6.0f + 0.5f * (float)w[g].off_half[w[g].kind == kWeight ? 1 : 0];
+    n_total += m.n;
+  }
+  if (a.count == 0) return hipSuccess;
   const bool unit2 = a.k % 32 == 0;
   a.nchunk = a.k / (unit2 ? 32 : 16);
-  const GemvPlan p = plan_gemv(a.n, a.nchunk, device_cu_count(), 8);
+  // one plan for the summed rows; each weight gets whole workgroups of it
+  GemvPlan p = plan_gemv(n_total, a.nchunk, device_cu_count(), 8);
+  int64_t wg = 0;
+  for (int g = 0; g < a.count; g++) {
+    a.w[g].wg0 = (int)wg;
+    wg += (a.w[g].n + p.rpw - 1) / p.rpw;
+  }
+  for (int g = a.count; g < kGemvGroupMax; g++) a.w[g] = a.w[0];
+  p.grid = wg;
   if (x_dtype == kF16) return unit2 ? dispatch<_Float16, 2>(a, p, stream) : dispatch<_Float16, 1>(a, p, stream);
   return unit2 ? dispatch<__bf16, 2>(a, p, stream) : dispatch<__bf16, 1>(a, p, stream);
+}
+
+hipError_t launch_gemv(const void* x, int x_dtype, const PackedView& w, void* y, int y_dtype,
+                       void*, size_t, hipStream_t stream) {
+  return launch_gemv_group(x, x_dtype, &w, &y, 1, y_dtype, stream);
 }
 
 }  // namespace rz

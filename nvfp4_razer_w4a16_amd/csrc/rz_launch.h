@@ -52,6 +52,10 @@ hipError_t launch_gemm_w4a4(const PackedView& x, const PackedView& w, void* y, i
                             size_t ws_bytes, hipStream_t stream);
 
 size_t gemv_ws_bytes(int64_t n, int64_t k);
+// Up to four weights with the same K and one input x in one launch
+// (members that the small-batch kernel serves better are launched on their own).
+hipError_t launch_gemv_group(const void* x, int x_dtype, const PackedView* w, void* const* y,
+                             int count, int y_dtype, hipStream_t stream);
 hipError_t launch_gemv(const void* x, int x_dtype, const PackedView& w, void* y, int y_dtype,
                        void* ws, size_t ws_bytes, hipStream_t stream);
 

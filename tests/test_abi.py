@@ -183,3 +183,42 @@ def test_gemm_w4a4_workspace_holds_both_intermediates():
     m, n, k = 7, 40, 96
     assert rz.razer_workspace_bytes(rz.RAZER_OP_GEMM_W4A4, m, n, k) >= m * k * 2 + m * n * 4
     assert rz.razer_workspace_bytes(rz.RAZER_OP_GEMM_W4A4, 0, n, k) == 0
+
+
+def _group_call(ws, ys, count=None, x=FAKE_X, x_dt=rz.RAZER_F16, y_dt=rz.RAZER_F16):
+    P = ctypes.POINTER(rz.razer_packed)
+    arr = (P * max(1, len(ws)))(*[ctypes.pointer(s) for s in ws])
+    yarr = (ctypes.c_void_p * max(1, len(ys)))(*ys)
+    n = len(ws) if count is None else count
+    return rz.lib().razer_gemv_group(x, x_dt, arr, yarr, n, y_dt, None)
+
+
+@pytest.mark.parametrize("case", ["count0", "count5", "unequal_k", "bad_packed", "null_y", "misaligned_y",
+                                  "null_x", "bad_dtype"])
+def test_gemv_group_rejects_bad_arguments(case):
+    a, b = _packed(rows=8, cols=64), _packed(rows=4, cols=64)
+    ws, ys, kw = [a, b], [0x6000, 0x7000], {}
+    if case == "count0":
+        kw["count"] = 0
+    elif case == "count5":
+        ws, ys = [a] * 5, [0x6000] * 5
+    elif case == "unequal_k":
+        b.cols = 80
+    elif case == "bad_packed":
+        b.sv_off_half[0] = 9
+    elif case == "null_y":
+        ys = [0x6000, 0]
+    elif case == "misaligned_y":
+        ys = [0x6008, 0x7000]
+    elif case == "null_x":
+        kw["x"] = None
+    elif case == "bad_dtype":
+        kw["y_dt"] = 7
+    assert _group_call(ws, ys, **kw) == rz.RAZER_E_INVALID
+
+
+def test_gemv_group_unsupported_like_gemv():
+    a = _packed(rows=8, cols=64)
+    assert _group_call([a], [0x6000], x_dt=rz.RAZER_F32) == rz.RAZER_E_UNSUPPORTED
+    big = _packed(rows=8, cols=65536 + 16)
+    assert _group_call([big], [0x6000]) == rz.RAZER_E_UNSUPPORTED

@@ -404,6 +404,50 @@ def test_gemv_ragged_shapes(n, k, xdt):
     assert_product_close(y[None, :], y_ref, nrm, f"gemv {n}x{k}")
 
 
+def test_gemv_group_llama3_8b_gate_up():
+    """Gate and up of the decode layer in one launch: each output within
+    tolerance of the oracle and bitwise equal to its own razer_gemv."""
+    _need_gpu()
+    x = synth.llama3_8b_decode_x(4096).reshape(-1)
+    ref = {n: llama_ref(n) for n in ("gate", "up")}
+    ws = [to_device(ref["gate"]), to_device(ref["up"])]
+    xd = x.cuda()
+    ys = rz.razer_gemv_group(xd, ws)
+    torch.cuda.synchronize()
+    for n, w, y in zip(("gate", "up"), ws, ys):
+        y_ref, nrm = oracle.gemm(as_f32(x), ref[n])
+        assert_product_close(y.float().cpu().numpy()[None], y_ref, nrm, f"group {n}", torch.float16)
+        assert torch.equal(y, rz.razer_gemv(xd, w)), n
+
+
+@pytest.mark.parametrize("xdt", [torch.float16, torch.bfloat16])
+def test_gemv_group_ragged_members(xdt):
+    # four members with different rows (one empty, one a single row), both
+    # kinds, different offsets and tensor scales; a member with K > 8192 on
+    # few rows takes the small-batch kernel on its own
+    _need_gpu()
+    rng = np.random.default_rng(111)
+    for k in (1040, 16384):
+        shapes = [(300, (-2, 4), oracle.WEIGHT), (0, (-2, 4), oracle.WEIGHT), (1, (-7, 7), oracle.WEIGHT),
+                  (77, (-2,), oracle.ACT)]
+        refs, ws = [], []
+        for i, (n, offs, kind) in enumerate(shapes):
+            w = (rng.standard_t(5, (n, k)) * 0.02 * (i + 1)).astype(np.float32)
+            r = oracle.quantize(kind, w, offs)
+            refs.append(r)
+            ws.append(to_device(r))
+        x = torch.from_numpy(rng.standard_normal(k).astype(np.float32)).to(xdt)
+        ys = rz.razer_gemv_group(x.cuda(), ws, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        for i, (r, w, y) in enumerate(zip(refs, ws, ys)):
+            assert y.shape == (r.rows,)
+            if r.rows == 0:
+                continue
+            y_ref, nrm = oracle.gemm(as_f32(x), r)
+            assert_product_close(y.cpu().numpy()[None], y_ref, nrm, f"group member {i} k {k}")
+            assert torch.equal(y, rz.razer_gemv(x.cuda(), w, out_dtype=torch.float32)), (i, k)
+
+
 def test_gemv_nan_tensor_scale_gives_nan():
     _need_gpu()
     x = EDGE["nan"]
