@@ -25,6 +25,8 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 
 WEIGHT = 0
 ACT = 1
+SCALE_BYTE, SCALE_F16 = 0, 1  # block-scale storage: one E3M3/E4M3 byte, or the FP16 group scale
+BLOCK_SIZES = (16, 32, 64, 128)
 
 
 def build_oracle() -> str:
@@ -73,6 +75,17 @@ def lib():
         L.rzo_dequant_f64.argtypes = [i, vp, vp, f, vp, i64, i64, vp]
         L.rzo_dequant_f32.restype = None
         L.rzo_dequant_f32.argtypes = [i, vp, vp, f, vp, i64, i64, vp]
+        L.rzo_scale_value_fmt.restype = d
+        L.rzo_scale_value_fmt.argtypes = [i, i, i]
+        L.rzo_scale_round_fmt.restype = i
+        L.rzo_scale_round_fmt.argtypes = [i, i, f]
+        L.rzo_scale_max_fmt.restype = d
+        L.rzo_scale_max_fmt.argtypes = [i, i]
+        L.rzo_quantize_fmt.restype = i
+        L.rzo_quantize_fmt.argtypes = [i, vp, i64, i64, vp, i, i, i, vp, vp, vp]
+        for name in ("rzo_dequant_fmt_f64", "rzo_dequant_fmt_f32"):
+            getattr(L, name).restype = None
+            getattr(L, name).argtypes = [i, i, i, vp, vp, f, vp, i64, i64, vp]
         L.rzo_gemm.restype = None
         L.rzo_gemm.argtypes = [vp, i64, i64, i, vp, vp, f, vp, i64, vp, i64, vp, vp]
         _lib = L
@@ -116,6 +129,18 @@ def scale_max(kind: int) -> float:
     return lib().rzo_scale_max(kind)
 
 
+def scale_value_fmt(kind: int, sfmt: int, code: int) -> float:
+    return lib().rzo_scale_value_fmt(kind, sfmt, code)
+
+
+def scale_round_fmt(kind: int, sfmt: int, v: float) -> int:
+    return lib().rzo_scale_round_fmt(kind, sfmt, float(np.float32(v)))
+
+
+def scale_max_fmt(kind: int, sfmt: int) -> float:
+    return lib().rzo_scale_max_fmt(kind, sfmt)
+
+
 def special_value(neg: int, off_half: int) -> float:
     return lib().rzo_special_value(neg, off_half)
 
@@ -135,8 +160,8 @@ def encode_block_scaled(y, candidates, remap: bool = True):
     """Remap one block of already-scaled values; returns (codes[n], sel)."""
     y = np.ascontiguousarray(np.asarray(y, dtype=np.float32))
     cand = np.ascontiguousarray(np.asarray(candidates, dtype=np.float64))
-    if y.size > 64:
-        raise ValueError("at most 64 values per block")
+    if y.size > 128:
+        raise ValueError("at most 128 values per block")
     codes = np.zeros(y.size, dtype=np.uint8)
     sel = ctypes.c_int(0)
     lib().rzo_encode_block_scaled(_ptr(y), y.size, _ptr(cand), cand.size, int(remap), _ptr(codes),
@@ -147,11 +172,13 @@ def encode_block_scaled(y, candidates, remap: bool = True):
 class Packed:
     """Host copy of a packed RaZeR tensor."""
 
-    def __init__(self, kind, rows, cols, offsets, codes, scales, tensor_scale):
+    def __init__(self, kind, rows, cols, offsets, codes, scales, tensor_scale, block=16,
+                 scale_fmt=SCALE_BYTE):
         self.kind, self.rows, self.cols = kind, rows, cols
         self.offsets = tuple(int(o) for o in offsets)
-        self.codes, self.scales = codes, scales
+        self.codes, self.scales = codes, scales  # scales: uint8, or uint16 for SCALE_F16
         self.tensor_scale = np.float32(tensor_scale)
+        self.block, self.scale_fmt = block, scale_fmt
 
     def unpacked_codes(self) -> np.ndarray:
         c = self.codes.reshape(self.rows, self.cols // 2)
@@ -164,24 +191,27 @@ class Packed:
 MODE_PLAIN, MODE_RAZER, MODE_FOUR_OVER_SIX = 0, 1, 2
 
 
-def quantize(kind: int, x, offsets, remap: bool = True, four_over_six: bool = False) -> Packed:
+def quantize(kind: int, x, offsets, remap: bool = True, four_over_six: bool = False,
+             block: int = 16, scale_fmt: int = SCALE_BYTE) -> Packed:
     """Encode x (RaZeR, plain NVFP4 when not remap, or the Four Over Six
     baseline when four_over_six: plain FP4 with a per-block choice of the
-    max -> 6 or max -> 4 scale)."""
+    max -> 6 or max -> 4 scale), with `block` elements per block and byte or
+    FP16 group scales."""
     x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
     if x.ndim != 2:
         raise ValueError("x must be 2-D")
     rows, cols = x.shape
     off = _offsets(kind, offsets)
     codes = np.zeros(rows * cols // 2, dtype=np.uint8)
-    scales = np.zeros(rows * cols // 16, dtype=np.uint8)
+    nblk = rows * cols // block if block in BLOCK_SIZES else 0
+    scales = np.zeros(nblk, dtype=np.uint16 if scale_fmt == SCALE_F16 else np.uint8)
     ts = np.zeros(1, dtype=np.float32)
     mode = MODE_FOUR_OVER_SIX if four_over_six else (MODE_RAZER if remap else MODE_PLAIN)
-    rc = lib().rzo_quantize(kind, _ptr(x), rows, cols, _ptr(off), mode, _ptr(codes),
-                            _ptr(scales), _ptr(ts))
+    rc = lib().rzo_quantize_fmt(kind, _ptr(x), rows, cols, _ptr(off), mode, block, scale_fmt,
+                                _ptr(codes), _ptr(scales), _ptr(ts))
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
-    return Packed(kind, rows, cols, offsets, codes, scales, ts[0])
+    return Packed(kind, rows, cols, offsets, codes, scales, ts[0], block, scale_fmt)
 
 
 def quantize_weight(w, offsets=(-2, 4), remap: bool = True, four_over_six: bool = False) -> Packed:
@@ -225,17 +255,22 @@ def best_second_offset(w, off0: int = -2):
 def dequant_f64(p: Packed) -> np.ndarray:
     out = np.empty((p.rows, p.cols), dtype=np.float64)
     off = _offsets(p.kind, p.offsets)
-    lib().rzo_dequant_f64(p.kind, _ptr(p.codes), _ptr(p.scales), float(p.tensor_scale), _ptr(off),
-                          p.rows, p.cols, _ptr(out))
+    lib().rzo_dequant_fmt_f64(p.kind, p.block, p.scale_fmt, _ptr(p.codes), _ptr(p.scales),
+                              float(p.tensor_scale), _ptr(off), p.rows, p.cols, _ptr(out))
     return out
 
 
 def dequant_f32(p: Packed) -> np.ndarray:
     out = np.empty((p.rows, p.cols), dtype=np.float32)
     off = _offsets(p.kind, p.offsets)
-    lib().rzo_dequant_f32(p.kind, _ptr(p.codes), _ptr(p.scales), float(p.tensor_scale), _ptr(off),
-                          p.rows, p.cols, _ptr(out))
+    lib().rzo_dequant_fmt_f32(p.kind, p.block, p.scale_fmt, _ptr(p.codes), _ptr(p.scales),
+                              float(p.tensor_scale), _ptr(off), p.rows, p.cols, _ptr(out))
     return out
+
+
+def _default_layout(p: Packed):
+    if p.block != 16 or p.scale_fmt != SCALE_BYTE:
+        raise ValueError("the products take 16-element blocks with byte scales")
 
 
 def gemm(x, p: Packed, cols=None):
@@ -243,6 +278,7 @@ def gemm(x, p: Packed, cols=None):
 
     ``cols`` selects weight rows (output columns); None means all.  Returns
     (y [m, ncols], norm [m, ncols])."""
+    _default_layout(p)
     x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
     if x.ndim == 1:
         x = x[None, :]
@@ -273,6 +309,8 @@ def gemm_w4a4(xp: Packed, wp: Packed, cols=None):
     weights the offline 4-candidate one; the product is over the decoded
     values.  ``cols`` selects weight rows (output columns).  Returns
     (y [m, ncols], norm [m, ncols])."""
+    _default_layout(xp)
+    _default_layout(wp)
     if xp.cols != wp.cols:
         raise ValueError("inner dimensions differ")
     xd = dequant_f64(xp)

@@ -98,6 +98,45 @@ int rzo_scale_round(int kind, float v) {
   return best;
 }
 
+/* Group-scale variant: an FP16 block scale whose sign bit and top exponent
+ * bit hold the metadata ([notes] Key design 3: the Blackwell kernels use block
+ * size 128 and store the metadata in those two bits of the FP16 scale).  The
+ * scale itself is the 14-bit remainder: an FP16 number with exponent field
+ * 0..15, so values from 2^-24 (subnormal) up to 2 - 2^-10. */
+static double f16s_value(int code) {
+  int e = (code >> 10) & 15, m = code & 1023;
+  return e == 0 ? ldexp((double)m, -24) : ldexp((double)(1024 + m), e - 25);
+}
+
+static double f16s_max(void) { return f16s_value(0x3FFF); }
+
+static int f16s_round(float v) {
+  /* nearest of the 16384 codes by scan, ties to the even code, saturating */
+  if ((double)v >= f16s_max()) return 0x3FFF;
+  int best = 0;
+  double bd = fabs((double)v);
+  for (int c = 1; c < 0x4000; c++) {
+    double d = fabs((double)v - f16s_value(c));
+    if (d < bd || (d == bd && (c & 1) == 0)) {
+      best = c;
+      bd = d;
+    }
+  }
+  return best;
+}
+
+double rzo_scale_value_fmt(int kind, int sfmt, int code) {
+  return sfmt == RZO_SCALE_F16 ? f16s_value(code & 0x3FFF) : rzo_scale_value(kind, code);
+}
+
+int rzo_scale_round_fmt(int kind, int sfmt, float v) {
+  return sfmt == RZO_SCALE_F16 ? f16s_round(v) : rzo_scale_round(kind, v);
+}
+
+double rzo_scale_max_fmt(int kind, int sfmt) {
+  return sfmt == RZO_SCALE_F16 ? f16s_max() : rzo_scale_max(kind);
+}
+
 double rzo_special_value(int neg, int off_half) {
   /* [notes] Key design 3: a 4-bit offset register holds a fixed-point offset
    * in [-3.5, 3.5] with step 0.5; the decoder adds it to the base 6.0 and
@@ -120,8 +159,8 @@ void rzo_encode_block_scaled(const float* y, int n, const double* cand, int ncan
    * difference is exact (v, q0 are multiples of 0.5 below 16; a moved element
    * has |y| > 2 so y is a multiple of 2^-22 and |y| stays below 2^4), so the
    * sums are exact and the comparison is exact. */
-  double q0[64];
-  int m0[64];
+  double q0[128];
+  int m0[128];
   for (int j = 0; j < n; j++) {
     double yj = (double)y[j];
     m0[j] = rzo_fp4_round_mag(fabs(yj));
@@ -166,46 +205,63 @@ static int valid_offsets(int kind, const int8_t* off) {
  * decoded scale times st and rounded (with the special-value search when
  * remap).  Returns the scale code; 0 means the block is stored as zero (the
  * code underflows or the scale product does), and then c16 is all +0. */
-static int encode_at_scale(int kind, const float* xb, float sb_real, float st, const double* cand,
-                           int ncand, int remap, uint8_t* c16, int* sel) {
-  memset(c16, 0, 16);
+static int encode_at_scale(int kind, int sfmt, int n, const float* xb, float sb_real, float st,
+                           const double* cand, int ncand, int remap, uint8_t* cb, int* sel) {
+  memset(cb, 0, (size_t)n);
   *sel = 0;
-  int scode = rzo_scale_round(kind, sb_real);
+  int scode = rzo_scale_round_fmt(kind, sfmt, sb_real);
   if (scode == 0) return 0;
-  float sb = (float)rzo_scale_value(kind, scode);
+  float sb = (float)rzo_scale_value_fmt(kind, sfmt, scode);
   float d = sb * st;
   float rcp = 1.0f / d;
   if (!isfinite(rcp)) return 0;
-  float y[16];
-  for (int j = 0; j < 16; j++) y[j] = xb[j] * rcp;
-  rzo_encode_block_scaled(y, 16, cand, ncand, remap, c16, sel);
+  float y[128];
+  for (int j = 0; j < n; j++) y[j] = xb[j] * rcp;
+  rzo_encode_block_scaled(y, n, cand, ncand, remap, cb, sel);
   return scode;
 }
 
-/* Squared error of a plain-FP4 block (no special value) in real units:
- * sum over j = 0..15, in that order, of (x_j - value_j * sb * st)^2 in fp64.
- * value * sb * st is exact in fp64 (3 + 4 + 24 significant bits); the
- * difference, the square and each partial sum are rounded once each. */
-static double block_sse(int kind, const float* xb, const uint8_t* c16, int scode, float st) {
-  double sb = scode == 0 ? 0.0 : rzo_scale_value(kind, scode);
+/* Squared error of a plain-FP4 block (no special value) in real units: the
+ * sum of (x_j - value_j * sb * st)^2 in fp64, taken over each run of 16
+ * consecutive elements in order and then over the runs in order (for a
+ * 16-element block simply j = 0..15).  value * sb * st is exact in fp64 (at
+ * most 3 + 11 + 24 significant bits); the difference, the square and each
+ * partial sum are rounded once each. */
+static double block_sse(int kind, int sfmt, int n, const float* xb, const uint8_t* cb, int scode,
+                        float st) {
+  double sb = scode == 0 ? 0.0 : rzo_scale_value_fmt(kind, sfmt, scode);
   double sse = 0.0;
-  for (int j = 0; j < 16; j++) {
-    double q = rzo_fp4_value(c16[j]) * sb * (double)st;
-    double e = (double)xb[j] - q;
-    sse += e * e;
+  for (int r = 0; r < n; r += 16) {
+    double run = 0.0;
+    for (int j = r; j < r + 16; j++) {
+      double q = rzo_fp4_value(cb[j]) * sb * (double)st;
+      double e = (double)xb[j] - q;
+      run += e * e;
+    }
+    sse = r == 0 ? run : sse + run;
   }
   return sse;
 }
 
 int rzo_quantize(int kind, const float* x, int64_t rows, int64_t cols, const int8_t* off_half,
                  int mode, uint8_t* codes, uint8_t* scales, float* tensor_scale) {
-  if ((kind != RZO_WEIGHT && kind != RZO_ACT) || rows < 0 || cols < 0 || cols % 16 != 0 ||
+  return rzo_quantize_fmt(kind, x, rows, cols, off_half, mode, 16, RZO_SCALE_BYTE, codes, scales,
+                          tensor_scale);
+}
+
+int rzo_quantize_fmt(int kind, const float* x, int64_t rows, int64_t cols, const int8_t* off_half,
+                     int mode, int block, int sfmt, uint8_t* codes, void* scales,
+                     float* tensor_scale) {
+  if ((kind != RZO_WEIGHT && kind != RZO_ACT) || rows < 0 || cols < 0 ||
+      (block != 16 && block != 32 && block != 64 && block != 128) || cols % block != 0 ||
+      (sfmt != RZO_SCALE_BYTE && sfmt != RZO_SCALE_F16) || (sfmt == RZO_SCALE_F16 && kind != RZO_WEIGHT) ||
       mode < RZO_MODE_PLAIN || mode > RZO_MODE_FOUR_OVER_SIX ||
       !off_half || !valid_offsets(kind, off_half))
     return -1;
-  int64_t n = rows * cols, nblk = n / 16;
+  int64_t n = rows * cols, nblk = n / block;
+  const size_t sbytes = sfmt == RZO_SCALE_F16 ? 2 : 1;
   memset(codes, 0, (size_t)(n / 2));
-  memset(scales, 0, (size_t)nblk);
+  memset(scales, 0, (size_t)nblk * sbytes);
   if (n == 0) {
     *tensor_scale = 0.0f;
     return 0;
@@ -229,7 +285,7 @@ int rzo_quantize(int kind, const float* x, int64_t rows, int64_t cols, const int
     *tensor_scale = 0.0f;
     return 0;
   }
-  const float smax = (float)rzo_scale_max(kind);
+  const float smax = (float)rzo_scale_max_fmt(kind, sfmt);
   const float st = amax / (6.0f * smax);
   *tensor_scale = st;
 
@@ -251,38 +307,46 @@ int rzo_quantize(int kind, const float* x, int64_t rows, int64_t cols, const int
   }
 
   for (int64_t b = 0; b < nblk; b++) {
-    const float* xb = x + 16 * b;
+    const float* xb = x + (int64_t)block * b;
     float amax_b = 0.0f;
-    for (int j = 0; j < 16; j++) {
+    for (int j = 0; j < block; j++) {
       float a = fabsf(xb[j]);
       if (a > amax_b) amax_b = a;
     }
     float r = amax_b / amax;
     float sb_real = r * smax;
-    uint8_t c16[16];
+    uint8_t cb[128];
     int sel = 0;
-    int scode = encode_at_scale(kind, xb, sb_real, st, cand, ncand, mode == RZO_MODE_RAZER, c16, &sel);
+    int scode = encode_at_scale(kind, sfmt, block, xb, sb_real, st, cand, ncand,
+                                mode == RZO_MODE_RAZER, cb, &sel);
     if (mode == RZO_MODE_FOUR_OVER_SIX) {
       /* [Four Over Six] Technical framework / key innovation: a block may
        * instead be scaled so that its maximum lands on 4 rather than 6 (block
        * scale 6/4 times larger); the block keeps whichever of the two plain
        * NVFP4 encodings has the smaller squared error in real units (ties keep
        * the usual max -> 6 scale). */
-      uint8_t c4[16];
+      uint8_t c4[128];
       int sel4 = 0;
-      int scode4 = encode_at_scale(kind, xb, sb_real * 1.5f, st, cand, ncand, 0, c4, &sel4);
-      if (block_sse(kind, xb, c4, scode4, st) < block_sse(kind, xb, c16, scode, st)) {
-        memcpy(c16, c4, sizeof c16);
+      int scode4 = encode_at_scale(kind, sfmt, block, xb, sb_real * 1.5f, st, cand, ncand, 0, c4, &sel4);
+      if (block_sse(kind, sfmt, block, xb, c4, scode4, st) <
+          block_sse(kind, sfmt, block, xb, cb, scode, st)) {
+        memcpy(cb, c4, (size_t)block);
         scode = scode4;
       }
     }
-    if (scode == 0) continue; /* zero block: all +0, scale byte 0 */
-    for (int j = 0; j < 8; j++) codes[8 * b + j] = (uint8_t)(c16[2 * j] | (c16[2 * j + 1] << 4));
+    if (scode == 0) continue; /* zero block: all +0, scale 0 */
+    for (int j = 0; j < block / 2; j++)
+      codes[(int64_t)block / 2 * b + j] = (uint8_t)(cb[2 * j] | (cb[2 * j + 1] << 4));
     /* Metadata in the freed scale bits ([notes] Key design 1 and the complete
-     * example): bit 7 = sign of the chosen special value; for weights bit 6
-     * selects the pair. */
-    int meta = kind == RZO_WEIGHT ? (((sel & 1) << 7) | ((sel >> 1) << 6)) : (sel << 7);
-    scales[b] = (uint8_t)(meta | scode);
+     * example): the top bit = sign of the chosen special value; for weights
+     * the next bit selects the pair (bits 7/6 of a byte scale, 15/14 of an
+     * FP16 scale). */
+    if (sfmt == RZO_SCALE_F16) {
+      ((uint16_t*)scales)[b] = (uint16_t)(((sel & 1) << 15) | ((sel >> 1) << 14) | scode);
+    } else {
+      int meta = kind == RZO_WEIGHT ? (((sel & 1) << 7) | ((sel >> 1) << 6)) : (sel << 7);
+      ((uint8_t*)scales)[b] = (uint8_t)(meta | scode);
+    }
   }
   return 0;
 }
@@ -308,26 +372,58 @@ static int code_at(const uint8_t* codes, int64_t idx) {
   return (idx & 1) ? (byte >> 4) : (byte & 15);
 }
 
-void rzo_dequant_f64(int kind, const uint8_t* codes, const uint8_t* scales, float tensor_scale,
-                     const int8_t* off_half, int64_t rows, int64_t cols, double* out) {
+/* Value and block scale of element i of a tensor in either scale format. */
+static void element_fmt(int kind, int sfmt, int block, const uint8_t* codes, const void* scales,
+                        const int8_t* off_half, int64_t i, double* val, double* sb) {
+  int code = code_at(codes, i);
+  if (sfmt == RZO_SCALE_F16) {
+    int sw = ((const uint16_t*)scales)[i / block];
+    if ((code & 15) == 8) {
+      int neg = (sw >> 15) & 1, pair = (sw >> 14) & 1;
+      *val = rzo_special_value(neg, off_half[pair]);
+    } else {
+      *val = rzo_fp4_value(code & 15);
+    }
+    *sb = f16s_value(sw & 0x3FFF);
+  } else {
+    int sbyte = ((const uint8_t*)scales)[i / block];
+    *val = rzo_decode_value(kind, code, sbyte, off_half);
+    *sb = rzo_block_scale(kind, sbyte);
+  }
+}
+
+void rzo_dequant_fmt_f64(int kind, int block, int sfmt, const uint8_t* codes, const void* scales,
+                         float tensor_scale, const int8_t* off_half, int64_t rows, int64_t cols,
+                         double* out) {
   int64_t n = rows * cols;
   for (int64_t i = 0; i < n; i++) {
-    int sbyte = scales[i / 16];
-    out[i] = rzo_decode_value(kind, code_at(codes, i), sbyte, off_half) *
-             rzo_block_scale(kind, sbyte) * (double)tensor_scale;
+    double v, sb;
+    element_fmt(kind, sfmt, block, codes, scales, off_half, i, &v, &sb);
+    out[i] = v * sb * (double)tensor_scale;
   }
+}
+
+void rzo_dequant_fmt_f32(int kind, int block, int sfmt, const uint8_t* codes, const void* scales,
+                         float tensor_scale, const int8_t* off_half, int64_t rows, int64_t cols,
+                         float* out) {
+  int64_t n = rows * cols;
+  for (int64_t i = 0; i < n; i++) {
+    double v, sb;
+    element_fmt(kind, sfmt, block, codes, scales, off_half, i, &v, &sb);
+    /* value * block scale has at most 5 + 11 significant bits: exact in fp32 */
+    float vs = (float)(v * sb);
+    out[i] = vs * tensor_scale;
+  }
+}
+
+void rzo_dequant_f64(int kind, const uint8_t* codes, const uint8_t* scales, float tensor_scale,
+                     const int8_t* off_half, int64_t rows, int64_t cols, double* out) {
+  rzo_dequant_fmt_f64(kind, 16, RZO_SCALE_BYTE, codes, scales, tensor_scale, off_half, rows, cols, out);
 }
 
 void rzo_dequant_f32(int kind, const uint8_t* codes, const uint8_t* scales, float tensor_scale,
                      const int8_t* off_half, int64_t rows, int64_t cols, float* out) {
-  int64_t n = rows * cols;
-  for (int64_t i = 0; i < n; i++) {
-    int sbyte = scales[i / 16];
-    /* value * block scale has at most 9 significant bits: exact in fp32 */
-    float vs = (float)(rzo_decode_value(kind, code_at(codes, i), sbyte, off_half) *
-                       rzo_block_scale(kind, sbyte));
-    out[i] = vs * tensor_scale;
-  }
+  rzo_dequant_fmt_f32(kind, 16, RZO_SCALE_BYTE, codes, scales, tensor_scale, off_half, rows, cols, out);
 }
 
 void rzo_gemm(const float* x, int64_t m, int64_t k, int kind, const uint8_t* codes,

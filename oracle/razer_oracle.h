@@ -47,6 +47,12 @@ enum { RZO_WEIGHT = 0, RZO_ACT = 1 };
  * squared error in real units, ties to max -> 6). */
 enum { RZO_MODE_PLAIN = 0, RZO_MODE_RAZER = 1, RZO_MODE_FOUR_OVER_SIX = 2 };
 
+/* Block-scale storage: one byte per block (E3M3 weights / E4M3 activations,
+ * metadata in bits 7-6), or the group-scale variant for weights: a 16-bit FP16
+ * scale per block whose sign bit and top exponent bit hold the metadata (bits
+ * 15-14) and whose other 14 bits are the scale. */
+enum { RZO_SCALE_BYTE = 0, RZO_SCALE_F16 = 1 };
+
 /* FP4-E2M1 value of a 4-bit code (bit 3 = sign); code 8 is -0.0. */
 double rzo_fp4_value(int code);
 /* Index 0..7 of the FP4 magnitude nearest to a >= 0; ties go to the even index. */
@@ -57,6 +63,11 @@ double rzo_scale_value(int kind, int code);
 int rzo_scale_round(int kind, float v);
 /* Largest block-scale value: 30 (E3M3) or 448 (E4M3). */
 double rzo_scale_max(int kind);
+/* The same three for either scale format (RZO_SCALE_*): the FP16 variant
+ * holds 14-bit codes (exponent field 0..15), maximum 2 - 2^-10. */
+double rzo_scale_value_fmt(int kind, int sfmt, int code);
+int rzo_scale_round_fmt(int kind, int sfmt, float v);
+double rzo_scale_max_fmt(int kind, int sfmt);
 /* Special value selected by the metadata: (neg ? -1 : 1) * (6 + off_half/2). */
 double rzo_special_value(int neg, int off_half);
 
@@ -75,6 +86,24 @@ void rzo_encode_block_scaled(const float* y, int n, const double* cand, int ncan
 int rzo_quantize(int kind, const float* x, int64_t rows, int64_t cols,
                  const int8_t* off_half, int mode, uint8_t* codes, uint8_t* scales,
                  float* tensor_scale);
+
+/* Block-size and scale-format variants ([notes] Key findings, block sizes 32,
+ * 64 and 128; Key design 3, FP16 group scales): block in {16, 32, 64, 128}
+ * elements along a row (cols % block == 0), sfmt RZO_SCALE_BYTE or (weights
+ * only) RZO_SCALE_F16.  scales holds rows*cols/block entries of 1 or 2 bytes.
+ * The tensor scale is amax / (6 * S_MAX) with S_MAX the format's largest scale.
+ * In the Four Over Six mode a block's squared error is summed per run of 16
+ * elements, then over the runs in order.  rzo_quantize is this with block 16
+ * and byte scales. */
+int rzo_quantize_fmt(int kind, const float* x, int64_t rows, int64_t cols,
+                     const int8_t* off_half, int mode, int block, int sfmt, uint8_t* codes,
+                     void* scales, float* tensor_scale);
+void rzo_dequant_fmt_f64(int kind, int block, int sfmt, const uint8_t* codes, const void* scales,
+                         float tensor_scale, const int8_t* off_half, int64_t rows, int64_t cols,
+                         double* out);
+void rzo_dequant_fmt_f32(int kind, int block, int sfmt, const uint8_t* codes, const void* scales,
+                         float tensor_scale, const int8_t* off_half, int64_t rows, int64_t cols,
+                         float* out);
 
 /* Decoded value (no scaling) of element code `code` in a block with scale byte `sbyte`. */
 double rzo_decode_value(int kind, int code, int sbyte, const int8_t* off_half);

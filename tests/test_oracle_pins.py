@@ -486,21 +486,22 @@ def _fos_inputs(kind):
     return x
 
 
-@pytest.mark.parametrize("kind", [oracle.WEIGHT, oracle.ACT])
-def test_four_over_six_is_the_better_of_two_plain_encodings(kind):
+@pytest.mark.parametrize("kind,block", [(oracle.WEIGHT, 16), (oracle.ACT, 16), (oracle.WEIGHT, 64)])
+def test_four_over_six_is_the_better_of_two_plain_encodings(kind, block):
     # Independent of the oracle's encoder: the two candidate scale codes are the
     # exact-rational nearest codes of S_MAX*amax_b/amax and 1.5x that (up to the
     # fp32 op-order convention near a midpoint), the codes are the closed-form
     # E2M1 rounding, and the kept candidate must have the exactly smaller error.
     x = _fos_inputs(kind)
-    p = oracle.quantize(kind, x, (-2, 4) if kind == oracle.WEIGHT else (-2,), four_over_six=True)
+    p = oracle.quantize(kind, x, (-2, 4) if kind == oracle.WEIGHT else (-2,), four_over_six=True,
+                        block=block)
     smax = oracle.scale_max(kind)
     ncode = 64 if kind == oracle.WEIGHT else 127
     grid = [F(oracle.scale_value(kind, c)) for c in range(ncode)]
     mids = [(grid[c] + grid[c + 1]) / 2 for c in range(ncode - 1)]
     st = np.float32(p.tensor_scale)
     amax = F(float(np.abs(x).max()))
-    codes = p.unpacked_codes().reshape(-1, 16)
+    codes = p.unpacked_codes().reshape(-1, block)
     took4 = strict = skipped = 0
 
     def nearest(v):
@@ -510,7 +511,7 @@ def test_four_over_six_is_the_better_of_two_plain_encodings(kind):
 
     def encode(xb, scode):
         if scode == 0:
-            return [0] * 16, [0.0] * 16
+            return [0] * block, [0.0] * block
         sb = np.float32(oracle.scale_value(kind, scode))
         rcp = np.float32(1.0) / (sb * st)
         out, val = [], []
@@ -521,7 +522,7 @@ def test_four_over_six_is_the_better_of_two_plain_encodings(kind):
         return out, val
 
     for b in range(codes.shape[0]):
-        xb = x.reshape(-1, 16)[b]
+        xb = x.reshape(-1, block)[b]
         exact6 = F(smax) * F(float(np.abs(xb).max())) / amax
         c6, c4 = nearest(exact6), nearest(exact6 * F(3, 2))
         # within 2^-20 of a rounding midpoint the fp32 op order may pick either
@@ -590,3 +591,136 @@ def test_four_over_six_never_worse_than_nvfp4_and_degenerate_inputs():
         bad[1, 3] = np.inf
         nb = oracle.quantize(kind, bad, offs, four_over_six=True)
         assert np.isnan(nb.tensor_scale) and not nb.codes.any() and not nb.scales.any()
+
+
+# ---- block-size and FP16 group-scale variants ---------------------------------------
+# RaZeR notes, Key findings (block sizes 32, 64 and 128) and Key design 3 (the
+# Blackwell kernels keep FP16 block scales for 128-element groups, with the
+# metadata in the scale's sign bit and top exponent bit).
+
+def test_f16_group_scale_table_and_rounding_match_numpy_float16():
+    W, F16 = oracle.WEIGHT, oracle.SCALE_F16
+    vals = np.arange(0x4000, dtype=np.uint16).view(np.float16).astype(np.float64)
+    for c in list(range(0, 0x4000, 37)) + [0, 1, 1023, 1024, 0x3BFF, 0x3C00, 0x3FFF]:
+        assert oracle.scale_value_fmt(W, F16, c) == vals[c], c
+        # metadata bits never change the scale
+        assert oracle.scale_value_fmt(W, F16, c | 0xC000) == vals[c]
+    smax = oracle.scale_max_fmt(W, F16)
+    assert smax == 2.0 - 2.0 ** -10 == float(np.float16(smax))
+    rng = np.random.default_rng(17)
+    probes = list(rng.uniform(0, smax, 3000)) + list(np.exp(rng.uniform(-20, 0.6, 3000)))
+    for c in range(0, 0x3FFF, 97):  # midpoints between neighbours and one fp32 ulp either side
+        m = np.float32((vals[c] + vals[c + 1]) / 2)
+        probes += [float(m), float(np.nextafter(m, np.float32(0))), float(np.nextafter(m, np.float32(9)))]
+    for v in probes:
+        v = float(np.float32(v))
+        if v > smax:
+            continue
+        got = oracle.scale_value_fmt(W, F16, oracle.scale_round_fmt(W, F16, v))
+        ref = float(np.float16(v))  # numpy rounds to nearest even
+        if ref == 2.0:              # past the largest 14-bit code: saturates
+            ref = smax
+        assert got == ref, v
+    assert oracle.scale_round_fmt(W, F16, 7.0) == 0x3FFF
+
+
+def _variant_inputs(kind, cols=256, rows=8, seed=5):
+    rng = np.random.default_rng(seed + kind)
+    x = (rng.standard_t(5, (rows, cols)) * 0.02).astype(np.float32)
+    x.reshape(-1)[rng.choice(x.size, 5, replace=False)] *= 12
+    return x
+
+
+@pytest.mark.parametrize("kind,block,sfmt", [(oracle.WEIGHT, 32, 0), (oracle.WEIGHT, 128, 0),
+                                             (oracle.ACT, 64, 0), (oracle.WEIGHT, 128, 1),
+                                             (oracle.WEIGHT, 16, 1)])
+def test_block_variants_match_brute_force(kind, block, sfmt):
+    # Each block of `block` elements: the scale code is the nearest code to
+    # S_MAX * amax_block / amax (exact rationals, up to the fp32 op-order slack
+    # near a midpoint); scaled by the oracle's own scale, its codes and
+    # selection are the exact brute-force argmin over the block; the metadata
+    # sits in bits 7-6 (byte) or 15-14 (FP16) of the scale.
+    x = _variant_inputs(kind)
+    offs = (-2, -5) if kind == oracle.WEIGHT else (-2,)
+    cand = [5.0, -5.0, 3.5, -3.5] if kind == oracle.WEIGHT else [5.0, -5.0]
+    p = oracle.quantize(kind, x, offs, block=block, scale_fmt=sfmt)
+    smax = oracle.scale_max_fmt(kind, sfmt)
+    st = np.float32(p.tensor_scale)
+    assert st == np.float32(np.abs(x).max()) / np.float32(6.0 * smax)
+    amax = F(float(np.abs(x).max()))
+    codes = p.unpacked_codes().reshape(-1, block)
+    cmask = 0x3FFF if sfmt else (0x3F if kind == oracle.WEIGHT else 0x7F)
+    nsel = [0] * len(cand)
+    for b in range(codes.shape[0]):
+        xb = x.reshape(-1, block)[b]
+        sw = int(p.scales[b])
+        scode = sw & cmask
+        exact = F(smax) * F(float(np.abs(xb).max())) / amax
+        sb = oracle.scale_value_fmt(kind, sfmt, scode)
+        if sfmt:
+            near = float(np.float16(float(exact)))
+        else:
+            grid = [F(oracle.scale_value(kind, c)) for c in range(64 if kind == oracle.WEIGHT else 127)]
+            near = float(min(grid, key=lambda g: abs(exact - g)))
+        if sb != near:  # only where the exact value is within 2^-20 of a rounding midpoint
+            assert abs(F(sb) - exact) <= abs(F(near) - exact) * (1 + F(1, 2 ** 18)) + exact * F(1, 2 ** 20)
+        rcp = np.float32(1.0) / (np.float32(sb) * st)
+        y = (xb * rcp).astype(np.float32)
+        bc, bs = _brute_force_block(y, cand)
+        assert codes[b].tolist() == bc, b
+        if sfmt:
+            meta = ((bs & 1) << 15) | ((bs >> 1) << 14)
+        elif kind == oracle.WEIGHT:
+            meta = ((bs & 1) << 7) | ((bs >> 1) << 6)
+        else:
+            meta = bs << 7
+        assert sw == meta | scode, b
+        nsel[bs] += 1
+    assert nsel[0] > 0 and sum(nsel[1:]) > 0
+
+
+@pytest.mark.parametrize("block,sfmt", [(64, 0), (128, 1)])
+def test_block_variant_decode_and_error_invariants(block, sfmt):
+    # RaZeR never does worse than plain NVFP4 of the same layout (exact
+    # rationals per block), Four Over Six neither, and the decode of a
+    # remapped code is sign * (6 + off/2) * sb * st with the sign and pair
+    # read from the scale's top two bits.
+    x = _variant_inputs(oracle.WEIGHT, cols=512, rows=6, seed=9)
+    offs = (-2, 4)
+    pr = oracle.quantize(oracle.WEIGHT, x, offs, block=block, scale_fmt=sfmt)
+    p0 = oracle.quantize(oracle.WEIGHT, x, offs, remap=False, block=block, scale_fmt=sfmt)
+    pf = oracle.quantize(oracle.WEIGHT, x, offs, four_over_six=True, block=block, scale_fmt=sfmt)
+    xb = x.reshape(-1, block)
+    dr, d0, df = (oracle.dequant_f64(q).reshape(-1, block) for q in (pr, p0, pf))
+    for i in range(xb.shape[0]):
+        e0 = _exact_block_sse(xb[i], d0[i])
+        assert _exact_block_sse(xb[i], dr[i]) <= e0
+        assert _exact_block_sse(xb[i], df[i]) <= e0
+    top = 15 if sfmt else 7
+    cmask = 0x3FFF if sfmt else 0x3F
+    codes = pr.unpacked_codes().reshape(-1, block)
+    hits = 0
+    for b in range(codes.shape[0]):
+        sw = int(pr.scales[b])
+        neg, pair = (sw >> top) & 1, (sw >> (top - 1)) & 1
+        sb = oracle.scale_value_fmt(oracle.WEIGHT, sfmt, sw & cmask)
+        for j in np.nonzero(codes[b] == 8)[0]:
+            want = (-1 if neg else 1) * (6 + offs[pair] / 2) * sb * float(pr.tensor_scale)
+            assert dr[b, j] == want
+            hits += 1
+    assert hits > 0
+    # f32 decode is the single rounding of the exact value
+    np.testing.assert_array_equal(oracle.dequant_f32(pr), oracle.dequant_f64(pr).astype(np.float32))
+
+
+def test_block_16_byte_variant_is_the_default_layout():
+    x = _variant_inputs(oracle.WEIGHT)
+    a = oracle.quantize_weight(x, (-2, 4))
+    b = oracle.quantize(oracle.WEIGHT, x, (-2, 4), block=16, scale_fmt=oracle.SCALE_BYTE)
+    assert np.array_equal(a.codes, b.codes) and np.array_equal(a.scales, b.scales)
+    with pytest.raises(ValueError):
+        oracle.quantize(oracle.ACT, x, (-2,), scale_fmt=oracle.SCALE_F16)  # FP16 scales: weights only
+    with pytest.raises(ValueError):
+        oracle.quantize(oracle.WEIGHT, x[:, :48], (-2, 4), block=32)    # cols % block != 0
+    with pytest.raises(ValueError):  # the products take the default layout only
+        oracle.gemm(np.zeros((1, 256), np.float32), oracle.quantize(oracle.WEIGHT, x, (-2, 4), block=32))
