@@ -57,7 +57,8 @@ def gemv_bytes(n, k, xb=2, yb=2):
 
 
 def clone_packed(rz, p):
-    q = rz.PackedTensor(p.kind, p.rows, p.cols, p.offsets, p.codes.device, p.flags)
+    q = rz.PackedTensor(p.kind, p.rows, p.cols, p.offsets, p.codes.device, p.flags, p.block,
+                        p.scale_fmt)
     q.codes.copy_(p.codes)
     q.scales.copy_(p.scales)
     q.tensor_scale.copy_(p.tensor_scale)

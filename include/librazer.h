@@ -101,18 +101,38 @@ enum {
   RAZER_FLAG_FOUR_OVER_SIX = 2u
 };
 
+/* Block-scale storage of a packed tensor (razer_packed.scale_fmt). */
+enum {
+  /* One byte per block: E3M3 (weights) / E4M3 (activations) scale code with
+   * the metadata in bits 7-6 ([notes] Key design 1).  The default. */
+  RAZER_SCALE_BYTE = 0,
+  /* Weights only: one 16-bit FP16 scale per block whose sign bit and top
+   * exponent bit hold the metadata (bit 15 = sign of the special value, bit
+   * 14 = pair) and whose other 14 bits are the scale, an FP16 number with
+   * exponent field 0..15, at most 2 - 2^-10 ([notes] Key design 3: the
+   * layout of the pages' Blackwell kernels, there with 128-element blocks).
+   * The tensor scale is amax / (6 * (2 - 2^-10)). */
+  RAZER_SCALE_F16 = 1
+};
+
 typedef struct razer_packed {
   int32_t kind;          /* razer_kind */
   uint32_t flags;        /* RAZER_FLAG_* (read by the encoder only) */
   int64_t rows;          /* >= 0 */
-  int64_t cols;          /* >= 0, multiple of 16 */
+  int64_t cols;          /* >= 0, multiple of the block size */
   int8_t sv_off_half[2]; /* special-value offsets in units of 0.5, each in [-7, 7];
                             weights use both, activations use [0] only */
-  int8_t reserved[6];
+  uint8_t block_log2;    /* elements per block = 2^block_log2, 4..7 (16..128, [notes]
+                            Key findings: block sizes 32, 64, 128); 0 reads as 4 */
+  uint8_t scale_fmt;     /* RAZER_SCALE_BYTE or RAZER_SCALE_F16 */
+  int8_t reserved[4];
   uint8_t* codes;        /* device, rows*cols/2 bytes */
-  uint8_t* scales;       /* device, rows*cols/16 bytes */
+  uint8_t* scales;       /* device, rows*cols/block entries of 1 (byte) or 2 (F16) bytes */
   float* tensor_scale;   /* device, 1 float */
 } razer_packed;
+/* The encoders and razer_dequant take every layout; the product calls
+ * (razer_gemv, razer_gemv_group, razer_gemm, razer_gemm_w4a4) take 16-element
+ * blocks with byte scales and return RAZER_E_UNSUPPORTED for the others. */
 
 /* Operation ids for razer_workspace_bytes. */
 enum {

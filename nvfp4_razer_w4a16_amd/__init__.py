@@ -24,6 +24,8 @@ RAZER_OK, RAZER_E_INVALID, RAZER_E_UNSUPPORTED, RAZER_E_HIP = 0, 1, 2, 3
 RAZER_F32, RAZER_F16, RAZER_BF16 = 0, 1, 2
 RAZER_WEIGHT, RAZER_ACT = 0, 1
 RAZER_FLAG_NO_REMAP, RAZER_FLAG_FOUR_OVER_SIX = 1, 2
+RAZER_SCALE_BYTE, RAZER_SCALE_F16 = 0, 1
+BLOCK_SIZES = (16, 32, 64, 128)
 RAZER_OP_QUANTIZE_WEIGHT, RAZER_OP_QUANTIZE_ACT, RAZER_OP_GEMV, RAZER_OP_GEMM = 0, 1, 2, 3
 RAZER_OP_OFFSET_SEARCH, RAZER_OP_GEMM_W4A4 = 4, 5
 SECOND_PAIR_OFFSETS = tuple(range(-7, 8))  # entry i of razer_weight_offset_sse is offset i - 7
@@ -41,7 +43,8 @@ _DT = {torch.float32: RAZER_F32, torch.float16: RAZER_F16, torch.bfloat16: RAZER
 class razer_packed(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("flags", ctypes.c_uint32), ("rows", ctypes.c_int64),
                 ("cols", ctypes.c_int64), ("sv_off_half", ctypes.c_int8 * 2),
-                ("reserved", ctypes.c_int8 * 6), ("codes", ctypes.c_void_p),
+                ("block_log2", ctypes.c_uint8), ("scale_fmt", ctypes.c_uint8),
+                ("reserved", ctypes.c_int8 * 4), ("codes", ctypes.c_void_p),
                 ("scales", ctypes.c_void_p), ("tensor_scale", ctypes.c_void_p)]
 
 
@@ -110,17 +113,23 @@ def _dtype_code(dt: torch.dtype) -> int:
 class PackedTensor:
     """A RaZeR-packed tensor in device memory (torch tensors own the bytes).
 
-    codes: uint8 [rows, cols // 2]; scales: uint8 [rows, cols // 16];
-    tensor_scale: float32 [1]; kind: RAZER_WEIGHT or RAZER_ACT; offsets:
-    special-value offsets in units of 0.5."""
+    codes: uint8 [rows, cols // 2]; scales: uint8 [rows, cols // block] (two
+    bytes per block, little-endian, for RAZER_SCALE_F16); tensor_scale: float32
+    [1]; kind: RAZER_WEIGHT or RAZER_ACT; offsets: special-value offsets in
+    units of 0.5; block: elements per block (16, 32, 64 or 128)."""
 
-    def __init__(self, kind: int, rows: int, cols: int, offsets, device, flags: int = 0):
-        if cols % 16:
-            raise ValueError("cols must be a multiple of 16")
+    def __init__(self, kind: int, rows: int, cols: int, offsets, device, flags: int = 0,
+                 block: int = 16, scale_fmt: int = RAZER_SCALE_BYTE):
+        if block not in BLOCK_SIZES:
+            raise ValueError(f"block must be one of {BLOCK_SIZES}")
+        if cols % block:
+            raise ValueError("cols must be a multiple of the block size")
         self.kind, self.rows, self.cols, self.flags = kind, rows, cols, flags
+        self.block, self.scale_fmt = block, scale_fmt
         self.offsets = tuple(int(o) for o in offsets)
+        sbytes = 2 if scale_fmt == RAZER_SCALE_F16 else 1
         self.codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=device)
-        self.scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=device)
+        self.scales = torch.empty((rows, cols // block * sbytes), dtype=torch.uint8, device=device)
         self.tensor_scale = torch.empty(1, dtype=torch.float32, device=device)
 
     @property
@@ -132,6 +141,7 @@ class PackedTensor:
         s.kind, s.flags, s.rows, s.cols = self.kind, self.flags, self.rows, self.cols
         off = list(self.offsets) + [self.offsets[0]] * (2 - len(self.offsets))
         s.sv_off_half[0], s.sv_off_half[1] = off[0], off[1]
+        s.block_log2, s.scale_fmt = self.block.bit_length() - 1, self.scale_fmt
         s.codes, s.scales = self.codes.data_ptr(), self.scales.data_ptr()
         s.tensor_scale = self.tensor_scale.data_ptr()
         return s
@@ -155,13 +165,13 @@ def _encoder_flags(remap: bool, four_over_six: bool) -> int:
     return 0 if remap else RAZER_FLAG_NO_REMAP
 
 
-def _quantize(fn, op, kind, x, offsets, flags, out, workspace, stream):
+def _quantize(fn, op, kind, x, offsets, flags, out, workspace, stream, block, scale_fmt):
     if x.dim() != 2:
         raise ValueError("expected a 2-D tensor")
     x = x.contiguous()
     rows, cols = x.shape
     if out is None:
-        out = PackedTensor(kind, rows, cols, offsets, x.device, flags)
+        out = PackedTensor(kind, rows, cols, offsets, x.device, flags, block, scale_fmt)
     s = out.struct()
     ws, wsb = _workspace(op, rows, 0, cols, x.device, workspace)
     _check(fn(ctypes.c_void_p(x.data_ptr()), _dtype_code(x.dtype), ctypes.byref(s),
@@ -172,21 +182,25 @@ def _quantize(fn, op, kind, x, offsets, flags, out, workspace, stream):
 
 def razer_quantize_weight(w: torch.Tensor, offsets=DEFAULT_WEIGHT_OFFSETS, remap: bool = True,
                           out: PackedTensor | None = None, workspace=None, stream=None,
-                          four_over_six: bool = False):
+                          four_over_six: bool = False, block: int = 16,
+                          scale_fmt: int = RAZER_SCALE_BYTE):
     """Offline RaZeR weight encoding of w [N, K] (fp32/fp16/bf16, on the GPU).
     remap=False gives plain NVFP4, four_over_six=True the Four Over Six
-    baseline; a given `out` carries its own flags instead."""
+    baseline; block / scale_fmt pick a layout variant; a given `out` carries
+    its own flags and layout instead."""
     return _quantize(lib().razer_quantize_weight, RAZER_OP_QUANTIZE_WEIGHT, RAZER_WEIGHT, w,
-                     offsets, _encoder_flags(remap, four_over_six), out, workspace, stream)
+                     offsets, _encoder_flags(remap, four_over_six), out, workspace, stream, block,
+                     scale_fmt)
 
 
 def razer_quantize_act(x: torch.Tensor, offsets=DEFAULT_ACT_OFFSETS, remap: bool = True,
                        out: PackedTensor | None = None, workspace=None, stream=None,
-                       four_over_six: bool = False):
+                       four_over_six: bool = False, block: int = 16):
     """Online RaZeR activation encoding of x [rows, cols] (fp16/bf16, on the GPU).
-    remap / four_over_six / out as for razer_quantize_weight."""
+    remap / four_over_six / block / out as for razer_quantize_weight."""
     return _quantize(lib().razer_quantize_act, RAZER_OP_QUANTIZE_ACT, RAZER_ACT, x, offsets,
-                     _encoder_flags(remap, four_over_six), out, workspace, stream)
+                     _encoder_flags(remap, four_over_six), out, workspace, stream, block,
+                     RAZER_SCALE_BYTE)
 
 
 def razer_dequant(t: PackedTensor, dtype: torch.dtype = torch.float32, out=None, stream=None):

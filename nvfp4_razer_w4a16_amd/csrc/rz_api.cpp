@@ -40,7 +40,11 @@ bool dtype_ok(int dt) { return dt == RAZER_F32 || dt == RAZER_F16 || dt == RAZER
 razer_status check_packed(const razer_packed* p, bool need_data) {
   if (!p) return RAZER_E_INVALID;
   if (p->kind != RAZER_WEIGHT && p->kind != RAZER_ACT) return RAZER_E_INVALID;
-  if (p->rows < 0 || p->cols < 0 || p->cols % 16 != 0) return RAZER_E_INVALID;
+  const int blog2 = p->block_log2 ? p->block_log2 : 4;
+  if (blog2 < 4 || blog2 > 7) return RAZER_E_INVALID;
+  if (p->scale_fmt != RAZER_SCALE_BYTE && p->scale_fmt != RAZER_SCALE_F16) return RAZER_E_INVALID;
+  if (p->scale_fmt == RAZER_SCALE_F16 && p->kind != RAZER_WEIGHT) return RAZER_E_INVALID;
+  if (p->rows < 0 || p->cols < 0 || p->cols % (1 << blog2) != 0) return RAZER_E_INVALID;
   if (p->cols > 0 && p->rows > INT64_MAX / 2 / p->cols) return RAZER_E_INVALID;
   const int npairs = p->kind == RAZER_WEIGHT ? 2 : 1;
   for (int i = 0; i < npairs; i++)
@@ -61,6 +65,8 @@ rz::PackedView view_of(const razer_packed* p) {
   v.cols = p->cols;
   v.off_half[0] = p->sv_off_half[0];
   v.off_half[1] = p->kind == RAZER_WEIGHT ? p->sv_off_half[1] : p->sv_off_half[0];
+  v.blog2 = p->block_log2 ? p->block_log2 : 4;
+  v.sfmt = p->scale_fmt;
   v.codes = p->codes;
   v.scales = p->scales;
   v.tensor_scale = p->tensor_scale;
@@ -69,6 +75,11 @@ rz::PackedView view_of(const razer_packed* p) {
 
 static_assert(RAZER_FLAG_NO_REMAP == rz::kFlagNoRemap && RAZER_FLAG_FOUR_OVER_SIX == rz::kFlagFourOverSix,
               "encoder flag values");
+
+// The product kernels read 16-element blocks with byte scales only.
+bool product_layout(const razer_packed* p) {
+  return (p->block_log2 == 0 || p->block_log2 == 4) && p->scale_fmt == RAZER_SCALE_BYTE;
+}
 
 razer_status status_of(hipError_t e) { return e == hipSuccess ? RAZER_OK : RAZER_E_HIP; }
 
@@ -115,7 +126,7 @@ razer_status razer_gemv(const void* x, razer_dtype x_dt, const razer_packed* w, 
   razer_status s = check_packed(w, true);
   if (s != RAZER_OK) return s;
   if (!dtype_ok(x_dt) || !dtype_ok(y_dt)) return RAZER_E_INVALID;
-  if (x_dt == RAZER_F32) return RAZER_E_UNSUPPORTED;
+  if (x_dt == RAZER_F32 || !product_layout(w)) return RAZER_E_UNSUPPORTED;
   if (w->cols > kGemvMaxK) return RAZER_E_UNSUPPORTED;
   if (w->rows == 0) return RAZER_OK;
   if (!y || !aligned(y, 16)) return RAZER_E_INVALID;
@@ -139,6 +150,8 @@ razer_status razer_gemv_group(const void* x, razer_dtype x_dt, const razer_packe
     v[g] = view_of(w[g]);
     yy[g] = y[g];
   }
+  for (int g = 0; g < count; g++)
+    if (!product_layout(w[g])) return RAZER_E_UNSUPPORTED;
   if (x_dt == RAZER_F32) return RAZER_E_UNSUPPORTED;
   if (w[0]->cols > kGemvMaxK) return RAZER_E_UNSUPPORTED;
   if (w[0]->cols > 0 && (!x || !aligned(x, 16))) return RAZER_E_INVALID;
@@ -150,7 +163,7 @@ razer_status razer_gemm(const void* x, razer_dtype x_dt, int64_t m, const razer_
   razer_status s = check_packed(w, true);
   if (s != RAZER_OK) return s;
   if (!dtype_ok(x_dt) || !dtype_ok(y_dt) || m < 0) return RAZER_E_INVALID;
-  if (x_dt == RAZER_F32) return RAZER_E_UNSUPPORTED;
+  if (x_dt == RAZER_F32 || !product_layout(w)) return RAZER_E_UNSUPPORTED;
   if (m == 0 || w->rows == 0) return RAZER_OK;
   if (m == 1) return razer_gemv(x, x_dt, w, y, y_dt, ws, ws_bytes, stream);
   if (!y || !aligned(y, 16)) return RAZER_E_INVALID;
@@ -170,6 +183,7 @@ razer_status razer_gemm_w4a4(const razer_packed* x, const razer_packed* w, void*
   s = check_packed(w, true);
   if (s != RAZER_OK) return s;
   if (!dtype_ok(y_dt) || x->cols != w->cols) return RAZER_E_INVALID;
+  if (!product_layout(x) || !product_layout(w)) return RAZER_E_UNSUPPORTED;
   if (x->rows == 0 || w->rows == 0) return RAZER_OK;
   if (x->cols == 0) return RAZER_E_UNSUPPORTED;
   if (w->cols > kGemvMaxK && x->rows == 1) return RAZER_E_UNSUPPORTED;

@@ -83,6 +83,43 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict
   }
 }
 
+// Block-size and scale-format variants (blocks of 16 << (blog2 - 4) elements,
+// byte or FP16 group scales): one code dword per lane and step, its block's
+// scale word read directly; the same value rule and fp32 operation order.
+template <int KIND, typename OT>
+__global__ __launch_bounds__(256) void dequant_variant_kernel(const uint32_t* __restrict__ codes,
+                                                              const uint8_t* __restrict__ scales,
+                                                              const float* __restrict__ ts, int64_t ndw,
+                                                              float m0, float m1, int blog2, int sfmt,
+                                                              OT* __restrict__ out) {
+  const float st = ts ? *ts : 1.0f;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t d = (int64_t)blockIdx.x * 256 + threadIdx.x; d < ndw; d += stride) {
+    const uint32_t w = codes[d];
+    const int64_t blk = (8 * d) >> blog2;
+    const uint32_t sw = sfmt ? (uint32_t)((const uint16_t*)scales)[blk] : (uint32_t)scales[blk];
+    const float sb = sfmt ? scale_of_f16word(sw) : scale_of_byte<KIND>(sw);
+    const float sv = sfmt ? special_of_f16word(sw, m0, m1) : special_of_byte<KIND>(sw, m0, m1);
+    const float svt = (sv * sb) * st;
+    float v[8];
+#pragma unroll
+    for (int p = 0; p < 4; p++) {
+      float2_t f;
+      switch (p) {
+        case 0: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0); break;
+        case 1: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1); break;
+        case 2: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2); break;
+        default: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3); break;
+      }
+      float f0 = f[0], f1 = f[1];
+      asm volatile("" : "+v"(f0), "+v"(f1));  // keeps the two -0 tests apart (see above)
+      v[2 * p] = __builtin_bit_cast(uint32_t, f0) == 0x80000000u ? svt : (f0 * sb) * st;
+      v[2 * p + 1] = __builtin_bit_cast(uint32_t, f1) == 0x80000000u ? svt : (f1 * sb) * st;
+    }
+    Out8<OT>::store(out + 8 * d, v);
+  }
+}
+
 template <int KIND, typename OT>
 static void run(const PackedView& t, OT* out, bool scaled, hipStream_t stream) {
   const int64_t ndw = t.rows * t.cols / 8;
@@ -92,8 +129,13 @@ static void run(const PackedView& t, OT* out, bool scaled, hipStream_t stream) {
   if (g < 1) g = 1;
   const float m0 = 6.0f + 0.5f * (float)t.off_half[0];
   const float m1 = 6.0f + 0.5f * (float)t.off_half[KIND == kWeight ? 1 : 0];
-  hipLaunchKernelGGL((dequant_kernel<KIND, OT>), dim3((unsigned)g), dim3(256), 0, stream,
-                     (const uint32_t*)t.codes, t.scales, scaled ? t.tensor_scale : nullptr, ndw, m0, m1, out);
+  if (!default_layout(t))
+    hipLaunchKernelGGL((dequant_variant_kernel<KIND, OT>), dim3((unsigned)g), dim3(256), 0, stream,
+                       (const uint32_t*)t.codes, t.scales, scaled ? t.tensor_scale : nullptr, ndw, m0, m1,
+                       t.blog2, t.sfmt, out);
+  else
+    hipLaunchKernelGGL((dequant_kernel<KIND, OT>), dim3((unsigned)g), dim3(256), 0, stream,
+                       (const uint32_t*)t.codes, t.scales, scaled ? t.tensor_scale : nullptr, ndw, m0, m1, out);
 }
 
 static hipError_t dequant_dispatch(const PackedView& t, void* out, int out_dtype, bool scaled,

@@ -86,6 +86,18 @@ __device__ __forceinline__ float special_of_byte(uint32_t byte, float m0, float 
   return (byte & 0x80u) ? -mag : mag;
 }
 
+// Group-scale variant: an FP16 block scale whose sign bit and top exponent bit
+// carry the metadata (sign of the special value, pair); the other 14 bits are
+// the scale, an FP16 number with exponent field 0..15.
+constexpr float kF16ScaleMax = 1.9990234375f;  // 14-bit code 0x3FFF
+__device__ __forceinline__ float scale_of_f16word(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0x3FFFu));
+}
+__device__ __forceinline__ float special_of_f16word(uint32_t w, float m0, float m1) {
+  float mag = (w & 0x4000u) ? m1 : m0;
+  return (w & 0x8000u) ? -mag : mag;
+}
+
 // FP4-E2M1 magnitude of a 3-bit magnitude field, times 2 (an integer):
 // {0, 1, 2, 3, 4, 6, 8, 12} packed as nibbles.
 __device__ __forceinline__ uint32_t fp4_mag_x2(uint32_t m) { return (0xC8643210u >> (4u * m)) & 15u; }

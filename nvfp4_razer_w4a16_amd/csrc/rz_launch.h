@@ -17,6 +17,8 @@ struct PackedView {
   uint32_t flags;    // kFlag* bits
   int64_t rows, cols;
   int off_half[2];   // special-value offsets in units of 0.5
+  int blog2 = 4;     // log2 of the elements per block (4..7)
+  int sfmt = 0;      // 0: byte scales (E3M3 / E4M3); 1: FP16 group scales (weights)
   uint8_t* codes;
   uint8_t* scales;
   float* tensor_scale;
@@ -56,6 +58,9 @@ size_t gemv_ws_bytes(int64_t n, int64_t k);
 // (members that the small-batch kernel serves better are launched on their own).
 hipError_t launch_gemv_group(const void* x, int x_dtype, const PackedView* w, void* const* y,
                              int count, int y_dtype, hipStream_t stream);
+// The layout every product kernel reads: 16-element blocks, byte scales.
+inline bool default_layout(const PackedView& v) { return v.blog2 == 4 && v.sfmt == 0; }
+
 hipError_t launch_gemv(const void* x, int x_dtype, const PackedView& w, void* y, int y_dtype,
                        void* ws, size_t ws_bytes, hipStream_t stream);
 

@@ -754,9 +754,266 @@ hipError_t launch_offset_search(const void* x, int dtype, int64_t rows, int64_t 
   return run_offset_search((const __bf16*)x, n, off0, sse, ws, stream);
 }
 
+// ---- block-size and scale-format variants ------------------------------------
+// "RaZeR ..." notes, Key findings (blocks of 32, 64 and 128 elements) and Key
+// design 3 (FP16 block scales for 128-element groups with the metadata in the
+// scale's sign bit and top exponent bit).  The same steps as encode_block for
+// a block of 16 << glog2 elements: each lane still holds 16 consecutive
+// elements, and the 2^glog2 lanes of a block (adjacent lanes of one wave)
+// combine their block maximum, their candidate error changes and, for Four
+// Over Six, their squared errors.  Candidate changes are summed in fp64,
+// where every change (v - q)(v + q - 2y) and every sum of them is exact (a
+// moved element has |y| > 2, so each term is a multiple of 2^-23 below 2^5),
+// so the comparison does not depend on the order of the sums.  Four Over Six
+// errors are not exact: each lane sums its 16 elements in order and the
+// block adds the lanes' sums in lane order.
+struct VariantParams {
+  double cand[4];  // +M0, -M0 (, +M1, -M1), in selection-index order
+  int ncand;
+  int glog2;       // lanes per block = 2^glog2
+  int sfmt;        // 0 byte scales, 1 FP16 group scales
+  int mode;        // 0 plain NVFP4, 1 RaZeR, 2 Four Over Six
+};
+
+__device__ __forceinline__ float group_max(float v, int glog2) {
+  for (int m = 1; m < (1 << glog2); m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
+
+// exact fp64 sums only: the butterfly adds in a lane-dependent order
+__device__ __forceinline__ double group_sum_exact(double v, int glog2) {
+  for (int m = 1; m < (1 << glog2); m <<= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+__device__ __forceinline__ double group_sum_ordered(double v, int glog2, int lane) {
+  const int g0 = lane & ~((1 << glog2) - 1);
+  double s = __shfl(v, g0);
+  for (int i = 1; i < (1 << glog2); i++) s = s + __shfl(v, g0 + i);
+  return s;
+}
+
+// One plain-FP4 encoding of the lane's 16 elements at real block scale sb_real:
+// scale code (0: zero block, then sb = 0 and all codes +0), the decoded scale,
+// the scaled values and the codes.
+template <int KIND>
+__device__ __forceinline__ uint32_t variant_at_scale(const float (&xf)[16], float sb_real, float st,
+                                                     int sfmt, uint32_t (&w)[2], float (&y)[16],
+                                                     float& sb) {
+  w[0] = 0u;
+  w[1] = 0u;
+#pragma unroll
+  for (int j = 0; j < 16; j++) y[j] = 0.0f;
+  uint32_t scode = sfmt ? min((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)sb_real), 0x3FFFu)
+                        : round_scale<KIND>(sb_real);
+  sb = 0.0f;
+  if (scode == 0u) return 0u;
+  sb = sfmt ? scale_of_f16word(scode) : scale_of_code<KIND>(scode);
+  const float d = sb * st;
+  const float rcp = 1.0f / d;
+  if (!(rcp < INFINITY)) {
+    sb = 0.0f;
+    return 0u;
+  }
+#pragma unroll
+  for (int j = 0; j < 16; j++) y[j] = xf[j] * rcp;
+  fp4_pack16(y, w);
+  return scode;
+}
+
+template <int KIND>
+__device__ __forceinline__ void encode_variant(const float (&xf)[16], float amax, float st,
+                                               const VariantParams& vp, int lane, uint2& cw,
+                                               uint32_t& sword) {
+#pragma clang fp contract(off)
+  const float smax = vp.sfmt ? kF16ScaleMax : (KIND == kWeight ? 30.0f : 448.0f);
+  float amax_b = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 16; j++) amax_b = fmaxf(amax_b, fabsf(xf[j]));
+  amax_b = group_max(amax_b, vp.glog2);
+  const float r = amax_b / amax;
+  const float sb_real = r * smax;
+  uint32_t w[2];
+  float y[16], sb;
+  uint32_t scode = variant_at_scale<KIND>(xf, sb_real, st, vp.sfmt, w, y, sb);
+  uint32_t sel = 0u;
+  if (vp.mode == 2) {
+    uint32_t w4[2];
+    float y4[16], sb4;
+    const uint32_t c4 = variant_at_scale<KIND>(xf, sb_real * 1.5f, st, vp.sfmt, w4, y4, sb4);
+    const double e6 = group_sum_ordered(plain_block_sse(xf, w, sb, st), vp.glog2, lane);
+    const double e4 = group_sum_ordered(plain_block_sse(xf, w4, sb4, st), vp.glog2, lane);
+    if (e4 < e6) {
+      w[0] = w4[0];
+      w[1] = w4[1];
+      scode = c4;
+    }
+  } else if (vp.mode == 1 && scode != 0u) {  // scode is the same on every lane of the block
+    double q0[16];
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+      const uint32_t c = (w[j >> 3] >> (4 * (j & 7))) & 15u;
+      const double m = 0.5 * (double)fp4_mag_x2(c & 7u);
+      q0[j] = (c & 8u) ? -m : m;
+    }
+    double delta[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+      if (c < vp.ncand) {
+        const double v = vp.cand[c];
+        double acc = 0.0;
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+          const double yj = (double)y[j];
+          if (fabs(yj - v) < fabs(yj - q0[j])) acc += (v - q0[j]) * (v + q0[j] - 2.0 * yj);
+        }
+        delta[c] = group_sum_exact(acc, vp.glog2);
+      }
+    }
+    double best = delta[0];
+#pragma unroll
+    for (int c = 1; c < 4; c++)
+      if (c < vp.ncand && delta[c] < best) {
+        best = delta[c];
+        sel = (uint32_t)c;
+      }
+    const double v = sel == 0u ? vp.cand[0] : sel == 1u ? vp.cand[1] : sel == 2u ? vp.cand[2] : vp.cand[3];
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+      const double yj = (double)y[j];
+      const uint32_t sh = 4 * (j & 7);
+      if (fabs(yj - v) < fabs(yj - q0[j])) w[j >> 3] = (w[j >> 3] & ~(15u << sh)) | (8u << sh);
+    }
+  }
+  cw = make_uint2(w[0], w[1]);
+  if (scode == 0u) sel = 0u;
+  if (vp.sfmt)
+    sword = ((sel & 1u) << 15) | ((sel >> 1) << 14) | scode;
+  else
+    sword = KIND == kWeight ? (((sel & 1u) << 7) | ((sel >> 1) << 6) | scode) : ((sel << 7) | scode);
+}
+
+// Same staging as encode_kernel (64 consecutive 16-element runs per wave and
+// step); the first lane of each block writes its scale (1 or 2 bytes).
+template <int KIND, typename T>
+__global__ __launch_bounds__(256) void encode_variant_kernel(const T* __restrict__ x, int64_t nsub,
+                                                             const uint32_t* __restrict__ partial,
+                                                             int npartial, uint2* __restrict__ codes,
+                                                             uint8_t* __restrict__ scales,
+                                                             float* __restrict__ ts_out, VariantParams vp) {
+  constexpr int kBB = 16 * (int)sizeof(T);
+  constexpr int kNI = kBB * 64 / 1024;
+  __shared__ __attribute__((aligned(16))) uint8_t stage[4][64 * kBB];
+  uint32_t m = 0u;
+  for (int i = threadIdx.x; i < npartial; i += 256) m = max(m, partial[i]);
+  m = wave_max_u32(m);
+  __shared__ uint32_t sm[4];
+  if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = max(max(sm[0], sm[1]), max(sm[2], sm[3]));
+  const bool nonfinite = m >= 0x7F800000u;
+  const float amax = u2f(m);
+  const float smax = vp.sfmt ? kF16ScaleMax : (KIND == kWeight ? 30.0f : 448.0f);
+  const float st = amax / (6.0f * smax);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *ts_out = nonfinite ? __builtin_nanf("") : st;
+  const bool all_zero = nonfinite || amax == 0.0f;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool leader = (lane & ((1 << vp.glog2) - 1)) == 0;
+  const int64_t step = (int64_t)gridDim.x * 4 * 64;
+  int64_t bb = ((int64_t)blockIdx.x * 4 + wave) * 64;
+  auto store = [&](int64_t sub, uint2 cw, uint32_t sword) {
+    if (sub >= nsub) return;
+    codes[sub] = cw;
+    if (leader) {
+      const int64_t blk = sub >> vp.glog2;
+      if (vp.sfmt) ((uint16_t*)scales)[blk] = (uint16_t)sword;
+      else scales[blk] = (uint8_t)sword;
+    }
+  };
+  if (all_zero) {
+    for (; bb < nsub; bb += step) store(bb + lane, make_uint2(0u, 0u), 0u);
+    return;
+  }
+  const uint8_t* xb = (const uint8_t*)x;
+  const int64_t total = nsub * kBB;
+  auto load = [&](int64_t b0, u32x4_t (&v)[kNI]) {
+    const int64_t rem = total - b0 * kBB;
+    const int nrec = rem <= 0 ? 0 : (int)min(rem, (int64_t)64 * kBB);
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(xb + (rem <= 0 ? 0 : b0 * kBB)), (short)0, nrec, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < kNI; i++) v[i] = __builtin_amdgcn_raw_buffer_load_b128(r, (i * 64 + lane) * 16, 0, 2);
+  };
+  u32x4_t cur[kNI], nxt[kNI];
+  load(bb, cur);
+  uint8_t* stg = stage[wave];
+  for (; bb < nsub; bb += step) {
+    load(bb + step, nxt);
+#pragma unroll
+    for (int i = 0; i < kNI; i++) *(u32x4_t*)(stg + (i * 64 + lane) * 16) = cur[i];
+    wave_lds_sync();
+    u32x4_t q[kBB / 16];
+#pragma unroll
+    for (int i = 0; i < kBB / 16; i++) q[i] = *(const u32x4_t*)(stg + lane * kBB + 16 * i);
+    wave_lds_sync();
+    float xf[16];
+    unpack_block<T>(q, xf);
+    uint2 cw;
+    uint32_t sword;
+    encode_variant<KIND>(xf, amax, st, vp, lane, cw, sword);
+    store(bb + lane, cw, sword);
+#pragma unroll
+    for (int i = 0; i < kNI; i++) cur[i] = nxt[i];
+  }
+}
+
+template <int KIND, typename T>
+static hipError_t run_quantize_variant(const T* x, const PackedView& out, uint32_t* partial,
+                                       hipStream_t stream) {
+  const int64_t n = out.rows * out.cols;
+  const int64_t nsub = n / 16;
+  const int64_t nvec = n / (16 / (int64_t)sizeof(T));
+  int64_t g1 = (nvec + 4 * 256 - 1) / (4 * 256);
+  if (g1 < 1) g1 = 1;
+  if (g1 > kAmaxMaxPartials) g1 = kAmaxMaxPartials;
+  hipLaunchKernelGGL(amax_partial_kernel<T>, dim3((unsigned)g1), dim3(256), 0, stream,
+                     (const uint4*)x, nvec, partial);
+  VariantParams vp;
+  const int npairs = KIND == kWeight ? 2 : 1;
+  for (int p = 0; p < npairs; p++) {
+    const double M = 6.0 + 0.5 * out.off_half[p];
+    vp.cand[2 * p] = M;
+    vp.cand[2 * p + 1] = -M;
+  }
+  for (int c = 2 * npairs; c < 4; c++) vp.cand[c] = 0.0;
+  vp.ncand = 2 * npairs;
+  vp.glog2 = out.blog2 - 4;
+  vp.sfmt = out.sfmt;
+  vp.mode = (out.flags & kFlagFourOverSix) ? 2 : (out.flags & kFlagNoRemap) ? 0 : 1;
+  int64_t g2 = (nsub + 255) / 256;
+  const int64_t cap = (int64_t)device_cu_count() * 8;
+  if (g2 > cap) g2 = cap;
+  if (g2 < 1) g2 = 1;
+  hipLaunchKernelGGL((encode_variant_kernel<KIND, T>), dim3((unsigned)g2), dim3(256), 0, stream, x,
+                     nsub, partial, (int)g1, (uint2*)out.codes, out.scales, out.tensor_scale, vp);
+  return hipGetLastError();
+}
+
 hipError_t launch_quantize(const void* x, int dtype, const PackedView& out, void* ws,
                            hipStream_t stream) {
   uint32_t* partial = (uint32_t*)ws;
+  if (!default_layout(out)) {
+    if (out.kind == kWeight) {
+      if (dtype == kF32) return run_quantize_variant<kWeight>((const float*)x, out, partial, stream);
+      if (dtype == kF16) return run_quantize_variant<kWeight>((const _Float16*)x, out, partial, stream);
+      return run_quantize_variant<kWeight>((const __bf16*)x, out, partial, stream);
+    }
+    if (dtype == kF32) return run_quantize_variant<kAct>((const float*)x, out, partial, stream);
+    if (dtype == kF16) return run_quantize_variant<kAct>((const _Float16*)x, out, partial, stream);
+    return run_quantize_variant<kAct>((const __bf16*)x, out, partial, stream);
+  }
   if (out.kind == kWeight) {
     if (dtype == kF32) return run_quantize<kWeight>((const float*)x, out, partial, stream);
     if (dtype == kF16) return run_quantize<kWeight>((const _Float16*)x, out, partial, stream);

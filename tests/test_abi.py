@@ -33,8 +33,10 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_struct_layout_matches_header():
-    # int32 kind, uint32 flags, int64 rows, int64 cols, int8[2] + 6 reserved, 3 pointers
+    # int32 kind, uint32 flags, int64 rows, int64 cols, int8[2] offsets, uint8 block_log2,
+    # uint8 scale_fmt, 4 reserved, 3 pointers
     assert ctypes.sizeof(rz.razer_packed) == 4 + 4 + 8 + 8 + 8 + 3 * 8
+    assert rz.razer_packed.block_log2.offset == 26 and rz.razer_packed.scale_fmt.offset == 27
     assert rz.razer_packed.codes.offset == 32
 
 
@@ -74,6 +76,10 @@ FAKE_WS = ctypes.c_void_p(0x5000)
     lambda s: setattr(s, "codes", 0x1008),             # misaligned codes
     lambda s: setattr(s, "kind", rz.RAZER_ACT),        # wrong kind for the weight encoder
     lambda s: setattr(s, "kind", 7),
+    lambda s: setattr(s, "block_log2", 3),             # block sizes are 16..128
+    lambda s: setattr(s, "block_log2", 8),
+    lambda s: setattr(s, "block_log2", 6),             # cols (32) not a multiple of 64
+    lambda s: setattr(s, "scale_fmt", 2),
     lambda s: setattr(s, "flags", 4),                  # unknown encoder flag bit
     lambda s: setattr(s, "flags", 0x80000002),
 ])
@@ -222,3 +228,20 @@ def test_gemv_group_unsupported_like_gemv():
     assert _group_call([a], [0x6000], x_dt=rz.RAZER_F32) == rz.RAZER_E_UNSUPPORTED
     big = _packed(rows=8, cols=65536 + 16)
     assert _group_call([big], [0x6000]) == rz.RAZER_E_UNSUPPORTED
+
+
+def test_layout_variants_host_checks():
+    L = rz.lib()
+    a = _packed(kind=rz.RAZER_ACT, off=(-2, 0), cols=128)
+    a.scale_fmt = rz.RAZER_SCALE_F16  # FP16 group scales are for weights only
+    assert L.razer_quantize_act(FAKE_X, rz.RAZER_BF16, ctypes.byref(a), FAKE_WS, 4096, None) == rz.RAZER_E_INVALID
+    # the products take 16-element blocks with byte scales only
+    for blog2, fmt in ((5, 0), (7, 0), (4, 1), (7, 1)):
+        w = _packed(rows=8, cols=128)
+        w.block_log2, w.scale_fmt = blog2, fmt
+        y = ctypes.c_void_p(0x6000)
+        assert L.razer_gemv(FAKE_X, rz.RAZER_F16, ctypes.byref(w), y, rz.RAZER_F16, None, 0, None) == rz.RAZER_E_UNSUPPORTED
+        assert L.razer_gemm(FAKE_X, rz.RAZER_F16, 4, ctypes.byref(w), y, rz.RAZER_F16, FAKE_WS, 1 << 20, None) == rz.RAZER_E_UNSUPPORTED
+        assert _group_call([w], [0x6000]) == rz.RAZER_E_UNSUPPORTED
+        x = _packed(kind=rz.RAZER_ACT, off=(-2, 0), rows=2, cols=128)
+        assert L.razer_gemm_w4a4(ctypes.byref(x), ctypes.byref(w), y, rz.RAZER_BF16, FAKE_WS, 1 << 20, None) == rz.RAZER_E_UNSUPPORTED

@@ -56,26 +56,28 @@ def as_f32(x_cpu: torch.Tensor) -> np.ndarray:
 
 def assert_same_encoding(p: rz.PackedTensor, ref: oracle.Packed, x=None, what=""):
     codes = p.codes.cpu().numpy().reshape(-1)
-    scales = p.scales.cpu().numpy().reshape(-1)
+    scales = p.scales.cpu().numpy().reshape(-1).view(ref.scales.dtype)  # 2-byte FP16 scales
     ts = p.tensor_scale.cpu().numpy().view(np.uint32)[0]
     ts_ref = np.array([ref.tensor_scale], dtype=np.float32).view(np.uint32)[0]
     assert ts == ts_ref, f"{what}: tensor scale {ts:#x} vs {ts_ref:#x}"
     bad_s = np.nonzero(scales != ref.scales)[0]
     bad_c = np.nonzero(codes != ref.codes)[0]
     if bad_s.size or bad_c.size:
-        blk = int(bad_s[0]) if bad_s.size else int(bad_c[0]) // 8
-        msg = (f"{what}: {bad_s.size} scale bytes and {bad_c.size} code bytes differ; first block {blk}: "
-               f"gpu scale {scales[blk]:#04x} codes {codes[8*blk:8*blk+8].tolist()} / "
-               f"ref scale {ref.scales[blk]:#04x} codes {ref.codes[8*blk:8*blk+8].tolist()}")
+        B = getattr(ref, "block", 16)
+        blk = int(bad_s[0]) if bad_s.size else int(bad_c[0]) // (B // 2)
+        cb = slice(B // 2 * blk, B // 2 * blk + min(B // 2, 16))
+        msg = (f"{what}: {bad_s.size} scales and {bad_c.size} code bytes differ; first block {blk}: "
+               f"gpu scale {int(scales[blk]):#06x} codes {codes[cb].tolist()} / "
+               f"ref scale {int(ref.scales[blk]):#06x} codes {ref.codes[cb].tolist()}")
         if x is not None:
-            msg += f"; block input {np.asarray(x).reshape(-1)[16*blk:16*blk+16].tolist()}"
+            msg += f"; block input {np.asarray(x).reshape(-1)[B*blk:B*blk+min(B, 32)].tolist()}"
         raise AssertionError(msg)
 
 
 def to_device(pk: oracle.Packed) -> rz.PackedTensor:
-    t = rz.PackedTensor(pk.kind, pk.rows, pk.cols, pk.offsets, "cuda")
+    t = rz.PackedTensor(pk.kind, pk.rows, pk.cols, pk.offsets, "cuda", 0, pk.block, pk.scale_fmt)
     t.codes.copy_(torch.from_numpy(pk.codes.reshape(pk.rows, pk.cols // 2)))
-    t.scales.copy_(torch.from_numpy(pk.scales.reshape(pk.rows, pk.cols // 16)))
+    t.scales.copy_(torch.from_numpy(pk.scales.view(np.uint8).reshape(tuple(t.scales.shape))))
     t.tensor_scale.copy_(torch.tensor([float(pk.tensor_scale)], dtype=torch.float32))
     return t
 
@@ -338,6 +340,97 @@ def test_four_over_six_weights_decode_through_the_products():
     assert_product_close(y, y_ref, nrm, "4/6 gemm")
     y1 = rz.razer_gemv(xb[0].cuda(), p, out_dtype=torch.float32).cpu().numpy()
     assert_product_close(y1[None], y_ref[:1], nrm[:1], "4/6 gemv")
+
+
+# ---- block-size and FP16 group-scale variants -------------------------------------
+
+VARIANT_CASES = [  # kind, block, scale_fmt, mode, input dtype
+    (oracle.WEIGHT, 32, 0, "razer", torch.float32), (oracle.WEIGHT, 64, 0, "razer", torch.bfloat16),
+    (oracle.WEIGHT, 128, 0, "razer", torch.float16), (oracle.WEIGHT, 128, 1, "razer", torch.float32),
+    (oracle.WEIGHT, 16, 1, "razer", torch.bfloat16), (oracle.WEIGHT, 64, 1, "razer", torch.float16),
+    (oracle.ACT, 32, 0, "razer", torch.bfloat16), (oracle.ACT, 128, 0, "razer", torch.float16),
+    (oracle.WEIGHT, 128, 0, "plain", torch.float32), (oracle.WEIGHT, 128, 1, "plain", torch.float32),
+    (oracle.WEIGHT, 64, 0, "fos", torch.float32), (oracle.WEIGHT, 128, 1, "fos", torch.bfloat16),
+    (oracle.ACT, 128, 0, "fos", torch.bfloat16), (oracle.ACT, 64, 0, "plain", torch.float16),
+]
+
+
+def _variant_encode(kind, x, offs, block, sfmt, mode):
+    kw = dict(remap=mode != "plain", four_over_six=mode == "fos", block=block)
+    ref = oracle.quantize(kind, as_f32(x), offs, scale_fmt=sfmt, **kw)
+    xd = x.cuda()
+    if kind == oracle.WEIGHT:
+        p = rz.razer_quantize_weight(xd, offs, scale_fmt=sfmt, **kw)
+    else:
+        p = rz.razer_quantize_act(xd, offs, **kw)
+    torch.cuda.synchronize()
+    return p, ref
+
+
+@pytest.mark.parametrize("kind,block,sfmt,mode,dtype", VARIANT_CASES)
+def test_quantize_variant_parity(kind, block, sfmt, mode, dtype):
+    _need_gpu()
+    if kind == oracle.WEIGHT:
+        x, offs = pr1()[0].to(dtype), (-2, -5)
+    else:
+        x, offs = synth.act_quant_x(64, 4096).to(dtype), (-2,)
+    p, ref = _variant_encode(kind, x, offs, block, sfmt, mode)
+    assert_same_encoding(p, ref, as_f32(x), f"variant kind {kind} block {block} fmt {sfmt} {mode} {dtype}")
+    if mode == "razer":  # both candidates of every pair in use somewhere
+        top = 15 if sfmt else 7
+        sw = ref.scales.astype(np.int64)
+        assert (sw >> top & 1).any() and (~sw >> top & 1).any()
+    # the decoder reads the variant back exactly as the oracle's decoder does
+    d32 = rz.razer_dequant(p, torch.float32).cpu().numpy()
+    np.testing.assert_array_equal(d32, oracle.dequant_f32(ref))
+    d16 = rz.razer_dequant(p, torch.bfloat16).cpu()
+    assert torch.equal(d16, torch.from_numpy(oracle.dequant_f32(ref)).to(torch.bfloat16))
+
+
+@pytest.mark.parametrize("name", [n for n in sorted(EDGE) if EDGE[n].shape[1] % 32 == 0])
+@pytest.mark.parametrize("kind,block,sfmt", [(oracle.WEIGHT, 32, 1), (oracle.ACT, 32, 0), (oracle.WEIGHT, 32, 0)])
+def test_quantize_variant_edge_cases(name, kind, block, sfmt):
+    _need_gpu()
+    x = EDGE[name]
+    offs = (-2, -5) if kind == oracle.WEIGHT else (-2,)
+    p, ref = _variant_encode(kind, torch.from_numpy(x), offs, block, sfmt, "razer")
+    assert_same_encoding(p, ref, x, f"variant edge {name} kind {kind} block {block} fmt {sfmt}")
+    if not np.isnan(ref.tensor_scale):
+        np.testing.assert_array_equal(rz.razer_dequant(p, torch.float32).cpu().numpy(), oracle.dequant_f32(ref))
+
+
+def test_quantize_variant_group128_f16_prefill_weight_sampled():
+    """The pages' kernel layout (128-element blocks, FP16 scales with the
+    metadata in the sign and top exponent bits) on the full W[28672, 8192]:
+    rows sampled against the oracle with the tensor-maximum row included."""
+    _need_gpu()
+    w = synth.prefill_weight()
+    log("g128 f16 prefill W: gpu ...")
+    p = rz.razer_quantize_weight(torch.from_numpy(w).cuda(), (-2, 4), block=128, scale_fmt=rz.RAZER_SCALE_F16)
+    torch.cuda.synchronize()
+    rmax = int(np.abs(w).max(axis=1).argmax())
+    rows = sorted(set(np.random.default_rng(97).choice(w.shape[0], 64, replace=False).tolist()) | {rmax})
+    log("g128 f16 prefill W: oracle on", len(rows), "rows ...")
+    ref = oracle.quantize(oracle.WEIGHT, w[rows], (-2, 4), block=128, scale_fmt=oracle.SCALE_F16)
+    k = w.shape[1]
+    codes = p.codes.cpu().numpy().reshape(w.shape[0], k // 2)[rows].reshape(-1)
+    scales = p.scales.cpu().numpy().reshape(w.shape[0], -1)[rows].reshape(-1).view(np.uint16)
+    assert p.tensor_scale.cpu().numpy().view(np.uint32)[0] == np.array([ref.tensor_scale], np.float32).view(np.uint32)[0]
+    np.testing.assert_array_equal(scales, ref.scales)
+    np.testing.assert_array_equal(codes, ref.codes)
+    del p
+    torch.cuda.empty_cache()
+
+
+def test_products_reject_variant_layouts():
+    _need_gpu()
+    w = rz.razer_quantize_weight(pr1()[0].cuda(), (-2, 4), block=64)
+    x = torch.randn(1024, device="cuda", dtype=torch.float16)
+    with pytest.raises(rz.RazerError) as e:
+        rz.razer_gemv(x, w)
+    assert e.value.status == rz.RAZER_E_UNSUPPORTED
+    with pytest.raises(rz.RazerError):
+        rz.razer_gemm(x.reshape(1, -1).repeat(4, 1), w)
 
 
 # ---- decoder parity ------------------------------------------------------------
