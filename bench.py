@@ -319,9 +319,33 @@ def bench_rows(torch, rz, synth, args, decode_base):
              "four_over_six": rel_sse(torch, rz, w, wf),
              "razer_pairs_-2_4": rel_sse(torch, rz, w, wp),
              f"razer_pairs_-2_{best}": rel_sse(torch, rz, w, rz.razer_quantize_weight(w, (-2, best)))}
-    del t, w, wso, wf
+    # layout variants (block sizes 16..128 with byte scales, and the FP16
+    # group scale): relative squared error of each encoder on this weight, and
+    # the RaZeR encode time of each layout
+    var_w = {}
+    for block, sfmt in ((16, 0), (32, 0), (64, 0), (128, 0), (128, 1), (16, 1)):
+        name = f"b{block}_{'f16' if sfmt else 'byte'}"
+        pv = rz.PackedTensor(rz.RAZER_WEIGHT, 28672, 8192, (-2, 4), dev, 0, block, sfmt)
+        t = GraphTimer(torch, lambda: rz.razer_quantize_weight(w, out=pv))
+        ms_v = t.time(3)
+        var_w[name] = {
+            "encode_ms": ms_v,
+            "rel_sse": {
+                "nvfp4": rel_sse(torch, rz, w, rz.razer_quantize_weight(w, (-2, 4), remap=False, block=block,
+                                                                      scale_fmt=sfmt)),
+                "four_over_six": rel_sse(torch, rz, w, rz.razer_quantize_weight(
+                    w, (-2, 4), four_over_six=True, block=block, scale_fmt=sfmt)),
+                "razer_pairs_-2_4": rel_sse(torch, rz, w, pv)}}
+        del t, pv
+    del w, wso, wf
     torch.cuda.empty_cache()
     xa = synth.act_quant_x().to(dev)
+    var_a = {}
+    for block in (16, 32, 64, 128):
+        var_a[f"b{block}_byte"] = {"rel_sse": {
+            "nvfp4": rel_sse(torch, rz, xa, rz.razer_quantize_act(xa, remap=False, block=block)),
+            "four_over_six": rel_sse(torch, rz, xa, rz.razer_quantize_act(xa, four_over_six=True, block=block)),
+            "razer_pair_-2": rel_sse(torch, rz, xa, rz.razer_quantize_act(xa, block=block))}}
     err_a = {"nvfp4": rel_sse(torch, rz, xa, rz.razer_quantize_act(xa, remap=False)),
              "four_over_six": rel_sse(torch, rz, xa, rz.razer_quantize_act(xa, four_over_six=True)),
              "razer_pair_-2": rel_sse(torch, rz, xa, rz.razer_quantize_act(xa))}
@@ -332,6 +356,10 @@ def bench_rows(torch, rz, synth, args, decode_base):
                            "X [4096,8192] bf16",
                "ms": ms_f, "gelem_per_s": 28672 * 8192 / ms_f / 1e6,
                "rel_sse_weight": err_w, "rel_sse_act": err_a}
+    var_row = {"workload": "layout variants: RaZeR encode time of W [28672,8192] fp32 and the relative "
+                           "squared error of NVFP4 / Four Over Six / RaZeR per layout on that weight and "
+                           "on X [4096,8192] bf16 (the b16_byte encode time is the default kernel)",
+               "weight": var_w, "act": var_a}
     x = synth.prefill_x().to(dev)
     y = torch.empty((2048, 28672), dtype=torch.bfloat16, device=dev)
     t = GraphTimer(torch, lambda: rz.razer_gemm(x, wp, out=y))
@@ -343,6 +371,7 @@ def bench_rows(torch, rz, synth, args, decode_base):
     n_el = 28672 * 8192
     rows["offset_search_prefill"] = off_row
     rows["four_over_six_prefill"] = fos_row
+    rows["layout_variants"] = var_row
     rows["quantize_weight_prefill"] = {
         "workload": "W [28672,8192] fp32, 4 candidates", "ms": ms_q, "gelem_per_s": n_el / ms_q / 1e6,
         "gbs_1read": n_el * (4 + 0.5625) / ms_q / 1e6,
