@@ -142,13 +142,16 @@ __global__ __launch_bounds__(256) void gemm_kernel(const XT* __restrict__ x, int
 
 // ---- large tiles: 256 x 256 x 64, double-buffered LDS, register prefetch -------
 //
-// For M >= 256 (prefill).  Four waves, each owning a 128 x 128 sub-tile (4 x 4
-// MFMA 32x32x16 tiles, 256 fp32 accumulators per lane).  Per K step each
-// thread prefetches 128 bytes of x and one weight row's 32 code bytes + 4
-// scale bytes into registers while the waves run the step's 64 MFMAs; then
-// it writes the x bytes and the decoded weight row (64 values) into the other
-// LDS buffer.  LDS rows are padded by 16 bytes so the 16-byte fragment reads
-// of 32 consecutive rows hit distinct banks.
+// For M >= 256 (prefill).  Eight waves, two per SIMD, laid out 2 (M) x 4 (N),
+// each owning a 128 x 64 sub-tile (4 x 2 MFMA 32x32x16 tiles, 128 fp32
+// accumulators per lane), so that while one wave of a SIMD waits on LDS or
+// runs its decode the other keeps the matrix unit busy (four waves with
+// 128 x 128 sub-tiles ran 20-28 % slower: one wave per SIMD left the matrix
+// unit idle through its own decode and LDS waits).  Per K step each thread
+// prefetches 64 bytes of x and half a weight row (32 elements) into registers
+// while the waves run the step's MFMAs; then it writes the x bytes and the 32
+// decoded values into the other LDS buffer.  LDS rows are padded by 16 bytes
+// so the 16-byte fragment reads of 32 consecutive rows hit distinct banks.
 //
 // Decode (per pair of codes): the packed FP4 conversion, an exact multiply by
 // sb, and a bit select that puts the block's SV * sb where the remapped code
@@ -257,35 +260,35 @@ __device__ __forceinline__ uint32_t decode_one_pair(uint32_t w, int sel, float s
 }
 
 template <typename XT, int KIND, typename OT>
-__global__ __launch_bounds__(256) void gemm_tile256_kernel(const XT* __restrict__ x, int64_t m,
-                                                           const uint8_t* __restrict__ codes,
-                                                           const uint8_t* __restrict__ scales,
-                                                           const float* __restrict__ ts, int64_t n,
-                                                           int64_t k, float m0, float m1,
-                                                           OT* __restrict__ y) {
+__global__ __launch_bounds__(512) void gemm_tile256_kernel(const XT* __restrict__ x, int64_t m,
+                                                      const uint8_t* __restrict__ codes,
+                                                      const uint8_t* __restrict__ scales,
+                                                      const float* __restrict__ ts, int64_t n,
+                                                      int64_t k, float m0, float m1, OT* __restrict__ y) {
   typedef typename Mfma32<XT>::V V;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  XT* As = (XT*)smem;                    // [2][kTM * kTS]
-  XT* Bs = As + 2 * kTM * kTS;           // [2][kTN * kTS]
-  float2* lut = (float2*)(Bs + 2 * kTN * kTS);  // scale byte -> (sb, SV*sb bits x2)
+  XT* As = (XT*)smem;
+  XT* Bs = As + 2 * kTM * kTS;
+  float2* lut = (float2*)(Bs + 2 * kTN * kTS);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   const int64_t ntn = (n + kTN - 1) / kTN;
   const int64_t m_base = (int64_t)(blockIdx.x / ntn) * kTM;
   const int64_t n_base = (int64_t)(blockIdx.x % ntn) * kTN;
   const int ktiles = (int)(k / kTK);
-  {
+  if (tid < 256) {
     const uint32_t b = (uint32_t)tid;
     const float sb = scale_of_byte<KIND>(b);
     const uint32_t svd = bits16<XT>(special_of_byte<KIND>(b, m0, m1) * sb) ^ 0x8000u;
     lut[b] = make_float2(sb, __builtin_bit_cast(float, svd | (svd << 16)));
   }
-
   // Two register sets: the tile two K steps ahead is in flight while the
-  // next tile is decoded into LDS under the current tile's MFMAs.
+  // next tile is decoded into LDS under the current tile's MFMAs.  Per K step
+  // a thread carries 64 bytes of x and half a weight row (16 code bytes, 32
+  // elements) with its row's four scale bytes.
   struct Stage {
-    uint4 a[8];
-    uint4 c[2];
+    uint4 a[4];
+    uint4 c;
     uint32_t s;
   };
   Stage st0, st1;
@@ -300,162 +303,100 @@ __global__ __launch_bounds__(256) void gemm_tile256_kernel(const XT* __restrict_
                                                     (int)(rows_n * (k / 2)), 0x00020000);
   const Rsrc sr = __builtin_amdgcn_make_buffer_rsrc((void*)(scales + n_base * (k / 16)), (short)0,
                                                     (int)(rows_n * (k / 16)), 0x00020000);
-  int xo[8];
+  int xo[4];
 #pragma unroll
-  for (int i = 0; i < 8; i++) {
-    const int idx = i * 256 + tid;
+  for (int i = 0; i < 4; i++) {
+    const int idx = i * 512 + tid;
     xo[i] = (idx >> 3) < rows_m ? (int)(((int64_t)(idx >> 3) * k + (idx & 7) * 8) * (int64_t)sizeof(XT)) : kOob;
   }
-  const int co = tid < rows_n ? (int)((int64_t)tid * (k / 2)) : kOob;
-  const int so = tid < rows_n ? (int)((int64_t)tid * (k / 16)) : kOob;
-  // issued in the order the next step consumes them: scale word, codes, x
+  const int br = tid >> 1, bh = tid & 1;  // the weight row and half this thread decodes
+  const int co = br < rows_n ? (int)((int64_t)br * (k / 2)) + 16 * bh : kOob;
+  const int so = br < rows_n ? (int)((int64_t)br * (k / 16)) : kOob;
   auto gload = [&](int kt, Stage& r) {
     const int k0 = kt * kTK;
     r.s = __builtin_amdgcn_raw_buffer_load_b32(sr, so, k0 / 16, 0);
-    // codes are read by every row tile of the grid: keep them cacheable
     const u32x4_t c0 = __builtin_amdgcn_raw_buffer_load_b128(cr, co, k0 / 2, 0);
-    const u32x4_t c1 = __builtin_amdgcn_raw_buffer_load_b128(cr, co + 16, k0 / 2, 0);
-    r.c[0] = make_uint4(c0[0], c0[1], c0[2], c0[3]);
-    r.c[1] = make_uint4(c1[0], c1[1], c1[2], c1[3]);
+    r.c = make_uint4(c0[0], c0[1], c0[2], c0[3]);
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
+    for (int i = 0; i < 4; i++) {
       const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(xr, xo[i], k0 * (int)sizeof(XT), 0);
       r.a[i] = make_uint4(v[0], v[1], v[2], v[3]);
     }
   };
-  // part `blk` (0..3) of writing stage r into LDS buffer buf: two x vectors
-  // and the decode of 16-element block blk of this thread's weight row.
-  auto lstore_part = [&](const Stage& r, int buf, int blk, float2 f) {
+  auto cword = [](const uint4& c, int kk) { return kk == 0 ? c.x : kk == 1 ? c.y : kk == 2 ? c.z : c.w; };
+  auto lstore = [&](const Stage& r, int buf) {
     XT* a = As + buf * kTM * kTS;
 #pragma unroll
-    for (int i = 2 * blk; i < 2 * blk + 2; i++) {
-      const int idx = i * 256 + tid;
+    for (int i = 0; i < 4; i++) {
+      const int idx = i * 512 + tid;
       *(uint4*)(a + (idx >> 3) * kTS + (idx & 7) * 8) = r.a[i];
     }
-    const uint32_t svd = __builtin_bit_cast(uint32_t, f.y);
-    const uint4 cw = r.c[blk >> 1];
-    uint4* b = (uint4*)(Bs + buf * kTN * kTS + tid * kTS) + 2 * blk;
-    b[0] = decode_dword<XT>((blk & 1) ? cw.z : cw.x, f.x, svd);
-    b[1] = decode_dword<XT>((blk & 1) ? cw.w : cw.y, f.x, svd);
+#pragma unroll
+    for (int kk = 0; kk < 4; kk++) {
+      const float2 f = lut[(r.s >> (8 * (2 * bh + (kk >> 1)))) & 0xFFu];
+      *(uint4*)(Bs + buf * kTN * kTS + br * kTS + 32 * bh + 8 * kk) =
+          decode_dword<XT>(cword(r.c, kk), f.x, __builtin_bit_cast(uint32_t, f.y));
+    }
   };
-
-  floatx16 acc[4][4];
+  floatx16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; i++)
 #pragma unroll
-    for (int j = 0; j < 4; j++)
+    for (int j = 0; j < 2; j++)
 #pragma unroll
       for (int e = 0; e < 16; e++) acc[i][j][e] = 0.0f;
 
-  // One K step, branch free so the scheduler can interleave the next tile's
-  // decode (VALU) and LDS writes with this tile's MFMAs: the prefetch index
-  // is clamped to the last tile and the final step's decode lands in the
-  // buffer that is never read again.
   auto step = [&](int kt, Stage& cur_stage, Stage& next_stage) {
     const int cur = kt & 1;
     gload(kt + 2 < ktiles ? kt + 2 : ktiles - 1, next_stage);
-    float2 f[4];
+    float2 f[2];
 #pragma unroll
-    for (int blk = 0; blk < 4; blk++) f[blk] = lut[(cur_stage.s >> (8 * blk)) & 0xFFu];
+    for (int j = 0; j < 2; j++) f[j] = lut[(cur_stage.s >> (8 * (2 * bh + j))) & 0xFFu];
     const XT* a = As + cur * kTM * kTS;
     const XT* b = Bs + cur * kTN * kTS;
-    // fragments of sub-step kk + 1 are read from LDS while sub-step kk's MFMAs
-    // run, so only the first sub-step after the barrier waits for LDS
-    V av[2][4], bv[2][4];
-    auto frags = [&](int kk, V* ar, V* br) {
+    V av[2][4], bv[2][2];
+    auto frags = [&](int kk, V* ar, V* bq) {
 #pragma unroll
       for (int i = 0; i < 4; i++)
         ar[i] = *(const V*)(a + (wm * 128 + i * 32 + (lane & 31)) * kTS + 16 * kk + 8 * (lane >> 5));
 #pragma unroll
-      for (int j = 0; j < 4; j++)
-        br[j] = *(const V*)(b + (wn * 128 + j * 32 + (lane & 31)) * kTS + 16 * kk + 8 * (lane >> 5));
+      for (int j = 0; j < 2; j++)
+        bq[j] = *(const V*)(b + (wn * 64 + j * 32 + (lane & 31)) * kTS + 16 * kk + 8 * (lane >> 5));
     };
     frags(0, av[0], bv[0]);
 #pragma unroll
     for (int kk = 0; kk < 4; kk++) {
       if (kk < 3) frags(kk + 1, av[(kk + 1) & 1], bv[(kk + 1) & 1]);
-      // the next tile's x vectors for this sub-step go straight to LDS
       XT* an = As + (cur ^ 1) * kTM * kTS;
-#pragma unroll
-      for (int i = 2 * kk; i < 2 * kk + 2; i++) {
-        const int idx = i * 256 + tid;
-        *(uint4*)(an + (idx >> 3) * kTS + (idx & 7) * 8) = cur_stage.a[i];
+      {
+        const int idx = kk * 512 + tid;
+        *(uint4*)(an + (idx >> 3) * kTS + (idx & 7) * 8) = cur_stage.a[kk];
       }
-      const uint4 cw = cur_stage.c[kk >> 1];
-      const uint32_t w0 = (kk & 1) ? cw.z : cw.x, w1 = (kk & 1) ? cw.w : cw.y;
-      const uint32_t svd = __builtin_bit_cast(uint32_t, f[kk].y);
-      uint32_t dec[8];
-#ifndef RZ_GEMM_SCHED
-#define RZ_GEMM_SCHED 2
-#endif
-#if RZ_GEMM_SCHED == 0
-      // two MFMAs, then one decoded pair behind scheduling fences
+      const uint32_t w = cword(cur_stage.c, kk);
+      const float2 fk = f[kk >> 1];
+      const uint32_t svd = __builtin_bit_cast(uint32_t, fk.y);
+      uint32_t dec[4];
 #pragma unroll
-      for (int g = 0; g < 8; g++) {
-        const int i = g >> 1, j = 2 * (g & 1);
-        acc[i][j] = Mfma32<XT>::run(av[kk & 1][i], bv[kk & 1][j], acc[i][j]);
-        acc[i][j + 1] = Mfma32<XT>::run(av[kk & 1][i], bv[kk & 1][j + 1], acc[i][j + 1]);
-        __builtin_amdgcn_sched_barrier(0);
-        dec[g] = decode_one_pair<XT>(g < 4 ? w0 : w1, g & 3, f[kk].x, svd);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#else
-      // the eight pair decodes are independent chains; the scheduler is asked
-      // to alternate one MFMA with a few VALU instructions drawn from them, so
-      // the decode latency is hidden by the chains' interleaving and the
-      // matrix unit never waits for a whole chain
-#pragma unroll
-      for (int g = 0; g < 8; g++) dec[g] = decode_one_pair<XT>(g < 4 ? w0 : w1, g & 3, f[kk].x, svd);
+      for (int g = 0; g < 4; g++) dec[g] = decode_one_pair<XT>(w, g, fk.x, svd);
 #pragma unroll
       for (int i = 0; i < 4; i++)
 #pragma unroll
-        for (int j = 0; j < 4; j++) acc[i][j] = Mfma32<XT>::run(av[kk & 1][i], bv[kk & 1][j], acc[i][j]);
-#if RZ_GEMM_SCHED == 2
-#pragma unroll
-      for (int g = 0; g < 16; g++) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // up to five VALU
-      }
-#elif RZ_GEMM_SCHED == 3
-#pragma unroll
-      for (int g = 0; g < 16; g++) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // up to five VALU
-      }
-#elif RZ_GEMM_SCHED == 4
-#pragma unroll
-      for (int g = 0; g < 16; g++) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
-      }
-#elif RZ_GEMM_SCHED == 5
+        for (int j = 0; j < 2; j++) acc[i][j] = Mfma32<XT>::run(av[kk & 1][i], bv[kk & 1][j], acc[i][j]);
+      // one MFMA, then up to four VALU instructions of the pair decodes
 #pragma unroll
       for (int g = 0; g < 8; g++) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
-      }
-#elif RZ_GEMM_SCHED == 6
-#pragma unroll
-      for (int g = 0; g < 16; g++) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // one LDS write
       }
-#endif
-#endif
-      uint4* bn = (uint4*)(Bs + (cur ^ 1) * kTN * kTS + tid * kTS) + 2 * kk;
-      bn[0] = make_uint4(dec[0], dec[1], dec[2], dec[3]);
-      bn[1] = make_uint4(dec[4], dec[5], dec[6], dec[7]);
+      *(uint4*)(Bs + (cur ^ 1) * kTN * kTS + br * kTS + 32 * bh + 8 * kk) = make_uint4(dec[0], dec[1], dec[2], dec[3]);
     }
     __syncthreads();
   };
 
   gload(0, st0);
   gload(ktiles > 1 ? 1 : 0, st1);
-  __syncthreads();  // lut ready
-#pragma unroll
-  for (int blk = 0; blk < 4; blk++) lstore_part(st0, 0, blk, lut[(st0.s >> (8 * blk)) & 0xFFu]);
+  __syncthreads();
+  lstore(st0, 0);
   __syncthreads();
   int kt = 0;
   for (; kt + 1 < ktiles; kt += 2) {
@@ -463,13 +404,12 @@ __global__ __launch_bounds__(256) void gemm_tile256_kernel(const XT* __restrict_
     step(kt + 1, st0, st1);
   }
   if (kt < ktiles) step(kt, st1, st0);
-
   const float scale = *ts;
 #pragma unroll
   for (int i = 0; i < 4; i++)
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const int64_t gc = n_base + wn * 128 + j * 32 + (lane & 31);
+    for (int j = 0; j < 2; j++) {
+      const int64_t gc = n_base + wn * 64 + j * 32 + (lane & 31);
 #pragma unroll
       for (int e = 0; e < 16; e++) {
         const int64_t gr = m_base + wm * 128 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
@@ -955,7 +895,7 @@ static hipError_t run_gemm(const XT* x, int64_t m, const PackedView& w, OT* y, v
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     const int64_t tiles = ((m + kTM - 1) / kTM) * ((n + kTN - 1) / kTN);
-    hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(256), lds, stream, x, m, w.codes,
+    hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(512), lds, stream, x, m, w.codes,
                        w.scales, w.tensor_scale, n, k, m0, m1, y);
     return hipGetLastError();
   }
