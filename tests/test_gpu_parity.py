@@ -792,3 +792,84 @@ def test_gemm_w4a4_prefill_sampled():
     y_ref, nrm = oracle.gemm_w4a4(xp, wp, cols)
     assert_product_close(yc, y_ref, nrm, "w4a4 prefill (16 sampled columns x 2048 rows)", torch.bfloat16)
     assert torch.isfinite(y).all()
+
+
+# ---- graph capture ---------------------------------------------------------------
+
+def test_graph_replays_match_eager_results():
+    """Every call enqueues kernels only (no allocation, no memset, no host
+    sync), so a captured sequence replays the eager results bit for bit; each
+    of three replays is checked, with eager work in between."""
+    _need_gpu()
+    rng = np.random.default_rng(121)
+    dev = "cuda"
+    w_np = (rng.standard_t(5, (512, 1024)) * 0.02).astype(np.float32)
+    w = torch.from_numpy(w_np).to(dev)
+    xa = torch.from_numpy(rng.standard_normal((300, 1024)).astype(np.float32)).to(dev).to(torch.bfloat16)
+    x1 = xa[0].to(torch.float16).contiguous()
+    xs = xa[:8].contiguous()
+    wq = rz.razer_quantize_weight(w, (-2, 4))
+    w2 = rz.razer_quantize_weight(w[:300].contiguous(), (-2, -5))
+    outs = {
+        "act": rz.PackedTensor(rz.RAZER_ACT, 300, 1024, (-2,), dev),
+        "wenc": rz.PackedTensor(rz.RAZER_WEIGHT, 512, 1024, (-2, 4), dev),
+        "gemv": torch.empty(512, dtype=torch.float16, device=dev),
+        "g0": torch.empty(512, dtype=torch.float16, device=dev),
+        "g1": torch.empty(300, dtype=torch.float16, device=dev),
+        "small": torch.empty((8, 512), dtype=torch.bfloat16, device=dev),
+        "prefill": torch.empty((300, 512), dtype=torch.bfloat16, device=dev),
+        "deq": torch.empty((512, 1024), dtype=torch.bfloat16, device=dev),
+    }
+    wsa = torch.empty(max(1, rz.razer_workspace_bytes(rz.RAZER_OP_QUANTIZE_ACT, 300, 0, 1024)),
+                      dtype=torch.uint8, device=dev)
+    wsw = torch.empty(max(1, rz.razer_workspace_bytes(rz.RAZER_OP_QUANTIZE_WEIGHT, 512, 0, 1024)),
+                      dtype=torch.uint8, device=dev)
+    wss = torch.empty(max(1, rz.razer_workspace_bytes(rz.RAZER_OP_GEMM, 8, 512, 1024)),
+                      dtype=torch.uint8, device=dev)
+
+    def seq():
+        rz.razer_quantize_act(xa, out=outs["act"], workspace=wsa)
+        rz.razer_quantize_weight(w, out=outs["wenc"], workspace=wsw)
+        rz.razer_gemv(x1, wq, out=outs["gemv"])
+        rz.razer_gemv_group(x1, [wq, w2], outs=[outs["g0"], outs["g1"]])
+        rz.razer_gemm(xs, wq, out=outs["small"], workspace=wss)
+        rz.razer_gemm(xa, wq, out=outs["prefill"])
+        rz.razer_dequant(wq, out=outs["deq"])
+
+    def snapshot():
+        snap = {}
+        for key, v in outs.items():
+            if isinstance(v, rz.PackedTensor):
+                snap[key] = (v.codes.clone(), v.scales.clone(), v.tensor_scale.clone())
+            else:
+                snap[key] = (v.clone(),)
+        return snap
+
+    def clear():
+        for v in outs.values():
+            for t in ((v.codes, v.scales, v.tensor_scale) if isinstance(v, rz.PackedTensor) else (v,)):
+                t.zero_()
+
+    seq()
+    torch.cuda.synchronize()
+    ref = snapshot()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        seq()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        seq()
+    for rep in range(3):
+        clear()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = snapshot()
+        for key in ref:
+            for a, b in zip(ref[key], got[key]):
+                assert torch.equal(a, b), f"replay {rep}: {key} differs"
+        rz.razer_gemv(x1, wq, out=torch.empty(512, dtype=torch.float16, device=dev))  # eager work between
+        torch.cuda.synchronize()
