@@ -48,8 +48,8 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def packed_bytes(n, k):
-    return n * k // 2 + n * k // 16 + 4
+def packed_bytes(n, k, block=16, scale_bytes=1):
+    return n * k // 2 + n * k // block * scale_bytes + 4
 
 
 def gemv_bytes(n, k, xb=2, yb=2):
@@ -177,15 +177,16 @@ def load_traffic(kernel_key, src_hash):
 
 # ---- headline: decode GEMV -----------------------------------------------------
 
-def setup_decode(torch, rz, synth, layers):
+def setup_decode(torch, rz, synth, layers, block=16, scale_fmt=0):
     """Decode step launches over `layers` copies of the layer's weights: grouped
-    (qkv; gate and up in one launch, they read the same x; down) and per matrix."""
+    (qkv; gate and up in one launch, they read the same x; down) and per matrix.
+    block / scale_fmt: the weights' layout (default: 16-element blocks, byte scales)."""
     dev = torch.device("cuda:0")
     names = ["qkv", "gate", "up", "down"]
     base = {}
     for name in names:
         w = torch.from_numpy(synth.llama3_8b_decode_weight(name)).to(dev)
-        base[name] = rz.razer_quantize_weight(w, (-2, 4))
+        base[name] = rz.razer_quantize_weight(w, (-2, 4), block=block, scale_fmt=scale_fmt)
         del w
     torch.cuda.synchronize()
     mats = [{n: (base[n] if li == 0 else clone_packed(rz, base[n])) for n in names}
@@ -199,8 +200,9 @@ def setup_decode(torch, rz, synth, layers):
         launches = [(xs[layer[g[0]].cols], [layer[n] for n in g], [ys[n] for n in g])
                     for layer in mats for g in groups]
         # algorithmic bytes: packed weights, x once per launch, y
-        step_bytes = sum(sum(packed_bytes(m.rows, m.cols) + 2 * m.rows for m in ws) + 2 * ws[0].cols
-                         for _, ws, _ in launches)
+        sbytes = 2 if scale_fmt else 1
+        step_bytes = sum(sum(packed_bytes(m.rows, m.cols, block, sbytes) + 2 * m.rows for m in ws)
+                         + 2 * ws[0].cols for _, ws, _ in launches)
         out[kind] = (launches, step_bytes)
     return out, base
 
@@ -502,8 +504,20 @@ def main():
         decode_other = {"workload": f"the same decode step, {other.replace('_', ' ')} launches",
                         "launches_per_step": len(l2), "us_per_step": ms2 * 1e3, "gbs": b2 / ms2 / 1e6,
                         "frac_hbm": b2 / ms2 / 1e6 / HBM_PEAK_GBS}
+        # the same step with the weights in the pages' kernel layout (128-element
+        # blocks, FP16 scales with the metadata in the sign and top exponent bits)
+        del l2
+        steps_g, _ = setup_decode(torch, rz, synth, args.layers, block=128, scale_fmt=rz.RAZER_SCALE_F16)
+        l3, b3 = steps_g["grouped"]
+        ms3 = GraphTimer(torch, lambda: run_launches(rz, l3), warmup=1).time(args.steps)
+        decode_g128 = {"workload": "the same decode step (grouped launches) with 128-element blocks and FP16 "
+                                   "scales (0.5156 B per weight)", "launches_per_step": len(l3),
+                       "us_per_step": ms3 * 1e3, "gbs": b3 / ms3 / 1e6, "frac_hbm": b3 / ms3 / 1e6 / HBM_PEAK_GBS,
+                       "bytes_per_step": b3}
+        del steps_g, l3
+        torch.cuda.empty_cache()
         log("rows: encoders, small-batch sweep, prefill ...")
-        rows = {f"decode_{other}": decode_other}
+        rows = {f"decode_{other}": decode_other, "decode_g128_f16": decode_g128}
         rows.update(bench_rows(torch, rz, synth, args, base))
 
     cpu = None

@@ -130,9 +130,11 @@ typedef struct razer_packed {
   uint8_t* scales;       /* device, rows*cols/block entries of 1 (byte) or 2 (F16) bytes */
   float* tensor_scale;   /* device, 1 float */
 } razer_packed;
-/* The encoders and razer_dequant take every layout; the product calls
- * (razer_gemv, razer_gemv_group, razer_gemm, razer_gemm_w4a4) take 16-element
- * blocks with byte scales and return RAZER_E_UNSUPPORTED for the others. */
+/* The encoders and razer_dequant take every layout.  The product calls take
+ * 16-element blocks with byte scales; razer_gemv, razer_gemv_group (all
+ * members in one layout) and razer_gemm with m == 1 also take the pages'
+ * kernel layout, 128-element blocks (block_log2 7) with RAZER_SCALE_F16.
+ * Other layouts return RAZER_E_UNSUPPORTED. */
 
 /* Operation ids for razer_workspace_bytes. */
 enum {

@@ -76,9 +76,13 @@ rz::PackedView view_of(const razer_packed* p) {
 static_assert(RAZER_FLAG_NO_REMAP == rz::kFlagNoRemap && RAZER_FLAG_FOUR_OVER_SIX == rz::kFlagFourOverSix,
               "encoder flag values");
 
-// The product kernels read 16-element blocks with byte scales only.
+// The product kernels read 16-element blocks with byte scales; the GEMV also
+// reads 128-element blocks with FP16 scales.
 bool product_layout(const razer_packed* p) {
   return (p->block_log2 == 0 || p->block_log2 == 4) && p->scale_fmt == RAZER_SCALE_BYTE;
+}
+bool gemv_layout(const razer_packed* p) {
+  return product_layout(p) || (p->block_log2 == 7 && p->scale_fmt == RAZER_SCALE_F16);
 }
 
 razer_status status_of(hipError_t e) { return e == hipSuccess ? RAZER_OK : RAZER_E_HIP; }
@@ -126,7 +130,7 @@ razer_status razer_gemv(const void* x, razer_dtype x_dt, const razer_packed* w, 
   razer_status s = check_packed(w, true);
   if (s != RAZER_OK) return s;
   if (!dtype_ok(x_dt) || !dtype_ok(y_dt)) return RAZER_E_INVALID;
-  if (x_dt == RAZER_F32 || !product_layout(w)) return RAZER_E_UNSUPPORTED;
+  if (x_dt == RAZER_F32 || !gemv_layout(w)) return RAZER_E_UNSUPPORTED;
   if (w->cols > kGemvMaxK) return RAZER_E_UNSUPPORTED;
   if (w->rows == 0) return RAZER_OK;
   if (!y || !aligned(y, 16)) return RAZER_E_INVALID;
@@ -151,7 +155,7 @@ razer_status razer_gemv_group(const void* x, razer_dtype x_dt, const razer_packe
     yy[g] = y[g];
   }
   for (int g = 0; g < count; g++)
-    if (!product_layout(w[g])) return RAZER_E_UNSUPPORTED;
+    if (!gemv_layout(w[g]) || product_layout(w[g]) != product_layout(w[0])) return RAZER_E_UNSUPPORTED;
   if (x_dt == RAZER_F32) return RAZER_E_UNSUPPORTED;
   if (w[0]->cols > kGemvMaxK) return RAZER_E_UNSUPPORTED;
   if (w[0]->cols > 0 && (!x || !aligned(x, 16))) return RAZER_E_INVALID;
@@ -163,7 +167,7 @@ razer_status razer_gemm(const void* x, razer_dtype x_dt, int64_t m, const razer_
   razer_status s = check_packed(w, true);
   if (s != RAZER_OK) return s;
   if (!dtype_ok(x_dt) || !dtype_ok(y_dt) || m < 0) return RAZER_E_INVALID;
-  if (x_dt == RAZER_F32 || !product_layout(w)) return RAZER_E_UNSUPPORTED;
+  if (x_dt == RAZER_F32 || !(m == 1 ? gemv_layout(w) : product_layout(w))) return RAZER_E_UNSUPPORTED;
   if (m == 0 || w->rows == 0) return RAZER_OK;
   if (m == 1) return razer_gemv(x, x_dt, w, y, y_dt, ws, ws_bytes, stream);
   if (!y || !aligned(y, 16)) return RAZER_E_INVALID;

@@ -32,6 +32,8 @@
 #include "rz_device.h"
 #include "rz_launch.h"
 
+#include <type_traits>
+
 namespace rz {
 
 typedef short short2_t __attribute__((ext_vector_type(2)));
@@ -227,6 +229,15 @@ template <> struct ScaleWord<1, false> {
   }
 };
 
+// FP16 group scales: one 2-byte word per lane and row quad (row lane / 16,
+// block lane % 16 of the chunk index's 16 blocks), always aligned and inside
+// the row.
+struct ScaleHalf {
+  uint32_t h;
+  __device__ __forceinline__ void load(Rsrc sr, int off) { h = __builtin_amdgcn_raw_buffer_load_b16(sr, off, 0, 0); }
+  __device__ __forceinline__ void store(uint8_t* p) const { *(uint16_t*)p = (uint16_t)h; }
+};
+
 constexpr int kGemvMaxRpw = 64;  // rows per workgroup (bounds the LDS partials)
 
 // Workgroup = 4 waves = KS K-slices x (4 / KS) row groups.  Row group rg owns
@@ -234,9 +245,16 @@ constexpr int kGemvMaxRpw = 64;  // rows per workgroup (bounds the LDS partials)
 // multiple of 4) and walks them four at a time; within a row, wave (ks, rg)
 // takes chunks (i * KS + ks) * 64 + lane for i < CPL.  The loads of the next
 // NQ - 1 row quads are in flight while a quad is decoded.
-template <typename XT, int UNIT, int CPL, int KS, int NQ, bool SW>
+//
+// F16S: weights in the 128-element FP16-scale layout (UNIT 2).  A row quad's
+// scales for one chunk index are 4 x 16 words; lane l loads word l % 16 of
+// row l / 16, and a lane's chunk reads the word of its block (chunk / 4) from
+// the stage.  Both 16-element halves of a chunk share that word, whose two
+// coefficients come from the word itself.
+template <typename XT, int UNIT, int CPL, int KS, int NQ, bool SW, bool F16S>
 __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   typedef typename Pair<XT>::T P;
+  typedef typename std::conditional<F16S, ScaleHalf, ScaleWord<UNIT, SW>>::type SWord;
   constexpr int kPairs = 8 * UNIT;  // x pairs per chunk
   constexpr int kSeg = 64 * UNIT;  // scale bytes of one chunk index, one row
   __shared__ float2 lut[256];
@@ -256,7 +274,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   const int r0 = rg * a.rpwv;                                  // first row of this wave in the run
   const int nrw = max(0, min(a.rpwv, rows_wg - r0));           // rows of this wave
   const int nq = (nrw + 3) >> 2;
-  const int rcb = (int)(a.k / 2), rsb = (int)(a.k / 16);
+  const int rcb = (int)(a.k / 2), rsb = (int)(F16S ? a.k / 64 : a.k / 16);
   const Rsrc crs = make_rsrc(w.codes + base * rcb, (int64_t)rows_wg * rcb);
   const Rsrc srs = make_rsrc(w.scales + base * rsb, (int64_t)rows_wg * rsb);
   const Rsrc xrs = make_rsrc(a.x, a.k * 2);
@@ -272,8 +290,13 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
     const int c = c0 + lane;
     coff[i] = c < a.nchunk ? c * 8 * UNIT : kOob;
     // scale segment i, lane's 4 * UNIT bytes; past the row's end reads zero
-    const int sb0 = (c0 + 4 * (lane & 15)) * UNIT;
-    sgo[i] = c0 + 4 * (lane & 15) < a.nchunk ? sb0 : kOob;
+    if (F16S) {
+      const int sb0 = c0 / 2 + 2 * (lane & 15);
+      sgo[i] = sb0 < rsb ? sb0 : kOob;
+    } else {
+      const int sb0 = (c0 + 4 * (lane & 15)) * UNIT;
+      sgo[i] = c0 + 4 * (lane & 15) < a.nchunk ? sb0 : kOob;
+    }
   }
 
   // x slice in registers, requested before any weight bytes.
@@ -289,7 +312,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   }
 
   Chunk<UNIT> buf[NQ][4][CPL];
-  ScaleWord<UNIT, SW> sbuf[NQ][CPL];
+  SWord sbuf[NQ][CPL];
   // scale bytes first: the table lookups wait on them, the dots on the codes
   auto load_quad = [&](int slot, int q) {
     const int js = 4 * q + (lane >> 4);
@@ -332,7 +355,13 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
       if (q < nq) {
         // this quad's scale bytes to their lanes (one wave: no barrier)
 #pragma unroll
-        for (int i = 0; i < CPL; i++) sbuf[s][i].store(stg[i][lane >> 4] + 4 * UNIT * (lane & 15));
+        for (int i = 0; i < CPL; i++) {
+          if (F16S) {
+            sbuf[s][i].store(stg[i][lane >> 4] + 2 * (lane & 15));
+          } else {
+            sbuf[s][i].store(stg[i][lane >> 4] + 4 * UNIT * (lane & 15));
+          }
+        }
         wave_lds_sync();
         float acc[4];
 #pragma unroll
@@ -340,7 +369,16 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
           acc[r] = 0.0f;
 #pragma unroll
           for (int i = 0; i < CPL; i++) {
-            if (i < ni) {
+            if (F16S && i < ni) {
+              const Chunk<UNIT>& ch = buf[s][r][i];
+              const uint32_t sw = (uint32_t)*(const uint16_t*)(stg[i][r] + 2 * (lane >> 2));
+              float d0a, d1a, d0b, d1b;
+              block_dot<XT>(ch.w(0), ch.w(1), xv[i], d0a, d1a);
+              block_dot<XT>(ch.w(2), ch.w(3), xv[i] + 8, d0b, d1b);
+              const float sb = scale_of_f16word(sw), sv = special_of_f16word(sw, w.m0, w.m1);
+              acc[r] = fmaf(d0a + d0b, sb * (1.0f + 4.0f * sv), acc[r]);
+              acc[r] = fmaf(d1a + d1b, -4.0f * sb * sv, acc[r]);
+            } else if (!F16S && i < ni) {
               const Chunk<UNIT>& ch = buf[s][r][i];
               const uint32_t sw = UNIT == 2 ? (uint32_t)*(const uint16_t*)(stg[i][r] + 2 * lane)
                                             : (uint32_t)stg[i][r][lane];
@@ -385,15 +423,22 @@ struct GemvPlan {
 };
 
 template <typename XT, int UNIT, int CPL, int KS, int NQ>
-static hipError_t launch_cfg(GemvArgs a, const GemvPlan& p, hipStream_t stream) {
+static hipError_t launch_cfg(GemvArgs a, const GemvPlan& p, bool f16s, hipStream_t stream) {
   a.rpw = p.rpw;
   a.rpwv = p.rpwv;
+  if constexpr (UNIT == 2) {
+    if (f16s) {
+      hipLaunchKernelGGL((gemv_kernel<XT, UNIT, CPL, KS, NQ, true, true>), dim3((unsigned)p.grid), dim3(256),
+                         0, stream, a);
+      return hipGetLastError();
+    }
+  }
   // wide scale loads need the scale row stride (K / 16 bytes) to keep 4 * UNIT alignment
   if ((a.k / 16) % (4 * UNIT) == 0)
-    hipLaunchKernelGGL((gemv_kernel<XT, UNIT, CPL, KS, NQ, true>), dim3((unsigned)p.grid), dim3(256), 0,
+    hipLaunchKernelGGL((gemv_kernel<XT, UNIT, CPL, KS, NQ, true, false>), dim3((unsigned)p.grid), dim3(256), 0,
                        stream, a);
   else
-    hipLaunchKernelGGL((gemv_kernel<XT, UNIT, CPL, KS, NQ, false>), dim3((unsigned)p.grid), dim3(256), 0,
+    hipLaunchKernelGGL((gemv_kernel<XT, UNIT, CPL, KS, NQ, false, false>), dim3((unsigned)p.grid), dim3(256), 0,
                        stream, a);
   return hipGetLastError();
 }
@@ -421,9 +466,9 @@ static GemvPlan plan_gemv(int64_t n, int64_t nchunk, int cus, int wg_per_cu) {
 }
 
 template <typename XT, int UNIT>
-static hipError_t dispatch(const GemvArgs& a, const GemvPlan& p, hipStream_t stream) {
+static hipError_t dispatch(const GemvArgs& a, const GemvPlan& p, bool f16s, hipStream_t stream) {
 #define RZ_CASE(C_, K_, Q_) \
-  if (p.cpl == C_ && p.ks == K_ && p.nq == Q_) return launch_cfg<XT, UNIT, C_, K_, Q_>(a, p, stream);
+  if (p.cpl == C_ && p.ks == K_ && p.nq == Q_) return launch_cfg<XT, UNIT, C_, K_, Q_>(a, p, f16s, stream);
   RZ_CASE(1, 1, 1) RZ_CASE(1, 2, 1) RZ_CASE(1, 4, 1) RZ_CASE(2, 4, 1) RZ_CASE(4, 4, 1)
   RZ_CASE(8, 4, 1)
   if constexpr (UNIT == 1) {
@@ -437,12 +482,18 @@ static hipError_t dispatch(const GemvArgs& a, const GemvPlan& p, hipStream_t str
 // 8192) on up to 4096 rows, where its K split keeps enough waves busy
 // (measured faster there only).
 static bool gemv_to_smallm(const PackedView& w) {
-  return w.rows <= 4096 && w.cols > 8192 && smallm_supported(1, w.rows, w.cols);
+  return default_layout(w) && w.rows <= 4096 && w.cols > 8192 && smallm_supported(1, w.rows, w.cols);
 }
 
 hipError_t launch_gemv_group(const void* x, int x_dtype, const PackedView* w, void* const* y,
                              int count, int y_dtype, hipStream_t stream) {
   if (count < 1 || count > kGemvGroupMax) return hipErrorInvalidValue;
+  // one layout per launch: 16-element blocks with byte scales, or 128-element
+  // blocks with FP16 scales (K a multiple of 128)
+  const bool f16s = !default_layout(w[0]);
+  for (int g = 0; g < count; g++)
+    if (default_layout(w[g]) == f16s || (f16s && (w[g].blog2 != 7 || w[g].sfmt != 1)))
+      return hipErrorInvalidValue;
   // members for the small-batch kernel, and empty ones, are launched on their own
   GemvArgs a;
   a.x = x;
@@ -470,6 +521,7 @@ hipError_t launch_gemv_group(const void* x, int x_dtype, const PackedView* w, vo
   }
   if (a.count == 0) return hipSuccess;
   const bool unit2 = a.k % 32 == 0;
+  if (f16s && !unit2) return hipErrorInvalidValue;
   a.nchunk = a.k / (unit2 ? 32 : 16);
   // one plan for the summed rows; each weight gets whole workgroups of it
   GemvPlan p = plan_gemv(n_total, a.nchunk, device_cu_count(), 8);
@@ -480,8 +532,9 @@ hipError_t launch_gemv_group(const void* x, int x_dtype, const PackedView* w, vo
   }
   for (int g = a.count; g < kGemvGroupMax; g++) a.w[g] = a.w[0];
   p.grid = wg;
-  if (x_dtype == kF16) return unit2 ? dispatch<_Float16, 2>(a, p, stream) : dispatch<_Float16, 1>(a, p, stream);
-  return unit2 ? dispatch<__bf16, 2>(a, p, stream) : dispatch<__bf16, 1>(a, p, stream);
+  if (x_dtype == kF16)
+    return unit2 ? dispatch<_Float16, 2>(a, p, f16s, stream) : dispatch<_Float16, 1>(a, p, f16s, stream);
+  return unit2 ? dispatch<__bf16, 2>(a, p, f16s, stream) : dispatch<__bf16, 1>(a, p, f16s, stream);
 }
 
 hipError_t launch_gemv(const void* x, int x_dtype, const PackedView& w, void* y, int y_dtype,

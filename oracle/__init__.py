@@ -299,6 +299,17 @@ def gemm(x, p: Packed, cols=None):
     return y, nrm
 
 
+def gemm_any(x, p: Packed):
+    """fp64 product y = x @ w^T and norm |x| @ |w|^T over the exactly decoded
+    weights of any layout (block sizes, FP16 group scales): the oracle's
+    decoder followed by a numpy matmul.  Returns (y [m, n], norm [m, n])."""
+    x = np.asarray(x, dtype=np.float64)
+    if x.ndim == 1:
+        x = x[None, :]
+    w = dequant_f64(p)
+    return x @ w.T, np.abs(x) @ np.abs(w).T
+
+
 def gemm_w4a4(xp: Packed, wp: Packed, cols=None):
     """fp64 product of two packed tensors, y = dequant(x) @ dequant(w)^T, plus
     the norm sum |dequant(x)| |dequant(w)|.

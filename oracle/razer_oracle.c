@@ -111,18 +111,22 @@ static double f16s_value(int code) {
 static double f16s_max(void) { return f16s_value(0x3FFF); }
 
 static int f16s_round(float v) {
-  /* nearest of the 16384 codes by scan, ties to the even code, saturating */
+  /* nearest of the 16384 codes (values increase with the code): the largest
+   * code at or below v by bisection, then the nearer of it and the next code,
+   * ties to the even code; saturating at the largest code */
   if ((double)v >= f16s_max()) return 0x3FFF;
-  int best = 0;
-  double bd = fabs((double)v);
-  for (int c = 1; c < 0x4000; c++) {
-    double d = fabs((double)v - f16s_value(c));
-    if (d < bd || (d == bd && (c & 1) == 0)) {
-      best = c;
-      bd = d;
-    }
+  int lo = 0, hi = 0x3FFF; /* value(lo) <= v < value(hi) */
+  while (hi - lo > 1) {
+    int mid = (lo + hi) / 2;
+    if (f16s_value(mid) <= (double)v)
+      lo = mid;
+    else
+      hi = mid;
   }
-  return best;
+  double dlo = (double)v - f16s_value(lo), dhi = f16s_value(hi) - (double)v;
+  if (dlo < dhi) return lo;
+  if (dhi < dlo) return hi;
+  return (lo & 1) == 0 ? lo : hi;
 }
 
 double rzo_scale_value_fmt(int kind, int sfmt, int code) {

@@ -235,13 +235,19 @@ def test_layout_variants_host_checks():
     a = _packed(kind=rz.RAZER_ACT, off=(-2, 0), cols=128)
     a.scale_fmt = rz.RAZER_SCALE_F16  # FP16 group scales are for weights only
     assert L.razer_quantize_act(FAKE_X, rz.RAZER_BF16, ctypes.byref(a), FAKE_WS, 4096, None) == rz.RAZER_E_INVALID
-    # the products take 16-element blocks with byte scales only
+    # the products take 16-element blocks with byte scales; the GEMV calls also
+    # take 128-element blocks with FP16 scales (not checked here: that would launch)
+    y = ctypes.c_void_p(0x6000)
+    x = _packed(kind=rz.RAZER_ACT, off=(-2, 0), rows=2, cols=128)
     for blog2, fmt in ((5, 0), (7, 0), (4, 1), (7, 1)):
         w = _packed(rows=8, cols=128)
         w.block_log2, w.scale_fmt = blog2, fmt
-        y = ctypes.c_void_p(0x6000)
-        assert L.razer_gemv(FAKE_X, rz.RAZER_F16, ctypes.byref(w), y, rz.RAZER_F16, None, 0, None) == rz.RAZER_E_UNSUPPORTED
+        if (blog2, fmt) != (7, 1):
+            assert L.razer_gemv(FAKE_X, rz.RAZER_F16, ctypes.byref(w), y, rz.RAZER_F16, None, 0, None) == rz.RAZER_E_UNSUPPORTED
+            assert _group_call([w], [0x6000]) == rz.RAZER_E_UNSUPPORTED
         assert L.razer_gemm(FAKE_X, rz.RAZER_F16, 4, ctypes.byref(w), y, rz.RAZER_F16, FAKE_WS, 1 << 20, None) == rz.RAZER_E_UNSUPPORTED
-        assert _group_call([w], [0x6000]) == rz.RAZER_E_UNSUPPORTED
-        x = _packed(kind=rz.RAZER_ACT, off=(-2, 0), rows=2, cols=128)
         assert L.razer_gemm_w4a4(ctypes.byref(x), ctypes.byref(w), y, rz.RAZER_BF16, FAKE_WS, 1 << 20, None) == rz.RAZER_E_UNSUPPORTED
+    # one layout per grouped launch
+    g128 = _packed(rows=8, cols=128)
+    g128.block_log2, g128.scale_fmt = 7, 1
+    assert _group_call([_packed(rows=8, cols=128), g128], [0x6000, 0x7000]) == rz.RAZER_E_UNSUPPORTED

@@ -422,6 +422,44 @@ def test_quantize_variant_group128_f16_prefill_weight_sampled():
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("n,k,xdt", [(300, 1024, torch.float16), (77, 128, torch.bfloat16),
+                                     (6144, 4096, torch.float16), (4096, 14336, torch.float16),
+                                     (5, 65536, torch.bfloat16), (1000, 2944, torch.bfloat16)])
+def test_gemv_group128_f16_layout(n, k, xdt):
+    """The pages' kernel layout (128-element blocks, FP16 scales) through the
+    GEMV: within tolerance of the fp64 product over the oracle's decoded
+    weights; razer_gemm with m = 1 gives the same bytes."""
+    _need_gpu()
+    rng = np.random.default_rng(n + k)
+    w = (rng.standard_t(5, (n, k)) * 0.02).astype(np.float32)
+    ref = oracle.quantize(oracle.WEIGHT, w, (-2, -5), block=128, scale_fmt=oracle.SCALE_F16)
+    x = torch.from_numpy(rng.standard_normal(k).astype(np.float32)).to(xdt)
+    t = to_device(ref)
+    y_ref, nrm = oracle.gemm_any(as_f32(x), ref)
+    y32 = rz.razer_gemv(x.cuda(), t, torch.float32)
+    y16 = rz.razer_gemv(x.cuda(), t, xdt)
+    torch.cuda.synchronize()
+    assert_product_close(y32.cpu().numpy()[None], y_ref, nrm, f"g128 gemv {n}x{k}")
+    assert_product_close(y16.float().cpu().numpy()[None], y_ref, nrm, f"g128 gemv {n}x{k} 16-bit", xdt)
+    assert torch.equal(rz.razer_gemm(x.cuda()[None], t, torch.float32)[0], y32)
+
+
+def test_gemv_group_group128_f16_members():
+    _need_gpu()
+    rng = np.random.default_rng(141)
+    refs = [oracle.quantize(oracle.WEIGHT, (rng.standard_t(5, (n, 2048)) * 0.02).astype(np.float32), offs,
+                            block=128, scale_fmt=oracle.SCALE_F16)
+            for n, offs in ((640, (-2, 4)), (96, (-2, -5)), (1, (-7, 7)))]
+    ws = [to_device(r) for r in refs]
+    x = torch.from_numpy(rng.standard_normal(2048).astype(np.float32)).to(torch.float16).cuda()
+    ys = rz.razer_gemv_group(x, ws, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for r, wt, y in zip(refs, ws, ys):
+        y_ref, nrm = oracle.gemm_any(x.float().cpu().numpy(), r)
+        assert_product_close(y.cpu().numpy()[None], y_ref, nrm, "g128 group")
+        assert torch.equal(y, rz.razer_gemv(x, wt, torch.float32))
+
+
 def test_products_reject_variant_layouts():
     _need_gpu()
     w = rz.razer_quantize_weight(pr1()[0].cuda(), (-2, 4), block=64)

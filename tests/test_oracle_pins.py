@@ -724,3 +724,16 @@ def test_block_16_byte_variant_is_the_default_layout():
         oracle.quantize(oracle.WEIGHT, x[:, :48], (-2, 4), block=32)    # cols % block != 0
     with pytest.raises(ValueError):  # the products take the default layout only
         oracle.gemm(np.zeros((1, 256), np.float32), oracle.quantize(oracle.WEIGHT, x, (-2, 4), block=32))
+
+
+def test_gemm_any_equals_the_product_oracle_on_the_default_layout():
+    # The any-layout product (decoder + library matmul) against the oracle's
+    # own fp64 product loop on 16-element blocks.
+    rng = np.random.default_rng(131)
+    w = (rng.standard_t(5, (40, 256)) * 0.02).astype(np.float32)
+    x = rng.standard_normal((3, 256)).astype(np.float32)
+    p = oracle.quantize_weight(w, (-2, 4))
+    y, n = oracle.gemm(x, p)
+    ya, na = oracle.gemm_any(x, p)
+    np.testing.assert_allclose(ya, y, rtol=1e-12, atol=1e-12 * float(n.max()))
+    np.testing.assert_allclose(na, n, rtol=1e-12)
