@@ -16,7 +16,7 @@ Also measured in the same run (the ``rows`` object): the weight and activation
 encoders (Gelem/s, GB/s, special-value-search overhead), the small-batch GEMM
 sweep (M = 1..32, GB/s) and the M=2048 prefill GEMM (TFLOP/s), each on its own
 synthetic workload; ``roofline`` for the GEMV kernel; ``cpu_baseline`` = the CPU
-oracle on one layer.
+oracle over one decode step (single thread, about 14 s).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L]
                        [--no-rows] [--no-cpu-baseline] [--eager] [--per-matrix]
@@ -402,7 +402,9 @@ def bench_rows(torch, rz, synth, args, decode_base):
 
 # ---- CPU oracle baseline ------------------------------------------------------------
 
-def cpu_baseline(synth):
+def cpu_baseline(synth, layers):
+    """The oracle's product over one decode step: `layers` passes over the
+    layer's four GEMVs (the step's layer copies hold the same weights)."""
     import numpy as np
     import oracle
 
@@ -414,15 +416,16 @@ def cpu_baseline(synth):
           14336: synth.llama3_8b_decode_x(14336).float().numpy()}
     byts = 0
     t0 = time.perf_counter()
-    for n in names:
-        p = packs[n]
-        oracle.gemm(xs[p.cols], p)
-        byts += gemv_bytes(p.rows, p.cols)
+    for _ in range(layers):
+        for n in names:
+            p = packs[n]
+            oracle.gemm(xs[p.cols], p)
+            byts += gemv_bytes(p.rows, p.cols)
     dt = time.perf_counter() - t0
     return {"value": byts / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "one layer (qkv, gate, up, down GEMVs, 201M weights) of the decode workload, "
-                      "weights encoded by the oracle (encode not timed), fp64 accumulation, "
-                      f"{dt:.1f} s single-threaded",
+            "sample": f"one decode step: {layers} x (qkv, gate, up, down GEMVs, 201M weights) of the "
+                      "decode workload, weights encoded by the oracle (encode not timed), fp64 "
+                      f"accumulation, {dt:.1f} s single-threaded",
             "seconds": dt, "host_cpus": os.cpu_count()}
 
 
@@ -522,8 +525,8 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        log("cpu baseline: oracle on one layer ...")
-        cpu = cpu_baseline(synth)
+        log("cpu baseline: oracle on one decode step ...")
+        cpu = cpu_baseline(synth, args.layers)
         cpu["value"] = round(cpu["value"], 4)
 
     out = {
