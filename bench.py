@@ -20,10 +20,13 @@ oracle over one decode step (single thread, about 14 s).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L]
                        [--no-rows] [--no-cpu-baseline] [--eager] [--per-matrix]
+       python bench.py --counters {prefill,w4a4,quantize_weight,quantize_act,dequant}
        python bench.py --copy-calibration
        python bench.py --traffic-summary FETCH.csv WRITE.csv CAL_FETCH.csv CAL_WRITE.csv
 
 --eager replays the decode launches without a graph (for counter passes);
+--counters W runs one row's launches (prefill, w4a4, quantize_weight,
+quantize_act, dequant) three times, untimed, for counter passes;
 --copy-calibration runs a plain elementwise copy (negation) of 512 MiB, the reference for
 scaling the FETCH_SIZE / WRITE_SIZE counters; --traffic-summary turns the four
 rocprofv3 counter CSVs (decode GEMV fetch, write; copy fetch, write) into
@@ -109,6 +112,53 @@ COPY_BYTES = 512 << 20  # the calibration copy reads and writes this many bytes
 # razer_gemv runs gemv_kernel for more than 4096 rows and smallm_kernel up to 4096
 DECODE_KERNELS = ("gemv_kernel", "smallm_kernel")
 DECODE_SOURCES = ("rz_gemv.hip", "rz_smallm.hip", "rz_device.h")
+
+
+COUNTER_WORKLOADS = ("prefill", "w4a4", "quantize_weight", "quantize_act", "dequant")
+
+
+def run_counter_workload(torch, rz, synth, name):
+    """The launches of one row's workload, three times each, eager and untimed,
+    so that counter passes see only those kernels (plus input setup)."""
+    dev = torch.device("cuda:0")
+    if name in ("prefill", "w4a4", "quantize_weight", "dequant"):
+        w = torch.from_numpy(synth.prefill_weight()).to(dev)
+        wp = rz.razer_quantize_weight(w, (-2, 4))
+    if name == "quantize_weight":
+        ws = torch.empty(rz.razer_workspace_bytes(rz.RAZER_OP_QUANTIZE_WEIGHT, 28672, 0, 8192),
+                         dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            rz.razer_quantize_weight(w, out=wp, workspace=ws)
+    elif name == "quantize_act":
+        x = synth.act_quant_x().to(dev)
+        out = rz.PackedTensor(rz.RAZER_ACT, 4096, 8192, (-2,), dev)
+        ws = torch.empty(rz.razer_workspace_bytes(rz.RAZER_OP_QUANTIZE_ACT, 4096, 0, 8192),
+                         dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            rz.razer_quantize_act(x, out=out, workspace=ws)
+    elif name == "prefill":
+        x = synth.prefill_x().to(dev)
+        y = torch.empty((2048, 28672), dtype=torch.bfloat16, device=dev)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            rz.razer_gemm(x, wp, out=y)
+    elif name == "w4a4":
+        xq = rz.razer_quantize_act(synth.prefill_x().to(dev))
+        y = torch.empty((2048, 28672), dtype=torch.bfloat16, device=dev)
+        w4 = torch.empty(rz.razer_workspace_bytes(rz.RAZER_OP_GEMM_W4A4, 2048, 28672, 8192),
+                         dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            rz.razer_gemm_w4a4(xq, wp, out=y, workspace=w4)
+    elif name == "dequant":
+        out = torch.empty((28672, 8192), dtype=torch.bfloat16, device=dev)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            rz.razer_dequant(wp, out=out)
+    torch.cuda.synchronize()
+    log(f"counters: {name} x3 done")
 
 
 def copy_calibration():
@@ -442,6 +492,8 @@ def main():
     ap.add_argument("--eager", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--traffic-summary", nargs=4, metavar="CSV")
+    ap.add_argument("--counters", choices=sorted(COUNTER_WORKLOADS),
+                    help="run one workload's launches three times, untimed (for counter passes)")
     args = ap.parse_args()
     if args.traffic_summary:
         traffic_summary(*args.traffic_summary)
@@ -463,6 +515,9 @@ def main():
     log(f"device: {torch.cuda.get_device_name(0)}")
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.counters:
+        run_counter_workload(torch, rz, synth, args.counters)
         return
 
     log("decode: generating and encoding weights ...")
