@@ -62,8 +62,8 @@ def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
-                               "(or python nvfp4_razer_w4a16_amd/build.py)")
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "python nvfp4_razer_w4a16_amd/build.py")
         L = ctypes.CDLL(LIB_PATH)
         vp, sz, i32, i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int64
         P = ctypes.POINTER(razer_packed)
