@@ -251,3 +251,17 @@ def test_layout_variants_host_checks():
     g128 = _packed(rows=8, cols=128)
     g128.block_log2, g128.scale_fmt = 7, 1
     assert _group_call([_packed(rows=8, cols=128), g128], [0x6000, 0x7000]) == rz.RAZER_E_UNSUPPORTED
+
+
+def test_gemm_rejects_a_workspace_smaller_than_its_k_split():
+    # M = 16 on a 28672 x 8192 weight splits K across workgroups, whose fp32
+    # partial sums need a workspace; a smaller or missing one is refused on the
+    # host before anything is enqueued.
+    L = rz.lib()
+    need = rz.razer_workspace_bytes(rz.RAZER_OP_GEMM, 16, 28672, 8192)
+    assert need >= 2 * 16 * 28672 * 4
+    w = _packed(rows=28672, cols=8192)
+    y = ctypes.c_void_p(0x6000)
+    for ws, nbytes in ((None, need), (FAKE_WS, need - 4), (FAKE_WS, 256)):
+        assert L.razer_gemm(FAKE_X, rz.RAZER_BF16, 16, ctypes.byref(w), y, rz.RAZER_BF16, ws, nbytes,
+                            None) == rz.RAZER_E_INVALID
