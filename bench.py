@@ -20,13 +20,13 @@ oracle over one decode step (single thread, about 14 s).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L]
                        [--no-rows] [--no-cpu-baseline] [--eager] [--per-matrix]
-       python bench.py --counters {prefill,w4a4,quantize_weight,quantize_act,dequant}
+       python bench.py --counters {prefill,w4a4,quantize_weight,quantize_act,dequant,small_batch}
        python bench.py --copy-calibration
        python bench.py --traffic-summary FETCH.csv WRITE.csv CAL_FETCH.csv CAL_WRITE.csv
 
 --eager replays the decode launches without a graph (for counter passes);
 --counters W runs one row's launches (prefill, w4a4, quantize_weight,
-quantize_act, dequant) three times, untimed, for counter passes;
+quantize_act, dequant, small_batch) three times, untimed, for counter passes;
 --copy-calibration runs a plain elementwise copy (negation) of 512 MiB, the reference for
 scaling the FETCH_SIZE / WRITE_SIZE counters; --traffic-summary turns the four
 rocprofv3 counter CSVs (decode GEMV fetch, write; copy fetch, write) into
@@ -114,7 +114,7 @@ DECODE_KERNELS = ("gemv_kernel", "smallm_kernel")
 DECODE_SOURCES = ("rz_gemv.hip", "rz_smallm.hip", "rz_device.h")
 
 
-COUNTER_WORKLOADS = ("prefill", "w4a4", "quantize_weight", "quantize_act", "dequant")
+COUNTER_WORKLOADS = ("prefill", "w4a4", "quantize_weight", "quantize_act", "dequant", "small_batch")
 
 
 def run_counter_workload(torch, rz, synth, name):
@@ -152,6 +152,16 @@ def run_counter_workload(torch, rz, synth, name):
         torch.cuda.synchronize()
         for _ in range(3):
             rz.razer_gemm_w4a4(xq, wp, out=y, workspace=w4)
+    elif name == "small_batch":
+        wsb = rz.razer_quantize_weight(torch.from_numpy(synth.small_batch_weight(28672, 8192)).to(dev), (-2, 4))
+        for m in (8, 32):
+            x = synth.small_batch_x(m, 8192).to(dev)
+            y = torch.empty((m, 28672), dtype=torch.bfloat16, device=dev)
+            ws = torch.empty(max(1, rz.razer_workspace_bytes(rz.RAZER_OP_GEMM, m, 28672, 8192)),
+                             dtype=torch.uint8, device=dev)
+            torch.cuda.synchronize()
+            for _ in range(3):
+                rz.razer_gemm(x, wsb, out=y, workspace=ws)
     elif name == "dequant":
         out = torch.empty((28672, 8192), dtype=torch.bfloat16, device=dev)
         torch.cuda.synchronize()
