@@ -263,7 +263,8 @@ template <typename XT, int KIND, typename OT>
 __global__ __launch_bounds__(512) void gemm_tile256_kernel(const XT* __restrict__ x, int64_t m,
                                                       const uint8_t* __restrict__ codes,
                                                       const uint8_t* __restrict__ scales,
-                                                      const float* __restrict__ ts, int64_t n,
+                                                      const float* __restrict__ ts,
+                                                      const float* __restrict__ ts2, int64_t n,
                                                       int64_t k, float m0, float m1, OT* __restrict__ y) {
   typedef typename Mfma32<XT>::V V;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -404,7 +405,9 @@ __global__ __launch_bounds__(512) void gemm_tile256_kernel(const XT* __restrict_
     step(kt + 1, st0, st1);
   }
   if (kt < ktiles) step(kt, st1, st0);
-  const float scale = *ts;
+  // ts2: a second factor applied after the weight's tensor scale (the
+  // activations' tensor scale of the W4A4 product), 1 when absent
+  const float scale = *ts, scale2 = ts2 ? *ts2 : 1.0f;
 #pragma unroll
   for (int i = 0; i < 4; i++)
 #pragma unroll
@@ -413,7 +416,7 @@ __global__ __launch_bounds__(512) void gemm_tile256_kernel(const XT* __restrict_
 #pragma unroll
       for (int e = 0; e < 16; e++) {
         const int64_t gr = m_base + wm * 128 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        if (gr < m && gc < n) y[gr * n + gc] = from_f32<OT>(acc[i][j][e] * scale);
+        if (gr < m && gc < n) y[gr * n + gc] = from_f32<OT>((acc[i][j][e] * scale) * scale2);
       }
     }
 }
@@ -840,6 +843,26 @@ size_t gemm_ws_bytes(int64_t m, int64_t n, int64_t k) {
   return (size_t)p.split * (size_t)m * (size_t)n * sizeof(float);
 }
 
+static bool tile256_fits(int64_t m, int64_t k, size_t xsize) {
+  return m >= kTM && k % kTK == 0 && (int64_t)kTM * k * (int64_t)xsize < (1LL << 30);
+}
+
+template <typename XT, int KIND, typename OT>
+static hipError_t run_tile256(const XT* x, int64_t m, const PackedView& w, OT* y, const float* ts2,
+                              hipStream_t stream) {
+  const int64_t n = w.rows, k = w.cols;
+  const float m0 = 6.0f + 0.5f * (float)w.off_half[0];
+  const float m1 = 6.0f + 0.5f * (float)w.off_half[KIND == kWeight ? 1 : 0];
+  auto kern = gemm_tile256_kernel<XT, KIND, OT>;
+  const size_t lds = (size_t)2 * (kTM + kTN) * kTS * sizeof(XT) + 256 * sizeof(float2);
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  const int64_t tiles = ((m + kTM - 1) / kTM) * ((n + kTN - 1) / kTN);
+  hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(512), lds, stream, x, m, w.codes, w.scales,
+                     w.tensor_scale, ts2, n, k, m0, m1, y);
+  return hipGetLastError();
+}
+
 template <typename XT, int KIND, typename OT>
 static hipError_t run_gemm(const XT* x, int64_t m, const PackedView& w, OT* y, void* ws,
                            hipStream_t stream) {
@@ -888,17 +911,7 @@ static hipError_t run_gemm(const XT* x, int64_t m, const PackedView& w, OT* y, v
                        p.split, mn, w.tensor_scale, y);
     return hipGetLastError();
   }
-  if (m >= kTM && k % kTK == 0 && (int64_t)kTM * k * (int64_t)sizeof(XT) < (1LL << 30)) {
-    auto kern = gemm_tile256_kernel<XT, KIND, OT>;
-    const size_t lds = (size_t)2 * (kTM + kTN) * kTS * sizeof(XT) + 256 * sizeof(float2);
-    hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    const int64_t tiles = ((m + kTM - 1) / kTM) * ((n + kTN - 1) / kTN);
-    hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(512), lds, stream, x, m, w.codes,
-                       w.scales, w.tensor_scale, n, k, m0, m1, y);
-    return hipGetLastError();
-  }
+  if (tile256_fits(m, k, sizeof(XT))) return run_tile256<XT, KIND, OT>(x, m, w, y, nullptr, stream);
   dim3 grid((unsigned)((n + kBN - 1) / kBN), (unsigned)((m + kBM - 1) / kBM));
   hipLaunchKernelGGL((gemm_kernel<XT, KIND, OT>), grid, dim3(256), 0, stream, x, m, w.codes,
                      w.scales, w.tensor_scale, n, k, m0, m1, y);
@@ -911,6 +924,27 @@ static hipError_t gemm_out_dispatch(const XT* x, int64_t m, const PackedView& w,
   if (y_dtype == kF32) return run_gemm<XT, KIND>(x, m, w, (float*)y, ws, stream);
   if (y_dtype == kF16) return run_gemm<XT, KIND>(x, m, w, (_Float16*)y, ws, stream);
   return run_gemm<XT, KIND>(x, m, w, (__bf16*)y, ws, stream);
+}
+
+template <typename XT, int KIND>
+static hipError_t tile256_out_dispatch(const XT* x, int64_t m, const PackedView& w, void* y, int y_dtype,
+                                       const float* ts2, hipStream_t stream) {
+  if (y_dtype == kF32) return run_tile256<XT, KIND>(x, m, w, (float*)y, ts2, stream);
+  if (y_dtype == kF16) return run_tile256<XT, KIND>(x, m, w, (_Float16*)y, ts2, stream);
+  return run_tile256<XT, KIND>(x, m, w, (__bf16*)y, ts2, stream);
+}
+
+bool gemm_prefill_fits(int64_t m, int64_t k, int x_dtype) { return tile256_fits(m, k, 2); }
+
+hipError_t launch_gemm_prefill_scaled(const void* x, int x_dtype, int64_t m, const PackedView& w, void* y,
+                                      int y_dtype, const float* ts2, hipStream_t stream) {
+  if (!tile256_fits(m, w.cols, 2)) return hipErrorNotSupported;
+  if (x_dtype == kF16) {
+    if (w.kind == kWeight) return tile256_out_dispatch<_Float16, kWeight>((const _Float16*)x, m, w, y, y_dtype, ts2, stream);
+    return tile256_out_dispatch<_Float16, kAct>((const _Float16*)x, m, w, y, y_dtype, ts2, stream);
+  }
+  if (w.kind == kWeight) return tile256_out_dispatch<__bf16, kWeight>((const __bf16*)x, m, w, y, y_dtype, ts2, stream);
+  return tile256_out_dispatch<__bf16, kAct>((const __bf16*)x, m, w, y, y_dtype, ts2, stream);
 }
 
 hipError_t launch_gemm(const void* x, int x_dtype, int64_t m, const PackedView& w, void* y,

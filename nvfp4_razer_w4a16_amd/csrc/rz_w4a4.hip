@@ -12,8 +12,10 @@
 //   2. the W4A16 product runs on that fp16 matrix into an fp32 buffer
 //      (y32 = st_w * sum(...));
 //   3. y = y32 * st_x, rounded once to the output type.
-// Every pass is one of this library's kernels; the workspace holds the fp16
-// activations, the fp32 product and the product's own workspace.
+// For prefill shapes passes 2 and 3 are one: the product's epilogue multiplies
+// by st_w, then by st_x, and rounds once (the same operations in the same
+// order).  Every pass is one of this library's kernels; the workspace holds the
+// fp16 activations, the fp32 product and the product's own workspace.
 #include "rz_device.h"
 #include "rz_launch.h"
 
@@ -57,6 +59,10 @@ hipError_t launch_gemm_w4a4(const PackedView& x, const PackedView& w, void* y, i
   const size_t pws_bytes = ws_bytes - (up((size_t)m * k * 2) + up((size_t)m * n * 4));
   hipError_t e = launch_dequant_unscaled(x, xb, kF16, stream);
   if (e != hipSuccess) return e;
+  // prefill shapes: the product's epilogue applies st_x after st_w and writes
+  // y directly -- the same two fp32 multiplies and one rounding as passes 2-3
+  if (gemm_prefill_fits(m, k, kF16))
+    return launch_gemm_prefill_scaled(xb, kF16, m, w, y, y_dtype, x.tensor_scale, stream);
   e = m == 1 ? launch_gemv(xb, kF16, w, y32, kF32, pws, pws_bytes, stream)
              : launch_gemm(xb, kF16, m, w, y32, kF32, pws, pws_bytes, stream);
   if (e != hipSuccess) return e;
