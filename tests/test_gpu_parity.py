@@ -784,7 +784,9 @@ def test_offset_sse_full_size_prefill_weight():
 
 W4A4_CASES = [(1, 512, 1024, torch.float32), (1, 4096, 14336, torch.float16), (3, 100, 48, torch.bfloat16),
               (8, 4096, 4096, torch.bfloat16), (32, 1000, 512, torch.float32), (256, 512, 1024, torch.bfloat16),
-              (300, 130, 272, torch.float16)]
+              (300, 130, 272, torch.float16),
+              # prefill shapes whose product applies both tensor scales in its epilogue
+              (512, 200, 640, torch.float32), (260, 96, 128, torch.float16)]
 
 
 def _w4a4_operands(m, n, k, x_kind=oracle.ACT, x_offsets=(-2,)):
