@@ -285,9 +285,28 @@ def rel_sse(torch, rz, x, packed):
     return e / float(torch.sum(x.double().square()))
 
 
+def hbm_copy_floor(torch, dev):
+    """Context for the GEMV's roofline fraction: a plain device-to-device copy
+    (torch's copy kernel, graph-replayed like the decode step) at the sizes one
+    decode launch moves, and at 512 MiB.  GB/s counts bytes read + written."""
+    out = {}
+    for mb in (14, 33, 66, 512):
+        nbytes = mb * (1 << 20)
+        copies = max(1, int(1024e6 // nbytes))  # cycle through > 1 GB so reads come from HBM
+        src = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(copies)]
+        dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        t = GraphTimer(torch, lambda: [dst.copy_(sv) for sv in src])
+        ms = t.time(10) / copies
+        out[f"{mb}MiB"] = {"us": ms * 1e3, "gbs": 2 * nbytes / ms / 1e6,
+                           "frac_hbm": 2 * nbytes / ms / 1e6 / HBM_PEAK_GBS}
+        del src, dst, t
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_rows(torch, rz, synth, args, decode_base):
     dev = torch.device("cuda:0")
-    rows = {}
+    rows = {"hbm_copy_floor": hbm_copy_floor(torch, dev)}
 
     # weight encoder on the decode layer's weights (offline path, 4 candidates)
     ws = {}
