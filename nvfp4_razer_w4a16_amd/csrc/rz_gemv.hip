@@ -240,10 +240,11 @@ struct ScaleHalf {
 
 constexpr int kGemvMaxRpw = 64;  // rows per workgroup (bounds the LDS partials)
 
-// Workgroup = 4 waves = KS K-slices x (4 / KS) row groups.  Row group rg owns
-// the rows [rg * rpwv, (rg + 1) * rpwv) of the workgroup's run (rpwv a
-// multiple of 4) and walks them four at a time; within a row, wave (ks, rg)
-// takes chunks (i * KS + ks) * 64 + lane for i < CPL.  The loads of the next
+// Workgroup = 4 waves = KS K-slices x (4 / KS) row groups.  The workgroup's
+// run of rows is walked in quads, dealt round-robin to the row groups (row
+// group rg takes quads rg, rg + 4 / KS, ...: rpwv rows each), so at every quad
+// step the workgroup reads one contiguous block of rows; within a row, wave
+// (ks, rg) takes chunks (i * KS + ks) * 64 + lane for i < CPL.  The loads of the next
 // NQ - 1 row quads are in flight while a quad is decoded.
 //
 // F16S: weights in the 128-element FP16-scale layout (UNIT 2).  A row quad's
@@ -271,9 +272,11 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
     if (g < a.count && (int)blockIdx.x >= a.w[g].wg0) w = a.w[g];
   const int64_t base = (int64_t)((int)blockIdx.x - w.wg0) * a.rpw;
   const int rows_wg = (int)min((int64_t)a.rpw, w.n - base);
-  const int r0 = rg * a.rpwv;                                  // first row of this wave in the run
-  const int nrw = max(0, min(a.rpwv, rows_wg - r0));           // rows of this wave
-  const int nq = (nrw + 3) >> 2;
+  // Quad q of row group rg covers rows 4 (q RW + rg) .. + 4 of the run, so the
+  // row groups of a workgroup read one contiguous block of rows per quad step.
+  constexpr int RW = 4 / KS;
+  const int nquad = (rows_wg + 3) >> 2;
+  const int nq = nquad > rg ? (nquad - rg + RW - 1) / RW : 0;  // quads of this wave
   const int rcb = (int)(a.k / 2), rsb = (int)(F16S ? a.k / 64 : a.k / 16);
   const Rsrc crs = make_rsrc(w.codes + base * rcb, (int64_t)rows_wg * rcb);
   const Rsrc srs = make_rsrc(w.scales + base * rsb, (int64_t)rows_wg * rsb);
@@ -315,14 +318,14 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   SWord sbuf[NQ][CPL];
   // scale bytes first: the table lookups wait on them, the dots on the codes
   auto load_quad = [&](int slot, int q) {
-    const int js = 4 * q + (lane >> 4);
-    const int sbase = js < nrw ? (r0 + js) * rsb : kOob;
+    const int srow = 4 * (q * RW + rg) + (lane >> 4);
+    const int sbase = srow < rows_wg ? srow * rsb : kOob;
 #pragma unroll
     for (int i = 0; i < CPL; i++) sbuf[slot][i].load(srs, sbase + sgo[i]);
 #pragma unroll
     for (int r = 0; r < 4; r++) {
-      const int j = 4 * q + r;
-      const int cb = j < nrw ? (r0 + j) * rcb : kOob;
+      const int crow = 4 * (q * RW + rg) + r;
+      const int cb = crow < rows_wg ? crow * rcb : kOob;
 #pragma unroll
       for (int i = 0; i < CPL; i++) buf[slot][r][i].load(crs, cb + coff[i]);
     }
@@ -396,10 +399,10 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
         wave_lds_sync();       // stage reads done before the next quad's writes
         load_quad(s, q + NQ);  // refill the slot
         const float v = quad_sum(acc);
-        const int j = 4 * q + my_row;
-        if ((lane & 15) == 0 && j < nrw) {
-          if (KS == 1) store_out(w.y, base + r0 + j, v * st, a.ydt);
-          else part[ks * kGemvMaxRpw + r0 + j] = v;
+        const int orow = 4 * (q * RW + rg) + my_row;
+        if ((lane & 15) == 0 && orow < rows_wg) {
+          if (KS == 1) store_out(w.y, base + orow, v * st, a.ydt);
+          else part[ks * kGemvMaxRpw + orow] = v;
         }
       }
     }
