@@ -78,6 +78,10 @@ struct EncodeParams {
   int mag_x2[2];
   PairFast f[2];
   int remap;
+  // Activations whose candidate M is the midpoint of its FP4 neighbours (M =
+  // 2.5, 3.5 or 5, half-gap h = 0.5, 0.5, 1): the midpoint search below.
+  int sym = 0;
+  float sym_m = 0.0f, sym_h = 0.0f;
 };
 
 constexpr float kFastCap = 10.0f;
@@ -204,8 +208,38 @@ __device__ __forceinline__ uint32_t search_fast(const float (&y)[16], float ymax
   uint32_t bits[kPairs];         // bit j: element j is inside the pair's window
 #pragma unroll
   for (int p = 0; p < kPairs; p++) pos[p] = neg[p] = 0, bits[p] = 0u;
+  // Midpoint candidate (activations): with u = |y| - M and h half the gap
+  // between M's FP4 neighbours, an element moves iff |u| < h / 2, and its
+  // change is -h (h - 2|u|) whichever neighbour it rounds to.  So
+  // D = sum over the block of sign(y) * max(h - 2|u|, 0) orders the two
+  // candidates: +M loses (sel 1) iff D < 0.  Near the window a is within a
+  // factor of two of M, so u is exact, and h - 2|u| is a multiple of 2^-20
+  // (a >= 4) or 2^-21 (a >= 2) of magnitude at most 1, so every partial sum
+  // of 16 of them is exact in fp32; away from the window the term is 0
+  // whatever the rounding.  Five operations per element instead of the
+  // integer form's window tests, fma, conversion and multiply-add.
+  bool sym_done = false;
+  uint32_t sym_sel = 0u;
+  if constexpr (kPairs == 1) {
+    if (prm.sym) {
+      sym_done = true;
+      if (ymax > prm.lo[0]) {
+        float dsum = 0.0f;
+#pragma unroll
+        for (int j = 15; j >= 0; j--) {
+          const float e = __builtin_fmaf(fabsf(fabsf(y[j]) - prm.sym_m), -2.0f, prm.sym_h);
+          const float t = fmaxf(e, 0.0f);
+          dsum += __builtin_bit_cast(
+              float, __builtin_bit_cast(uint32_t, t) | (__builtin_bit_cast(uint32_t, y[j]) & 0x80000000u));
+          bits[0] = bits[0] + bits[0] + (e > 0.0f ? 1u : 0u);
+        }
+        sym_sel = dsum < 0.0f ? 1u : 0u;
+      }
+    }
+  }
 #pragma unroll
   for (int p = 0; p < kPairs; p++) {
+    if (sym_done) continue;
     const PairFast& f = prm.f[p];
     const int dlo = f.ddlo, dhi = f.ddhi;
     // ymax = max |y| of the block exactly (rounding is monotone): at or below
@@ -238,7 +272,7 @@ __device__ __forceinline__ uint32_t search_fast(const float (&y)[16], float ymax
   // candidates +M0, -M0 (, +M1, -M1): lowest change wins, ties to the lower index
   uint32_t sel = 0u;
   if constexpr (kPairs == 1) {
-    sel = pos[0] > 0 ? 1u : 0u;  // (+M change) > (-M change)
+    sel = sym_done ? sym_sel : (pos[0] > 0 ? 1u : 0u);  // (+M change) > (-M change)
   } else {
     int best = pos[0] * (1 << prm.f[0].shift);
     const int c1 = neg[0] * (1 << prm.f[0].shift);
@@ -555,6 +589,14 @@ static hipError_t run_quantize(const T* x, const PackedView& out, uint32_t* part
     prm.f[p] = make_pair_fast(out.off_half[p < npairs ? p : 0]);
   }
   prm.remap = (out.flags & kFlagNoRemap) ? 0 : 1;
+  if (KIND == kAct && prm.f[0].hi > prm.f[0].lo && std::isfinite(prm.f[0].hi)) {
+    const float m = 6.0f + 0.5f * (float)out.off_half[0];
+    if (m - prm.lo[0] == prm.hi[0] - m) {  // M midway between its FP4 neighbours
+      prm.sym = 1;
+      prm.sym_m = m;
+      prm.sym_h = 2.0f * (m - prm.lo[0]);
+    }
+  }
   int64_t g2 = (nblk + 255) / 256;
   const int64_t cap = (int64_t)device_cu_count() * 8;
   if (g2 > cap) g2 = cap;

@@ -1,0 +1,88 @@
+"""CPU models of arithmetic shortcuts the HIP kernels take, checked against the oracle.
+
+These tests need no GPU: each one restates, in float32 numpy, a rule a kernel
+uses in place of the plain definition, and compares its decisions with the
+oracle's (which the pin tests tie to exact rational brute force).
+
+Midpoint candidate search (activation encoder).  "RaZeR summary" (gist.science
+technical summary of "RaZeR: Pushing the Limits of NVFP4 Quantization with
+Redundant Zero Remapping"), §2.2: an activation block picks one of the two
+special values +M, -M by the lower block squared error.  When M lies halfway
+between its FP4 neighbours (M = 2.5, 3.5, 5 with half-gap h = 0.5, 0.5, 1), an
+element y moves to sign(y) * M iff |u| < h / 2 with u = |y| - M, and the move
+changes the error by -h * (h - 2|u|) whichever neighbour y rounds to.  The
+kernel therefore sums sign(y) * max(h - 2|u|, 0) over the block in fp32
+(exact: every term is a multiple of 2^-21 of magnitude at most 1) and picks -M
+iff the sum is negative.
+"""
+import numpy as np
+import pytest
+
+import oracle
+
+MIDPOINTS = [(5.0, 1.0), (3.5, 0.5), (2.5, 0.5)]
+
+
+def _kernel_midpoint_rule(y, m, h):
+    """The kernel's fp32 steps for one block: (candidate index, window mask)."""
+    y = np.asarray(y, dtype=np.float32)
+    m32, h32, two = np.float32(m), np.float32(h), np.float32(2.0)
+    dsum = np.float32(0.0)
+    window = []
+    for v in y[::-1]:  # the kernel's order (any order gives the same exact sum)
+        u = np.float32(abs(v)) - m32
+        e = h32 - two * np.float32(abs(u))  # the kernel's fma; exact where it matters
+        t = max(e, np.float32(0.0))
+        dsum = np.float32(dsum + (-t if np.signbit(v) else t))
+        window.append(bool(e > 0))
+    return (1 if dsum < 0 else 0), window[::-1]
+
+
+def _blocks(m, h, n, seed):
+    """Blocks of 16 scaled values, many placed on the window edges, on M and
+    within two ulps of them."""
+    rng = np.random.default_rng(seed)
+    edges = [m - h / 2, m + h / 2, m, m - h / 4, m + h / 4]
+    for _ in range(n):
+        y = (rng.normal(0.0, 1.5, 16) * (m / 3)).astype(np.float32)
+        for i in rng.choice(16, int(rng.integers(1, 9)), replace=False):
+            if rng.integers(4) == 0:
+                v = np.float32(m - h / 2 + rng.random() * h)
+            else:
+                v = np.float32(edges[rng.integers(len(edges))])
+                k = int(rng.integers(-2, 3))
+                for _ in range(abs(k)):
+                    v = np.nextafter(v, np.float32(np.inf if k > 0 else -np.inf), dtype=np.float32)
+            y[i] = -v if rng.integers(2) else v
+        yield y
+
+
+@pytest.mark.parametrize("m,h", MIDPOINTS)
+def test_midpoint_search_matches_oracle_selection(m, h):
+    n_neg = 0
+    for y in _blocks(m, h, 400, seed=int(m * 10)):
+        codes, sel = oracle.encode_block_scaled(y, [m, -m])
+        ksel, window = _kernel_midpoint_rule(y, m, h)
+        assert ksel == sel, (y.tolist(), m)
+        # the remap step: window elements whose sign matches the chosen
+        # candidate become code 0b1000
+        moved = [w and (bool(np.signbit(v)) == (sel == 1)) for v, w in zip(y, window)]
+        assert [c == 8 for c in codes.tolist()] == moved, (y.tolist(), m)
+        n_neg += sel
+    assert 0 < n_neg < 400  # both candidates are exercised
+
+
+def test_midpoint_rule_applies_only_to_midpoint_candidates():
+    # the candidates the encoder sends down this path: M halfway between its
+    # FP4 neighbours; every other offset in [-7, 7] keeps the integer search
+    grid = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    found = []
+    for off in range(-7, 8):
+        m = 6.0 + off / 2.0
+        below = max(g for g in grid if g < m) if m > 0 else None
+        above = [g for g in grid if g > m]
+        if m in grid or not above:
+            continue
+        if m - below == above[0] - m:
+            found.append((m, above[0] - m))
+    assert found == [(2.5, 0.5), (3.5, 0.5), (5.0, 1.0)]
