@@ -15,8 +15,10 @@ counted once) over the timed steps.
 Also measured in the same run (the ``rows`` object): the weight and activation
 encoders (Gelem/s, GB/s, special-value-search overhead), the small-batch GEMM
 sweep (M = 1..32, GB/s) and the M=2048 prefill GEMM (TFLOP/s), each on its own
-synthetic workload; ``roofline`` for the GEMV kernel; ``cpu_baseline`` = the CPU
-oracle over one decode step (single thread, about 14 s).
+synthetic workload, with two practical ceilings beside them: a plain device copy
+at the decode launch sizes and the library's dense bf16 GEMM at the prefill
+shape; ``roofline`` for the GEMV kernel; ``cpu_baseline`` = the CPU oracle over
+one decode step (single thread, about 14 s).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L]
                        [--no-rows] [--no-cpu-baseline] [--eager] [--per-matrix]
@@ -474,6 +476,27 @@ def bench_rows(torch, rz, synth, args, decode_base):
     byts = packed_bytes(28672, 8192) + n_el * 2
     rows["dequant"] = {"workload": "W [28672,8192] -> bf16", "ms": ms_d, "gbs": byts / ms_d / 1e6,
                        "frac_hbm": byts / ms_d / 1e6 / HBM_PEAK_GBS}
+    # Context for the prefill GEMM's MFMA fraction: the library's dense bf16
+    # GEMM (torch.mm) on the same shape and the same (dequantized) weight
+    # values, which decodes nothing.  The part is power-limited, so its rate
+    # depends on the operands; this is the practical ceiling at these values.
+    for _ in range(3):
+        torch.mm(x, out.t(), out=y)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(10):
+        torch.mm(x, out.t(), out=y)
+    e1.record(st)
+    e1.synchronize()
+    ms_dense = e0.elapsed_time(e1) / 10
+    rows["dense_bf16_gemm_ceiling"] = {
+        "workload": "torch.mm bf16 x [2048,8192] x W^T, W [28672,8192] row-major (the dequantized RaZeR "
+                    "weight of gemm_prefill) -> bf16; library GEMM, no decode",
+        "ms": ms_dense, "tflops": flops / ms_dense / 1e9,
+        "frac_mfma": flops / ms_dense / 1e9 / MFMA_BF16_PEAK_TFLOPS,
+        "gemm_prefill_over_dense": rows["gemm_prefill"]["tflops"] / (flops / ms_dense / 1e9)}
     del t, x, y, wp, out
     torch.cuda.empty_cache()
     return rows
