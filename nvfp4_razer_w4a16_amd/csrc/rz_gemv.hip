@@ -483,9 +483,11 @@ static hipError_t dispatch(const GemvArgs& a, const GemvPlan& p, bool f16s, hipS
 
 // Weights that go to the MFMA small-batch kernel instead: long rows (K above
 // 8192) on up to 4096 rows, where its K split keeps enough waves busy
-// (measured faster there only).
+// (measured faster there only); both the default layout and 128-element
+// blocks with FP16 scales.
 static bool gemv_to_smallm(const PackedView& w) {
-  return default_layout(w) && w.rows <= 4096 && w.cols > 8192 && smallm_supported(1, w.rows, w.cols);
+  const bool layout_ok = default_layout(w) || (w.blog2 == 7 && w.sfmt == 1);
+  return layout_ok && w.rows <= 4096 && w.cols > 8192 && smallm_supported(1, w.rows, w.cols);
 }
 
 hipError_t launch_gemv_group(const void* x, int x_dtype, const PackedView* w, void* const* y,

@@ -146,8 +146,14 @@ constexpr int kSection = 256 * 2 + 16;  // LDS bytes per K group: M x (256 / M) 
 constexpr int kUnitRow = 128 + 16;              // staged code bytes per row
 constexpr int kStageBytes = 16 * kUnitRow + 16 * 16;  // codes + scales of one unit
 
-template <typename XT, int M, int T, int KS>
+// F16S (M = 1 only): weights in the 128-element FP16-scale layout.  A unit's
+// scales are one dword per row (two words, one per 128-element block), loaded
+// by lanes 0..15 into the row's scale slot of the stage; a lane's D rows are
+// four 16-element slots of one 128-element block, so both coefficients come
+// from one word of that dword.
+template <typename XT, int M, int T, int KS, bool F16S>
 __global__ __launch_bounds__(64 * KS) void smallm_kernel(SmArgs a) {
+  static_assert(!F16S || M == 1, "the FP16-scale layout is read for one activation row");
   typedef typename Ops<XT>::V V;
   constexpr int S = 16 / M;        // block slots per K group
   constexpr int G = 8 / M;         // MFMAs per K group
@@ -164,7 +170,7 @@ __global__ __launch_bounds__(64 * KS) void smallm_kernel(SmArgs a) {
   const int c = lane & 15, q = lane >> 4;
   const int64_t row0 = (int64_t)blockIdx.x * (16 * T);
   const int rows_wg = (int)min((int64_t)(16 * T), a.n - row0);
-  const int rcb = (int)(a.k / 2), rsb = (int)(a.k / 16);
+  const int rcb = (int)(a.k / 2), rsb = (int)(F16S ? a.k / 64 : a.k / 16);
   const Rsrc crs = make_rsrc(a.codes + row0 * rcb, (int64_t)rows_wg * rcb);
   const Rsrc srs = make_rsrc(a.scales + row0 * rsb, (int64_t)rows_wg * rsb);
   const Rsrc xrs = make_rsrc(a.x, (int64_t)a.m * a.k * 2);
@@ -197,7 +203,10 @@ __global__ __launch_bounds__(64 * KS) void smallm_kernel(SmArgs a) {
   for (int t = 0; t < T; t++) {
     cvo0[t] = 16 * t + lr < rows_wg ? (16 * t + lr) * rcb + lb : kOob;
     cvo1[t] = 16 * t + lr + 8 < rows_wg ? (16 * t + lr + 8) * rcb + lb : kOob;
-    svo[t] = 16 * t + (lane >> 2) < rows_wg ? (16 * t + (lane >> 2)) * rsb + (lane & 3) * 4 : kOob;
+    if (F16S)
+      svo[t] = lane < 16 && 16 * t + lane < rows_wg ? (16 * t + lane) * rsb : kOob;
+    else
+      svo[t] = 16 * t + (lane >> 2) < rows_wg ? (16 * t + (lane >> 2)) * rsb + (lane & 3) * 4 : kOob;
   }
   struct UnitRegs {
     u32x4_t c0[T], c1[T];
@@ -205,7 +214,7 @@ __global__ __launch_bounds__(64 * KS) void smallm_kernel(SmArgs a) {
   };
   auto load_unit = [&](UnitRegs& r, int u) {
     const bool ok = u < u1;
-    const int cso = ok ? u * 128 : kOob, sso = ok ? u * 16 : kOob;
+    const int cso = ok ? u * 128 : kOob, sso = ok ? u * (F16S ? 4 : 16) : kOob;
 #pragma unroll
     for (int t = 0; t < T; t++) {
       r.c0[t] = __builtin_amdgcn_raw_buffer_load_b128(crs, cvo0[t], cso, kNt);
@@ -218,7 +227,10 @@ __global__ __launch_bounds__(64 * KS) void smallm_kernel(SmArgs a) {
     for (int t = 0; t < T; t++) {
       *(u32x4_t*)(st[t] + lr * kUnitRow + lb) = r.c0[t];
       *(u32x4_t*)(st[t] + (lr + 8) * kUnitRow + lb) = r.c1[t];
-      *(uint32_t*)(st[t] + 16 * kUnitRow + lane * 4) = r.s[t];
+      if (!F16S)
+        *(uint32_t*)(st[t] + 16 * kUnitRow + lane * 4) = r.s[t];
+      else if (lane < 16)
+        *(uint32_t*)(st[t] + 16 * kUnitRow + lane * 16) = r.s[t];
     }
   };
   int xo[G];  // LDS byte offset of this lane's A fragment inside a section
@@ -280,7 +292,8 @@ __global__ __launch_bounds__(64 * KS) void smallm_kernel(SmArgs a) {
         const u32x2_t v = *(const u32x2_t*)crow;
         cw[t][0] = v[0]; cw[t][1] = v[1];
       }
-      sw[t] = *(const uint32_t*)(st[t] + 16 * kUnitRow + c * 16 + gi * S + (4 * q) % S);
+      sw[t] = F16S ? *(const uint32_t*)(st[t] + 16 * kUnitRow + c * 16)
+                   : *(const uint32_t*)(st[t] + 16 * kUnitRow + c * 16 + gi * S + (4 * q) % S);
     }
     f32x4_t d0[T], d1[T];
 #pragma unroll
@@ -305,13 +318,25 @@ __global__ __launch_bounds__(64 * KS) void smallm_kernel(SmArgs a) {
       }
     }
 #pragma unroll
-    for (int t = 0; t < T; t++)
+    for (int t = 0; t < T; t++) {
+      if constexpr (F16S) {
+        const uint32_t wd = (sw[t] >> (16 * (q >> 1))) & 0xFFFFu;  // block (4q) / 8 of the unit
+        const float sb = scale_of_f16word(wd), sv = special_of_f16word(wd, a.m0, a.m1);
+        const float c0 = sb * (1.0f + 4.0f * sv), c1 = -4.0f * sb * sv;
 #pragma unroll
-      for (int e = 0; e < 4; e++) {
-        const float2 f = lut[(sw[t] >> (8 * e)) & 0xFFu];
-        acc[t] = fmaf(d0[t][e], f.x, acc[t]);
-        acc[t] = fmaf(d1[t][e], f.y, acc[t]);
+        for (int e = 0; e < 4; e++) {
+          acc[t] = fmaf(d0[t][e], c0, acc[t]);
+          acc[t] = fmaf(d1[t][e], c1, acc[t]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          const float2 f = lut[(sw[t] >> (8 * e)) & 0xFFu];
+          acc[t] = fmaf(d0[t][e], f.x, acc[t]);
+          acc[t] = fmaf(d1[t][e], f.y, acc[t]);
+        }
       }
+    }
   };
 
   for (int u = u0; u < u1; u += 2) {
@@ -378,9 +403,9 @@ SmPlan plan_smallm(int64_t m, int64_t n, int64_t k, int cus) {
   return p;
 }
 
-template <typename XT, int M, int T, int KS>
+template <typename XT, int M, int T, int KS, bool F16S>
 hipError_t launch_cfg(const SmArgs& a, hipStream_t stream, int64_t grid) {
-  auto kern = smallm_kernel<XT, M, T, KS>;
+  auto kern = smallm_kernel<XT, M, T, KS, F16S>;
   const size_t lds = (size_t)KS * a.gpw * kSection;
   if (lds + 2048 + KS * T * 256 + KS * 2 * T * kStageBytes > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -390,20 +415,21 @@ hipError_t launch_cfg(const SmArgs& a, hipStream_t stream, int64_t grid) {
   return hipGetLastError();
 }
 
-template <typename XT, int M, int T>
+template <typename XT, int M, int T, bool F16S = false>
 hipError_t dispatch_ks(const SmArgs& a, const SmPlan& p, hipStream_t stream) {
   switch (p.ks) {
-    case 1: return launch_cfg<XT, M, T, 1>(a, stream, p.grid);
-    case 2: return launch_cfg<XT, M, T, 2>(a, stream, p.grid);
-    case 4: return launch_cfg<XT, M, T, 4>(a, stream, p.grid);
-    case 8: return launch_cfg<XT, M, T, 8>(a, stream, p.grid);
+    case 1: return launch_cfg<XT, M, T, 1, F16S>(a, stream, p.grid);
+    case 2: return launch_cfg<XT, M, T, 2, F16S>(a, stream, p.grid);
+    case 4: return launch_cfg<XT, M, T, 4, F16S>(a, stream, p.grid);
+    case 8: return launch_cfg<XT, M, T, 8, F16S>(a, stream, p.grid);
   }
   return hipErrorInvalidValue;
 }
 
 template <typename XT>
-hipError_t dispatch(const SmArgs& a, const SmPlan& p, hipStream_t stream) {
+hipError_t dispatch(const SmArgs& a, const SmPlan& p, bool f16s, hipStream_t stream) {
   if (p.t != 1) return hipErrorInvalidValue;  // two tiles per workgroup measured slower
+  if (f16s) return p.mt == 1 ? dispatch_ks<XT, 1, 1, true>(a, p, stream) : hipErrorNotSupported;
   if (p.mt == 1) return dispatch_ks<XT, 1, 1>(a, p, stream);
   if (p.mt == 2) return dispatch_ks<XT, 2, 1>(a, p, stream);
   return dispatch_ks<XT, 4, 1>(a, p, stream);
@@ -424,6 +450,9 @@ bool smallm_supported(int64_t m, int64_t n, int64_t k) {
 hipError_t launch_smallm(const void* x, int x_dtype, int64_t m, const PackedView& w, void* y,
                          int y_dtype, hipStream_t stream) {
   if (!smallm_supported(m, w.rows, w.cols)) return hipErrorNotSupported;
+  // the default layout, or (one activation row) 128-element blocks with FP16 scales
+  const bool f16s = !default_layout(w);
+  if (f16s && (m != 1 || w.blog2 != 7 || w.sfmt != 1)) return hipErrorNotSupported;
   SmArgs a;
   a.x = x;
   a.codes = w.codes;
@@ -439,7 +468,7 @@ hipError_t launch_smallm(const void* x, int x_dtype, int64_t m, const PackedView
   a.m1 = 6.0f + 0.5f * (float)w.off_half[w.kind == kWeight ? 1 : 0];
   const SmPlan p = plan_smallm(m, w.rows, w.cols, device_cu_count());
   a.gpw = p.gpw;
-  return x_dtype == kF16 ? dispatch<_Float16>(a, p, stream) : dispatch<__bf16>(a, p, stream);
+  return x_dtype == kF16 ? dispatch<_Float16>(a, p, f16s, stream) : dispatch<__bf16>(a, p, f16s, stream);
 }
 
 }  // namespace rz

@@ -424,11 +424,14 @@ def test_quantize_variant_group128_f16_prefill_weight_sampled():
 
 @pytest.mark.parametrize("n,k,xdt", [(300, 1024, torch.float16), (77, 128, torch.bfloat16),
                                      (6144, 4096, torch.float16), (4096, 14336, torch.float16),
-                                     (5, 65536, torch.bfloat16), (1000, 2944, torch.bfloat16)])
+                                     (5, 65536, torch.bfloat16), (1000, 2944, torch.bfloat16),
+                                     (1000, 8448, torch.bfloat16), (16, 12288, torch.float16)])
 def test_gemv_group128_f16_layout(n, k, xdt):
     """The pages' kernel layout (128-element blocks, FP16 scales) through the
     GEMV: within tolerance of the fp64 product over the oracle's decoded
-    weights; razer_gemm with m = 1 gives the same bytes."""
+    weights; razer_gemm with m = 1 gives the same bytes.  Rows of more than
+    8192 elements on up to 4096 rows (4096 x 14336, 1000 x 8448, 16 x 12288)
+    go to the MFMA small-batch kernel."""
     _need_gpu()
     rng = np.random.default_rng(n + k)
     w = (rng.standard_t(5, (n, k)) * 0.02).astype(np.float32)
