@@ -277,6 +277,97 @@ def run_launches(rz, launches):
             rz.razer_gemv_group(x, ws, outs=ys)
 
 
+def launch_bytes(launch):
+    """Algorithmic bytes of one decode launch: packed weights, y, x once."""
+    _, ws, _ = launch
+    return sum(packed_bytes(m.rows, m.cols, m.block, 2 if m.scale_fmt else 1) + 2 * m.rows for m in ws) \
+        + 2 * ws[0].cols
+
+
+DECODE_CLASSES = ("qkv", "gate_up", "down")  # the grouped step's launches, in order per layer
+
+
+def per_kernel_rates(torch, rz, launches, steps):
+    """Each launch class of the grouped decode step (qkv: gemv_kernel; gate and
+    up: one gemv_kernel launch; down: smallm_kernel) timed on its own: the
+    class's launches over the layer copies in one HIP graph, HIP events on the
+    launch stream; average duration per launch and the GB/s it implies."""
+    out = {}
+    for ci, name in enumerate(DECODE_CLASSES):
+        ls = launches[ci::len(DECODE_CLASSES)]
+        ms = GraphTimer(torch, lambda: run_launches(rz, ls), warmup=1).time(steps) / len(ls)
+        b = launch_bytes(ls[0])
+        out[name] = {"avg_launch_us": round(ms * 1e3, 3), "algorithmic_bytes": b,
+                     "achieved_gbs": round(b / ms / 1e6, 1), "frac": round(b / ms / 1e6 / HBM_PEAK_GBS, 4)}
+    return out
+
+
+def ceiling_lib():
+    """libceiling.so: the plain-read and register-only MFMA probes (bench only)."""
+    import ctypes
+
+    L = ctypes.CDLL(os.path.join(ROOT, "nvfp4_razer_w4a16_amd", "libceiling.so"))
+    L.rzc_read.restype = ctypes.c_int
+    L.rzc_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+                           ctypes.c_void_p]
+    L.rzc_mfma_loop.restype = ctypes.c_int
+    L.rzc_mfma_loop.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    return L
+
+
+def step_read_floor(torch, launches, step_bytes, steps, cus):
+    """The decode step's plain-read floor: for every GEMV launch of the step,
+    one launch that only reads the same weight bytes (codes and scales of each
+    weight in it) with 16-byte non-temporal loads, 8 workgroups per CU, in the
+    step's order, replayed from a HIP graph like the step itself."""
+    import ctypes
+
+    L = ceiling_lib()
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    prepared = []
+    for _, ws, _ in launches:
+        bufs = [t for w in ws for t in (w.codes, w.scales)]
+        prepared.append(((ctypes.c_void_p * len(bufs))(*[b.data_ptr() for b in bufs]),
+                         (ctypes.c_int64 * len(bufs))(*[b.numel() for b in bufs]), len(bufs)))
+
+    def run():
+        st = torch.cuda.current_stream().cuda_stream
+        for ptrs, ns, c in prepared:
+            if L.rzc_read(ptrs, ns, c, sink.data_ptr(), 8 * cus, st) != 0:
+                raise RuntimeError("rzc_read failed")
+
+    ms = GraphTimer(torch, run, warmup=1).time(steps)
+    return {"workload": "plain read of the decode step's weight bytes, one read launch per GEMV launch "
+                        f"({len(launches)} per step), 8 workgroups per CU, HIP graph",
+            "us_per_step": ms * 1e3, "gbs_on_step_bytes": step_bytes / ms / 1e6,
+            "frac_hbm": step_bytes / ms / 1e6 / HBM_PEAK_GBS}
+
+
+def mfma_loop_ceiling(torch, cus, reps=5, iters=20000):
+    """Register-only v_mfma_f32_32x32x16_bf16 loop: random bf16 operands, two
+    waves per SIMD on every CU (the prefill product's layout), no memory
+    traffic; TFLOP/s from HIP events."""
+    L = ceiling_lib()
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    wgs = 2 * cus
+    st = torch.cuda.current_stream()
+    for _ in range(2):
+        L.rzc_mfma_loop(iters // 4, wgs, sink.data_ptr(), st.cuda_stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(reps):
+        if L.rzc_mfma_loop(iters, wgs, sink.data_ptr(), st.cuda_stream) != 0:
+            raise RuntimeError("rzc_mfma_loop failed")
+    e1.record(st)
+    e1.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flops = wgs * 4 * iters * 2 * (2.0 * 32 * 32 * 16)
+    return {"workload": f"v_mfma_f32_32x32x16_bf16 on register operands (random bf16), {wgs} workgroups of "
+                        "4 waves (2 waves per SIMD), no memory traffic",
+            "ms": ms, "tflops": flops / ms / 1e9, "frac_mfma": flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS}
+
+
 # ---- other rows --------------------------------------------------------------------
 
 def rel_sse(torch, rz, x, packed):
@@ -332,24 +423,30 @@ def bench_rows(torch, rz, synth, args, decode_base):
     del ws, t, t0
     torch.cuda.empty_cache()
 
-    # activation encoder X[4096, 8192] bf16 (online path, 2 candidates)
-    x = synth.act_quant_x().to(dev)
-    out = rz.PackedTensor(rz.RAZER_ACT, 4096, 8192, (-2,), dev)
-    out0 = rz.PackedTensor(rz.RAZER_ACT, 4096, 8192, (-2,), dev, rz.RAZER_FLAG_NO_REMAP)
+    # activation encoder X[4096, 8192] bf16 (online path, 2 candidates), over
+    # 8 distinct copies of X and of the output (690 MB in all, well above the
+    # 256 MB Infinity Cache), so every read of X comes from HBM
+    x0 = synth.act_quant_x().to(dev)
+    ncopy = 8
+    xs_ = [x0] + [x0.clone() for _ in range(ncopy - 1)]
+    outs = [rz.PackedTensor(rz.RAZER_ACT, 4096, 8192, (-2,), dev) for _ in range(ncopy)]
+    outs0 = [rz.PackedTensor(rz.RAZER_ACT, 4096, 8192, (-2,), dev, rz.RAZER_FLAG_NO_REMAP) for _ in range(ncopy)]
     wsp = torch.empty(rz.razer_workspace_bytes(rz.RAZER_OP_QUANTIZE_ACT, 4096, 0, 8192),
                       dtype=torch.uint8, device=dev)
-    t = GraphTimer(torch, lambda: rz.razer_quantize_act(x, out=out, workspace=wsp))
-    ms = t.time(50)
-    t0 = GraphTimer(torch, lambda: rz.razer_quantize_act(x, out=out0, workspace=wsp))
-    ms0 = t0.time(50)
-    n_el = x.numel()
+    t = GraphTimer(torch, lambda: [rz.razer_quantize_act(xi, out=o, workspace=wsp) for xi, o in zip(xs_, outs)])
+    ms = t.time(10) / ncopy
+    t0 = GraphTimer(torch, lambda: [rz.razer_quantize_act(xi, out=o, workspace=wsp) for xi, o in zip(xs_, outs0)])
+    ms0 = t0.time(10) / ncopy
+    n_el = x0.numel()
     rows["quantize_act"] = {
-        "workload": "X [4096,8192] bf16 N(0,1), 16 channels x50, 1% tokens x5",
+        "workload": "X [4096,8192] bf16 N(0,1), 16 channels x50, 1% tokens x5; 8 distinct copies of X and "
+                    "of the packed output cycled (X read from HBM)",
         "gelem_per_s": n_el / ms / 1e6, "ms": ms,
         "gbs_1read": n_el * (2 + 0.5625) / ms / 1e6,
         "frac_hbm_1read": n_el * (2 + 0.5625) / ms / 1e6 / HBM_PEAK_GBS,
+        "gbs_2pass": n_el * (2 * 2 + 0.5625) / ms / 1e6,
         "no_remap_ms": ms0, "search_overhead_pct": 100.0 * (ms - ms0) / ms0}
-    del x, t, t0
+    del x0, xs_, outs, outs0, t, t0
     torch.cuda.empty_cache()
 
     # small-batch GEMM sweep
@@ -504,10 +601,20 @@ def bench_rows(torch, rz, synth, args, decode_base):
 
 # ---- CPU oracle baseline ------------------------------------------------------------
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(synth, layers):
     """The oracle's product over one decode step: `layers` passes over the
-    layer's four GEMVs (the step's layer copies hold the same weights)."""
-    import numpy as np
+    layer's four GEMVs (the step's layer copies hold the same weights), on
+    one host core: the calling thread is pinned to a single CPU while it runs."""
     import oracle
 
     names = ["qkv", "gate", "up", "down"]
@@ -516,19 +623,26 @@ def cpu_baseline(synth, layers):
         packs[n] = oracle.quantize_weight(synth.llama3_8b_decode_weight(n), (-2, 4))
     xs = {4096: synth.llama3_8b_decode_x(4096).float().numpy(),
           14336: synth.llama3_8b_decode_x(14336).float().numpy()}
-    byts = 0
-    t0 = time.perf_counter()
-    for _ in range(layers):
-        for n in names:
-            p = packs[n]
-            oracle.gemm(xs[p.cols], p)
-            byts += gemv_bytes(p.rows, p.cols)
-    dt = time.perf_counter() - t0
+    allowed = sorted(os.sched_getaffinity(0))
+    core = allowed[-1]
+    os.sched_setaffinity(0, {core})
+    try:
+        byts = 0
+        t0 = time.perf_counter()
+        for _ in range(layers):
+            for n in names:
+                p = packs[n]
+                oracle.gemm(xs[p.cols], p)
+                byts += gemv_bytes(p.rows, p.cols)
+        dt = time.perf_counter() - t0
+    finally:
+        os.sched_setaffinity(0, set(allowed))
     return {"value": byts / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"one decode step: {layers} x (qkv, gate, up, down GEMVs, 201M weights) of the "
                       "decode workload, weights encoded by the oracle (encode not timed), fp64 "
-                      f"accumulation, {dt:.1f} s single-threaded",
-            "seconds": dt, "host_cpus": os.cpu_count()}
+                      f"accumulation, {dt:.1f} s on one pinned core",
+            "seconds": dt, "cpu_model": cpu_model(), "pinned_cpu": core,
+            "host_cpus_visible": len(allowed)}
 
 
 def main():
@@ -605,6 +719,15 @@ def main():
                 "avg_launch_us": round(avg_us, 3),
                 "algorithmic_bytes_per_launch": bytes_per_launch}
 
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if not args.per_matrix:
+        roofline["per_kernel"] = per_kernel_rates(torch, rz, launches, args.steps)
+    floor = step_read_floor(torch, launches, step_bytes, args.steps, cus)
+    roofline["step_read_floor_us"] = round(floor["us_per_step"], 2)
+    roofline["frac_of_step_read_floor"] = round(floor["us_per_step"] / (ms_step * 1e3), 4)
+    log(f"decode: read floor {floor['us_per_step']:.1f} us/step; per kernel "
+        + ", ".join(f"{k} {v['avg_launch_us']:.2f} us ({v['frac']:.2f})" for k, v in roofline.get("per_kernel", {}).items()))
+
     rows = None
     if not args.no_rows:
         # the other launch arrangement of the same step, for comparison
@@ -627,8 +750,11 @@ def main():
         del steps_g, l3
         torch.cuda.empty_cache()
         log("rows: encoders, small-batch sweep, prefill ...")
-        rows = {f"decode_{other}": decode_other, "decode_g128_f16": decode_g128}
+        rows = {f"decode_{other}": decode_other, "decode_g128_f16": decode_g128,
+                "decode_step_read_floor": floor, "mfma_loop_ceiling": mfma_loop_ceiling(torch, cus)}
         rows.update(bench_rows(torch, rz, synth, args, base))
+        pf, ml = rows["gemm_prefill"], rows["mfma_loop_ceiling"]
+        pf["frac_of_mfma_loop"] = pf["tflops"] / ml["tflops"]
 
     cpu = None
     if not args.no_cpu_baseline:

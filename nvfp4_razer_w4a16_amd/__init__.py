@@ -110,6 +110,36 @@ def _dtype_code(dt: torch.dtype) -> int:
     return _DT[dt]
 
 
+def _check_device(t: torch.Tensor, device: torch.device, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU, not {t.device}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, not {t.device}")
+
+
+def _check_buffer(t: torch.Tensor, shape, device: torch.device, name: str, dtype=None):
+    """A caller-supplied output or workspace: the C ABI cannot see its size, so
+    shape, dtype, device and contiguity are checked here, before any launch."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if dtype is None and shape is not None and t.dtype not in _DT:
+        raise TypeError(f"{name}: unsupported dtype {t.dtype}")
+    if device is not None:
+        _check_device(t, device, name)
+
+
+def _check_input(x: torch.Tensor, device: torch.device, name: str):
+    _check_device(x, device, name)
+    if x.dtype not in _DT:
+        raise TypeError(f"{name}: unsupported dtype {x.dtype}")
+
+
 class PackedTensor:
     """A RaZeR-packed tensor in device memory (torch tensors own the bytes).
 
@@ -149,6 +179,25 @@ class PackedTensor:
     def nbytes(self) -> int:
         return self.codes.numel() + self.scales.numel() + 4
 
+    @property
+    def device(self) -> torch.device:
+        return self.codes.device
+
+    def check(self, name: str = "packed tensor"):
+        """Its buffers still match its shape and layout (they are plain
+        attributes a caller can replace)."""
+        sbytes = 2 if self.scale_fmt == RAZER_SCALE_F16 else 1
+        bufs = ((self.codes, (self.rows, self.cols // 2), "codes"),
+                (self.scales, (self.rows, self.cols // self.block * sbytes), "scales"),
+                (self.tensor_scale, (1,), "tensor_scale"))
+        for t, shape, what in bufs:
+            _check_buffer(t, shape, None, f"{name}.{what}",
+                          torch.float32 if what == "tensor_scale" else torch.uint8)
+        dev = self.codes.device
+        for t, _, what in bufs:
+            _check_device(t, dev, f"{name}.{what}")
+        return dev
+
 
 def _workspace(op, m, n, k, device, workspace):
     need = razer_workspace_bytes(op, m, n, k)
@@ -156,6 +205,8 @@ def _workspace(op, m, n, k, device, workspace):
         return None, 0
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    else:
+        _check_buffer(workspace, None, device, "workspace")
     return workspace, workspace.numel() * workspace.element_size()
 
 
@@ -168,10 +219,15 @@ def _encoder_flags(remap: bool, four_over_six: bool) -> int:
 def _quantize(fn, op, kind, x, offsets, flags, out, workspace, stream, block, scale_fmt):
     if x.dim() != 2:
         raise ValueError("expected a 2-D tensor")
+    _check_input(x, x.device, "x")
     x = x.contiguous()
     rows, cols = x.shape
     if out is None:
         out = PackedTensor(kind, rows, cols, offsets, x.device, flags, block, scale_fmt)
+    elif (out.rows, out.cols) != (rows, cols):
+        raise ValueError(f"out is {out.rows}x{out.cols}, the input {rows}x{cols}")
+    else:
+        _check_device(out.check("out"), x.device, "out")
     s = out.struct()
     ws, wsb = _workspace(op, rows, 0, cols, x.device, workspace)
     _check(fn(ctypes.c_void_p(x.data_ptr()), _dtype_code(x.dtype), ctypes.byref(s),
@@ -204,8 +260,11 @@ def razer_quantize_act(x: torch.Tensor, offsets=DEFAULT_ACT_OFFSETS, remap: bool
 
 
 def razer_dequant(t: PackedTensor, dtype: torch.dtype = torch.float32, out=None, stream=None):
+    dev = t.check("t")
     if out is None:
-        out = torch.empty((t.rows, t.cols), dtype=dtype, device=t.codes.device)
+        out = torch.empty((t.rows, t.cols), dtype=dtype, device=dev)
+    else:
+        _check_buffer(out, (t.rows, t.cols), dev, "out")
     s = t.struct()
     _check(lib().razer_dequant(ctypes.byref(s), ctypes.c_void_p(out.data_ptr()),
                                _dtype_code(out.dtype), ctypes.c_void_p(_stream(stream))),
@@ -216,11 +275,17 @@ def razer_dequant(t: PackedTensor, dtype: torch.dtype = torch.float32, out=None,
 def razer_gemv(x: torch.Tensor, w: PackedTensor, out_dtype: torch.dtype | None = None, out=None,
                workspace=None, stream=None):
     """y[N] = x[K] . W^T for a packed weight W [N, K]."""
+    dev = w.check("w")
+    _check_input(x, dev, "x")
     x = x.contiguous()
     if x.numel() != w.cols:
         raise ValueError("x must hold K elements")
     if out is None:
         out = torch.empty(w.rows, dtype=out_dtype or x.dtype, device=x.device)
+    else:
+        _check_buffer(out, None, dev, "out")
+        if out.numel() != w.rows or out.dtype not in _DT:
+            raise ValueError(f"out must hold N = {w.rows} elements of f32, f16 or bf16")
     ws, wsb = _workspace(RAZER_OP_GEMV, 1, w.rows, w.cols, x.device, workspace)
     s = w.struct()
     _check(lib().razer_gemv(ctypes.c_void_p(x.data_ptr()), _dtype_code(x.dtype), ctypes.byref(s),
@@ -236,14 +301,28 @@ RAZER_GEMV_GROUP_MAX = 4
 def razer_gemv_group(x: torch.Tensor, ws, out_dtype: torch.dtype | None = None, outs=None,
                      stream=None):
     """[x[K] . W^T for W in ws] in one launch (weights sharing x, e.g. gate and up)."""
-    x = x.contiguous()
     ws = list(ws)
     if not 1 <= len(ws) <= RAZER_GEMV_GROUP_MAX:
         raise ValueError(f"1..{RAZER_GEMV_GROUP_MAX} weights")
+    dev = ws[0].check("ws[0]")
+    for i, w in enumerate(ws):
+        _check_device(w.check(f"ws[{i}]"), dev, f"ws[{i}]")
+    _check_input(x, dev, "x")
+    x = x.contiguous()
     if any(w.cols != x.numel() for w in ws):
         raise ValueError("x must hold K elements for every weight")
     if outs is None:
         outs = [torch.empty(w.rows, dtype=out_dtype or x.dtype, device=x.device) for w in ws]
+    else:
+        outs = list(outs)
+        if len(outs) != len(ws):
+            raise ValueError("one output per weight")
+        for i, (o, w) in enumerate(zip(outs, ws)):
+            _check_buffer(o, None, dev, f"outs[{i}]")
+            if o.numel() != w.rows:
+                raise ValueError(f"outs[{i}] must hold {w.rows} elements")
+            if o.dtype != outs[0].dtype or o.dtype not in _DT:
+                raise ValueError("every output must have the same dtype (f32, f16 or bf16)")
     structs = [w.struct() for w in ws]
     ptrs = (ctypes.POINTER(razer_packed) * len(ws))(*[ctypes.pointer(s) for s in structs])
     ys = (ctypes.c_void_p * len(ws))(*[o.data_ptr() for o in outs])
@@ -256,12 +335,16 @@ def razer_gemv_group(x: torch.Tensor, ws, out_dtype: torch.dtype | None = None, 
 def razer_gemm(x: torch.Tensor, w: PackedTensor, out_dtype: torch.dtype | None = None, out=None,
                workspace=None, stream=None):
     """y[M, N] = x[M, K] . W^T for a packed weight W [N, K]."""
+    dev = w.check("w")
+    _check_input(x, dev, "x")
     x = x.contiguous()
     if x.dim() != 2 or x.shape[1] != w.cols:
         raise ValueError("x must be [M, K]")
     m = x.shape[0]
     if out is None:
         out = torch.empty((m, w.rows), dtype=out_dtype or x.dtype, device=x.device)
+    else:
+        _check_buffer(out, (m, w.rows), dev, "out")
     ws, wsb = _workspace(RAZER_OP_GEMM, m, w.rows, w.cols, x.device, workspace)
     s = w.struct()
     _check(lib().razer_gemm(ctypes.c_void_p(x.data_ptr()), _dtype_code(x.dtype), m, ctypes.byref(s),
@@ -277,10 +360,13 @@ def razer_weight_offset_sse(w: torch.Tensor, off0: int = DEFAULT_WEIGHT_OFFSETS[
     (off0, o), for o = -7..7 (device float64 [15], entry o + 7)."""
     if w.dim() != 2:
         raise ValueError("expected a 2-D tensor")
+    _check_input(w, w.device, "w")
     w = w.contiguous()
     rows, cols = w.shape
     if out is None:
         out = torch.empty(len(SECOND_PAIR_OFFSETS), dtype=torch.float64, device=w.device)
+    else:
+        _check_buffer(out, (len(SECOND_PAIR_OFFSETS),), w.device, "out", torch.float64)
     ws, wsb = _workspace(RAZER_OP_OFFSET_SEARCH, 0, rows, cols, w.device, workspace)
     _check(lib().razer_weight_offset_sse(ctypes.c_void_p(w.data_ptr()), _dtype_code(w.dtype), rows, cols,
                                          int(off0), ctypes.c_void_p(out.data_ptr()),
@@ -302,12 +388,17 @@ def razer_gemm_w4a4(x: PackedTensor, w: PackedTensor, out_dtype: torch.dtype = t
     activation encoding) and packed w [N, K]."""
     if x.cols != w.cols:
         raise ValueError("x and w must have the same K")
-    dev = x.codes.device
+    dev = x.check("x")
+    _check_device(w.check("w"), dev, "w")
     if out is None:
         out = torch.empty((x.rows, w.rows), dtype=out_dtype, device=dev)
+    else:
+        _check_buffer(out, (x.rows, w.rows), dev, "out")
     need = razer_workspace_bytes(RAZER_OP_GEMM_W4A4, x.rows, w.rows, w.cols)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    elif workspace is not None:
+        _check_buffer(workspace, None, dev, "workspace")
     wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
     sx, sw = x.struct(), w.struct()
     _check(lib().razer_gemm_w4a4(ctypes.byref(sx), ctypes.byref(sw), ctypes.c_void_p(out.data_ptr()),

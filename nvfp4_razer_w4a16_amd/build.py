@@ -16,6 +16,9 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "librazer.so")
+# measurement probes loaded only by the bench (plain read, register-only MFMA loop)
+CEILING_LIB = os.path.join(HERE, "libceiling.so")
+CEILING_SRC = "rz_ceiling.hip"
 BUILD_DIR = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -49,18 +52,24 @@ def _compile(src: str, extra: list[str]) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda kv: _compile(*kv), SOURCES.items()))
-    tmp = LIB + ".tmp"
+def _link(objs: list[str], out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    jobs = list(SOURCES.items()) + [(CEILING_SRC, [])]
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        objs = list(ex.map(lambda kv: _compile(*kv), jobs))
+    _link(objs[:-1], LIB)
+    _link(objs[-1:], CEILING_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {CEILING_LIB}")
     return LIB
 
 

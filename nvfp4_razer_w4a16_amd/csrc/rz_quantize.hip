@@ -401,10 +401,9 @@ __device__ __forceinline__ void encode_block(const float (&xf)[16], float amax, 
 // difference, the square and each partial sum round once each, so no
 // contraction into fused multiply-adds.
 __device__ __forceinline__ double plain_block_sse(const float (&xf)[16], const uint32_t (&w)[2],
-                                                  float sb, float st) {
+                                                  float sb, float st, double sse = 0.0) {
 #pragma clang fp contract(off)
   const double s = (double)sb * (double)st;
-  double sse = 0.0;
 #pragma unroll
   for (int j = 0; j < 16; j++) {
     const uint32_t c = (w[j >> 3] >> (4 * (j & 7))) & 15u;
@@ -807,8 +806,8 @@ hipError_t launch_offset_search(const void* x, int dtype, int64_t rows, int64_t 
 // where every change (v - q)(v + q - 2y) and every sum of them is exact (a
 // moved element has |y| > 2, so each term is a multiple of 2^-23 below 2^5),
 // so the comparison does not depend on the order of the sums.  Four Over Six
-// errors are not exact: each lane sums its 16 elements in order and the
-// block adds the lanes' sums in lane order.
+// errors are not exact, so they are added in element order: the running sum
+// passes from lane to lane of the block (block_sse_in_order).
 struct VariantParams {
   double cand[4];  // +M0, -M0 (, +M1, -M1), in selection-index order
   int ncand;
@@ -828,10 +827,15 @@ __device__ __forceinline__ double group_sum_exact(double v, int glog2) {
   return v;
 }
 
-__device__ __forceinline__ double group_sum_ordered(double v, int glog2, int lane) {
+// Squared error of a plain-FP4 block spread over 2^glog2 adjacent lanes (16
+// elements each), summed in element order: lane i of the block continues the
+// running sum of lanes 0 .. i-1 over its own 16 elements.  Every lane computes
+// its continuation of the current sum and the block takes lane i's.
+__device__ __forceinline__ double block_sse_in_order(const float (&xf)[16], const uint32_t (&w)[2],
+                                                     float sb, float st, int glog2, int lane) {
   const int g0 = lane & ~((1 << glog2) - 1);
-  double s = __shfl(v, g0);
-  for (int i = 1; i < (1 << glog2); i++) s = s + __shfl(v, g0 + i);
+  double s = 0.0;
+  for (int i = 0; i < (1 << glog2); i++) s = __shfl(plain_block_sse(xf, w, sb, st, s), g0 + i);
   return s;
 }
 
@@ -883,8 +887,8 @@ __device__ __forceinline__ void encode_variant(const float (&xf)[16], float amax
     uint32_t w4[2];
     float y4[16], sb4;
     const uint32_t c4 = variant_at_scale<KIND>(xf, sb_real * 1.5f, st, vp.sfmt, w4, y4, sb4);
-    const double e6 = group_sum_ordered(plain_block_sse(xf, w, sb, st), vp.glog2, lane);
-    const double e4 = group_sum_ordered(plain_block_sse(xf, w4, sb4, st), vp.glog2, lane);
+    const double e6 = block_sse_in_order(xf, w, sb, st, vp.glog2, lane);
+    const double e4 = block_sse_in_order(xf, w4, sb4, st, vp.glog2, lane);
     if (e4 < e6) {
       w[0] = w4[0];
       w[1] = w4[1];

@@ -299,6 +299,29 @@ def gemm(x, p: Packed, cols=None):
     return y, nrm
 
 
+def gemm_pairs(x, p: Packed, rows_m, cols_n):
+    """The product oracle at individual outputs: y[i] = x[rows_m[i]] . w[cols_n[i]]
+    and its norm, for sampled (m, n) pairs of a large product.  Returns
+    (y [npairs], norm [npairs])."""
+    _default_layout(p)
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    if x.ndim != 2 or x.shape[1] != p.cols:
+        raise ValueError("x must be [m, K]")
+    rows_m = np.asarray(rows_m, dtype=np.int64)
+    cols_n = np.asarray(cols_n, dtype=np.int64)
+    off = _offsets(p.kind, p.offsets)
+    y = np.zeros(rows_m.size, dtype=np.float64)
+    nrm = np.zeros(rows_m.size, dtype=np.float64)
+    one_y, one_n = np.zeros(1, np.float64), np.zeros(1, np.float64)
+    for i, (mi, ni) in enumerate(zip(rows_m, cols_n)):
+        xr = np.ascontiguousarray(x[mi])
+        idx = np.array([ni], dtype=np.int64)
+        lib().rzo_gemm(_ptr(xr), 1, p.cols, p.kind, _ptr(p.codes), _ptr(p.scales), float(p.tensor_scale),
+                       _ptr(off), p.rows, _ptr(idx), 1, _ptr(one_y), _ptr(one_n))
+        y[i], nrm[i] = one_y[0], one_n[0]
+    return y, nrm
+
+
 def gemm_any(x, p: Packed):
     """fp64 product y = x @ w^T and norm |x| @ |w|^T over the exactly decoded
     weights of any layout (block sizes, FP16 group scales): the oracle's
@@ -326,10 +349,27 @@ def gemm_w4a4(xp: Packed, wp: Packed, cols=None):
         raise ValueError("inner dimensions differ")
     xd = dequant_f64(xp)
     if cols is not None:  # decode only the selected weight rows (same tensor scale)
-        idx = np.asarray(cols, dtype=np.int64)
-        wp = Packed(wp.kind, idx.size, wp.cols, wp.offsets,
-                    np.ascontiguousarray(wp.codes.reshape(wp.rows, wp.cols // 2)[idx]).reshape(-1),
-                    np.ascontiguousarray(wp.scales.reshape(wp.rows, wp.cols // 16)[idx]).reshape(-1),
-                    wp.tensor_scale)
+        wp = select_rows(wp, cols)
     wd = dequant_f64(wp)
     return xd @ wd.T, np.abs(xd) @ np.abs(wd).T
+
+
+def select_rows(p: Packed, idx) -> Packed:
+    """The packed rows idx of a default-layout tensor (same tensor scale and
+    offsets), for decoding a sample of a large tensor."""
+    _default_layout(p)
+    idx = np.asarray(idx, dtype=np.int64)
+    return Packed(p.kind, idx.size, p.cols, p.offsets,
+                  np.ascontiguousarray(p.codes.reshape(p.rows, p.cols // 2)[idx]).reshape(-1),
+                  np.ascontiguousarray(p.scales.reshape(p.rows, p.cols // 16)[idx]).reshape(-1),
+                  p.tensor_scale)
+
+
+def gemm_w4a4_pairs(xp: Packed, wp: Packed, rows_m, cols_n):
+    """gemm_w4a4 at individual outputs (m, n): the decoded rows' fp64 dot
+    products and norms.  Returns (y [npairs], norm [npairs])."""
+    if xp.cols != wp.cols:
+        raise ValueError("inner dimensions differ")
+    xd = dequant_f64(select_rows(xp, rows_m))
+    wd = dequant_f64(select_rows(wp, cols_n))
+    return np.einsum("ik,ik->i", xd, wd), np.einsum("ik,ik->i", np.abs(xd), np.abs(wd))

@@ -226,23 +226,18 @@ static int encode_at_scale(int kind, int sfmt, int n, const float* xb, float sb_
 }
 
 /* Squared error of a plain-FP4 block (no special value) in real units: the
- * sum of (x_j - value_j * sb * st)^2 in fp64, taken over each run of 16
- * consecutive elements in order and then over the runs in order (for a
- * 16-element block simply j = 0..15).  value * sb * st is exact in fp64 (at
- * most 3 + 11 + 24 significant bits); the difference, the square and each
- * partial sum are rounded once each. */
+ * sum of (x_j - value_j * sb * st)^2 in fp64, added in element order
+ * j = 0 .. n-1.  value * sb * st is exact in fp64 (at most 3 + 11 + 24
+ * significant bits); the difference, the square and each partial sum are
+ * rounded once each. */
 static double block_sse(int kind, int sfmt, int n, const float* xb, const uint8_t* cb, int scode,
                         float st) {
   double sb = scode == 0 ? 0.0 : rzo_scale_value_fmt(kind, sfmt, scode);
   double sse = 0.0;
-  for (int r = 0; r < n; r += 16) {
-    double run = 0.0;
-    for (int j = r; j < r + 16; j++) {
-      double q = rzo_fp4_value(cb[j]) * sb * (double)st;
-      double e = (double)xb[j] - q;
-      run += e * e;
-    }
-    sse = r == 0 ? run : sse + run;
+  for (int j = 0; j < n; j++) {
+    double q = rzo_fp4_value(cb[j]) * sb * (double)st;
+    double e = (double)xb[j] - q;
+    sse += e * e;
   }
   return sse;
 }

@@ -92,9 +92,8 @@ int rzo_quantize(int kind, const float* x, int64_t rows, int64_t cols,
  * elements along a row (cols % block == 0), sfmt RZO_SCALE_BYTE or (weights
  * only) RZO_SCALE_F16.  scales holds rows*cols/block entries of 1 or 2 bytes.
  * The tensor scale is amax / (6 * S_MAX) with S_MAX the format's largest scale.
- * In the Four Over Six mode a block's squared error is summed per run of 16
- * elements, then over the runs in order.  rzo_quantize is this with block 16
- * and byte scales. */
+ * In the Four Over Six mode a block's squared error is summed in fp64 in
+ * element order.  rzo_quantize is this with block 16 and byte scales. */
 int rzo_quantize_fmt(int kind, const float* x, int64_t rows, int64_t cols,
                      const int8_t* off_half, int mode, int block, int sfmt, uint8_t* codes,
                      void* scales, float* tensor_scale);

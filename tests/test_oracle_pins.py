@@ -486,53 +486,61 @@ def _fos_inputs(kind):
     return x
 
 
-@pytest.mark.parametrize("kind,block", [(oracle.WEIGHT, 16), (oracle.ACT, 16), (oracle.WEIGHT, 64)])
-def test_four_over_six_is_the_better_of_two_plain_encodings(kind, block):
-    # Independent of the oracle's encoder: the two candidate scale codes are the
-    # exact-rational nearest codes of S_MAX*amax_b/amax and 1.5x that (up to the
-    # fp32 op-order convention near a midpoint), the codes are the closed-form
-    # E2M1 rounding, and the kept candidate must have the exactly smaller error.
-    x = _fos_inputs(kind)
-    p = oracle.quantize(kind, x, (-2, 4) if kind == oracle.WEIGHT else (-2,), four_over_six=True,
-                        block=block)
-    smax = oracle.scale_max(kind)
+def _fos_grid(kind):
     ncode = 64 if kind == oracle.WEIGHT else 127
-    grid = [F(oracle.scale_value(kind, c)) for c in range(ncode)]
-    mids = [(grid[c] + grid[c + 1]) / 2 for c in range(ncode - 1)]
+    return [F(oracle.scale_value(kind, c)) for c in range(ncode)]
+
+
+def _fos_nearest(kind, v):
+    """Exact-rational nearest scale code of v >= 0 (ties to the even code),
+    saturating at the largest code."""
+    grid = _fos_grid(kind)
+    if v >= F(oracle.scale_max(kind)):
+        return len(grid) - 1
+    return min(range(len(grid)), key=lambda c: (abs(v - grid[c]), c % 2))
+
+
+def _fos_encode(kind, xb, scode, st):
+    """Plain FP4 of a block at scale code scode: the closed-form E2M1 rounding
+    of the fp32 scaled values; returns (codes, decoded values)."""
+    if scode == 0:
+        return [0] * len(xb), [0.0] * len(xb)
+    sb = np.float32(oracle.scale_value(kind, scode))
+    rcp = np.float32(1.0) / (sb * st)
+    out, val = [], []
+    for a in (xb * rcp).astype(np.float32):
+        m = _fp4_rne_closed_form(abs(float(a)))
+        out.append(0 if m == 0 else (8 if a < 0 else 0) | FP4_SET.index(m))
+        val.append(math.copysign(m, float(a)) * float(sb) * float(st) if m else 0.0)
+    return out, val
+
+
+def _fos_check_exact(kind, x, p, block):
+    """Every block of p (a Four Over Six encoding of x) against the exact
+    choice: the two candidate scale codes are the exact-rational nearest codes
+    of S_MAX*amax_b/amax and 1.5x that, the codes are the closed-form E2M1
+    rounding, and the kept candidate must have the exactly smaller squared
+    error (ties keep max -> 6).  Blocks within 2^-20 of a scale-rounding
+    midpoint, where the fp32 op order may pick either neighbour, are left
+    out.  Returns (blocks that took max -> 4, blocks with unequal errors,
+    blocks left out)."""
+    smax = oracle.scale_max(kind)
+    grid = _fos_grid(kind)
+    mids = [(grid[c] + grid[c + 1]) / 2 for c in range(len(grid) - 1)]
     st = np.float32(p.tensor_scale)
     amax = F(float(np.abs(x).max()))
     codes = p.unpacked_codes().reshape(-1, block)
     took4 = strict = skipped = 0
-
-    def nearest(v):
-        if v >= F(smax):
-            return ncode - 1
-        return min(range(ncode), key=lambda c: (abs(v - grid[c]), c % 2))
-
-    def encode(xb, scode):
-        if scode == 0:
-            return [0] * block, [0.0] * block
-        sb = np.float32(oracle.scale_value(kind, scode))
-        rcp = np.float32(1.0) / (sb * st)
-        out, val = [], []
-        for a in (xb * rcp).astype(np.float32):
-            m = _fp4_rne_closed_form(abs(float(a)))
-            out.append(0 if m == 0 else (8 if a < 0 else 0) | FP4_SET.index(m))
-            val.append(math.copysign(m, float(a)) * float(sb) * float(st) if m else 0.0)
-        return out, val
-
     for b in range(codes.shape[0]):
         xb = x.reshape(-1, block)[b]
         exact6 = F(smax) * F(float(np.abs(xb).max())) / amax
-        c6, c4 = nearest(exact6), nearest(exact6 * F(3, 2))
-        # within 2^-20 of a rounding midpoint the fp32 op order may pick either
-        # neighbour: such blocks are left out here (and counted)
+        c6, c4 = _fos_nearest(kind, exact6), _fos_nearest(kind, exact6 * F(3, 2))
         if any(e < F(smax) and min(abs(e - m) for m in mids) <= e * F(1, 2 ** 20)
                for e in (exact6, exact6 * F(3, 2))):
             skipped += 1
             continue
-        k6, v6 = encode(xb, c6)
-        k4, v4 = encode(xb, c4)
+        k6, v6 = _fos_encode(kind, xb, c6, st)
+        k4, v4 = _fos_encode(kind, xb, c4, st)
         e6, e4 = _exact_block_sse(xb, v6), _exact_block_sse(xb, v4)
         sbyte = int(p.scales[b])
         assert sbyte >> (6 if kind == oracle.WEIGHT else 7) == 0  # no metadata bits
@@ -543,7 +551,67 @@ def test_four_over_six_is_the_better_of_two_plain_encodings(kind, block):
             assert sbyte == c6 and codes[b].tolist() == k6, b
         strict += e4 != e6
     assert 8 not in codes.reshape(-1).tolist()  # plain FP4: zero is always +0
-    assert 0 < took4 < codes.shape[0] and strict > 0 and skipped <= codes.shape[0] // 50
+    return took4, strict, skipped
+
+
+@pytest.mark.parametrize("kind,block", [(oracle.WEIGHT, 16), (oracle.ACT, 16), (oracle.WEIGHT, 32),
+                                        (oracle.WEIGHT, 64), (oracle.WEIGHT, 128), (oracle.ACT, 32)])
+def test_four_over_six_is_the_better_of_two_plain_encodings(kind, block):
+    # Independent of the oracle's encoder (exact rationals, closed-form FP4).
+    x = _fos_inputs(kind)
+    p = oracle.quantize(kind, x, (-2, 4) if kind == oracle.WEIGHT else (-2,), four_over_six=True,
+                        block=block)
+    nblk = x.size // block
+    took4, strict, skipped = _fos_check_exact(kind, x, p, block)
+    assert 0 < took4 < nblk and strict > 0 and skipped <= max(1, nblk // 50)
+
+
+def _fos_planted_block(block, kind_of_tie):
+    """A block of `block` elements with maximum 0.75 whose two Four Over Six
+    candidates (scale 8 and 12 at tensor scale 2^-6: grid steps 1/8 and 3/16)
+    have equal squared errors, or errors that differ by one fp32 ulp's worth.
+    Per 16-element run: +-0.28125 are on the max -> 4 grid and 1/32 off the
+    max -> 6 grid, +-0.125 the other way round, so the two errors tie; 0.21875
+    (1/32 off both) and values on both grids add equally to each.  kind_of_tie: "tie",
+    "four" (0.28125 one ulp up: max -> 4 better by 2^-4 ulp) or "six" (one ulp
+    down: max -> 6 better by the same)."""
+    run = np.array([0.28125, 0.125, 0.21875, -0.375, 0.1875, 0.0, -0.75, 0.0,
+                    0.375, -0.28125, 0.0, 0.75, -0.1875, 0.0, -0.125, 0.0], dtype=np.float32)
+    blk = np.tile(run, block // 16)
+    if kind_of_tie == "four":
+        blk[0] = np.nextafter(np.float32(0.28125), np.float32(1.0))
+    elif kind_of_tie == "six":
+        blk[0] = np.nextafter(np.float32(0.28125), np.float32(0.0))
+    return blk
+
+
+@pytest.mark.parametrize("kind,block", [(oracle.WEIGHT, 32), (oracle.WEIGHT, 64), (oracle.WEIGHT, 128),
+                                        (oracle.ACT, 32), (oracle.ACT, 128)])
+def test_four_over_six_planted_ties_and_near_ties(kind, block):
+    # Tensor scale 2^-6 (amax = 6 * S_MAX / 64).  Planted blocks whose two
+    # candidate errors tie exactly (max -> 6 kept), or differ by a single
+    # fp32 ulp of one element in either direction; every error is a short
+    # dyadic number, so the exact-rational choice is the only correct one.
+    smax = oracle.scale_max(kind)
+    kinds = ["tie", "four", "six", "tie", "six", "four"]
+    x = np.zeros((1, block * (1 + len(kinds))), dtype=np.float32)
+    x[0, 1] = 6.0 * smax / 64.0
+    for i, k in enumerate(kinds):
+        x[0, block * (i + 1):block * (i + 2)] = _fos_planted_block(block, k)
+    offs = (-2, 4) if kind == oracle.WEIGHT else (-2,)
+    p = oracle.quantize(kind, x, offs, four_over_six=True, block=block)
+    assert p.tensor_scale == np.float32(2.0 ** -6)
+    _fos_check_exact(kind, x, p, block)
+    sc = [oracle.scale_value(kind, int(c)) for c in p.scales[1:]]
+    want = {"tie": 8.0, "six": 8.0, "four": 12.0}
+    assert sc == [want[k] for k in kinds], sc
+    # the planted errors really are (near-)ties, in exact rationals
+    st = np.float32(2.0 ** -6)
+    for i, k in enumerate(kinds):
+        xb = x[0, block * (i + 1):block * (i + 2)]
+        e6 = _exact_block_sse(xb, _fos_encode(kind, xb, _fos_nearest(kind, F(8)), st)[1])
+        e4 = _exact_block_sse(xb, _fos_encode(kind, xb, _fos_nearest(kind, F(12)), st)[1])
+        assert (e4 == e6) if k == "tie" else (0 < abs(e4 - e6) <= e6 * F(1, 2 ** 16)), (k, e4, e6)
 
 
 @pytest.mark.parametrize("kind", [oracle.WEIGHT, oracle.ACT])
@@ -737,3 +805,24 @@ def test_gemm_any_equals_the_product_oracle_on_the_default_layout():
     ya, na = oracle.gemm_any(x, p)
     np.testing.assert_allclose(ya, y, rtol=1e-12, atol=1e-12 * float(n.max()))
     np.testing.assert_allclose(na, n, rtol=1e-12)
+
+
+def test_sampled_output_helpers_equal_the_full_products():
+    # gemm_pairs / gemm_w4a4_pairs (used to check sampled outputs of products
+    # too large to compute in full) give the full products' entries.
+    rng = np.random.default_rng(77)
+    w = (rng.standard_t(4, (200, 512)) * 0.015).astype(np.float32)
+    x = rng.normal(0, 1, (30, 512)).astype(np.float32)
+    p = oracle.quantize_weight(w, (-2, -5))
+    y, nrm = oracle.gemm(x, p)
+    mi, ni = rng.integers(0, 30, 300), rng.integers(0, 200, 300)
+    yp, np_ = oracle.gemm_pairs(x, p, mi, ni)
+    np.testing.assert_array_equal(yp, y[mi, ni])
+    np.testing.assert_array_equal(np_, nrm[mi, ni])
+    xp = oracle.quantize_act(x, (-2,))
+    y4, n4 = oracle.gemm_w4a4(xp, p)
+    yq, nq = oracle.gemm_w4a4_pairs(xp, p, mi, ni)
+    np.testing.assert_allclose(yq, y4[mi, ni], rtol=1e-12, atol=1e-12 * float(np.abs(n4).max()))
+    np.testing.assert_allclose(nq, n4[mi, ni], rtol=1e-12)
+    sub = oracle.select_rows(p, ni[:7])
+    np.testing.assert_array_equal(oracle.dequant_f64(sub), oracle.dequant_f64(p)[ni[:7]])
