@@ -24,15 +24,16 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L]
                        [--no-rows] [--no-cpu-baseline] [--eager] [--per-matrix]
        python bench.py --counters {prefill,w4a4,quantize_weight,quantize_act,dequant,small_batch}
        python bench.py --copy-calibration
-       python bench.py --traffic-summary FETCH.csv WRITE.csv CAL_FETCH.csv CAL_WRITE.csv
+       python bench.py --traffic-summary RD.csv WR.csv FS.csv CAL_RD.csv CAL_WR.csv CAL_FS.csv
 
 --eager replays the decode launches without a graph (for counter passes);
 --counters W runs one row's launches (prefill, w4a4, quantize_weight,
 quantize_act, dequant, small_batch) three times, untimed, for counter passes;
---copy-calibration runs a plain elementwise copy (negation) of 512 MiB, the reference for
-scaling the FETCH_SIZE / WRITE_SIZE counters; --traffic-summary turns the four
-rocprofv3 counter CSVs (decode GEMV fetch, write; copy fetch, write) into
-profiles/traffic.json, stamped with the hash of the GEMV source.
+--copy-calibration runs a plain elementwise copy (negation) of 512 MiB, the check
+that the request counters are byte-exact; --traffic-summary turns six rocprofv3
+counter CSVs (decode launches: TCC_EA0_RDREQ_{32B,64B,128B}_sum, TCC_EA0_WRREQ{,_64B}_sum,
+FETCH_SIZE; the same three for the copy) into profiles/traffic.json, stamped with
+the hash of the GEMV sources.
 """
 import argparse
 import hashlib
@@ -184,41 +185,71 @@ def copy_calibration():
     log(f"copy calibration: 5 elementwise copies of {COPY_BYTES} bytes")
 
 
-def _counter_per_dispatch(path, name_parts):
-    """Mean over dispatches of the kernels whose names contain one of name_parts
-    of the counter summed over its instances, from a rocprofv3
-    counter_collection CSV."""
+def _counters_per_dispatch(path, name_parts):
+    """{dispatch id: {counter: value summed over its instances}} for the
+    dispatches of kernels whose names contain one of name_parts, from a
+    rocprofv3 counter_collection CSV, plus each dispatch's kernel name and grid."""
     import csv
     from collections import defaultdict
 
-    per = defaultdict(float)
+    per = defaultdict(lambda: defaultdict(float))
+    what = {}
     for r in csv.DictReader(open(path)):
         if any(p in r["Kernel_Name"] for p in name_parts):
-            per[r["Dispatch_Id"]] += float(r["Counter_Value"])
+            per[r["Dispatch_Id"]][r["Counter_Name"]] += float(r["Counter_Value"])
+            what[r["Dispatch_Id"]] = (r["Kernel_Name"], int(r["Grid_Size"]))
     if not per:
         raise SystemExit(f"no dispatch of {name_parts!r} in {path}")
-    return sum(per.values()) / len(per), len(per)
+    return per, what
 
 
-def traffic_summary(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv):
-    """FETCH_SIZE / WRITE_SIZE are KiB per dispatch; each is scaled by what the
-    same counter reads for the calibration copy (COPY_BYTES read, COPY_BYTES
-    written), so the factor absorbs any per-channel sampling of the counter."""
-    f_k, nf = _counter_per_dispatch(fetch_csv, DECODE_KERNELS)
-    w_k, nw = _counter_per_dispatch(write_csv, DECODE_KERNELS)
-    cf, _ = _counter_per_dispatch(cal_fetch_csv, ("elementwise",))
-    cw, _ = _counter_per_dispatch(cal_write_csv, ("elementwise",))
-    f_scale = COPY_BYTES / (cf * 1024.0)
-    w_scale = COPY_BYTES / (cw * 1024.0)
-    fetch = f_k * 1024.0 * f_scale
-    write = w_k * 1024.0 * w_scale
+def _read_bytes(c):
+    return 32 * c["TCC_EA0_RDREQ_32B_sum"] + 64 * c["TCC_EA0_RDREQ_64B_sum"] + 128 * c["TCC_EA0_RDREQ_128B_sum"]
+
+
+def _write_bytes(c):
+    return 32 * (c["TCC_EA0_WRREQ_sum"] - c["TCC_EA0_WRREQ_64B_sum"]) + 64 * c["TCC_EA0_WRREQ_64B_sum"]
+
+
+def traffic_summary(rd_csv, wr_csv, fs_csv, cal_rd_csv, cal_wr_csv, cal_fs_csv):
+    """HBM bytes per decode launch from the L2-to-memory request counters:
+    reads = 32 n32 + 64 n64 + 128 n128 (TCC_EA0_RDREQ_{32B,64B,128B}, summed
+    over the L2 channels), writes = 32 n32 + 64 n64 (TCC_EA0_WRREQ, _64B).
+    The calibration copy (COPY_BYTES read and written) checks that these
+    counts are byte-exact.  FETCH_SIZE, scaled by what it reads for the same
+    copy, is kept beside them as a cross-check."""
+    rd, what = _counters_per_dispatch(rd_csv, DECODE_KERNELS)
+    wr, _ = _counters_per_dispatch(wr_csv, DECODE_KERNELS)
+    fs, _ = _counters_per_dispatch(fs_csv, DECODE_KERNELS)
+    crd, _ = _counters_per_dispatch(cal_rd_csv, ("elementwise",))
+    cwr, _ = _counters_per_dispatch(cal_wr_csv, ("elementwise",))
+    cfs, _ = _counters_per_dispatch(cal_fs_csv, ("elementwise",))
+    big = lambda d, f: max(f(c) for c in d.values())  # the copy dispatch (others are tiny fills)
+    cal_read, cal_write = big(crd, _read_bytes), big(cwr, _write_bytes)
+    fs_scale = COPY_BYTES / (big(cfs, lambda c: c["FETCH_SIZE"]) * 1024.0)
+    classes = {}
+    for d, (name, grid) in what.items():
+        key = f"{'smallm_kernel' if 'smallm' in name else 'gemv_kernel'} grid {grid}"
+        cl = classes.setdefault(key, {"read": [], "write": [], "fetch_size_scaled": []})
+        cl["read"].append(_read_bytes(rd[d]))
+        if d in wr:
+            cl["write"].append(_write_bytes(wr[d]))
+    for d, (name, grid) in _counters_per_dispatch(fs_csv, DECODE_KERNELS)[1].items():
+        key = f"{'smallm_kernel' if 'smallm' in name else 'gemv_kernel'} grid {grid}"
+        classes[key]["fetch_size_scaled"].append(fs[d]["FETCH_SIZE"] * 1024.0 * fs_scale)
+    mean = lambda v: sum(v) / len(v) if v else None
+    per_class = {k: {"read_bytes": mean(v["read"]), "write_bytes": mean(v["write"]),
+                     "fetch_size_scaled_bytes": mean(v["fetch_size_scaled"]), "dispatches": len(v["read"])}
+                 for k, v in sorted(classes.items())}
+    n = len(per_class)
+    total = sum(v["read_bytes"] + v["write_bytes"] for v in per_class.values()) / n
     src = source_hash(*DECODE_SOURCES)
     out = {"gemv_decode": {
-        "source_hash": src, "bytes_per_launch": round(fetch + write),
-        "fetch_bytes_per_launch": round(fetch), "write_bytes_per_launch": round(write),
-        "fetch_kib_raw": f_k, "write_kib_raw": w_k, "dispatches": [nf, nw],
-        "copy_fetch_kib_raw": cf, "copy_write_kib_raw": cw,
-        "fetch_scale": f_scale, "write_scale": w_scale}}
+        "source_hash": src, "bytes_per_launch": round(total),
+        "method": "TCC_EA0_RDREQ_{32B,64B,128B} and TCC_EA0_WRREQ{,_64B} request counts x request size",
+        "per_launch_class": per_class,
+        "copy_check": {"read_bytes": cal_read, "write_bytes": cal_write, "copy_bytes": COPY_BYTES,
+                       "fetch_size_scale": fs_scale}}}
     path = os.path.join(ROOT, "profiles", "traffic.json")
     json.dump(out, open(path, "w"), indent=1)
     print(json.dumps(out))
@@ -308,18 +339,17 @@ def ceiling_lib():
 
     L = ctypes.CDLL(os.path.join(ROOT, "nvfp4_razer_w4a16_amd", "libceiling.so"))
     L.rzc_read.restype = ctypes.c_int
-    L.rzc_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
-                           ctypes.c_void_p]
+    L.rzc_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     L.rzc_mfma_loop.restype = ctypes.c_int
     L.rzc_mfma_loop.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     return L
 
 
-def step_read_floor(torch, launches, step_bytes, steps, cus):
+def step_read_floor(torch, launches, step_bytes, steps):
     """The decode step's plain-read floor: for every GEMV launch of the step,
     one launch that only reads the same weight bytes (codes and scales of each
-    weight in it) with 16-byte non-temporal loads, 8 workgroups per CU, in the
-    step's order, replayed from a HIP graph like the step itself."""
+    weight in it), 16 KiB per 256-thread workgroup in 16-byte non-temporal
+    loads, in the step's order, replayed from a HIP graph like the step itself."""
     import ctypes
 
     L = ceiling_lib()
@@ -333,12 +363,12 @@ def step_read_floor(torch, launches, step_bytes, steps, cus):
     def run():
         st = torch.cuda.current_stream().cuda_stream
         for ptrs, ns, c in prepared:
-            if L.rzc_read(ptrs, ns, c, sink.data_ptr(), 8 * cus, st) != 0:
+            if L.rzc_read(ptrs, ns, c, sink.data_ptr(), st) != 0:
                 raise RuntimeError("rzc_read failed")
 
     ms = GraphTimer(torch, run, warmup=1).time(steps)
     return {"workload": "plain read of the decode step's weight bytes, one read launch per GEMV launch "
-                        f"({len(launches)} per step), 8 workgroups per CU, HIP graph",
+                        f"({len(launches)} per step), 16 KiB per workgroup, HIP graph",
             "us_per_step": ms * 1e3, "gbs_on_step_bytes": step_bytes / ms / 1e6,
             "frac_hbm": step_bytes / ms / 1e6 / HBM_PEAK_GBS}
 
@@ -657,7 +687,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--traffic-summary", nargs=4, metavar="CSV")
+    ap.add_argument("--traffic-summary", nargs=6, metavar="CSV",
+                    help="decode read, write, FETCH_SIZE CSVs, then the copy's three")
     ap.add_argument("--counters", choices=sorted(COUNTER_WORKLOADS),
                     help="run one workload's launches three times, untimed (for counter passes)")
     args = ap.parse_args()
@@ -722,7 +753,7 @@ def main():
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     if not args.per_matrix:
         roofline["per_kernel"] = per_kernel_rates(torch, rz, launches, args.steps)
-    floor = step_read_floor(torch, launches, step_bytes, args.steps, cus)
+    floor = step_read_floor(torch, launches, step_bytes, args.steps)
     roofline["step_read_floor_us"] = round(floor["us_per_step"], 2)
     roofline["frac_of_step_read_floor"] = round(floor["us_per_step"] / (ms_step * 1e3), 4)
     log(f"decode: read floor {floor['us_per_step']:.1f} us/step; per kernel "

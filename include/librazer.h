@@ -68,14 +68,25 @@
 extern "C" {
 #endif
 
+/* The two enums below carry range markers so that every 32-bit value a C
+ * caller may pass is a valid value of the type (the library rejects the ones
+ * that are not a listed constant). */
 typedef enum razer_status {
   RAZER_OK = 0,
   RAZER_E_INVALID = 1,     /* bad argument: null pointer, shape, alignment, offsets, workspace */
   RAZER_E_UNSUPPORTED = 2, /* valid but not implemented (dtype/kind/shape combination) */
-  RAZER_E_HIP = 3          /* the HIP runtime refused a launch */
+  RAZER_E_HIP = 3,         /* the HIP runtime refused a launch */
+  RAZER_STATUS_RANGE_MIN_ = -0x7FFFFFFF - 1,
+  RAZER_STATUS_RANGE_MAX_ = 0x7FFFFFFF
 } razer_status;
 
-typedef enum razer_dtype { RAZER_F32 = 0, RAZER_F16 = 1, RAZER_BF16 = 2 } razer_dtype;
+typedef enum razer_dtype {
+  RAZER_F32 = 0,
+  RAZER_F16 = 1,
+  RAZER_BF16 = 2,
+  RAZER_DTYPE_RANGE_MIN_ = -0x7FFFFFFF - 1,
+  RAZER_DTYPE_RANGE_MAX_ = 0x7FFFFFFF
+} razer_dtype;
 
 /* Which scale format and candidate set a packed tensor uses ([notes] Key
  * design 1: weights free 2 scale bits, activations 1). */

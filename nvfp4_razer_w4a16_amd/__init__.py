@@ -117,6 +117,11 @@ def _check_device(t: torch.Tensor, device: torch.device, name: str):
         raise ValueError(f"{name} must be on {device}, not {t.device}")
 
 
+def _same_device(dev: torch.device, want: torch.device, name: str):
+    if dev != want:
+        raise ValueError(f"{name} must be on {want}, not {dev}")
+
+
 def _check_buffer(t: torch.Tensor, shape, device: torch.device, name: str, dtype=None):
     """A caller-supplied output or workspace: the C ABI cannot see its size, so
     shape, dtype, device and contiguity are checked here, before any launch."""
@@ -227,7 +232,7 @@ def _quantize(fn, op, kind, x, offsets, flags, out, workspace, stream, block, sc
     elif (out.rows, out.cols) != (rows, cols):
         raise ValueError(f"out is {out.rows}x{out.cols}, the input {rows}x{cols}")
     else:
-        _check_device(out.check("out"), x.device, "out")
+        _same_device(out.check("out"), x.device, "out")
     s = out.struct()
     ws, wsb = _workspace(op, rows, 0, cols, x.device, workspace)
     _check(fn(ctypes.c_void_p(x.data_ptr()), _dtype_code(x.dtype), ctypes.byref(s),
@@ -306,7 +311,7 @@ def razer_gemv_group(x: torch.Tensor, ws, out_dtype: torch.dtype | None = None, 
         raise ValueError(f"1..{RAZER_GEMV_GROUP_MAX} weights")
     dev = ws[0].check("ws[0]")
     for i, w in enumerate(ws):
-        _check_device(w.check(f"ws[{i}]"), dev, f"ws[{i}]")
+        _same_device(w.check(f"ws[{i}]"), dev, f"ws[{i}]")
     _check_input(x, dev, "x")
     x = x.contiguous()
     if any(w.cols != x.numel() for w in ws):
@@ -389,7 +394,7 @@ def razer_gemm_w4a4(x: PackedTensor, w: PackedTensor, out_dtype: torch.dtype = t
     if x.cols != w.cols:
         raise ValueError("x and w must have the same K")
     dev = x.check("x")
-    _check_device(w.check("w"), dev, "w")
+    _same_device(w.check("w"), dev, "w")
     if out is None:
         out = torch.empty((x.rows, w.rows), dtype=out_dtype, device=dev)
     else:

@@ -4,8 +4,9 @@
 // They give the two practical ceilings the product kernels are compared with
 // on this part, measured live in the same run:
 //   rzc_read       a plain one-pass read of up to four buffers (the bytes of
-//                  one GEMV launch: codes and scales of each weight), 16-byte
-//                  non-temporal loads, nothing computed;
+//                  one GEMV launch: codes and scales of each weight), 16 KiB
+//                  per workgroup in 16-byte non-temporal loads, nothing
+//                  computed;
 //   rzc_mfma_loop  v_mfma_f32_32x32x16_bf16 on register operands only (random
 //                  bf16 values), two waves per SIMD on every CU, as the
 //                  prefill product runs its matrix units.
@@ -26,10 +27,12 @@ struct ReadArgs {
   uint32_t* sink;
 };
 
-// Chunk c of the concatenated buffers; each thread keeps four loads in flight.
+// Workgroup w reads 16 KiB tile w of the concatenated buffers (4 x 16 bytes
+// per thread, each load one contiguous 4 KiB wave access), once.
+constexpr int kTileChunks = 1024;  // 16-byte chunks per 16 KiB tile
+
 __global__ __launch_bounds__(256) void read_kernel(ReadArgs a) {
   const int64_t total = a.end[a.count - 1];
-  const int64_t stride = (int64_t)gridDim.x * 256;
   uint32_t acc = 0u;
   auto load = [&](int64_t c) -> u32x4_t {
     int b = 0;
@@ -39,16 +42,15 @@ __global__ __launch_bounds__(256) void read_kernel(ReadArgs a) {
     const int64_t off = c - (b ? a.end[b - 1] : 0);
     return __builtin_nontemporal_load(a.p[b] + off);
   };
-  for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < total; c += 4 * stride) {
-    u32x4_t v[4];
+  const int64_t c0 = (int64_t)blockIdx.x * kTileChunks + threadIdx.x;
+  u32x4_t v[4];
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const int64_t cj = c + j * stride;
-      v[j] = cj < total ? load(cj) : (u32x4_t){0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int j = 0; j < 4; j++) acc ^= v[j][0] ^ v[j][1] ^ v[j][2] ^ v[j][3];
+  for (int j = 0; j < 4; j++) {
+    const int64_t cj = c0 + j * 256;
+    v[j] = cj < total ? load(cj) : (u32x4_t){0u, 0u, 0u, 0u};
   }
+#pragma unroll
+  for (int j = 0; j < 4; j++) acc ^= v[j][0] ^ v[j][1] ^ v[j][2] ^ v[j][3];
   if (acc == 0x9E3779B9u) a.sink[0] = acc;  // keeps the loads; practically never taken
 }
 
@@ -98,10 +100,11 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(int64_t iters, float* si
 extern "C" {
 
 // Read each of the count (1..4) device buffers p[i] of n[i] bytes (16-byte
-// aligned, n[i] % 16 == 0) once; grid = workgroups of 256 threads.  sink: a
-// device word that is written only in a case that does not occur in practice.
-int rzc_read(const void* const* p, const int64_t* n, int count, uint32_t* sink, int grid, void* stream) {
-  if (count < 1 || count > 4 || grid < 1) return 1;
+// aligned, n[i] % 16 == 0) once, one 256-thread workgroup per 16 KiB.  sink:
+// a device word that is written only in a case that does not occur in
+// practice.
+int rzc_read(const void* const* p, const int64_t* n, int count, uint32_t* sink, void* stream) {
+  if (count < 1 || count > 4) return 1;
   ReadArgs a = {};
   int64_t run = 0;
   for (int i = 0; i < count; i++) {
@@ -114,6 +117,7 @@ int rzc_read(const void* const* p, const int64_t* n, int count, uint32_t* sink, 
   a.count = count;
   a.sink = sink;
   if (run == 0) return 0;
+  const int64_t grid = (run + kTileChunks - 1) / kTileChunks;
   hipLaunchKernelGGL(read_kernel, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, a);
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }

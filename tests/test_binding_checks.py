@@ -50,30 +50,30 @@ def test_mismatched_outputs_raise_and_enqueue_nothing():
     x = torch.randn(512, generator=g).to(torch.float16).to(dev)
     torch.cuda.synchronize()
     cases = []
-    y = _sentinel(95, torch.float32, dev)  # one element short
-    cases.append((lambda: rz.razer_gemv(x, w, out=y), y))
+    y = _sentinel((95,), torch.float32, dev)  # one element short
+    cases.append((lambda y=y: rz.razer_gemv(x, w, out=y), y))
     y = _sentinel((96, 2), torch.float32, dev)[:, 0]  # not contiguous
-    cases.append((lambda: rz.razer_gemv(x, w, out=y), y))
-    y = _sentinel(96, torch.float64, dev)  # unsupported dtype
-    cases.append((lambda: rz.razer_gemv(x, w, out=y), y))
-    ya, yb = _sentinel(96, torch.float32, dev), _sentinel(64, torch.float16, dev)  # mixed dtypes
-    cases.append((lambda: rz.razer_gemv_group(x, [w, w2], outs=[ya, yb]), ya))
-    ya, yb = _sentinel(96, torch.float32, dev), _sentinel(96, torch.float32, dev)  # second too big
-    cases.append((lambda: rz.razer_gemv_group(x, [w, w2], outs=[ya, yb]), ya))
+    cases.append((lambda y=y: rz.razer_gemv(x, w, out=y), y))
+    y = _sentinel((96,), torch.float64, dev)  # unsupported dtype
+    cases.append((lambda y=y: rz.razer_gemv(x, w, out=y), y))
+    ya, yb = _sentinel((96,), torch.float32, dev), _sentinel((64,), torch.float16, dev)  # mixed dtypes
+    cases.append((lambda ya=ya, yb=yb: rz.razer_gemv_group(x, [w, w2], outs=[ya, yb]), ya))
+    ya, yb = _sentinel((96,), torch.float32, dev), _sentinel((96,), torch.float32, dev)  # second too big
+    cases.append((lambda ya=ya, yb=yb: rz.razer_gemv_group(x, [w, w2], outs=[ya, yb]), ya))
     xm = torch.randn(4, 512, generator=g).to(torch.bfloat16).to(dev)
     y = _sentinel((4, 95), torch.float32, dev)
-    cases.append((lambda: rz.razer_gemm(xm, w, out=y), y))
+    cases.append((lambda y=y: rz.razer_gemm(xm, w, out=y), y))
     y = _sentinel((96, 256), torch.float32, dev)
-    cases.append((lambda: rz.razer_dequant(w, out=y), y))
+    cases.append((lambda y=y: rz.razer_dequant(w, out=y), y))
     # an encoder output larger than the input: its loads would run past x
     big = rz.PackedTensor(rz.RAZER_WEIGHT, 128, 512, (-2, 4), dev)
     big.codes.fill_(0x55)
     cases.append((lambda: rz.razer_quantize_weight(wf, out=big), big.codes))
-    y = _sentinel(15, torch.float32, dev)
-    cases.append((lambda: rz.razer_weight_offset_sse(wf, out=y), y))
+    y = _sentinel((15,), torch.float32, dev)
+    cases.append((lambda y=y: rz.razer_weight_offset_sse(wf, out=y), y))
     xq = rz.razer_quantize_act(xm)
     y = _sentinel((4, 97), torch.float32, dev)
-    cases.append((lambda: rz.razer_gemm_w4a4(xq, w, out=y), y))
+    cases.append((lambda y=y: rz.razer_gemm_w4a4(xq, w, out=y), y))
     torch.cuda.synchronize()
     for i, (call, buf) in enumerate(cases):
         before = buf.clone()
