@@ -44,7 +44,8 @@
  *   - Pointers marked "device" point to GPU memory on the current HIP device.
  *     The caller allocates and frees every buffer, including workspaces; the
  *     library never allocates, frees or synchronises, and keeps no mutable
- *     global state.
+ *     global state, except the 4 KiB per-device scratch array of
+ *     razer_quantize_act_noalloc.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
  *     work is enqueued on it, asynchronously, in stream order.
  *   - Host-side argument checks are synchronous: on RAZER_E_INVALID or
@@ -171,6 +172,21 @@ razer_status razer_quantize_weight(const void* w, razer_dtype w_dt, const razer_
  * F16 or BF16 (F32 also accepted).  out->kind must be RAZER_ACT. */
 razer_status razer_quantize_act(const void* x, razer_dtype x_dt, const razer_packed* out,
                                 void* ws, size_t ws_bytes, void* stream);
+
+/* razer_quantize_act without a workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Same arguments (minus ws / ws_bytes), checks and
+ * output bytes as razer_quantize_act.  The amax partials live in a 4 KiB
+ * static device array that the library holds on each device it runs on until
+ * the process ends; the first call on a device resolves that array's address
+ * (hipGetSymbolAddress), so make it outside stream capture.  Every call on one
+ * device shares the array: calls that overlap on one device (different
+ * streams, concurrent graph launches) race and must be ordered by the caller.
+ * The array is large enough for every input size (the partials never exceed
+ * it); RAZER_E_UNSUPPORTED would report a build where they did.  Allocates
+ * nothing, frees nothing, synchronises nothing. */
+razer_status razer_quantize_act_noalloc(const void* x, razer_dtype x_dt, const razer_packed* out,
+                                        void* stream);
 
 /* Decode a packed tensor ([notes] Key design 3 decoder): out[r, c] =
  * value(code) * sb * st, with value(0b1000) = (bit7 ? -1 : 1) * (6 + off/2).

@@ -30,7 +30,7 @@ RAZER_OP_QUANTIZE_WEIGHT, RAZER_OP_QUANTIZE_ACT, RAZER_OP_GEMV, RAZER_OP_GEMM = 
 RAZER_OP_OFFSET_SEARCH, RAZER_OP_GEMM_W4A4 = 4, 5
 SECOND_PAIR_OFFSETS = tuple(range(-7, 8))  # entry i of razer_weight_offset_sse is offset i - 7
 
-EXPORTED = ("razer_quantize_weight", "razer_quantize_act", "razer_dequant", "razer_gemv",
+EXPORTED = ("razer_quantize_weight", "razer_quantize_act", "razer_quantize_act_noalloc", "razer_dequant", "razer_gemv",
             "razer_gemv_group", "razer_gemm", "razer_gemm_w4a4", "razer_weight_offset_sse", "razer_workspace_bytes",
             "razer_status_string")
 
@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
         for name in ("razer_quantize_weight", "razer_quantize_act"):
             f = getattr(L, name)
             f.restype, f.argtypes = i32, [vp, i32, P, vp, sz, vp]
+        L.razer_quantize_act_noalloc.restype = i32
+        L.razer_quantize_act_noalloc.argtypes = [vp, i32, P, vp]
         L.razer_dequant.restype, L.razer_dequant.argtypes = i32, [P, vp, i32, vp]
         L.razer_gemv.restype, L.razer_gemv.argtypes = i32, [vp, i32, P, vp, i32, vp, sz, vp]
         L.razer_gemv_group.restype = i32
@@ -262,6 +264,26 @@ def razer_quantize_act(x: torch.Tensor, offsets=DEFAULT_ACT_OFFSETS, remap: bool
     return _quantize(lib().razer_quantize_act, RAZER_OP_QUANTIZE_ACT, RAZER_ACT, x, offsets,
                      _encoder_flags(remap, four_over_six), out, workspace, stream, block,
                      RAZER_SCALE_BYTE)
+
+
+def razer_quantize_act_noalloc(x: torch.Tensor, out: PackedTensor, stream=None):
+    """razer_quantize_act into a caller-allocated `out` without a workspace
+    (the library's per-device static scratch holds the partials): for code
+    that cannot allocate, e.g. under graph capture.  Calls that overlap on one
+    device race on that scratch."""
+    if x.dim() != 2:
+        raise ValueError("expected a 2-D tensor")
+    _check_input(x, x.device, "x")
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous (a copy would allocate)")
+    if (out.rows, out.cols) != tuple(x.shape):
+        raise ValueError(f"out is {out.rows}x{out.cols}, the input {tuple(x.shape)}")
+    _same_device(out.check("out"), x.device, "out")
+    s = out.struct()
+    _check(lib().razer_quantize_act_noalloc(ctypes.c_void_p(x.data_ptr()), _dtype_code(x.dtype),
+                                            ctypes.byref(s), ctypes.c_void_p(_stream(stream))),
+           "razer_quantize_act_noalloc")
+    return out
 
 
 def razer_dequant(t: PackedTensor, dtype: torch.dtype = torch.float32, out=None, stream=None):

@@ -24,6 +24,8 @@ hipError_t counted() {
 namespace rz {
 size_t quantize_ws_bytes() { return kAmaxMaxPartials * sizeof(uint32_t); }
 hipError_t launch_quantize(const void*, int, const PackedView&, void*, hipStream_t) { return counted(); }
+size_t noalloc_scratch_bytes() { return 4096; }
+hipError_t launch_quantize_noalloc(const void*, int, const PackedView&, hipStream_t) { return counted(); }
 size_t offset_search_ws_bytes(int64_t n) { return 4096 + (size_t)(n > 0 ? 1024 : 0) * 15 * 8; }
 hipError_t launch_offset_search(const void*, int, int64_t, int64_t, int, double*, void*, hipStream_t) {
   return counted();
@@ -101,6 +103,8 @@ int main() {
   expect(razer_quantize_weight(x, RAZER_F32, nullptr, ws, big, nullptr), RAZER_E_INVALID, "null out");
   expect(razer_quantize_weight(x, RAZER_F32, &a, ws, big, nullptr), RAZER_E_INVALID, "wrong kind");
   expect(razer_quantize_act(x, RAZER_BF16, &a, ws, big, nullptr), RAZER_OK, "quantize_act ok");
+  expect(razer_quantize_act_noalloc(x, RAZER_BF16, &a, nullptr), RAZER_OK, "noalloc ok");
+  expect(razer_quantize_act_noalloc(x, RAZER_BF16, &w, nullptr), RAZER_E_INVALID, "noalloc wrong kind");
   {
     razer_packed bad = w;
     bad.sv_off_half[1] = 8;
@@ -169,8 +173,8 @@ int main() {
     if (!razer_status_string((razer_status)s)) g_fail = 1;
   for (int op = -1; op < 8; op++) (void)razer_workspace_bytes(op, 4, 64, 256);
   (void)razer_workspace_bytes(RAZER_OP_OFFSET_SEARCH, 0, -1, 16);
-  if (g_launches != 8) {
-    fprintf(stderr, "host_check: %d launches reached, want 8\n", g_launches);
+  if (g_launches != 9) {
+    fprintf(stderr, "host_check: %d launches reached, want 9\n", g_launches);
     g_fail = 1;
   }
   printf("host_check: %s (%d launches)\n", g_fail ? "FAILED" : "ok", g_launches);

@@ -116,6 +116,18 @@ razer_status razer_quantize_act(const void* x, razer_dtype x_dt, const razer_pac
   return quantize_common(x, x_dt, out, ws, ws_bytes, stream, RAZER_ACT);
 }
 
+razer_status razer_quantize_act_noalloc(const void* x, razer_dtype x_dt, const razer_packed* out,
+                                        void* stream) {
+  razer_status s = check_packed(out, true);
+  if (s != RAZER_OK) return s;
+  if (out->flags & ~(uint32_t)(RAZER_FLAG_NO_REMAP | RAZER_FLAG_FOUR_OVER_SIX)) return RAZER_E_INVALID;
+  if (out->kind != RAZER_ACT || !dtype_ok(x_dt)) return RAZER_E_INVALID;
+  const int64_t n = out->rows * out->cols;
+  if (n > 0 && (!x || !aligned(x, 16))) return RAZER_E_INVALID;
+  if (rz::quantize_ws_bytes() > rz::noalloc_scratch_bytes()) return RAZER_E_UNSUPPORTED;
+  return status_of(rz::launch_quantize_noalloc(x, x_dt, view_of(out), (hipStream_t)stream));
+}
+
 razer_status razer_dequant(const razer_packed* t, void* out, razer_dtype out_dt, void* stream) {
   razer_status s = check_packed(t, true);
   if (s != RAZER_OK) return s;

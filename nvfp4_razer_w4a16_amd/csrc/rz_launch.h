@@ -38,6 +38,9 @@ constexpr int kAmaxMaxPartials = 1024;
 size_t quantize_ws_bytes();
 hipError_t launch_quantize(const void* x, int dtype, const PackedView& out, void* ws,
                            hipStream_t stream);
+// The same with the partials in a static per-device array (no workspace).
+size_t noalloc_scratch_bytes();
+hipError_t launch_quantize_noalloc(const void* x, int dtype, const PackedView& out, hipStream_t stream);
 
 // Second-pair offset search: sse[o + 7] = total fp64 squared error of the
 // weight tensor encoded with offsets (off0, o), o = -7..7.

@@ -37,6 +37,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 namespace rz {
 
 Candidate make_candidate(int off_half) {
@@ -1068,6 +1070,58 @@ hipError_t launch_quantize(const void* x, int dtype, const PackedView& out, void
   if (dtype == kF32) return run_quantize<kAct>((const float*)x, out, partial, stream);
   if (dtype == kF16) return run_quantize<kAct>((const _Float16*)x, out, partial, stream);
   return run_quantize<kAct>((const __bf16*)x, out, partial, stream);
+}
+
+// ---- allocation-free activation encoder ---------------------------------------
+// For callers that cannot allocate (code under HIP graph capture, tight
+// serving loops): the amax partials live in a file-scope device array instead
+// of a caller workspace.  Each device holds its own copy for the life of the
+// process; host code uses the address hipGetSymbolAddress returns for the
+// current device (the array's name is only a host-side stand-in).  Every call
+// on one device shares that copy, so calls that overlap on one device race.
+// Pass 1 writes every partial that pass 2 reads, so nothing needs clearing.
+constexpr size_t kNoAllocScratchBytes = 4096;
+static_assert(kAmaxMaxPartials * sizeof(uint32_t) <= kNoAllocScratchBytes,
+              "the encoder's partials must fit the static scratch");
+
+}  // namespace rz
+
+static __device__ __align__(256) uint8_t scratch[rz::kNoAllocScratchBytes];
+
+namespace rz {
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+size_t noalloc_scratch_bytes() { return kNoAllocScratchBytes; }
+
+// The current device's copy of the scratch array, resolved once per device.
+hipError_t noalloc_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_quantize_noalloc(const void* x, int dtype, const PackedView& out, hipStream_t stream) {
+  if (quantize_ws_bytes() > kNoAllocScratchBytes) return hipErrorInvalidValue;
+  void* ws = nullptr;
+  const hipError_t e = noalloc_scratch(&ws);
+  if (e != hipSuccess) return e;
+  return launch_quantize(x, dtype, out, ws, stream);
 }
 
 }  // namespace rz
