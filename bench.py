@@ -495,13 +495,46 @@ def bench_rows(torch, rz, synth, args, decode_base):
             t = GraphTimer(torch, lambda: [rz.razer_gemm(x, mm, out=y, workspace=wsp) for mm in mats])
             ms = t.time(5) / len(mats)
             byts = packed_bytes(n, k) + m * k * 2 + m * n * 2
+            # the same launches with the untrimmed plan (every CU, the most K splits)
+            umats = [mm.with_flags(rz.RAZER_FLAG_UNTRIMMED_PLAN) for mm in mats]
+            wsu = torch.empty(max(1, rz.razer_workspace_bytes(rz.RAZER_OP_GEMM_UNTRIMMED, m, n, k)),
+                              dtype=torch.uint8, device=dev)
+            tu = GraphTimer(torch, lambda: [rz.razer_gemm(x, mm, out=y, workspace=wsu) for mm in umats])
+            ms_u = tu.time(5) / len(mats)
             sweep[f"{n}x{k}_m{m}"] = {"us": ms * 1e3, "gbs": byts / ms / 1e6,
                                       "frac_hbm": byts / ms / 1e6 / HBM_PEAK_GBS,
-                                      "tflops": 2.0 * m * n * k / ms / 1e9}
-            del t
+                                      "tflops": 2.0 * m * n * k / ms / 1e9,
+                                      "untrimmed_us": ms_u * 1e3,
+                                      "plan_gain_pct": 100.0 * (ms_u - ms) / ms_u}
+            del t, tu, umats, wsu
         del mats, base
         torch.cuda.empty_cache()
     rows["gemm_small_batch"] = sweep
+
+    # the same sweep on the pages' kernel layout (128-element blocks, FP16
+    # scales with the metadata in the sign and top exponent bits), 28672 x 8192
+    n, k = 28672, 8192
+    w = torch.from_numpy(synth.small_batch_weight(n, k)).to(dev)
+    base = rz.razer_quantize_weight(w, (-2, 4), block=128, scale_fmt=rz.RAZER_SCALE_F16)
+    del w
+    pbytes = packed_bytes(n, k, 128, 2)
+    mats = [base] + [clone_packed(rz, base) for _ in range(max(1, int(640e6 // pbytes)) - 1)]
+    sweep = {}
+    for m in synth.SMALL_BATCH_M:
+        x = synth.small_batch_x(m, k).to(dev)
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        wsp = torch.empty(max(1, rz.razer_workspace_bytes(rz.RAZER_OP_GEMM, m, n, k)), dtype=torch.uint8,
+                          device=dev)
+        t = GraphTimer(torch, lambda: [rz.razer_gemm(x, mm, out=y, workspace=wsp) for mm in mats])
+        ms = t.time(5) / len(mats)
+        byts = pbytes + m * k * 2 + m * n * 2
+        sweep[f"{n}x{k}_m{m}"] = {"us": ms * 1e3, "gbs": byts / ms / 1e6,
+                                  "frac_hbm": byts / ms / 1e6 / HBM_PEAK_GBS,
+                                  "tflops": 2.0 * m * n * k / ms / 1e9}
+        del t
+    del mats, base
+    torch.cuda.empty_cache()
+    rows["gemm_small_batch_g128_f16"] = sweep
 
     # prefill GEMM M=2048, N=28672, K=8192 (+ its offline weight encode)
     w = torch.from_numpy(synth.prefill_weight()).to(dev)
@@ -547,6 +580,7 @@ def bench_rows(torch, rz, synth, args, decode_base):
                     w, (-2, 4), four_over_six=True, block=block, scale_fmt=sfmt)),
                 "razer_pairs_-2_4": rel_sse(torch, rz, w, pv)}}
         del t, pv
+    wg = rz.razer_quantize_weight(w, (-2, 4), block=128, scale_fmt=rz.RAZER_SCALE_F16)  # prefill, pages' layout
     del w, wso, wf
     torch.cuda.empty_cache()
     xa = synth.act_quant_x().to(dev)
@@ -578,6 +612,12 @@ def bench_rows(torch, rz, synth, args, decode_base):
     rows["gemm_prefill"] = {
         "workload": "x [2048,8192] bf16 x W [28672,8192] RaZeR-W4 (0.015*t(4)) -> bf16",
         "ms": ms, "tflops": flops / ms / 1e9, "frac_mfma": flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS}
+    t = GraphTimer(torch, lambda: rz.razer_gemm(x, wg, out=y))
+    ms = t.time(10)
+    rows["gemm_prefill_g128_f16"] = {
+        "workload": "the prefill product with W in 128-element blocks and FP16 scales",
+        "ms": ms, "tflops": flops / ms / 1e9, "frac_mfma": flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS}
+    del wg, t
     n_el = 28672 * 8192
     rows["offset_search_prefill"] = off_row
     rows["four_over_six_prefill"] = fos_row
@@ -781,7 +821,16 @@ def main():
         del steps_g, l3
         torch.cuda.empty_cache()
         log("rows: encoders, small-batch sweep, prefill ...")
+        # the same grouped step with the untrimmed launch plan (every CU, the most
+        # K splits, one row quad per wave): what the per-shape launch sizing gains
+        lu = [(x, [w.with_flags(rz.RAZER_FLAG_UNTRIMMED_PLAN) for w in ws], ys) for x, ws, ys in launches]
+        ms_u = GraphTimer(torch, lambda: run_launches(rz, lu), warmup=1).time(args.steps)
+        decode_untrimmed = {"workload": "the same decode step with the untrimmed launch plan",
+                            "us_per_step": ms_u * 1e3, "gbs": step_bytes / ms_u / 1e6,
+                            "plan_gain_pct": 100.0 * (ms_u - ms_step) / ms_u}
+        del lu
         rows = {f"decode_{other}": decode_other, "decode_g128_f16": decode_g128,
+                "decode_untrimmed_plan": decode_untrimmed,
                 "decode_step_read_floor": floor, "mfma_loop_ceiling": mfma_loop_ceiling(torch, cus)}
         rows.update(bench_rows(torch, rz, synth, args, base))
         pf, ml = rows["gemm_prefill"], rows["mfma_loop_ceiling"]

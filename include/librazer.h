@@ -110,7 +110,17 @@ enum {
    * tensor scale and the packed layout are unchanged, so every decoding call
    * reads such a tensor as plain NVFP4.  Takes precedence over NO_REMAP.
    * The quantize calls reject any other flag bit with RAZER_E_INVALID. */
-  RAZER_FLAG_FOUR_OVER_SIX = 2u
+  RAZER_FLAG_FOUR_OVER_SIX = 2u,
+  /* Read by the product calls only (the encoders reject it): launch the
+   * product with the untrimmed plan -- the K range split over the most waves
+   * or workgroups the kernel allows and the fewest rows per wave, so every CU
+   * gets work however small the matrix -- instead of the launch plan sized
+   * per shape.  For measuring what the launch sizing gains: the counterpart
+   * of the pages' adaptive trimming of SM launches for small matrices ([notes]
+   * Key design 3).  Outputs agree within the product tolerance (the
+   * summation order changes).  razer_gemm then needs
+   * razer_workspace_bytes(RAZER_OP_GEMM_UNTRIMMED, ...). */
+  RAZER_FLAG_UNTRIMMED_PLAN = 4u
 };
 
 /* Block-scale storage of a packed tensor (razer_packed.scale_fmt). */
@@ -129,7 +139,7 @@ enum {
 
 typedef struct razer_packed {
   int32_t kind;          /* razer_kind */
-  uint32_t flags;        /* RAZER_FLAG_* (read by the encoder only) */
+  uint32_t flags;        /* RAZER_FLAG_* (encoder flags; RAZER_FLAG_UNTRIMMED_PLAN for products) */
   int64_t rows;          /* >= 0 */
   int64_t cols;          /* >= 0, multiple of the block size */
   int8_t sv_off_half[2]; /* special-value offsets in units of 0.5, each in [-7, 7];
@@ -144,9 +154,10 @@ typedef struct razer_packed {
 } razer_packed;
 /* The encoders and razer_dequant take every layout.  The product calls take
  * 16-element blocks with byte scales; razer_gemv, razer_gemv_group (all
- * members in one layout) and razer_gemm with m == 1 also take the pages'
- * kernel layout, 128-element blocks (block_log2 7) with RAZER_SCALE_F16.
- * Other layouts return RAZER_E_UNSUPPORTED. */
+ * members in one layout) and razer_gemm (any m) also take the pages' kernel
+ * layout, 128-element blocks (block_log2 7) with RAZER_SCALE_F16.  Other
+ * layouts, and any layout but the default for razer_gemm_w4a4, return
+ * RAZER_E_UNSUPPORTED. */
 
 /* Operation ids for razer_workspace_bytes. */
 enum {
@@ -155,7 +166,8 @@ enum {
   RAZER_OP_GEMV = 2,
   RAZER_OP_GEMM = 3,
   RAZER_OP_OFFSET_SEARCH = 4, /* n = rows, k = cols of the weight */
-  RAZER_OP_GEMM_W4A4 = 5      /* m = rows of x, n = rows of w, k = cols */
+  RAZER_OP_GEMM_W4A4 = 5,     /* m = rows of x, n = rows of w, k = cols */
+  RAZER_OP_GEMM_UNTRIMMED = 6 /* razer_gemm of a weight with RAZER_FLAG_UNTRIMMED_PLAN */
 };
 
 /* Offline weight encoder: 4-candidate block-MSE search ([notes] Key design 2:
@@ -225,8 +237,10 @@ razer_status razer_gemv_group(const void* x, razer_dtype x_dt, const razer_packe
 /* Batched W4A16 product y[M, N] = x[M, K] * W^T ([notes] Key design 3;
  * [summary] §2.3: weight-only GEMM kernels for small and large batches).
  * x: device [m, K] row-major in F16 or BF16.  w: packed tensor [N, K] of either
- * kind.  y: device [m, N] in F32, F16 or BF16.  m >= 1; m == 1 runs the GEMV path.  ws: at least
- * razer_workspace_bytes(RAZER_OP_GEMM, m, N, K) bytes. */
+ * kind, default layout or 128-element blocks with FP16 scales.  y: device
+ * [m, N] in F32, F16 or BF16.  m >= 1; m == 1 runs the GEMV path.  ws: at least
+ * razer_workspace_bytes(RAZER_OP_GEMM, m, N, K) bytes (enough for either
+ * layout). */
 razer_status razer_gemm(const void* x, razer_dtype x_dt, int64_t m, const razer_packed* w, void* y,
                         razer_dtype y_dt, void* ws, size_t ws_bytes, void* stream);
 

@@ -23,11 +23,11 @@ LIB_PATH = os.path.join(_HERE, "librazer.so")
 RAZER_OK, RAZER_E_INVALID, RAZER_E_UNSUPPORTED, RAZER_E_HIP = 0, 1, 2, 3
 RAZER_F32, RAZER_F16, RAZER_BF16 = 0, 1, 2
 RAZER_WEIGHT, RAZER_ACT = 0, 1
-RAZER_FLAG_NO_REMAP, RAZER_FLAG_FOUR_OVER_SIX = 1, 2
+RAZER_FLAG_NO_REMAP, RAZER_FLAG_FOUR_OVER_SIX, RAZER_FLAG_UNTRIMMED_PLAN = 1, 2, 4
 RAZER_SCALE_BYTE, RAZER_SCALE_F16 = 0, 1
 BLOCK_SIZES = (16, 32, 64, 128)
 RAZER_OP_QUANTIZE_WEIGHT, RAZER_OP_QUANTIZE_ACT, RAZER_OP_GEMV, RAZER_OP_GEMM = 0, 1, 2, 3
-RAZER_OP_OFFSET_SEARCH, RAZER_OP_GEMM_W4A4 = 4, 5
+RAZER_OP_OFFSET_SEARCH, RAZER_OP_GEMM_W4A4, RAZER_OP_GEMM_UNTRIMMED = 4, 5, 6
 SECOND_PAIR_OFFSETS = tuple(range(-7, 8))  # entry i of razer_weight_offset_sse is offset i - 7
 
 EXPORTED = ("razer_quantize_weight", "razer_quantize_act", "razer_quantize_act_noalloc", "razer_dequant", "razer_gemv",
@@ -189,6 +189,14 @@ class PackedTensor:
     @property
     def device(self) -> torch.device:
         return self.codes.device
+
+    def with_flags(self, flags: int) -> "PackedTensor":
+        """The same tensor (buffers shared) with other descriptor flags, e.g.
+        RAZER_FLAG_UNTRIMMED_PLAN for the products."""
+        q = PackedTensor.__new__(PackedTensor)
+        q.__dict__.update(self.__dict__)
+        q.flags = flags
+        return q
 
     def check(self, name: str = "packed tensor"):
         """Its buffers still match its shape and layout (they are plain
@@ -372,7 +380,8 @@ def razer_gemm(x: torch.Tensor, w: PackedTensor, out_dtype: torch.dtype | None =
         out = torch.empty((m, w.rows), dtype=out_dtype or x.dtype, device=x.device)
     else:
         _check_buffer(out, (m, w.rows), dev, "out")
-    ws, wsb = _workspace(RAZER_OP_GEMM, m, w.rows, w.cols, x.device, workspace)
+    op = RAZER_OP_GEMM_UNTRIMMED if w.flags & RAZER_FLAG_UNTRIMMED_PLAN else RAZER_OP_GEMM
+    ws, wsb = _workspace(op, m, w.rows, w.cols, x.device, workspace)
     s = w.struct()
     _check(lib().razer_gemm(ctypes.c_void_p(x.data_ptr()), _dtype_code(x.dtype), m, ctypes.byref(s),
                             ctypes.c_void_p(out.data_ptr()), _dtype_code(out.dtype),

@@ -55,6 +55,7 @@ hipError_t launch_smallm(const void*, int, int64_t, const PackedView&, void*, in
   return counted();
 }
 size_t gemm_ws_bytes(int64_t m, int64_t n, int64_t) { return (size_t)(4 * m * n * 4); }
+size_t gemm_ws_need(int64_t m, int64_t n, int64_t k, bool, bool) { return gemm_ws_bytes(m, n, k); }
 hipError_t launch_gemm(const void*, int, int64_t, const PackedView&, void*, int, void*, size_t, hipStream_t) {
   return counted();
 }

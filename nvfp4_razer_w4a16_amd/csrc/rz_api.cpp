@@ -73,11 +73,12 @@ rz::PackedView view_of(const razer_packed* p) {
   return v;
 }
 
-static_assert(RAZER_FLAG_NO_REMAP == rz::kFlagNoRemap && RAZER_FLAG_FOUR_OVER_SIX == rz::kFlagFourOverSix,
-              "encoder flag values");
+static_assert(RAZER_FLAG_NO_REMAP == rz::kFlagNoRemap && RAZER_FLAG_FOUR_OVER_SIX == rz::kFlagFourOverSix &&
+                  RAZER_FLAG_UNTRIMMED_PLAN == rz::kFlagUntrimmed,
+              "flag values");
 
-// The product kernels read 16-element blocks with byte scales; the GEMV also
-// reads 128-element blocks with FP16 scales.
+// The product kernels read 16-element blocks with byte scales; the GEMV and
+// razer_gemm also read 128-element blocks with FP16 scales.
 bool product_layout(const razer_packed* p) {
   return (p->block_log2 == 0 || p->block_log2 == 4) && p->scale_fmt == RAZER_SCALE_BYTE;
 }
@@ -179,14 +180,15 @@ razer_status razer_gemm(const void* x, razer_dtype x_dt, int64_t m, const razer_
   razer_status s = check_packed(w, true);
   if (s != RAZER_OK) return s;
   if (!dtype_ok(x_dt) || !dtype_ok(y_dt) || m < 0) return RAZER_E_INVALID;
-  if (x_dt == RAZER_F32 || !(m == 1 ? gemv_layout(w) : product_layout(w))) return RAZER_E_UNSUPPORTED;
+  if (x_dt == RAZER_F32 || !gemv_layout(w)) return RAZER_E_UNSUPPORTED;
   if (m == 0 || w->rows == 0) return RAZER_OK;
   if (m == 1) return razer_gemv(x, x_dt, w, y, y_dt, ws, ws_bytes, stream);
   if (!y || !aligned(y, 16)) return RAZER_E_INVALID;
   if (w->cols > 0 && (!x || !aligned(x, 16))) return RAZER_E_INVALID;
   if (m > INT64_MAX / 2 / (w->rows > w->cols ? w->rows : (w->cols ? w->cols : 1)))
     return RAZER_E_INVALID;
-  const size_t need = rz::gemm_ws_bytes(m, w->rows, w->cols);
+  const size_t need = rz::gemm_ws_need(m, w->rows, w->cols, !product_layout(w),
+                                       (w->flags & RAZER_FLAG_UNTRIMMED_PLAN) != 0);
   if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 4))) return RAZER_E_INVALID;
   return status_of(
       rz::launch_gemm(x, x_dt, m, view_of(w), y, y_dt, ws, ws_bytes, (hipStream_t)stream));
@@ -233,6 +235,11 @@ size_t razer_workspace_bytes(int op, int64_t m, int64_t n, int64_t k) {
       return rz::gemv_ws_bytes(n, k);
     case RAZER_OP_GEMM:
       return m <= 1 ? rz::gemv_ws_bytes(n, k) : rz::gemm_ws_bytes(m, n, k);
+    case RAZER_OP_GEMM_UNTRIMMED: {
+      if (m <= 1) return rz::gemv_ws_bytes(n, k);
+      const size_t a = rz::gemm_ws_need(m, n, k, false, true), b = rz::gemm_ws_need(m, n, k, true, true);
+      return a > b ? a : b;
+    }
     case RAZER_OP_GEMM_W4A4:
       return rz::gemm_w4a4_ws_bytes(m, n, k);
     case RAZER_OP_OFFSET_SEARCH:

@@ -55,9 +55,26 @@ __device__ __forceinline__ void decode_block(uint2 cw, uint32_t sbyte, float m0,
   }
 }
 
+// The same for the 128-element FP16-scale layout: the block's scale and
+// special value come from its 16-bit word (metadata in bits 15-14).
+template <typename XT>
+__device__ __forceinline__ void decode_block_f16s(uint2 cw, uint32_t word, float m0, float m1, XT (&out)[16]) {
+  const float sb = scale_of_f16word(word);
+  const float sv = special_of_f16word(word, m0, m1) * sb;
+#pragma unroll
+  for (int j = 0; j < 16; j++) {
+    const uint32_t nib = ((j < 8 ? cw.x : cw.y) >> (4 * (j & 7))) & 15u;
+    const float mag = (float)fp4_mag_x2(nib & 7u) * (0.5f * sb);
+    const float val = (nib == 8u) ? sv : ((nib & 8u) ? -mag : mag);
+    out[j] = from_f32<XT>(val);
+  }
+}
+
 constexpr int kBM = 128, kBN = 128, kBK = 32, kLds = kBK + 8;
 
-template <typename XT, int KIND, typename OT>
+// F16S: weights in the 128-element FP16-scale layout (one 16-bit scale word
+// per 128 elements of a row) instead of 16-element blocks with byte scales.
+template <typename XT, int KIND, typename OT, bool F16S = false>
 __global__ __launch_bounds__(256) void gemm_kernel(const XT* __restrict__ x, int64_t m,
                                                    const uint8_t* __restrict__ codes,
                                                    const uint8_t* __restrict__ scales,
@@ -99,8 +116,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(const XT* __restrict__ x, int
       const int64_t gn = n_base + r;
       if (gn < n && kb < kblocks) {
         const uint2 cw = *(const uint2*)(codes + gn * (k / 2) + kb * 8);
-        const uint32_t sbyte = scales[gn * (k / 16) + kb];
-        decode_block<KIND, XT>(cw, sbyte, m0, m1, vals);
+        if constexpr (F16S) {
+          const uint32_t word = ((const uint16_t*)scales)[gn * (k / 128) + kb / 8];
+          decode_block_f16s<XT>(cw, word, m0, m1, vals);
+        } else {
+          const uint32_t sbyte = scales[gn * (k / 16) + kb];
+          decode_block<KIND, XT>(cw, sbyte, m0, m1, vals);
+        }
       } else {
 #pragma unroll
         for (int j = 0; j < 16; j++) vals[j] = from_f32<XT>(0.0f);
@@ -150,13 +172,22 @@ __global__ __launch_bounds__(256) void gemm_kernel(const XT* __restrict__ x, int
 // unit idle through its own decode and LDS waits).  Per K step each thread
 // prefetches 64 bytes of x and half a weight row (32 elements) into registers
 // while the waves run the step's MFMAs; then it writes the x bytes and the 32
-// decoded values into the other LDS buffer.  LDS rows are padded by 16 bytes
-// so the 16-byte fragment reads of 32 consecutive rows hit distinct banks.
+// decoded values into the other LDS buffer.  The x tile's LDS rows are padded
+// by 16 bytes so the 16-byte fragment reads of 32 consecutive rows hit
+// distinct banks; the decoded weight tile is swizzled instead (see bpos).
 //
 // Decode (per pair of codes): the packed FP4 conversion, an exact multiply by
 // sb, and a bit select that puts the block's SV * sb where the remapped code
 // (converted to -0) sits; see decode_pair_impl.
 constexpr int kTM = 256, kTN = 256, kTK = 64, kTS = kTK + 8;
+// The decoded B tile has unpadded 128-byte rows whose 16-byte chunks are
+// XOR-swizzled by row: chunk c of row r sits at position c ^ ((r >> 1) & 7).
+// Both the decode writes (16 lanes: 8 rows x 2 halves of a row) and the MFMA
+// fragment reads (16 consecutive rows, one chunk) then hit 16 distinct 16-byte
+// bank groups; padded rows (the A tile's layout) left two lanes of each write
+// on one group.
+constexpr int kBS = kTK;
+__device__ __forceinline__ int bpos(int row, int chunk) { return row * kBS + ((chunk ^ ((row >> 1) & 7)) << 3); }
 
 typedef short short2_t __attribute__((ext_vector_type(2)));
 typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
@@ -259,7 +290,10 @@ __device__ __forceinline__ uint32_t decode_one_pair(uint32_t w, int sel, float s
   }
 }
 
-template <typename XT, int KIND, typename OT>
+// F16S: weights in the 128-element FP16-scale layout; a K step of 64 lies in
+// one 128-element block, so one scale word per weight row and step gives both
+// coefficients (computed from the word instead of the table).
+template <typename XT, int KIND, typename OT, bool F16S = false>
 __global__ __launch_bounds__(512) void gemm_tile256_kernel(const XT* __restrict__ x, int64_t m,
                                                       const uint8_t* __restrict__ codes,
                                                       const uint8_t* __restrict__ scales,
@@ -270,7 +304,7 @@ __global__ __launch_bounds__(512) void gemm_tile256_kernel(const XT* __restrict_
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   XT* As = (XT*)smem;
   XT* Bs = As + 2 * kTM * kTS;
-  float2* lut = (float2*)(Bs + 2 * kTN * kTS);
+  float2* lut = (float2*)(Bs + 2 * kTN * kBS);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 2, wn = wave & 3;
   const int64_t ntn = (n + kTN - 1) / kTN;
@@ -302,8 +336,9 @@ __global__ __launch_bounds__(512) void gemm_tile256_kernel(const XT* __restrict_
                                                     (int)(rows_m * k * (int64_t)sizeof(XT)), 0x00020000);
   const Rsrc cr = __builtin_amdgcn_make_buffer_rsrc((void*)(codes + n_base * (k / 2)), (short)0,
                                                     (int)(rows_n * (k / 2)), 0x00020000);
-  const Rsrc sr = __builtin_amdgcn_make_buffer_rsrc((void*)(scales + n_base * (k / 16)), (short)0,
-                                                    (int)(rows_n * (k / 16)), 0x00020000);
+  const int64_t srb = F16S ? k / 64 : k / 16;  // scale bytes per weight row
+  const Rsrc sr = __builtin_amdgcn_make_buffer_rsrc((void*)(scales + n_base * srb), (short)0,
+                                                    (int)(rows_n * srb), 0x00020000);
   int xo[4];
 #pragma unroll
   for (int i = 0; i < 4; i++) {
@@ -312,10 +347,13 @@ __global__ __launch_bounds__(512) void gemm_tile256_kernel(const XT* __restrict_
   }
   const int br = tid >> 1, bh = tid & 1;  // the weight row and half this thread decodes
   const int co = br < rows_n ? (int)((int64_t)br * (k / 2)) + 16 * bh : kOob;
-  const int so = br < rows_n ? (int)((int64_t)br * (k / 16)) : kOob;
+  const int so = br < rows_n ? (int)((int64_t)br * srb) : kOob;
   auto gload = [&](int kt, Stage& r) {
     const int k0 = kt * kTK;
-    r.s = __builtin_amdgcn_raw_buffer_load_b32(sr, so, k0 / 16, 0);
+    if constexpr (F16S)
+      r.s = __builtin_amdgcn_raw_buffer_load_b16(sr, so, (k0 / 128) * 2, 0);
+    else
+      r.s = __builtin_amdgcn_raw_buffer_load_b32(sr, so, k0 / 16, 0);
     const u32x4_t c0 = __builtin_amdgcn_raw_buffer_load_b128(cr, co, k0 / 2, 0);
     r.c = make_uint4(c0[0], c0[1], c0[2], c0[3]);
 #pragma unroll
@@ -325,6 +363,16 @@ __global__ __launch_bounds__(512) void gemm_tile256_kernel(const XT* __restrict_
     }
   };
   auto cword = [](const uint4& c, int kk) { return kk == 0 ? c.x : kk == 1 ? c.y : kk == 2 ? c.z : c.w; };
+  // (sb, SV * sb bits ^ 0x8000 in both halves) of 16-element block j (0..3) of a step
+  auto coef = [&](uint32_t s, int j) -> float2 {
+    if constexpr (F16S) {
+      const float sb = scale_of_f16word(s);
+      const uint32_t svd = bits16<XT>(special_of_f16word(s, m0, m1) * sb) ^ 0x8000u;
+      return make_float2(sb, __builtin_bit_cast(float, svd | (svd << 16)));
+    } else {
+      return lut[(s >> (8 * j)) & 0xFFu];
+    }
+  };
   auto lstore = [&](const Stage& r, int buf) {
     XT* a = As + buf * kTM * kTS;
 #pragma unroll
@@ -334,8 +382,8 @@ __global__ __launch_bounds__(512) void gemm_tile256_kernel(const XT* __restrict_
     }
 #pragma unroll
     for (int kk = 0; kk < 4; kk++) {
-      const float2 f = lut[(r.s >> (8 * (2 * bh + (kk >> 1)))) & 0xFFu];
-      *(uint4*)(Bs + buf * kTN * kTS + br * kTS + 32 * bh + 8 * kk) =
+      const float2 f = coef(r.s, 2 * bh + (kk >> 1));
+      *(uint4*)(Bs + buf * kTN * kBS + bpos(br, 4 * bh + kk)) =
           decode_dword<XT>(cword(r.c, kk), f.x, __builtin_bit_cast(uint32_t, f.y));
     }
   };
@@ -352,9 +400,9 @@ __global__ __launch_bounds__(512) void gemm_tile256_kernel(const XT* __restrict_
     gload(kt + 2 < ktiles ? kt + 2 : ktiles - 1, next_stage);
     float2 f[2];
 #pragma unroll
-    for (int j = 0; j < 2; j++) f[j] = lut[(cur_stage.s >> (8 * (2 * bh + j))) & 0xFFu];
+    for (int j = 0; j < 2; j++) f[j] = coef(cur_stage.s, 2 * bh + j);
     const XT* a = As + cur * kTM * kTS;
-    const XT* b = Bs + cur * kTN * kTS;
+    const XT* b = Bs + cur * kTN * kBS;
     V av[2][4], bv[2][2];
     auto frags = [&](int kk, V* ar, V* bq) {
 #pragma unroll
@@ -362,7 +410,7 @@ __global__ __launch_bounds__(512) void gemm_tile256_kernel(const XT* __restrict_
         ar[i] = *(const V*)(a + (wm * 128 + i * 32 + (lane & 31)) * kTS + 16 * kk + 8 * (lane >> 5));
 #pragma unroll
       for (int j = 0; j < 2; j++)
-        bq[j] = *(const V*)(b + (wn * 64 + j * 32 + (lane & 31)) * kTS + 16 * kk + 8 * (lane >> 5));
+        bq[j] = *(const V*)(b + bpos(wn * 64 + j * 32 + (lane & 31), 2 * kk + (lane >> 5)));
     };
     frags(0, av[0], bv[0]);
 #pragma unroll
@@ -389,7 +437,7 @@ __global__ __launch_bounds__(512) void gemm_tile256_kernel(const XT* __restrict_
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
       }
-      *(uint4*)(Bs + (cur ^ 1) * kTN * kTS + br * kTS + 32 * bh + 8 * kk) = make_uint4(dec[0], dec[1], dec[2], dec[3]);
+      *(uint4*)(Bs + (cur ^ 1) * kTN * kBS + bpos(br, 4 * bh + kk)) = make_uint4(dec[0], dec[1], dec[2], dec[3]);
     }
     __syncthreads();
   };
@@ -608,7 +656,10 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const XT* __restrict__
 constexpr int kBxRow = 256 + 8;                    // staged x halves per row
 constexpr int kBStage = 16 * 144 + 16 * 16;        // one 16-row tile unit: codes + scales
 
-template <typename XT, int KIND, int MT, int TW>
+// F16S: weights in the 128-element FP16-scale layout: a unit's scales are one
+// dword (two words) per row, staged by lanes 0..15; a lane's 64 elements lie
+// in one 128-element block, whose word gives both coefficients.
+template <typename XT, int KIND, int MT, int TW, bool F16S = false>
 __global__ __launch_bounds__(256) void gemm_batch_kernel(const XT* __restrict__ x, int m,
                                                          const uint8_t* __restrict__ codes,
                                                          const uint8_t* __restrict__ scales,
@@ -635,7 +686,7 @@ __global__ __launch_bounds__(256) void gemm_batch_kernel(const XT* __restrict__ 
   const int64_t row0 = (int64_t)(blockIdx.x % wg_rows) * (64 * TW) + wave * (16 * TW);
   const int nunits = (int)(k / 256);
   const int u0 = sid * upw, u1 = min(nunits, u0 + upw);
-  const int rcb = (int)(k / 2), rsb = (int)(k / 16);
+  const int rcb = (int)(k / 2), rsb = (int)(F16S ? k / 64 : k / 16);
   const int rows_w = (int)max((int64_t)0, min((int64_t)(16 * TW), n - row0));
   const Rsrc crs = __builtin_amdgcn_make_buffer_rsrc((void*)(codes + (row0 < n ? row0 : 0) * rcb), (short)0,
                                                      rows_w * rcb, 0x00020000);
@@ -663,11 +714,14 @@ __global__ __launch_bounds__(256) void gemm_batch_kernel(const XT* __restrict__ 
   for (int t = 0; t < TW; t++) {
     cvo0[t] = 16 * t + lr < rows_w ? (16 * t + lr) * rcb + lb : kOob;
     cvo1[t] = 16 * t + lr + 8 < rows_w ? (16 * t + lr + 8) * rcb + lb : kOob;
-    svo[t] = 16 * t + (lane >> 2) < rows_w ? (16 * t + (lane >> 2)) * rsb + (lane & 3) * 4 : kOob;
+    if (F16S)
+      svo[t] = lane < 16 && 16 * t + lane < rows_w ? (16 * t + lane) * rsb : kOob;
+    else
+      svo[t] = 16 * t + (lane >> 2) < rows_w ? (16 * t + (lane >> 2)) * rsb + (lane & 3) * 4 : kOob;
   }
   auto load_unit = [&](Regs& r, int u) {
     const bool ok = u < u1;
-    const int xso = ok ? u * 512 : kOob, cso = ok ? u * 128 : kOob, sso = ok ? u * 16 : kOob;
+    const int xso = ok ? u * 512 : kOob, cso = ok ? u * 128 : kOob, sso = ok ? u * (F16S ? 4 : 16) : kOob;
 #pragma unroll
     for (int j = 0; j < 2 * MT; j++) r.xv[j] = __builtin_amdgcn_raw_buffer_load_b128(xrs, xvo[j], xso, 0);
 #pragma unroll
@@ -688,7 +742,10 @@ __global__ __launch_bounds__(256) void gemm_batch_kernel(const XT* __restrict__ 
       uint8_t* st = stage[wave][buf][t];
       *(u32x4_t*)(st + lr * 144 + lb) = r.c0[t];
       *(u32x4_t*)(st + (lr + 8) * 144 + lb) = r.c1[t];
-      *(uint32_t*)(st + 16 * 144 + lane * 4) = r.s[t];
+      if (!F16S)
+        *(uint32_t*)(st + 16 * 144 + lane * 4) = r.s[t];
+      else if (lane < 16)
+        *(uint32_t*)(st + 16 * 144 + lane * 16) = r.s[t];
     }
   };
 
@@ -704,11 +761,21 @@ __global__ __launch_bounds__(256) void gemm_batch_kernel(const XT* __restrict__ 
       const uint8_t* st = stage[wave][buf][t];
       const u32x4_t lo = *(const u32x4_t*)(st + c * 144 + 32 * q);
       const u32x4_t hi = *(const u32x4_t*)(st + c * 144 + 32 * q + 16);
-      const uint32_t sw = *(const uint32_t*)(st + 16 * 144 + c * 16 + 4 * q);
+      const uint32_t sw = F16S ? *(const uint32_t*)(st + 16 * 144 + c * 16)
+                               : *(const uint32_t*)(st + 16 * 144 + c * 16 + 4 * q);
       const uint32_t cw[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       float2 f[4];
+      if constexpr (F16S) {
+        const uint32_t wd = (sw >> (16 * (q >> 1))) & 0xFFFFu;  // block (64 q) / 128 of the unit
+        const float sb = scale_of_f16word(wd);
+        const uint32_t svd = bits16<XT>(special_of_f16word(wd, m0, m1) * sb) ^ 0x8000u;
+        f[0] = make_float2(sb, __builtin_bit_cast(float, svd | (svd << 16)));
 #pragma unroll
-      for (int b = 0; b < 4; b++) f[b] = lut[(sw >> (8 * b)) & 0xFFu];
+        for (int b = 1; b < 4; b++) f[b] = f[0];
+      } else {
+#pragma unroll
+        for (int b = 0; b < 4; b++) f[b] = lut[(sw >> (8 * b)) & 0xFFu];
+      }
 #pragma unroll
       for (int i = 0; i < 8; i++) {
         const uint4 bv = decode_dword<XT>(cw[i], f[i >> 1].x, __builtin_bit_cast(uint32_t, f[i >> 1].y));
@@ -771,21 +838,25 @@ struct BatchPlan {
 // row-count dependent target (more rows carry more MFMA and x work per weight
 // byte, so need fewer workgroups to cover HBM latency) and every split keeps
 // >= 2 units.
-static BatchPlan batch_plan(int64_t m, int64_t n, int64_t k) {
+static BatchPlan batch_plan(int64_t m, int64_t n, int64_t k, bool untrimmed = false) {
   BatchPlan p;
   const int64_t tiles = (n + 15) / 16;
   const int64_t cus = device_cu_count();
   p.tw = 1;
   p.wg_rows = (tiles + 4 * p.tw - 1) / (4 * p.tw);
   const int64_t nunits = k / 256;
-  const int64_t target = m <= 8 ? 8 * cus : m <= 16 ? 4 * cus : 3 * cus / 2;
+  const int64_t target = m <= 16 ? 8 * cus : 3 * cus / 2;
   p.split = 1;
   while (p.wg_rows * p.split * 2 <= target && nunits / (2 * p.split) >= 2) p.split *= 2;
+  if (untrimmed)  // the most splits: one 256-element unit per workgroup, at most 32
+    while (p.split < 32 && nunits / (2 * p.split) >= 1) p.split *= 2;
   p.upw = (int)((nunits + p.split - 1) / p.split);
   return p;
 }
 
 static bool use_batch(int64_t m, int64_t k) { return m >= 3 && m <= 32 && k >= 256 && k % 256 == 0 && k < (1LL << 24); }
+// The FP16-scale layout has no small-batch kernel: the batch kernel from 2 rows.
+static bool use_batch_f16s(int64_t m, int64_t k) { return m == 2 ? use_batch(3, k) : use_batch(m, k); }
 
 template <typename OT>
 __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restrict__ partial,
@@ -832,10 +903,15 @@ static bool use_smallm(int64_t m, int64_t n, int64_t k) {
   return m == 2 || n * k < (128LL << 20);
 }
 
-size_t gemm_ws_bytes(int64_t m, int64_t n, int64_t k) {
+size_t gemm_ws_need(int64_t m, int64_t n, int64_t k, bool f16s, bool untrimmed) {
+  if (f16s) {
+    if (!use_batch_f16s(m, k)) return 0;
+    const BatchPlan p = batch_plan(m, n, k, untrimmed);
+    return p.split > 1 ? (size_t)p.split * (size_t)m * (size_t)n * sizeof(float) : 0;
+  }
   if (use_smallm(m, n, k)) return 0;
   if (use_batch(m, k)) {
-    const BatchPlan p = batch_plan(m, n, k);
+    const BatchPlan p = batch_plan(m, n, k, untrimmed);
     return p.split > 1 ? (size_t)p.split * (size_t)m * (size_t)n * sizeof(float) : 0;
   }
   if (m < 2 || m > 32 || k % 32 != 0) return 0;
@@ -843,18 +919,25 @@ size_t gemm_ws_bytes(int64_t m, int64_t n, int64_t k) {
   return (size_t)p.split * (size_t)m * (size_t)n * sizeof(float);
 }
 
+// Enough for either layout (two rows need no workspace on the default layout
+// but may on the FP16-scale one).
+size_t gemm_ws_bytes(int64_t m, int64_t n, int64_t k) {
+  const size_t a = gemm_ws_need(m, n, k, false), b = gemm_ws_need(m, n, k, true);
+  return a > b ? a : b;
+}
+
 static bool tile256_fits(int64_t m, int64_t k, size_t xsize) {
   return m >= kTM && k % kTK == 0 && (int64_t)kTM * k * (int64_t)xsize < (1LL << 30);
 }
 
-template <typename XT, int KIND, typename OT>
+template <typename XT, int KIND, typename OT, bool F16S = false>
 static hipError_t run_tile256(const XT* x, int64_t m, const PackedView& w, OT* y, const float* ts2,
                               hipStream_t stream) {
   const int64_t n = w.rows, k = w.cols;
   const float m0 = 6.0f + 0.5f * (float)w.off_half[0];
   const float m1 = 6.0f + 0.5f * (float)w.off_half[KIND == kWeight ? 1 : 0];
-  auto kern = gemm_tile256_kernel<XT, KIND, OT>;
-  const size_t lds = (size_t)2 * (kTM + kTN) * kTS * sizeof(XT) + 256 * sizeof(float2);
+  auto kern = gemm_tile256_kernel<XT, KIND, OT, F16S>;
+  const size_t lds = (size_t)2 * (kTM * kTS + kTN * kBS) * sizeof(XT) + 256 * sizeof(float2);
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const int64_t tiles = ((m + kTM - 1) / kTM) * ((n + kTN - 1) / kTN);
@@ -863,20 +946,21 @@ static hipError_t run_tile256(const XT* x, int64_t m, const PackedView& w, OT* y
   return hipGetLastError();
 }
 
-template <typename XT, int KIND, typename OT>
-static hipError_t run_gemm(const XT* x, int64_t m, const PackedView& w, OT* y, void* ws,
-                           hipStream_t stream) {
+// The batch kernel (3..32 rows; 2..32 rows on the FP16-scale layout), with
+// the global K split's partial sums reduced by skinny_reduce_kernel.
+template <typename XT, int KIND, typename OT, bool F16S>
+static hipError_t run_batch(const XT* x, int64_t m, const PackedView& w, OT* y, void* ws, hipStream_t stream) {
   const int64_t n = w.rows, k = w.cols;
   const float m0 = 6.0f + 0.5f * (float)w.off_half[0];
   const float m1 = 6.0f + 0.5f * (float)w.off_half[KIND == kWeight ? 1 : 0];
-  if (use_batch(m, k)) {
-    const BatchPlan p = batch_plan(m, n, k);
+  {
+    const BatchPlan p = batch_plan(m, n, k, (w.flags & kFlagUntrimmed) != 0);
     float* partial = p.split > 1 ? (float*)ws : nullptr;
     if (p.split > 1 && !partial) return hipErrorInvalidValue;
     const int ydt = sizeof(OT) == 4 ? kF32 : __is_same(OT, _Float16) ? kF16 : kBF16;
     const int64_t grid = p.wg_rows * p.split;
 #define RZ_BATCH(MT_, TW_)                                                                                \
-  hipLaunchKernelGGL((gemm_batch_kernel<XT, KIND, MT_, TW_>), dim3((unsigned)grid), dim3(256), 0, stream, x, \
+  hipLaunchKernelGGL((gemm_batch_kernel<XT, KIND, MT_, TW_, F16S>), dim3((unsigned)grid), dim3(256), 0, stream, x, \
                      (int)m, w.codes, w.scales, w.tensor_scale, n, k, m0, m1, (int)p.wg_rows, p.upw,        \
                      partial, (void*)y, ydt)
     if (m <= 16) {
@@ -894,6 +978,33 @@ static hipError_t run_gemm(const XT* x, int64_t m, const PackedView& w, OT* y, v
     }
     return hipGetLastError();
   }
+}
+
+// The 128-element FP16-scale layout: the batch kernel for 2..32 rows, the
+// prefill kernel where it fits, else the generic tile kernel.
+template <typename XT, int KIND, typename OT>
+static hipError_t run_gemm_f16s(const XT* x, int64_t m, const PackedView& w, OT* y, void* ws,
+                                hipStream_t stream) {
+  const int64_t n = w.rows, k = w.cols;
+  if (k % 128 != 0) return hipErrorInvalidValue;
+  if (use_batch_f16s(m, k)) return run_batch<XT, KIND, OT, true>(x, m, w, y, ws, stream);
+  if (tile256_fits(m, k, sizeof(XT))) return run_tile256<XT, KIND, OT, true>(x, m, w, y, nullptr, stream);
+  const float m0 = 6.0f + 0.5f * (float)w.off_half[0];
+  const float m1 = 6.0f + 0.5f * (float)w.off_half[KIND == kWeight ? 1 : 0];
+  dim3 grid((unsigned)((n + kBN - 1) / kBN), (unsigned)((m + kBM - 1) / kBM));
+  hipLaunchKernelGGL((gemm_kernel<XT, KIND, OT, true>), grid, dim3(256), 0, stream, x, m, w.codes,
+                     w.scales, w.tensor_scale, n, k, m0, m1, y);
+  return hipGetLastError();
+}
+
+template <typename XT, int KIND, typename OT>
+static hipError_t run_gemm(const XT* x, int64_t m, const PackedView& w, OT* y, void* ws,
+                           hipStream_t stream) {
+  if (!default_layout(w)) return run_gemm_f16s<XT, KIND, OT>(x, m, w, y, ws, stream);
+  const int64_t n = w.rows, k = w.cols;
+  const float m0 = 6.0f + 0.5f * (float)w.off_half[0];
+  const float m1 = 6.0f + 0.5f * (float)w.off_half[KIND == kWeight ? 1 : 0];
+  if (use_batch(m, k)) return run_batch<XT, KIND, OT, false>(x, m, w, y, ws, stream);
   if (m >= 2 && m <= 32 && k % 32 == 0 && ws != nullptr) {
     const SkinnyPlan p = skinny_plan(n, k);
     float* partial = (float*)ws;
@@ -949,7 +1060,8 @@ hipError_t launch_gemm_prefill_scaled(const void* x, int x_dtype, int64_t m, con
 
 hipError_t launch_gemm(const void* x, int x_dtype, int64_t m, const PackedView& w, void* y,
                        int y_dtype, void* ws, size_t, hipStream_t stream) {
-  if (use_smallm(m, w.rows, w.cols)) return launch_smallm(x, x_dtype, m, w, y, y_dtype, stream);
+  if (default_layout(w) && use_smallm(m, w.rows, w.cols)) return launch_smallm(x, x_dtype, m, w, y, y_dtype, stream);
+  if (!default_layout(w) && (w.blog2 != 7 || w.sfmt != 1)) return hipErrorNotSupported;
   if (x_dtype == kF16) {
     if (w.kind == kWeight) return gemm_out_dispatch<_Float16, kWeight>((const _Float16*)x, m, w, y, y_dtype, ws, stream);
     return gemm_out_dispatch<_Float16, kAct>((const _Float16*)x, m, w, y, y_dtype, ws, stream);

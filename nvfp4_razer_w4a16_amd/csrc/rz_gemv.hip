@@ -451,9 +451,14 @@ static hipError_t launch_cfg(GemvArgs a, const GemvPlan& p, bool f16s, hipStream
 // x; each row group then gets a run of whole row quads, sized so that about
 // wg_per_cu workgroups land on each CU, and never more workgroups than the
 // rows need.
-static GemvPlan plan_gemv(int64_t n, int64_t nchunk, int cus, int wg_per_cu) {
+//
+// The untrimmed plan (RAZER_FLAG_UNTRIMMED_PLAN) instead splits K over as many
+// waves as keep every lane busy (up to 4) and gives each row group one quad,
+// so the launch has as many workgroups as the rows allow.
+static GemvPlan plan_gemv(int64_t n, int64_t nchunk, int cus, int wg_per_cu, bool untrimmed = false) {
   GemvPlan p;
   p.ks = nchunk <= 64 ? 1 : nchunk <= 128 ? 2 : 4;
+  if (untrimmed) p.ks = nchunk >= 256 ? 4 : nchunk >= 128 ? 2 : 1;
   const int64_t per_lane = (nchunk + 64LL * p.ks - 1) / (64LL * p.ks);
   p.cpl = per_lane <= 1 ? 1 : per_lane <= 2 ? 2 : per_lane <= 4 ? 4 : per_lane <= 8 ? 8 : 16;
   p.nq = 1;
@@ -462,6 +467,7 @@ static GemvPlan plan_gemv(int64_t n, int64_t nchunk, int cus, int wg_per_cu) {
   int64_t rpwv = (n + groups - 1) / groups;
   rpwv = (rpwv + 3) / 4 * 4;
   if (rpwv * rw > kGemvMaxRpw) rpwv = kGemvMaxRpw / rw;
+  if (untrimmed) rpwv = 4;
   p.rpwv = (int)rpwv;
   p.rpw = (int)(rpwv * rw);
   p.grid = (n + p.rpw - 1) / p.rpw;
@@ -525,11 +531,14 @@ hipError_t launch_gemv_group(const void* x, int x_dtype, const PackedView* w, vo
     n_total += m.n;
   }
   if (a.count == 0) return hipSuccess;
-  const bool unit2 = a.k % 32 == 0;
+  bool untrimmed = false;
+  for (int g = 0; g < count; g++) untrimmed = untrimmed || (w[g].flags & kFlagUntrimmed);
+  // the untrimmed plan takes 16-element chunks (twice the K split) where the layout allows
+  const bool unit2 = a.k % 32 == 0 && (f16s || !untrimmed);
   if (f16s && !unit2) return hipErrorInvalidValue;
   a.nchunk = a.k / (unit2 ? 32 : 16);
   // one plan for the summed rows; each weight gets whole workgroups of it
-  GemvPlan p = plan_gemv(n_total, a.nchunk, device_cu_count(), 8);
+  GemvPlan p = plan_gemv(n_total, a.nchunk, device_cu_count(), 8, untrimmed);
   int64_t wg = 0;
   for (int g = 0; g < a.count; g++) {
     a.w[g].wg0 = (int)wg;

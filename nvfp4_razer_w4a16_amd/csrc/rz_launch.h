@@ -11,6 +11,7 @@ namespace rz {
 // Encoder flags (the values of the public RAZER_FLAG_* constants).
 constexpr uint32_t kFlagNoRemap = 1u;       // plain NVFP4: no special value
 constexpr uint32_t kFlagFourOverSix = 2u;   // plain FP4, per-block max -> 6 or max -> 4 scale
+constexpr uint32_t kFlagUntrimmed = 4u;     // products: untrimmed launch plan (most splits)
 
 struct PackedView {
   int kind;          // 0 weight (E3M3, 4 candidates), 1 activation (E4M3, 2 candidates)
@@ -78,7 +79,8 @@ bool smallm_supported(int64_t m, int64_t n, int64_t k);
 hipError_t launch_smallm(const void* x, int x_dtype, int64_t m, const PackedView& w, void* y,
                          int y_dtype, hipStream_t stream);
 
-size_t gemm_ws_bytes(int64_t m, int64_t n, int64_t k);
+size_t gemm_ws_bytes(int64_t m, int64_t n, int64_t k);                // either layout
+size_t gemm_ws_need(int64_t m, int64_t n, int64_t k, bool f16s, bool untrimmed = false);  // one layout
 hipError_t launch_gemm(const void* x, int x_dtype, int64_t m, const PackedView& w, void* y,
                        int y_dtype, void* ws, size_t ws_bytes, hipStream_t stream);
 

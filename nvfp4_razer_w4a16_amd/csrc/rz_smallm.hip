@@ -387,7 +387,7 @@ struct SmPlan {
 // smallest power of two that puts about 8 waves on each CU, doubled while
 // every wave still keeps >= 8 K units and the grid stays under ~16 (one row)
 // or ~32 (two to four rows) waves per CU.
-SmPlan plan_smallm(int64_t m, int64_t n, int64_t k, int cus) {
+SmPlan plan_smallm(int64_t m, int64_t n, int64_t k, int cus, bool untrimmed = false) {
   SmPlan p;
   p.mt = m <= 1 ? 1 : m <= 2 ? 2 : 4;
   const int64_t nunits = k / 256;
@@ -397,6 +397,8 @@ SmPlan plan_smallm(int64_t m, int64_t n, int64_t k, int cus) {
   while (p.ks < 8 && tiles * p.ks < 8LL * cus && nunits / (2 * p.ks) >= 2) p.ks *= 2;
   const int64_t cap = (p.mt == 1 ? 16LL : 32LL) * cus;  // wider batches carry more LDS/epilogue work per byte
   while (p.ks < 8 && nunits / p.ks >= 8 && tiles * p.ks < cap) p.ks *= 2;
+  if (untrimmed)  // the most waves per tile: up to 8, each with at least one unit
+    while (p.ks < 8 && nunits / (2 * p.ks) >= 1) p.ks *= 2;
   const int64_t upw = (nunits + p.ks - 1) / p.ks;
   p.gpw = (int)(upw * p.mt);  // K groups per wave (whole units)
   p.grid = tiles;
@@ -466,7 +468,7 @@ hipError_t launch_smallm(const void* x, int x_dtype, int64_t m, const PackedView
   a.ydt = y_dtype;
   a.m0 = 6.0f + 0.5f * (float)w.off_half[0];
   a.m1 = 6.0f + 0.5f * (float)w.off_half[w.kind == kWeight ? 1 : 0];
-  const SmPlan p = plan_smallm(m, w.rows, w.cols, device_cu_count());
+  const SmPlan p = plan_smallm(m, w.rows, w.cols, device_cu_count(), (w.flags & kFlagUntrimmed) != 0);
   a.gpw = p.gpw;
   return x_dtype == kF16 ? dispatch<_Float16>(a, p, f16s, stream) : dispatch<__bf16>(a, p, f16s, stream);
 }

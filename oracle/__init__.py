@@ -322,14 +322,15 @@ def gemm_pairs(x, p: Packed, rows_m, cols_n):
     return y, nrm
 
 
-def gemm_any(x, p: Packed):
+def gemm_any(x, p: Packed, cols=None):
     """fp64 product y = x @ w^T and norm |x| @ |w|^T over the exactly decoded
     weights of any layout (block sizes, FP16 group scales): the oracle's
-    decoder followed by a numpy matmul.  Returns (y [m, n], norm [m, n])."""
+    decoder followed by a numpy matmul.  ``cols`` selects weight rows (output
+    columns); None means all.  Returns (y [m, ncols], norm [m, ncols])."""
     x = np.asarray(x, dtype=np.float64)
     if x.ndim == 1:
         x = x[None, :]
-    w = dequant_f64(p)
+    w = dequant_f64(p if cols is None else select_rows(p, cols))
     return x @ w.T, np.abs(x) @ np.abs(w).T
 
 
@@ -355,14 +356,13 @@ def gemm_w4a4(xp: Packed, wp: Packed, cols=None):
 
 
 def select_rows(p: Packed, idx) -> Packed:
-    """The packed rows idx of a default-layout tensor (same tensor scale and
-    offsets), for decoding a sample of a large tensor."""
-    _default_layout(p)
+    """The packed rows idx of a tensor of any layout (same tensor scale,
+    offsets and layout), for decoding a sample of a large tensor."""
     idx = np.asarray(idx, dtype=np.int64)
     return Packed(p.kind, idx.size, p.cols, p.offsets,
                   np.ascontiguousarray(p.codes.reshape(p.rows, p.cols // 2)[idx]).reshape(-1),
-                  np.ascontiguousarray(p.scales.reshape(p.rows, p.cols // 16)[idx]).reshape(-1),
-                  p.tensor_scale)
+                  np.ascontiguousarray(p.scales.reshape(p.rows, p.cols // p.block)[idx]).reshape(-1),
+                  p.tensor_scale, p.block, p.scale_fmt)
 
 
 def gemm_w4a4_pairs(xp: Packed, wp: Packed, rows_m, cols_n):

@@ -235,8 +235,9 @@ def test_layout_variants_host_checks():
     a = _packed(kind=rz.RAZER_ACT, off=(-2, 0), cols=128)
     a.scale_fmt = rz.RAZER_SCALE_F16  # FP16 group scales are for weights only
     assert L.razer_quantize_act(FAKE_X, rz.RAZER_BF16, ctypes.byref(a), FAKE_WS, 4096, None) == rz.RAZER_E_INVALID
-    # the products take 16-element blocks with byte scales; the GEMV calls also
-    # take 128-element blocks with FP16 scales (not checked here: that would launch)
+    # the products take 16-element blocks with byte scales; the GEMV calls and
+    # razer_gemm also take 128-element blocks with FP16 scales (not checked here:
+    # that would launch), razer_gemm_w4a4 does not
     y = ctypes.c_void_p(0x6000)
     x = _packed(kind=rz.RAZER_ACT, off=(-2, 0), rows=2, cols=128)
     for blog2, fmt in ((5, 0), (7, 0), (4, 1), (7, 1)):
@@ -245,7 +246,8 @@ def test_layout_variants_host_checks():
         if (blog2, fmt) != (7, 1):
             assert L.razer_gemv(FAKE_X, rz.RAZER_F16, ctypes.byref(w), y, rz.RAZER_F16, None, 0, None) == rz.RAZER_E_UNSUPPORTED
             assert _group_call([w], [0x6000]) == rz.RAZER_E_UNSUPPORTED
-        assert L.razer_gemm(FAKE_X, rz.RAZER_F16, 4, ctypes.byref(w), y, rz.RAZER_F16, FAKE_WS, 1 << 20, None) == rz.RAZER_E_UNSUPPORTED
+            assert L.razer_gemm(FAKE_X, rz.RAZER_F16, 4, ctypes.byref(w), y, rz.RAZER_F16, FAKE_WS, 1 << 20,
+                                None) == rz.RAZER_E_UNSUPPORTED
         assert L.razer_gemm_w4a4(ctypes.byref(x), ctypes.byref(w), y, rz.RAZER_BF16, FAKE_WS, 1 << 20, None) == rz.RAZER_E_UNSUPPORTED
     # one layout per grouped launch
     g128 = _packed(rows=8, cols=128)

@@ -826,3 +826,8 @@ def test_sampled_output_helpers_equal_the_full_products():
     np.testing.assert_allclose(nq, n4[mi, ni], rtol=1e-12)
     sub = oracle.select_rows(p, ni[:7])
     np.testing.assert_array_equal(oracle.dequant_f64(sub), oracle.dequant_f64(p)[ni[:7]])
+    pf = oracle.quantize(oracle.WEIGHT, w[:, :512], (-2, -5), block=128, scale_fmt=oracle.SCALE_F16)
+    ya, na = oracle.gemm_any(x, pf)
+    yc, nc = oracle.gemm_any(x, pf, ni[:9])
+    np.testing.assert_allclose(yc, ya[:, ni[:9]], rtol=1e-12, atol=1e-12 * float(na.max()))
+    np.testing.assert_allclose(nc, na[:, ni[:9]], rtol=1e-12)
