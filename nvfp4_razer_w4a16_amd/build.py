@@ -33,6 +33,8 @@ SOURCES = {
     "rz_gemv.hip": [],
     "rz_gemm.hip": [],
     "rz_smallm.hip": [],
+    # MFMA results in VGPRs: the epilogue of every block reads them with VALU
+    "rz_bdiag.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "rz_w4a4.hip": [],
     "rz_api.cpp": [],
 }

@@ -894,10 +894,16 @@ __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restr
   }
 }
 
-// Two rows go to the MFMA small-batch kernel (no workspace) where it covers the
-// shape, three and four rows too on weights under 128M elements (above that the
-// batch kernel streams them faster); the batch kernel takes up to 32 rows, the
-// skinny split-K kernel the shapes neither covers.
+// Routing on the default layout (no workspace for the first two): three to
+// eight rows with K % 256 == 0 go to the block-diagonal streaming kernel,
+// except three and four rows on weights under 128M elements; those and two
+// rows go to the MFMA small-batch kernel where it covers the shape; the batch
+// kernel takes up to 32 rows, the skinny split-K kernel the shapes none covers.
+static bool use_bdiag(int64_t m, int64_t n, int64_t k) {
+  if (m < 3 || m > 8 || !bdiag_supported(m, n, k)) return false;
+  return m >= 5 || n * k >= (128LL << 20);
+}
+
 static bool use_smallm(int64_t m, int64_t n, int64_t k) {
   if (m < 2 || m > 4 || !smallm_supported(m, n, k)) return false;
   return m == 2 || n * k < (128LL << 20);
@@ -909,7 +915,7 @@ size_t gemm_ws_need(int64_t m, int64_t n, int64_t k, bool f16s, bool untrimmed) 
     const BatchPlan p = batch_plan(m, n, k, untrimmed);
     return p.split > 1 ? (size_t)p.split * (size_t)m * (size_t)n * sizeof(float) : 0;
   }
-  if (use_smallm(m, n, k)) return 0;
+  if (use_bdiag(m, n, k) || use_smallm(m, n, k)) return 0;
   if (use_batch(m, k)) {
     const BatchPlan p = batch_plan(m, n, k, untrimmed);
     return p.split > 1 ? (size_t)p.split * (size_t)m * (size_t)n * sizeof(float) : 0;
@@ -1060,6 +1066,7 @@ hipError_t launch_gemm_prefill_scaled(const void* x, int x_dtype, int64_t m, con
 
 hipError_t launch_gemm(const void* x, int x_dtype, int64_t m, const PackedView& w, void* y,
                        int y_dtype, void* ws, size_t, hipStream_t stream) {
+  if (default_layout(w) && use_bdiag(m, w.rows, w.cols)) return launch_bdiag(x, x_dtype, m, w, y, y_dtype, stream);
   if (default_layout(w) && use_smallm(m, w.rows, w.cols)) return launch_smallm(x, x_dtype, m, w, y, y_dtype, stream);
   if (!default_layout(w) && (w.blog2 != 7 || w.sfmt != 1)) return hipErrorNotSupported;
   if (x_dtype == kF16) {

@@ -79,6 +79,12 @@ bool smallm_supported(int64_t m, int64_t n, int64_t k);
 hipError_t launch_smallm(const void* x, int x_dtype, int64_t m, const PackedView& w, void* y,
                          int y_dtype, hipStream_t stream);
 
+// Block-diagonal MFMA kernel for 2..8 activation rows (default layout,
+// K % 256 == 0); no workspace.
+bool bdiag_supported(int64_t m, int64_t n, int64_t k);
+hipError_t launch_bdiag(const void* x, int x_dtype, int64_t m, const PackedView& w, void* y, int y_dtype,
+                        hipStream_t stream);
+
 size_t gemm_ws_bytes(int64_t m, int64_t n, int64_t k);                // either layout
 size_t gemm_ws_need(int64_t m, int64_t n, int64_t k, bool f16s, bool untrimmed = false);  // one layout
 hipError_t launch_gemm(const void* x, int x_dtype, int64_t m, const PackedView& w, void* y,

@@ -515,7 +515,7 @@ def _small_batch_oracle_4096():
     return oracle.gemm(as_f32(synth.small_batch_x(32, 4096)), small_batch_ref(4096, 4096))
 
 
-@pytest.mark.parametrize("m", [2, 4, 8, 32])
+@pytest.mark.parametrize("m", [2, 3, 4, 6, 8, 32])
 def test_gemm_small_batch_70b_sampled(m):
     _need_gpu()
     log("gemm 70b: reference encode ...")
@@ -568,6 +568,24 @@ def test_gemm_ragged_shapes(m, n, k, xdt):
     for odt in (torch.float32, torch.bfloat16):
         y = rz.razer_gemm(x.cuda(), to_device(ref), odt).cpu().double().numpy()
         assert_product_close(y, y_ref, nrm, f"gemm {m}x{n}x{k} out {odt}", odt)
+
+
+@pytest.mark.parametrize("m", [3, 5, 6, 7, 8])
+def test_gemm_three_to_eight_rows(m):
+    """Three to eight rows on K % 256 == 0: every row count, weight rows that
+    leave part of the last 64-row workgroup empty, one-unit and split K, both
+    input types, checked element by element against the oracle."""
+    _need_gpu()
+    for n, k, xdt in [(200, 768, torch.bfloat16), (64, 256, torch.float16), (1000, 4096, torch.bfloat16),
+                      (17, 2048, torch.float16)]:
+        rng = np.random.default_rng(m * 7919 + n + k)
+        w = (rng.standard_t(4, (n, k)) * 0.015).astype(np.float32)
+        x = torch.from_numpy(rng.normal(0, 1, (m, k)).astype(np.float32)).to(xdt)
+        ref = oracle.quantize_weight(w, (-2, 4))
+        y_ref, nrm = oracle.gemm(as_f32(x), ref)
+        for odt in (torch.float32, torch.float16):
+            y = rz.razer_gemm(x.cuda(), to_device(ref), odt).cpu().double().numpy()
+            assert_product_close(y, y_ref, nrm, f"gemm {m}x{n}x{k} out {odt}", odt)
 
 
 @pytest.mark.parametrize("m,n,k", [(1, 200, 1024), (1, 5000, 512), (2, 96, 768), (4, 40, 512),
