@@ -28,8 +28,8 @@
 // 256-entry LDS table holds both coefficients times the block scale, indexed
 // by byte b of the lane's scale dword (dword q of the row's 16 scale bytes =
 // blocks 4q .. 4q+3).  Per code dword that is 4 conversions and 4 packed
-// maxes; per block and vector two fp32 FMAs.  Five to eight rows take a second
-// A group (vectors 4..7) against the same converted B.
+// maxes; per block and vector two fp32 FMAs.  Five to eight rows use a
+// two-slot variant (eight vectors per A operand, described at the kernel).
 //
 // Memory: HBM streams best when each load instruction covers whole 128-byte
 // row segments (16 rows x 64 bytes per instruction runs about 25 % slower), so
@@ -112,19 +112,31 @@ constexpr int kStage = 16 * 128 + 16 * 16;  // one unit of a tile: codes + scale
 // Chunk slot of code chunk j (16 bytes) of row r in a wave's stage.
 __device__ __forceinline__ int stage_slot(int r, int j) { return r * 8 + (j ^ ((r >> 1) & 7)); }
 
+// VG: 1 for the four-slot mapping above (up to four vectors; 2 would take a
+// second group of four against the same B), or 8 for the two-slot mapping of
+// five to eight vectors: A row r = vector r % 8,
+// K-slot groups {2 (r / 8), 2 (r / 8) + 1}; MFMA i covers blocks 2i and
+// 2i + 1, lane group q taking elements 32i + 8q .. +7 (code dword 4i + q of
+// the unit), so D[4q + e][c] is vector 4 (q & 1) + e times block 2i + q / 2
+// of row c.  Eight MFMAs per unit and product instead of sixteen.
 template <typename XT, int KIND, int VG, int TR, int KS, int D>
 __global__ __launch_bounds__(64 * TR * KS) void bdiag_kernel(BdArgs a) {
   typedef typename BdOps<XT>::V V;
+  constexpr bool TWO = VG == 8;                      // the two-slot mapping
+  constexpr int NG = TWO ? 1 : VG;                   // A groups per B operand
+  constexpr int NV = TWO ? 8 : 4 * VG;               // vectors
+  constexpr int NCH = TWO ? 256 : 128 * VG;          // 16-byte x chunks per unit
+  constexpr int XU = NCH * 16;                       // LDS bytes of x per K unit
+  constexpr int ZB = XU + 256;                       // zero region
   constexpr int NW = TR * KS;
-  constexpr int XU = VG * 2048;                      // LDS bytes of x per K unit (VG groups)
-  constexpr int ZB = VG * 2048 + 256;                // zero region
-  constexpr int XCH = (KS * XU / 16 + 64 * NW - 1) / (64 * NW);  // x chunks per thread and step
+  constexpr int XCH = (KS * NCH + 64 * NW - 1) / (64 * NW);  // x chunks per thread and step
   static_assert(D % 2 == 0, "the x buffers alternate with the step parity");
   __shared__ float2 lut[256];  // scale byte -> (sb (1 + 4 SV), -4 sb SV)
-  __shared__ float red[KS][TR][VG * 4][16];
+  __shared__ float red[KS][TR][NV][16];
   __shared__ __attribute__((aligned(16))) uint8_t stage[NW][kStage];
-  // zero region, then two x buffers of KS units: unit chunk
-  // (i * VG + g) * 16 + 4 q + v holds x[4g + v][elements 64q + 8i .. of the unit]
+  // zero region, then two x buffers of KS units.  Unit chunk, four-slot:
+  // (i * VG + g) * 16 + 4 q + v holds x[4g + v][elements 64q + 8i ..];
+  // two-slot: (i * 4 + q) * 8 + v holds x[v][elements 32i + 8q ..].
   __shared__ __attribute__((aligned(256))) uint8_t xl[ZB + 2 * KS * XU];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -166,13 +178,19 @@ __global__ __launch_bounds__(64 * TR * KS) void bdiag_kernel(BdArgs a) {
 #pragma unroll
   for (int h = 0; h < XCH; h++) {
     const int ch = tid + h * 64 * NW;
-    const int sl = ch / (XU / 16), w = ch % (XU / 16);
-    const int v = w & 3, qq = (w >> 2) & 3, r = w >> 4;
-    const int g = r % VG, i = r / VG;
-    const int vec = 4 * g + v;
-    const bool live = ch < KS * (XU / 16) && vec < a.m;
-    xoff[h] = live ? (int)(((int64_t)vec * a.k + 64 * qq + 8 * i) * 2) : kOob;
-    xdst[h] = ch < KS * (XU / 16) ? ZB + sl * XU + w * 16 : (ch % (ZB / 16)) * 16;
+    const int sl = ch / NCH, w = ch % NCH;
+    int vec, el;
+    if constexpr (TWO) {
+      vec = w & 7;
+      el = 32 * (w >> 5) + 8 * ((w >> 3) & 3);
+    } else {
+      const int r = w >> 4;
+      vec = 4 * (r % VG) + (w & 3);
+      el = 64 * ((w >> 2) & 3) + 8 * (r / VG);
+    }
+    const bool live = ch < KS * NCH && vec < a.m;
+    xoff[h] = live ? (int)(((int64_t)vec * a.k + el) * 2) : kOob;
+    xdst[h] = ch < KS * NCH ? ZB + sl * XU + w * 16 : (ch % (ZB / 16)) * 16;
     xu0[h] = min(nunits, sl * a.ups);
     xu1[h] = min(nunits, xu0[h] + a.ups);
   }
@@ -214,21 +232,61 @@ __global__ __launch_bounds__(64 * TR * KS) void bdiag_kernel(BdArgs a) {
   xstore(xv[0], 0);
   __syncthreads();
 
-  const bool diag = (c >> 2) == q;
-  // zero reads of lane group q land on banks 16 ((q + 1) & 3) .. + 15, away
-  // from the 64 bytes the group's diagonal lanes read (banks 16q .. 16q + 15)
-  const int xa_zero = 64 * ((q + 1) & 3);
-  const int xa_diag = ZB + s * XU + c * 16;
+  // Lanes off the diagonal read the zero region on banks away from those the
+  // diagonal lanes of their group read: four-slot, group q reads banks
+  // 16q .. 16q + 15 of a 256-byte window and its zeros sit at 64 ((q + 1) & 3);
+  // two-slot, group q reads the (q & 1) half and its zeros sit in the other.
+  const bool diag = TWO ? (c >> 3) == (q >> 1) : (c >> 2) == q;
+  const int xa_zero = TWO ? 128 * (~q & 1) : 64 * ((q + 1) & 3);
+  const int xa_diag = ZB + s * XU + (TWO ? (8 * q + (c & 7)) * 16 : c * 16);
   uint8_t* st = stage[wave];
   const int w0 = stage_slot(lr, lj) * 16, w1 = stage_slot(lr + 8, lj) * 16;
   const int r0 = stage_slot(c, 2 * q) * 16, r1 = stage_slot(c, 2 * q + 1) * 16;
-  float acc[VG][4];
+  float acc[NG][4];
 #pragma unroll
-  for (int g = 0; g < VG; g++)
+  for (int g = 0; g < NG; g++)
 #pragma unroll
     for (int e = 0; e < 4; e++) acc[g][e] = 0.0f;
 
+  auto compute_two = [&](const Unit& r, int buf) {
+    *(u32x4_t*)(st + w0) = r.c0;
+    *(u32x4_t*)(st + w1) = r.c1;
+    *(uint32_t*)(st + 2048 + 4 * lane) = r.s;
+    wave_lds_sync();
+    uint32_t cw[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) cw[i] = *(const uint32_t*)(st + stage_slot(c, i) * 16 + 4 * q);
+    const u32x4_t sr = *(const u32x4_t*)(st + 2048 + 16 * c);
+    wave_lds_sync();
+    const uint8_t* xb = xl + (diag ? xa_diag + buf * KS * XU : xa_zero);
+    const int sh = 8 * (q >> 1);
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const uint32_t w = cw[i];
+      const uint32_t p0 = BdOps<XT>::template cvt<0>(w), p1 = BdOps<XT>::template cvt<1>(w);
+      const uint32_t p2 = BdOps<XT>::template cvt<2>(w), p3 = BdOps<XT>::template cvt<3>(w);
+      const u32x4_t p = {p0, p1, p2, p3};
+      const u32x4_t pm = {mark_remapped(p0, BdOps<XT>::kQuarterNeg2), mark_remapped(p1, BdOps<XT>::kQuarterNeg2),
+                          mark_remapped(p2, BdOps<XT>::kQuarterNeg2), mark_remapped(p3, BdOps<XT>::kQuarterNeg2)};
+      const V xa = *(const V*)(xb + i * 512);
+      const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+      const f32x4_t d0 = BdOps<XT>::mfma(xa, __builtin_bit_cast(V, p), z);
+      const f32x4_t d1 = BdOps<XT>::mfma(xa, __builtin_bit_cast(V, pm), z);
+      // block 2i + q / 2: byte 2 (i & 1) + q / 2 of scale dword i / 2
+      const float2 f = lut[(sr[i >> 1] >> (16 * (i & 1) + sh)) & 0xFFu];
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        acc[0][e] = fmaf(d0[e], f.x, acc[0][e]);
+        acc[0][e] = fmaf(d1[e], f.y, acc[0][e]);
+      }
+    }
+  };
+
   auto compute = [&](const Unit& r, int buf) {
+    if constexpr (TWO) {
+      compute_two(r, buf);
+      return;
+    }
     *(u32x4_t*)(st + w0) = r.c0;
     *(u32x4_t*)(st + w1) = r.c1;
     *(uint32_t*)(st + 2048 + 4 * lane) = r.s;
@@ -240,9 +298,9 @@ __global__ __launch_bounds__(64 * TR * KS) void bdiag_kernel(BdArgs a) {
     const uint32_t cw[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
     for (int b = 0; b < 4; b++) {
-      f32x4_t d0[VG], d1[VG];
+      f32x4_t d0[NG], d1[NG];
 #pragma unroll
-      for (int g = 0; g < VG; g++) {
+      for (int g = 0; g < NG; g++) {
         d0[g] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
         d1[g] = d0[g];
       }
@@ -256,15 +314,15 @@ __global__ __launch_bounds__(64 * TR * KS) void bdiag_kernel(BdArgs a) {
         const u32x4_t pm = {mark_remapped(p0, BdOps<XT>::kQuarterNeg2), mark_remapped(p1, BdOps<XT>::kQuarterNeg2),
                             mark_remapped(p2, BdOps<XT>::kQuarterNeg2), mark_remapped(p3, BdOps<XT>::kQuarterNeg2)};
 #pragma unroll
-        for (int g = 0; g < VG; g++) {
-          const V xa = *(const V*)(xb + (i * VG + g) * 256);
+        for (int g = 0; g < NG; g++) {
+          const V xa = *(const V*)(xb + (i * NG + g) * 256);
           d0[g] = BdOps<XT>::mfma(xa, __builtin_bit_cast(V, p), d0[g]);
           d1[g] = BdOps<XT>::mfma(xa, __builtin_bit_cast(V, pm), d1[g]);
         }
       }
       const float2 f = lut[(sw >> (8 * b)) & 0xFFu];
 #pragma unroll
-      for (int g = 0; g < VG; g++)
+      for (int g = 0; g < NG; g++)
 #pragma unroll
         for (int e = 0; e < 4; e++) {
           acc[g][e] = fmaf(d0[g][e], f.x, acc[g][e]);
@@ -287,21 +345,26 @@ __global__ __launch_bounds__(64 * TR * KS) void bdiag_kernel(BdArgs a) {
     }
   }
 
-  // Lane (q, c) holds vector 4g + e over blocks 4q .. of its slice: add the
-  // four lane groups, then the KS slices.
+  // Four-slot: lane (q, c) holds vector 4g + e over blocks 4q .. of its
+  // slice; two-slot: vector 4 (q & 1) + e over blocks 2i + q / 2.  Add the
+  // lane groups that share vectors, then the KS slices.
 #pragma unroll
-  for (int g = 0; g < VG; g++)
+  for (int g = 0; g < NG; g++)
 #pragma unroll
     for (int e = 0; e < 4; e++) {
       float v = acc[g][e];
-      v += __shfl_xor(v, 16);
+      if constexpr (!TWO) v += __shfl_xor(v, 16);
       v += __shfl_xor(v, 32);
-      if (q == 0) red[s][t][g * 4 + e][c] = v;
+      if constexpr (TWO) {
+        if (q < 2) red[s][t][4 * q + e][c] = v;
+      } else {
+        if (q == 0) red[s][t][g * 4 + e][c] = v;
+      }
     }
   __syncthreads();
   const float sc = *a.ts;
-  for (int o = tid; o < TR * VG * 64; o += 64 * NW) {
-    const int tt = o / (VG * 64), vec = (o / 16) % (VG * 4), cc = o % 16;
+  for (int o = tid; o < TR * NV * 16; o += 64 * NW) {
+    const int tt = o / (NV * 16), vec = (o / 16) % NV, cc = o % 16;
     const int64_t row = ((int64_t)blockIdx.x * TR + tt) * 16 + cc;
     if (vec < a.m && row < a.n) {
       float v = 0.0f;
@@ -324,7 +387,7 @@ struct BdPlan {
 // power of two that still gives every CU a workgroup; the other waves split K.
 BdPlan plan_bdiag(int64_t m, int64_t n, int64_t k, bool untrimmed) {
   BdPlan p;
-  p.vg = m <= 4 ? 1 : 2;
+  p.vg = m <= 4 ? 1 : 8;
   const int64_t tiles = (n + 15) / 16, cus = device_cu_count();
   const int64_t nunits = k / 256;
   p.tr = 8;
@@ -362,7 +425,7 @@ hipError_t dispatch_tr(const BdArgs& a, const BdPlan& p, hipStream_t stream) {
 
 template <typename XT, int KIND>
 hipError_t dispatch_vg(const BdArgs& a, const BdPlan& p, hipStream_t stream) {
-  return p.vg == 1 ? dispatch_tr<XT, KIND, 1>(a, p, stream) : dispatch_tr<XT, KIND, 2>(a, p, stream);
+  return p.vg == 1 ? dispatch_tr<XT, KIND, 1>(a, p, stream) : dispatch_tr<XT, KIND, 8>(a, p, stream);
 }
 
 }  // namespace
