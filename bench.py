@@ -156,15 +156,17 @@ def run_counter_workload(torch, rz, synth, name):
         for _ in range(3):
             rz.razer_gemm_w4a4(xq, wp, out=y, workspace=w4)
     elif name == "small_batch":
-        wsb = rz.razer_quantize_weight(torch.from_numpy(synth.small_batch_weight(28672, 8192)).to(dev), (-2, 4))
-        for m in (8, 32):
-            x = synth.small_batch_x(m, 8192).to(dev)
-            y = torch.empty((m, 28672), dtype=torch.bfloat16, device=dev)
-            ws = torch.empty(max(1, rz.razer_workspace_bytes(rz.RAZER_OP_GEMM, m, 28672, 8192)),
-                             dtype=torch.uint8, device=dev)
-            torch.cuda.synchronize()
-            for _ in range(3):
-                rz.razer_gemm(x, wsb, out=y, workspace=ws)
+        for n, k in ((28672, 8192), (4096, 4096)):
+            wsb = rz.razer_quantize_weight(torch.from_numpy(synth.small_batch_weight(n, k)).to(dev), (-2, 4))
+            for m in (4, 8, 16, 32):
+                x = synth.small_batch_x(m, k).to(dev)
+                y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+                ws = torch.empty(max(1, rz.razer_workspace_bytes(rz.RAZER_OP_GEMM, m, n, k)),
+                                 dtype=torch.uint8, device=dev)
+                torch.cuda.synchronize()
+                for _ in range(3):
+                    rz.razer_gemm(x, wsb, out=y, workspace=ws)
+            del wsb
     elif name == "dequant":
         out = torch.empty((28672, 8192), dtype=torch.bfloat16, device=dev)
         torch.cuda.synchronize()
@@ -342,7 +344,26 @@ def ceiling_lib():
     L.rzc_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     L.rzc_mfma_loop.restype = ctypes.c_int
     L.rzc_mfma_loop.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    L.rzc_read_tiles.restype = ctypes.c_int
+    L.rzc_read_tiles.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                 ctypes.c_void_p, ctypes.c_void_p]
     return L
+
+
+def tile_read_floor(torch, mats, cus, steps=5):
+    """Plain read of each packed weight in mats with the load pattern and grid
+    of the small-batch streaming kernel (nothing computed), us per weight."""
+    L = ceiling_lib()
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+
+    def run():
+        st = torch.cuda.current_stream().cuda_stream
+        for mm in mats:
+            if L.rzc_read_tiles(mm.codes.data_ptr(), mm.scales.data_ptr(), mm.rows, mm.cols, cus,
+                                sink.data_ptr(), st) != 0:
+                raise RuntimeError("rzc_read_tiles failed")
+
+    return GraphTimer(torch, run, warmup=1).time(steps) / len(mats) * 1e3
 
 
 def step_read_floor(torch, launches, step_bytes, steps):
@@ -487,6 +508,11 @@ def bench_rows(torch, rz, synth, args, decode_base):
         del w
         copies = max(1, int(640e6 // packed_bytes(n, k)))  # > 2x the Infinity Cache
         mats = [base] + [clone_packed(rz, base) for _ in range(copies - 1)]
+        floor_us = tile_read_floor(torch, mats, torch.cuda.get_device_properties(0).multi_processor_count)
+        sweep[f"{n}x{k}_tile_read_floor"] = {
+            "workload": "plain read of the packed weight with the streaming kernel's loads and grid",
+            "us": floor_us, "gbs": packed_bytes(n, k) / floor_us / 1e3,
+            "frac_hbm": packed_bytes(n, k) / floor_us / 1e3 / HBM_PEAK_GBS}
         for m in synth.SMALL_BATCH_M:
             x = synth.small_batch_x(m, k).to(dev)
             y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
@@ -505,7 +531,8 @@ def bench_rows(torch, rz, synth, args, decode_base):
                                       "frac_hbm": byts / ms / 1e6 / HBM_PEAK_GBS,
                                       "tflops": 2.0 * m * n * k / ms / 1e9,
                                       "untrimmed_us": ms_u * 1e3,
-                                      "plan_gain_pct": 100.0 * (ms_u - ms) / ms_u}
+                                      "plan_gain_pct": 100.0 * (ms_u - ms) / ms_u,
+                                      "frac_of_tile_read_floor": floor_us / (ms * 1e3)}
             del t, tu, umats, wsu
         del mats, base
         torch.cuda.empty_cache()

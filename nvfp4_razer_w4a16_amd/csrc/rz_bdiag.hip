@@ -109,8 +109,12 @@ struct BdArgs {
 
 constexpr int kStage = 16 * 128 + 16 * 16;  // one unit of a tile: codes + scale bytes
 
-// Chunk slot of code chunk j (16 bytes) of row r in a wave's stage.
-__device__ __forceinline__ int stage_slot(int r, int j) { return r * 8 + (j ^ ((r >> 1) & 7)); }
+// Chunk slot of code chunk j (16 bytes) of row r in a wave's stage: the XOR
+// key takes 8 distinct values over any 8 consecutive rows and, paired with the
+// row parity, 16 distinct slots over 16 rows, so the reads of one chunk column
+// by 8 or 16 lanes fall on distinct banks (fewer conflict cycles in the
+// counters than the key (r >> 1) & 7).
+__device__ __forceinline__ int stage_slot(int r, int j) { return r * 8 + (j ^ ((r & 7) ^ ((r >> 3) & 1))); }
 
 // VG: 1 for the four-slot mapping above (up to four vectors; 2 would take a
 // second group of four against the same B), or 8 for the two-slot mapping of

@@ -9,7 +9,11 @@
 //                  computed;
 //   rzc_mfma_loop  v_mfma_f32_32x32x16_bf16 on register operands only (random
 //                  bf16 values), two waves per SIMD on every CU, as the
-//                  prefill product runs its matrix units.
+//                  prefill product runs its matrix units;
+//   rzc_read_tiles the weight loads of the small-batch streaming product and
+//                  nothing else: its grid, its 16-row tiles and K slices, its
+//                  two 8-row x 128-byte code loads and one scale load per
+//                  unit, four units in flight per wave.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -95,6 +99,71 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(int64_t iters, float* si
   if (s == 1.2345e-38f) sink[0] = s;  // keeps the loop; practically never taken
 }
 
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr int kOob = 0x40000000;
+
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
+}
+
+// Workgroup of TR x KS waves: wave (t, s) reads tile t (16 rows) of the
+// workgroup's TR tiles over the s-th of KS K slices, 256-element units of
+// 16 x 128 code bytes and 16 x 16 scale bytes.
+template <int TR, int KS>
+__global__ __launch_bounds__(64 * TR * KS) void read_tiles_kernel(const uint8_t* codes, const uint8_t* scales,
+                                                                  int64_t n, int64_t k, int ups, uint32_t* sink) {
+  constexpr int D = 4;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = wave % TR, s = wave / TR;
+  const int nunits = (int)(k / 256);
+  const int64_t row0 = ((int64_t)blockIdx.x * TR + t) * 16;
+  const int rows_w = (int)max((int64_t)0, min((int64_t)16, n - row0));
+  const int rcb = (int)(k / 2), rsb = (int)(k / 16);
+  const Rsrc crs = make_rsrc(codes + (row0 < n ? row0 : 0) * rcb, (int64_t)rows_w * rcb);
+  const Rsrc srs = make_rsrc(scales + (row0 < n ? row0 : 0) * rsb, (int64_t)rows_w * rsb);
+  const int su0 = min(nunits, s * ups), su1 = min(nunits, su0 + ups);
+  const int lr = lane >> 3, lj = lane & 7;
+  const int cvo0 = lr < rows_w ? lr * rcb + 16 * lj : kOob;
+  const int cvo1 = lr + 8 < rows_w ? (lr + 8) * rcb + 16 * lj : kOob;
+  const int svo = (lane >> 2) < rows_w ? (lane >> 2) * rsb + 4 * (lane & 3) : kOob;
+  struct Unit {
+    u32x4_t c0, c1;
+    uint32_t s;
+  };
+  auto load = [&](Unit& r, int u) {
+    const bool ok = u < su1;
+    const int co = ok ? u * 128 : kOob, so = ok ? u * 16 : kOob;
+    r.c0 = __builtin_amdgcn_raw_buffer_load_b128(crs, cvo0, co, 2);
+    r.c1 = __builtin_amdgcn_raw_buffer_load_b128(crs, cvo1, co, 2);
+    r.s = __builtin_amdgcn_raw_buffer_load_b32(srs, svo, so, 0);
+  };
+  Unit ring[D];
+#pragma unroll
+  for (int d = 0; d < D; d++) {
+    __builtin_amdgcn_sched_barrier(0);
+    load(ring[d], su0 + d);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  uint32_t acc = 0u;
+  for (int u = su0; u < su1; u += D) {
+#pragma unroll
+    for (int d = 0; d < D; d++) {
+      acc ^= ring[d].c0[0] ^ ring[d].c0[1] ^ ring[d].c0[2] ^ ring[d].c0[3] ^ ring[d].c1[0] ^ ring[d].c1[1] ^
+             ring[d].c1[2] ^ ring[d].c1[3] ^ ring[d].s;
+      load(ring[d], u + d + D);
+    }
+  }
+  if (acc == 0x9E3779B9u) sink[0] = acc;  // keeps the loads; practically never taken
+}
+
+template <int TR>
+int launch_read_tiles(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k, int ups, int64_t grid,
+                      uint32_t* sink, hipStream_t stream) {
+  hipLaunchKernelGGL((read_tiles_kernel<TR, 8 / TR>), dim3((unsigned)grid), dim3(512), 0, stream, codes, scales,
+                     n, k, ups, sink);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
 }  // namespace
 
 extern "C" {
@@ -120,6 +189,28 @@ int rzc_read(const void* const* p, const int64_t* n, int count, uint32_t* sink, 
   const int64_t grid = (run + kTileChunks - 1) / kTileChunks;
   hipLaunchKernelGGL(read_kernel, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, a);
   return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// The weight loads of the small-batch streaming product for a packed weight
+// of n rows and k columns (k % 256 == 0): codes (n x k/2 bytes) and scales
+// (n x k/16 bytes), the product's launch plan for cus CUs.
+int rzc_read_tiles(const void* codes, const void* scales, int64_t n, int64_t k, int cus, uint32_t* sink,
+                   void* stream) {
+  if (n < 1 || k < 256 || k % 256 || k >= (1LL << 24) || cus < 1) return 1;
+  const int64_t tiles = (n + 15) / 16, nunits = k / 256;
+  int tr = 8;
+  while (tr > 1 && (tiles + tr - 1) / tr < cus) tr /= 2;
+  const int ks = 8 / tr, ups = (int)((nunits + ks - 1) / ks);
+  const int64_t grid = (tiles + tr - 1) / tr;
+  const uint8_t* c = (const uint8_t*)codes;
+  const uint8_t* sc = (const uint8_t*)scales;
+  hipStream_t st = (hipStream_t)stream;
+  switch (tr) {
+    case 1: return launch_read_tiles<1>(c, sc, n, k, ups, grid, sink, st);
+    case 2: return launch_read_tiles<2>(c, sc, n, k, ups, grid, sink, st);
+    case 4: return launch_read_tiles<4>(c, sc, n, k, ups, grid, sink, st);
+    default: return launch_read_tiles<8>(c, sc, n, k, ups, grid, sink, st);
+  }
 }
 
 // iters pairs of independent MFMAs per wave on wgs workgroups of four waves;
