@@ -1,6 +1,6 @@
-// rz_bdiag.hip -- W4A16 product for 2..8 activation rows on weights in the
-// default layout (16-element blocks, byte scales), y[M, N] = x[M, K] * W^T,
-// K a multiple of 256.
+// rz_bdiag.hip -- W4A16 product for 2..8 activation rows, y[M, N] = x[M, K] * W^T,
+// K a multiple of 256, on weights in the default layout (16-element blocks,
+// byte scales) or in the 128-element FP16-scale layout.
 //
 // "RaZeR: Pushing the Limits of NVFP4 Quantization with Redundant Zero
 // Remapping" (papernotes.org notes), Key design 3: the weight-only kernels
@@ -123,7 +123,15 @@ __device__ __forceinline__ int stage_slot(int r, int j) { return r * 8 + (j ^ ((
 // 2i + 1, lane group q taking elements 32i + 8q .. +7 (code dword 4i + q of
 // the unit), so D[4q + e][c] is vector 4 (q & 1) + e times block 2i + q / 2
 // of row c.  Eight MFMAs per unit and product instead of sixteen.
-template <typename XT, int KIND, int VG, int TR, int KS, int D>
+//
+// F16S: weights in the 128-element FP16-scale layout (the scale word's sign
+// and top exponent bit carry the special value's sign and pair).  A lane's K
+// slots of one unit lie in one 128-element block (four-slot: group q in block
+// q / 2; two-slot: MFMAs 0..3 in block 0, 4..7 in block 1), so d0 and d1 are
+// accumulated over the whole unit (four-slot) or over four MFMAs (two-slot)
+// and the two coefficients, computed from the lane's scale word, are applied
+// once per unit or twice.
+template <typename XT, int KIND, int VG, int TR, int KS, int D, bool F16S>
 __global__ __launch_bounds__(64 * TR * KS) void bdiag_kernel(BdArgs a) {
   typedef typename BdOps<XT>::V V;
   constexpr bool TWO = VG == 8;                      // the two-slot mapping
@@ -150,7 +158,7 @@ __global__ __launch_bounds__(64 * TR * KS) void bdiag_kernel(BdArgs a) {
   const int nunits = (int)(a.k / 256);
   const int64_t row0 = ((int64_t)blockIdx.x * TR + t) * 16;
   const int rows_w = (int)max((int64_t)0, min((int64_t)16, a.n - row0));
-  const int rcb = (int)(a.k / 2), rsb = (int)(a.k / 16);
+  const int rcb = (int)(a.k / 2), rsb = (int)(F16S ? a.k / 64 : a.k / 16);
   const Rsrc crs = make_rsrc(a.codes + (row0 < a.n ? row0 : 0) * rcb, (int64_t)rows_w * rcb);
   const Rsrc srs = make_rsrc(a.scales + (row0 < a.n ? row0 : 0) * rsb, (int64_t)rows_w * rsb);
   const Rsrc xrs = make_rsrc(a.x, (int64_t)a.m * a.k * 2);
@@ -161,14 +169,17 @@ __global__ __launch_bounds__(64 * TR * KS) void bdiag_kernel(BdArgs a) {
   const int lr = lane >> 3, lj = lane & 7;
   const int cvo0 = lr < rows_w ? lr * rcb + 16 * lj : kOob;
   const int cvo1 = lr + 8 < rows_w ? (lr + 8) * rcb + 16 * lj : kOob;
-  const int svo = (lane >> 2) < rows_w ? (lane >> 2) * rsb + 4 * (lane & 3) : kOob;
+  // scales: byte layout, lane i -> row i >> 2, bytes 4 (i & 3) of the unit's
+  // 16; FP16-scale layout, lane i < 16 -> row i, the unit's two words
+  const int svo = F16S ? (lane < 16 && lane < rows_w ? lane * rsb : kOob)
+                       : ((lane >> 2) < rows_w ? (lane >> 2) * rsb + 4 * (lane & 3) : kOob);
   struct Unit {
     u32x4_t c0, c1;
     uint32_t s;
   };
   auto load = [&](Unit& r, int u) {
     const bool ok = u < su1;
-    const int co = ok ? u * 128 : kOob, so = ok ? u * 16 : kOob;
+    const int co = ok ? u * 128 : kOob, so = ok ? u * (F16S ? 4 : 16) : kOob;
     r.c0 = __builtin_amdgcn_raw_buffer_load_b128(crs, cvo0, co, kNt);
     r.c1 = __builtin_amdgcn_raw_buffer_load_b128(crs, cvo1, co, kNt);
     r.s = __builtin_amdgcn_raw_buffer_load_b32(srs, svo, so, 0);
@@ -261,8 +272,36 @@ __global__ __launch_bounds__(64 * TR * KS) void bdiag_kernel(BdArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; i++) cw[i] = *(const uint32_t*)(st + stage_slot(c, i) * 16 + 4 * q);
     const u32x4_t sr = *(const u32x4_t*)(st + 2048 + 16 * c);
+    const uint32_t sw16 = *(const uint32_t*)(st + 2048 + 4 * c);  // FP16-scale: row c's two words
     wave_lds_sync();
     const uint8_t* xb = xl + (diag ? xa_diag + buf * KS * XU : xa_zero);
+    if constexpr (F16S) {
+#pragma unroll
+      for (int h = 0; h < 2; h++) {  // block h: MFMAs 4h .. 4h + 3
+        f32x4_t d0 = {0.f, 0.f, 0.f, 0.f}, d1 = d0;
+#pragma unroll
+        for (int i = 4 * h; i < 4 * h + 4; i++) {
+          const uint32_t w = cw[i];
+          const uint32_t p0 = BdOps<XT>::template cvt<0>(w), p1 = BdOps<XT>::template cvt<1>(w);
+          const uint32_t p2 = BdOps<XT>::template cvt<2>(w), p3 = BdOps<XT>::template cvt<3>(w);
+          const u32x4_t p = {p0, p1, p2, p3};
+          const u32x4_t pm = {mark_remapped(p0, BdOps<XT>::kQuarterNeg2), mark_remapped(p1, BdOps<XT>::kQuarterNeg2),
+                              mark_remapped(p2, BdOps<XT>::kQuarterNeg2), mark_remapped(p3, BdOps<XT>::kQuarterNeg2)};
+          const V xa = *(const V*)(xb + i * 512);
+          d0 = BdOps<XT>::mfma(xa, __builtin_bit_cast(V, p), d0);
+          d1 = BdOps<XT>::mfma(xa, __builtin_bit_cast(V, pm), d1);
+        }
+        const uint32_t wd = (sw16 >> (16 * h)) & 0xFFFFu;
+        const float sb = scale_of_f16word(wd), sv = special_of_f16word(wd, a.m0, a.m1);
+        const float f0 = sb * (1.0f + 4.0f * sv), f1 = -4.0f * sb * sv;
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          acc[0][e] = fmaf(d0[e], f0, acc[0][e]);
+          acc[0][e] = fmaf(d1[e], f1, acc[0][e]);
+        }
+      }
+      return;
+    }
     const int sh = 8 * (q >> 1);
 #pragma unroll
     for (int i = 0; i < 8; i++) {
@@ -296,10 +335,44 @@ __global__ __launch_bounds__(64 * TR * KS) void bdiag_kernel(BdArgs a) {
     *(uint32_t*)(st + 2048 + 4 * lane) = r.s;
     wave_lds_sync();
     const u32x4_t lo = *(const u32x4_t*)(st + r0), hi = *(const u32x4_t*)(st + r1);
-    const uint32_t sw = *(const uint32_t*)(st + 2048 + 16 * c + 4 * q);
+    const uint32_t sw = F16S ? *(const uint32_t*)(st + 2048 + 4 * c) : *(const uint32_t*)(st + 2048 + 16 * c + 4 * q);
     wave_lds_sync();
     const uint8_t* xb = xl + (diag ? xa_diag + buf * KS * XU : xa_zero);
     const uint32_t cw[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    if constexpr (F16S) {  // the unit's K slots of lane group q lie in block q / 2
+      f32x4_t d0[NG], d1[NG];
+#pragma unroll
+      for (int g = 0; g < NG; g++) {
+        d0[g] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+        d1[g] = d0[g];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const uint32_t w = cw[i];
+        const uint32_t p0 = BdOps<XT>::template cvt<0>(w), p1 = BdOps<XT>::template cvt<1>(w);
+        const uint32_t p2 = BdOps<XT>::template cvt<2>(w), p3 = BdOps<XT>::template cvt<3>(w);
+        const u32x4_t p = {p0, p1, p2, p3};
+        const u32x4_t pm = {mark_remapped(p0, BdOps<XT>::kQuarterNeg2), mark_remapped(p1, BdOps<XT>::kQuarterNeg2),
+                            mark_remapped(p2, BdOps<XT>::kQuarterNeg2), mark_remapped(p3, BdOps<XT>::kQuarterNeg2)};
+#pragma unroll
+        for (int g = 0; g < NG; g++) {
+          const V xa = *(const V*)(xb + (i * NG + g) * 256);
+          d0[g] = BdOps<XT>::mfma(xa, __builtin_bit_cast(V, p), d0[g]);
+          d1[g] = BdOps<XT>::mfma(xa, __builtin_bit_cast(V, pm), d1[g]);
+        }
+      }
+      const uint32_t wd = (sw >> (16 * (q >> 1))) & 0xFFFFu;
+      const float sb = scale_of_f16word(wd), sv = special_of_f16word(wd, a.m0, a.m1);
+      const float f0 = sb * (1.0f + 4.0f * sv), f1 = -4.0f * sb * sv;
+#pragma unroll
+      for (int g = 0; g < NG; g++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          acc[g][e] = fmaf(d0[g][e], f0, acc[g][e]);
+          acc[g][e] = fmaf(d1[g][e], f1, acc[g][e]);
+        }
+      return;
+    }
 #pragma unroll
     for (int b = 0; b < 4; b++) {
       f32x4_t d0[NG], d1[NG];
@@ -404,32 +477,32 @@ BdPlan plan_bdiag(int64_t m, int64_t n, int64_t k, bool untrimmed) {
   return p;
 }
 
-template <typename XT, int KIND, int VG, int TR>
+template <typename XT, int KIND, int VG, int TR, bool F16S>
 hipError_t launch_cfg(const BdArgs& a, const BdPlan& p, hipStream_t stream) {
   constexpr int KS = 8 / TR;
   if (p.d == 4)
-    hipLaunchKernelGGL((bdiag_kernel<XT, KIND, VG, TR, KS, 4>), dim3((unsigned)p.grid), dim3(64 * TR * KS), 0,
-                       stream, a);
+    hipLaunchKernelGGL((bdiag_kernel<XT, KIND, VG, TR, KS, 4, F16S>), dim3((unsigned)p.grid), dim3(64 * TR * KS),
+                       0, stream, a);
   else
-    hipLaunchKernelGGL((bdiag_kernel<XT, KIND, VG, TR, KS, 2>), dim3((unsigned)p.grid), dim3(64 * TR * KS), 0,
-                       stream, a);
+    hipLaunchKernelGGL((bdiag_kernel<XT, KIND, VG, TR, KS, 2, F16S>), dim3((unsigned)p.grid), dim3(64 * TR * KS),
+                       0, stream, a);
   return hipGetLastError();
 }
 
-template <typename XT, int KIND, int VG>
+template <typename XT, int KIND, int VG, bool F16S>
 hipError_t dispatch_tr(const BdArgs& a, const BdPlan& p, hipStream_t stream) {
   switch (p.tr) {
-    case 1: return launch_cfg<XT, KIND, VG, 1>(a, p, stream);
-    case 2: return launch_cfg<XT, KIND, VG, 2>(a, p, stream);
-    case 4: return launch_cfg<XT, KIND, VG, 4>(a, p, stream);
-    case 8: return launch_cfg<XT, KIND, VG, 8>(a, p, stream);
+    case 1: return launch_cfg<XT, KIND, VG, 1, F16S>(a, p, stream);
+    case 2: return launch_cfg<XT, KIND, VG, 2, F16S>(a, p, stream);
+    case 4: return launch_cfg<XT, KIND, VG, 4, F16S>(a, p, stream);
+    case 8: return launch_cfg<XT, KIND, VG, 8, F16S>(a, p, stream);
   }
   return hipErrorInvalidValue;
 }
 
-template <typename XT, int KIND>
+template <typename XT, int KIND, bool F16S = false>
 hipError_t dispatch_vg(const BdArgs& a, const BdPlan& p, hipStream_t stream) {
-  return p.vg == 1 ? dispatch_tr<XT, KIND, 1>(a, p, stream) : dispatch_tr<XT, KIND, 8>(a, p, stream);
+  return p.vg == 1 ? dispatch_tr<XT, KIND, 1, F16S>(a, p, stream) : dispatch_tr<XT, KIND, 8, F16S>(a, p, stream);
 }
 
 }  // namespace
@@ -440,7 +513,8 @@ bool bdiag_supported(int64_t m, int64_t n, int64_t k) {
 
 hipError_t launch_bdiag(const void* x, int x_dtype, int64_t m, const PackedView& w, void* y, int y_dtype,
                         hipStream_t stream) {
-  if (!default_layout(w) || !bdiag_supported(m, w.rows, w.cols)) return hipErrorNotSupported;
+  const bool f16s = w.blog2 == 7 && w.sfmt == 1 && w.kind == kWeight;
+  if (!(default_layout(w) || f16s) || !bdiag_supported(m, w.rows, w.cols)) return hipErrorNotSupported;
   if (x_dtype != kF16 && x_dtype != kBF16) return hipErrorInvalidValue;
   const BdPlan p = plan_bdiag(m, w.rows, w.cols, (w.flags & kFlagUntrimmed) != 0);
   BdArgs a;
@@ -456,6 +530,9 @@ hipError_t launch_bdiag(const void* x, int x_dtype, int64_t m, const PackedView&
   a.m0 = 6.0f + 0.5f * (float)w.off_half[0];
   a.m1 = 6.0f + 0.5f * (float)w.off_half[w.kind == kWeight ? 1 : 0];
   a.ups = p.ups;
+  if (f16s)
+    return x_dtype == kBF16 ? dispatch_vg<__bf16, kWeight, true>(a, p, stream)
+                            : dispatch_vg<_Float16, kWeight, true>(a, p, stream);
   if (x_dtype == kBF16)
     return w.kind == kWeight ? dispatch_vg<__bf16, kWeight>(a, p, stream) : dispatch_vg<__bf16, kAct>(a, p, stream);
   return w.kind == kWeight ? dispatch_vg<_Float16, kWeight>(a, p, stream) : dispatch_vg<_Float16, kAct>(a, p, stream);

@@ -911,7 +911,7 @@ static bool use_smallm(int64_t m, int64_t n, int64_t k) {
 
 size_t gemm_ws_need(int64_t m, int64_t n, int64_t k, bool f16s, bool untrimmed) {
   if (f16s) {
-    if (!use_batch_f16s(m, k)) return 0;
+    if (bdiag_supported(m, n, k) || !use_batch_f16s(m, k)) return 0;
     const BatchPlan p = batch_plan(m, n, k, untrimmed);
     return p.split > 1 ? (size_t)p.split * (size_t)m * (size_t)n * sizeof(float) : 0;
   }
@@ -986,13 +986,17 @@ static hipError_t run_batch(const XT* x, int64_t m, const PackedView& w, OT* y, 
   }
 }
 
-// The 128-element FP16-scale layout: the batch kernel for 2..32 rows, the
-// prefill kernel where it fits, else the generic tile kernel.
+// The 128-element FP16-scale layout: the block-diagonal kernel for 2..8 rows
+// (K % 256 == 0), the batch kernel up to 32 rows, the prefill kernel where it
+// fits, else the generic tile kernel.
 template <typename XT, int KIND, typename OT>
 static hipError_t run_gemm_f16s(const XT* x, int64_t m, const PackedView& w, OT* y, void* ws,
                                 hipStream_t stream) {
   const int64_t n = w.rows, k = w.cols;
   if (k % 128 != 0) return hipErrorInvalidValue;
+  if (KIND == kWeight && bdiag_supported(m, n, k))
+    return launch_bdiag(x, __is_same(XT, __bf16) ? kBF16 : kF16, m, w, y,
+                        sizeof(OT) == 4 ? kF32 : __is_same(OT, _Float16) ? kF16 : kBF16, stream);
   if (use_batch_f16s(m, k)) return run_batch<XT, KIND, OT, true>(x, m, w, y, ws, stream);
   if (tile256_fits(m, k, sizeof(XT))) return run_tile256<XT, KIND, OT, true>(x, m, w, y, nullptr, stream);
   const float m0 = 6.0f + 0.5f * (float)w.off_half[0];

@@ -28,7 +28,9 @@ def _f16s_weight(n, k, seed, offsets=(-2, -5)):
                                        (8, 520, 2048, torch.bfloat16), (16, 64, 4096, torch.float16),
                                        (17, 130, 384, torch.bfloat16), (32, 4100, 1024, torch.bfloat16),
                                        (100, 257, 512, torch.float16), (300, 260, 1152, torch.bfloat16),
-                                       (256, 96, 128, torch.float16)])
+                                       (256, 96, 128, torch.float16), (4, 1000, 4096, torch.float16),
+                                       (5, 77, 768, torch.bfloat16), (6, 200, 256, torch.float16),
+                                       (7, 33, 1280, torch.bfloat16)])
 def test_gemm_group128_f16_layout(m, n, k, xdt):
     _need_gpu()
     ref = _f16s_weight(n, k, m * 131 + n + k)
@@ -49,7 +51,7 @@ def _prefill_f16s():
     return oracle.quantize(oracle.WEIGHT, w, (-2, 4), block=128, scale_fmt=oracle.SCALE_F16)
 
 
-@pytest.mark.parametrize("m", [8, 2048])
+@pytest.mark.parametrize("m", [3, 8, 2048])
 def test_gemm_group128_f16_layout_full_size_sampled(m):
     """The prefill weight W[28672, 8192] in the 128-element FP16 layout, with
     8 rows (small batch) and 2048 rows (prefill), on 257 columns that cover
