@@ -30,7 +30,8 @@ def _f16s_weight(n, k, seed, offsets=(-2, -5)):
                                        (100, 257, 512, torch.float16), (300, 260, 1152, torch.bfloat16),
                                        (256, 96, 128, torch.float16), (4, 1000, 4096, torch.float16),
                                        (5, 77, 768, torch.bfloat16), (6, 200, 256, torch.float16),
-                                       (7, 33, 1280, torch.bfloat16)])
+                                       (7, 33, 1280, torch.bfloat16), (10, 8320, 1024, torch.float16),
+                                       (16, 8200, 512, torch.bfloat16)])
 def test_gemm_group128_f16_layout(m, n, k, xdt):
     _need_gpu()
     ref = _f16s_weight(n, k, m * 131 + n + k)
