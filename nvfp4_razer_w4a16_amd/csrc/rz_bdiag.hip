@@ -131,15 +131,24 @@ __device__ __forceinline__ int stage_slot(int r, int j) { return r * 8 + (j ^ ((
 // accumulated over the whole unit (four-slot) or over four MFMAs (two-slot)
 // and the two coefficients, computed from the lane's scale word, are applied
 // once per unit or twice.
+//
+// VG 16 or 32 (FP16-scale layout only, 9..32 vectors): no block diagonal.
+// With one scale per 128 elements an MFMA of the two-slot K layout (MFMA i:
+// elements 32i .. 32i + 31) lies in one block, so A is x itself (row r =
+// vector 16t + r of x tile t) and D[4q + e][c] is vector 16t + 4q + e times
+// 32 elements of block i / 4 of row c; d0 and d1 accumulate over the four
+// MFMAs of a block and take the block's two coefficients once.
 template <typename XT, int KIND, int VG, int TR, int KS, int D, bool F16S>
 __global__ __launch_bounds__(64 * TR * KS) void bdiag_kernel(BdArgs a) {
   typedef typename BdOps<XT>::V V;
-  constexpr bool TWO = VG == 8;                      // the two-slot mapping
-  constexpr int NG = TWO ? 1 : VG;                   // A groups per B operand
-  constexpr int NV = TWO ? 8 : 4 * VG;               // vectors
-  constexpr int NCH = TWO ? 256 : 128 * VG;          // 16-byte x chunks per unit
+  constexpr bool DENSE = VG >= 16;                   // x tiles of 16 vectors, no diagonal
+  static_assert(!DENSE || F16S, "the dense form needs one scale per 128 elements");
+  constexpr bool TWO = VG == 8 || DENSE;             // the two-slot K layout
+  constexpr int NG = DENSE ? VG / 16 : TWO ? 1 : VG; // A groups (x tiles) per B operand
+  constexpr int NV = DENSE ? VG : TWO ? 8 : 4 * VG;  // vectors
+  constexpr int NCH = DENSE ? 512 * NG : TWO ? 256 : 128 * VG;  // 16-byte x chunks per unit
   constexpr int XU = NCH * 16;                       // LDS bytes of x per K unit
-  constexpr int ZB = XU + 256;                       // zero region
+  constexpr int ZB = DENSE ? 256 : XU + 256;         // zero region
   constexpr int NW = TR * KS;
   constexpr int XCH = (KS * NCH + 64 * NW - 1) / (64 * NW);  // x chunks per thread and step
   static_assert(D % 2 == 0, "the x buffers alternate with the step parity");
@@ -148,7 +157,8 @@ __global__ __launch_bounds__(64 * TR * KS) void bdiag_kernel(BdArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t stage[NW][kStage];
   // zero region, then two x buffers of KS units.  Unit chunk, four-slot:
   // (i * VG + g) * 16 + 4 q + v holds x[4g + v][elements 64q + 8i ..];
-  // two-slot: (i * 4 + q) * 8 + v holds x[v][elements 32i + 8q ..].
+  // two-slot: (i * 4 + q) * 8 + v holds x[v][elements 32i + 8q ..];
+  // dense: ((i * NG + g) * 4 + q) * 16 + v holds x[16g + v][elements 32i + 8q ..].
   __shared__ __attribute__((aligned(256))) uint8_t xl[ZB + 2 * KS * XU];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -195,7 +205,10 @@ __global__ __launch_bounds__(64 * TR * KS) void bdiag_kernel(BdArgs a) {
     const int ch = tid + h * 64 * NW;
     const int sl = ch / NCH, w = ch % NCH;
     int vec, el;
-    if constexpr (TWO) {
+    if constexpr (DENSE) {
+      vec = 16 * ((w >> 6) % NG) + (w & 15);
+      el = 32 * ((w >> 6) / NG) + 8 * ((w >> 4) & 3);
+    } else if constexpr (TWO) {
       vec = w & 7;
       el = 32 * (w >> 5) + 8 * ((w >> 3) & 3);
     } else {
@@ -251,9 +264,9 @@ __global__ __launch_bounds__(64 * TR * KS) void bdiag_kernel(BdArgs a) {
   // diagonal lanes of their group read: four-slot, group q reads banks
   // 16q .. 16q + 15 of a 256-byte window and its zeros sit at 64 ((q + 1) & 3);
   // two-slot, group q reads the (q & 1) half and its zeros sit in the other.
-  const bool diag = TWO ? (c >> 3) == (q >> 1) : (c >> 2) == q;
+  const bool diag = DENSE || (TWO ? (c >> 3) == (q >> 1) : (c >> 2) == q);
   const int xa_zero = TWO ? 128 * (~q & 1) : 64 * ((q + 1) & 3);
-  const int xa_diag = ZB + s * XU + (TWO ? (8 * q + (c & 7)) * 16 : c * 16);
+  const int xa_diag = ZB + s * XU + (DENSE ? (16 * q + c) * 16 : TWO ? (8 * q + (c & 7)) * 16 : c * 16);
   uint8_t* st = stage[wave];
   const int w0 = stage_slot(lr, lj) * 16, w1 = stage_slot(lr + 8, lj) * 16;
   const int r0 = stage_slot(c, 2 * q) * 16, r1 = stage_slot(c, 2 * q + 1) * 16;
@@ -278,7 +291,13 @@ __global__ __launch_bounds__(64 * TR * KS) void bdiag_kernel(BdArgs a) {
     if constexpr (F16S) {
 #pragma unroll
       for (int h = 0; h < 2; h++) {  // block h: MFMAs 4h .. 4h + 3
-        f32x4_t d0 = {0.f, 0.f, 0.f, 0.f}, d1 = d0;
+        constexpr int kFrag = DENSE ? 1024 : 512;  // bytes of the chunks of one A fragment
+        f32x4_t d0[NG], d1[NG];
+#pragma unroll
+        for (int g = 0; g < NG; g++) {
+          d0[g] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+          d1[g] = d0[g];
+        }
 #pragma unroll
         for (int i = 4 * h; i < 4 * h + 4; i++) {
           const uint32_t w = cw[i];
@@ -287,18 +306,23 @@ __global__ __launch_bounds__(64 * TR * KS) void bdiag_kernel(BdArgs a) {
           const u32x4_t p = {p0, p1, p2, p3};
           const u32x4_t pm = {mark_remapped(p0, BdOps<XT>::kQuarterNeg2), mark_remapped(p1, BdOps<XT>::kQuarterNeg2),
                               mark_remapped(p2, BdOps<XT>::kQuarterNeg2), mark_remapped(p3, BdOps<XT>::kQuarterNeg2)};
-          const V xa = *(const V*)(xb + i * 512);
-          d0 = BdOps<XT>::mfma(xa, __builtin_bit_cast(V, p), d0);
-          d1 = BdOps<XT>::mfma(xa, __builtin_bit_cast(V, pm), d1);
+#pragma unroll
+          for (int g = 0; g < NG; g++) {
+            const V xa = *(const V*)(xb + (i * NG + g) * kFrag);
+            d0[g] = BdOps<XT>::mfma(xa, __builtin_bit_cast(V, p), d0[g]);
+            d1[g] = BdOps<XT>::mfma(xa, __builtin_bit_cast(V, pm), d1[g]);
+          }
         }
         const uint32_t wd = (sw16 >> (16 * h)) & 0xFFFFu;
         const float sb = scale_of_f16word(wd), sv = special_of_f16word(wd, a.m0, a.m1);
         const float f0 = sb * (1.0f + 4.0f * sv), f1 = -4.0f * sb * sv;
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
-          acc[0][e] = fmaf(d0[e], f0, acc[0][e]);
-          acc[0][e] = fmaf(d1[e], f1, acc[0][e]);
-        }
+        for (int g = 0; g < NG; g++)
+#pragma unroll
+          for (int e = 0; e < 4; e++) {
+            acc[g][e] = fmaf(d0[g][e], f0, acc[g][e]);
+            acc[g][e] = fmaf(d1[g][e], f1, acc[g][e]);
+          }
       }
       return;
     }
@@ -430,6 +454,10 @@ __global__ __launch_bounds__(64 * TR * KS) void bdiag_kernel(BdArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; e++) {
       float v = acc[g][e];
+      if constexpr (DENSE) {  // lane group q holds vectors 16g + 4q + e
+        red[s][t][16 * g + 4 * q + e][c] = v;
+        continue;
+      }
       if constexpr (!TWO) v += __shfl_xor(v, 16);
       v += __shfl_xor(v, 32);
       if constexpr (TWO) {
@@ -462,14 +490,17 @@ struct BdPlan {
 
 // Eight waves per workgroup.  TR, the tiles per workgroup, is the largest
 // power of two that still gives every CU a workgroup; the other waves split K.
-BdPlan plan_bdiag(int64_t m, int64_t n, int64_t k, bool untrimmed) {
+// Dense x tiles (FP16-scale layout): 16 vectors take any plan (eight K slices
+// of 8 KiB of x per unit still fit in LDS); 32 vectors take 8 tiles x 1 slice
+// (see fp16s_supported).
+BdPlan plan_bdiag(int64_t m, int64_t n, int64_t k, bool untrimmed, bool f16s) {
   BdPlan p;
-  p.vg = m <= 4 ? 1 : 8;
+  p.vg = m <= 4 ? 1 : m <= 8 ? 8 : (f16s && m <= 16) ? 16 : 32;
   const int64_t tiles = (n + 15) / 16, cus = device_cu_count();
   const int64_t nunits = k / 256;
   p.tr = 8;
-  while (p.tr > 1 && (tiles + p.tr - 1) / p.tr < cus) p.tr /= 2;
-  if (untrimmed) p.tr = 1;  // the most waves per tile
+  while (p.vg != 32 && p.tr > 1 && (tiles + p.tr - 1) / p.tr < cus) p.tr /= 2;
+  if (untrimmed && p.vg != 32) p.tr = 1;  // the most waves per tile
   p.ks = 8 / p.tr;
   p.ups = (int)((nunits + p.ks - 1) / p.ks);
   p.d = p.ups >= 8 ? 4 : 2;
@@ -480,6 +511,9 @@ BdPlan plan_bdiag(int64_t m, int64_t n, int64_t k, bool untrimmed) {
 template <typename XT, int KIND, int VG, int TR, bool F16S>
 hipError_t launch_cfg(const BdArgs& a, const BdPlan& p, hipStream_t stream) {
   constexpr int KS = 8 / TR;
+  if constexpr (VG == 32 && KS > 1) {  // x of two slices of 32 vectors is too much LDS
+    return hipErrorNotSupported;
+  } else {
   if (p.d == 4)
     hipLaunchKernelGGL((bdiag_kernel<XT, KIND, VG, TR, KS, 4, F16S>), dim3((unsigned)p.grid), dim3(64 * TR * KS),
                        0, stream, a);
@@ -487,6 +521,7 @@ hipError_t launch_cfg(const BdArgs& a, const BdPlan& p, hipStream_t stream) {
     hipLaunchKernelGGL((bdiag_kernel<XT, KIND, VG, TR, KS, 2, F16S>), dim3((unsigned)p.grid), dim3(64 * TR * KS),
                        0, stream, a);
   return hipGetLastError();
+  }
 }
 
 template <typename XT, int KIND, int VG, bool F16S>
@@ -502,7 +537,13 @@ hipError_t dispatch_tr(const BdArgs& a, const BdPlan& p, hipStream_t stream) {
 
 template <typename XT, int KIND, bool F16S = false>
 hipError_t dispatch_vg(const BdArgs& a, const BdPlan& p, hipStream_t stream) {
-  return p.vg == 1 ? dispatch_tr<XT, KIND, 1, F16S>(a, p, stream) : dispatch_tr<XT, KIND, 8, F16S>(a, p, stream);
+  if (p.vg == 1) return dispatch_tr<XT, KIND, 1, F16S>(a, p, stream);
+  if (p.vg == 8) return dispatch_tr<XT, KIND, 8, F16S>(a, p, stream);
+  if constexpr (F16S) {
+    if (p.vg == 16) return dispatch_tr<XT, KIND, 16, F16S>(a, p, stream);
+    if (p.vg == 32) return dispatch_tr<XT, KIND, 32, F16S>(a, p, stream);
+  }
+  return hipErrorNotSupported;
 }
 
 }  // namespace
@@ -511,12 +552,20 @@ bool bdiag_supported(int64_t m, int64_t n, int64_t k) {
   return m >= 2 && m <= 8 && n >= 1 && n < (1LL << 31) && k >= 256 && k % 256 == 0 && k < (1LL << 24);
 }
 
+// FP16-scale layout: 2..16 rows, and 17..32 rows on weights of at least
+// 4 x 16 rows per CU (their plan puts 8 tiles in a workgroup).
+bool fp16s_supported(int64_t m, int64_t n, int64_t k) {
+  if (m > 16 && (n + 15) / 16 < 4LL * device_cu_count()) return false;
+  return m >= 2 && m <= 32 && n >= 1 && n < (1LL << 31) && k >= 256 && k % 256 == 0 && k < (1LL << 24);
+}
+
 hipError_t launch_bdiag(const void* x, int x_dtype, int64_t m, const PackedView& w, void* y, int y_dtype,
                         hipStream_t stream) {
   const bool f16s = w.blog2 == 7 && w.sfmt == 1 && w.kind == kWeight;
-  if (!(default_layout(w) || f16s) || !bdiag_supported(m, w.rows, w.cols)) return hipErrorNotSupported;
+  if (!(default_layout(w) || f16s)) return hipErrorNotSupported;
+  if (f16s ? !fp16s_supported(m, w.rows, w.cols) : !bdiag_supported(m, w.rows, w.cols)) return hipErrorNotSupported;
   if (x_dtype != kF16 && x_dtype != kBF16) return hipErrorInvalidValue;
-  const BdPlan p = plan_bdiag(m, w.rows, w.cols, (w.flags & kFlagUntrimmed) != 0);
+  const BdPlan p = plan_bdiag(m, w.rows, w.cols, (w.flags & kFlagUntrimmed) != 0, f16s);
   BdArgs a;
   a.x = x;
   a.codes = w.codes;

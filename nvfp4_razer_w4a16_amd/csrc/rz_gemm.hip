@@ -911,7 +911,7 @@ static bool use_smallm(int64_t m, int64_t n, int64_t k) {
 
 size_t gemm_ws_need(int64_t m, int64_t n, int64_t k, bool f16s, bool untrimmed) {
   if (f16s) {
-    if (bdiag_supported(m, n, k) || !use_batch_f16s(m, k)) return 0;
+    if (fp16s_supported(m, n, k) || !use_batch_f16s(m, k)) return 0;
     const BatchPlan p = batch_plan(m, n, k, untrimmed);
     return p.split > 1 ? (size_t)p.split * (size_t)m * (size_t)n * sizeof(float) : 0;
   }
@@ -986,15 +986,16 @@ static hipError_t run_batch(const XT* x, int64_t m, const PackedView& w, OT* y, 
   }
 }
 
-// The 128-element FP16-scale layout: the block-diagonal kernel for 2..8 rows
-// (K % 256 == 0), the batch kernel up to 32 rows, the prefill kernel where it
+// The 128-element FP16-scale layout: the streaming kernel for 2..32 rows
+// (K % 256 == 0; 17..32 on large weights), the batch kernel up to 32 rows
+// otherwise, the prefill kernel where it
 // fits, else the generic tile kernel.
 template <typename XT, int KIND, typename OT>
 static hipError_t run_gemm_f16s(const XT* x, int64_t m, const PackedView& w, OT* y, void* ws,
                                 hipStream_t stream) {
   const int64_t n = w.rows, k = w.cols;
   if (k % 128 != 0) return hipErrorInvalidValue;
-  if (KIND == kWeight && bdiag_supported(m, n, k))
+  if (KIND == kWeight && fp16s_supported(m, n, k))
     return launch_bdiag(x, __is_same(XT, __bf16) ? kBF16 : kF16, m, w, y,
                         sizeof(OT) == 4 ? kF32 : __is_same(OT, _Float16) ? kF16 : kBF16, stream);
   if (use_batch_f16s(m, k)) return run_batch<XT, KIND, OT, true>(x, m, w, y, ws, stream);

@@ -82,6 +82,8 @@ hipError_t launch_smallm(const void* x, int x_dtype, int64_t m, const PackedView
 // Block-diagonal MFMA kernel for 2..8 activation rows (default layout,
 // K % 256 == 0); no workspace.
 bool bdiag_supported(int64_t m, int64_t n, int64_t k);
+// The same kernel on the FP16-scale layout (2..32 rows, dense x tiles above 8).
+bool fp16s_supported(int64_t m, int64_t n, int64_t k);
 hipError_t launch_bdiag(const void* x, int x_dtype, int64_t m, const PackedView& w, void* y, int y_dtype,
                         hipStream_t stream);
 

@@ -31,7 +31,8 @@ def _f16s_weight(n, k, seed, offsets=(-2, -5)):
                                        (256, 96, 128, torch.float16), (4, 1000, 4096, torch.float16),
                                        (5, 77, 768, torch.bfloat16), (6, 200, 256, torch.float16),
                                        (7, 33, 1280, torch.bfloat16), (10, 8320, 1024, torch.float16),
-                                       (16, 8200, 512, torch.bfloat16)])
+                                       (16, 8200, 512, torch.bfloat16), (24, 16400, 512, torch.float16),
+                                       (9, 200, 768, torch.bfloat16)])
 def test_gemm_group128_f16_layout(m, n, k, xdt):
     _need_gpu()
     ref = _f16s_weight(n, k, m * 131 + n + k)
@@ -52,7 +53,7 @@ def _prefill_f16s():
     return oracle.quantize(oracle.WEIGHT, w, (-2, 4), block=128, scale_fmt=oracle.SCALE_F16)
 
 
-@pytest.mark.parametrize("m", [3, 8, 2048])
+@pytest.mark.parametrize("m", [3, 8, 12, 32, 2048])
 def test_gemm_group128_f16_layout_full_size_sampled(m):
     """The prefill weight W[28672, 8192] in the 128-element FP16 layout, with
     8 rows (small batch) and 2048 rows (prefill), on 257 columns that cover
