@@ -99,6 +99,22 @@ def test_untrimmed_plan_matches_the_oracle(m, n, k):
         assert torch.equal(yg, y[0])
 
 
+@pytest.mark.parametrize("m,n,k", [(4, 2048, 1024), (12, 2100, 768), (6, 300, 4096)])
+def test_untrimmed_plan_on_the_fp16_scale_layout(m, n, k):
+    """The FP16-scale products with the untrimmed plan (one tile and eight K
+    slices per workgroup on the streaming kernel) stay within tolerance of the
+    oracle, and so does the tuned plan on the same operands."""
+    _need_gpu()
+    ref = _f16s_weight(n, k, 7 * m + n + k, offsets=(-2, 4))
+    rng = np.random.default_rng(m + 3 * n + k)
+    x = torch.from_numpy(rng.standard_normal((m, k)).astype(np.float32)).to(torch.bfloat16)
+    y_ref, nrm = oracle.gemm_any(as_f32(x), ref)
+    t = to_device(ref)
+    for tt in (t, t.with_flags(rz.RAZER_FLAG_UNTRIMMED_PLAN)):
+        y = rz.razer_gemm(x.cuda(), tt, torch.float32).cpu().numpy()
+        assert_product_close(y, y_ref, nrm, f"g128 untrimmed {m}x{n}x{k}")
+
+
 def test_encoders_reject_the_untrimmed_flag():
     _need_gpu()
     x = torch.randn(16, 64, device="cuda")
