@@ -220,20 +220,31 @@ __device__ __forceinline__ uint32_t search_fast(const float (&y)[16], float ymax
   // of 16 of them is exact in fp32; away from the window the term is 0
   // whatever the rounding.  Five operations per element instead of the
   // integer form's window tests, fma, conversion and multiply-add.
+  // h <= 1, so max(h - 2|u|, 0) is the fma with its result clamped to [0, 1].
+  // The window marks go straight to their nibbles (bit 4i of dword i / 8).
   bool sym_done = false;
   uint32_t sym_sel = 0u;
+  uint32_t sym_nib[2] = {0u, 0u};
   if constexpr (kPairs == 1) {
     if (prm.sym) {
       sym_done = true;
       if (ymax > prm.lo[0]) {
-        float dsum = 0.0f;
+        float dsum;
 #pragma unroll
         for (int j = 15; j >= 0; j--) {
-          const float e = __builtin_fmaf(fabsf(fabsf(y[j]) - prm.sym_m), -2.0f, prm.sym_h);
-          const float t = fmaxf(e, 0.0f);
-          dsum += __builtin_bit_cast(
+          const float u = fabsf(y[j]) - prm.sym_m;
+          float t;
+          asm("v_fma_f32 %0, |%1|, -2.0, %2 clamp" : "=v"(t) : "v"(u), "v"(prm.sym_h));
+          const float term = __builtin_bit_cast(
               float, __builtin_bit_cast(uint32_t, t) | (__builtin_bit_cast(uint32_t, y[j]) & 0x80000000u));
-          bits[0] = bits[0] + bits[0] + (e > 0.0f ? 1u : 0u);
+          dsum = j == 15 ? term : dsum + term;
+          // window mark: min(bits of t, 1) into bit 4 (j % 8) (asm keeps the
+          // compiler from turning it into a compare and a select)
+          uint32_t one;
+          asm("v_min_u32 %0, %1, 1" : "=v"(one) : "v"(__builtin_bit_cast(uint32_t, t)));
+          asm("v_lshl_or_b32 %0, %1, %2, %3"
+              : "=v"(sym_nib[j >> 3])
+              : "v"(one), "i"(4 * (j & 7)), "v"(sym_nib[j >> 3]));
         }
         sym_sel = dsum < 0.0f ? 1u : 0u;
       }
@@ -290,12 +301,21 @@ __device__ __forceinline__ uint32_t search_fast(const float (&y)[16], float ymax
   const uint32_t keep = (sel & 1u) ? 0u : 0x11111111u;
 #pragma unroll
   for (int h = 0; h < 2; h++) {
-    uint32_t x = (b >> (8 * h)) & 0xFFu;  // element 8h + i -> bit 4i
-    x = (x | (x << 12)) & 0x000F000Fu;
-    x = (x | (x << 6)) & 0x03030303u;
-    x = (x | (x << 3)) & 0x11111111u;
+    uint32_t x;
+    if (sym_done) {
+      x = sym_nib[h];
+    } else {
+      x = (b >> (8 * h)) & 0xFFu;  // element 8h + i -> bit 4i
+      x = (x | (x << 12)) & 0x000F000Fu;
+      x = (x | (x << 6)) & 0x03030303u;
+      x = (x | (x << 3)) & 0x11111111u;
+    }
     const uint32_t hit = x & ((w[h] >> 3) ^ keep);
-    w[h] = (w[h] & ~(hit * 15u)) | (hit << 3);
+    // 15 per hit nibble, as a shift and a subtract (written as asm: the
+    // compiler would fold them into a quarter-rate 32-bit multiply)
+    uint32_t nib;
+    asm("v_sub_u32 %0, %1, %2" : "=v"(nib) : "v"(hit << 4), "v"(hit));
+    w[h] = (w[h] & ~nib) | (hit << 3);
   }
   return sel;
 }
@@ -317,8 +337,17 @@ __device__ __forceinline__ void fp4_pack16(const float (&y)[16], uint32_t (&w)[2
   }
 }
 
+// 1 / (sb * st) for every block-scale code (sb * st, then one IEEE division:
+// the same two operations a block would do itself), built once per workgroup.
+template <int KIND> constexpr int kScaleCodes = KIND == kWeight ? 64 : 128;
 template <int KIND>
-__device__ __forceinline__ void encode_block(const float (&xf)[16], float amax, float st,
+__device__ __forceinline__ void build_rcp_table(float* rtab, float st) {
+  for (int c = threadIdx.x; c < kScaleCodes<KIND>; c += blockDim.x)
+    rtab[c] = 1.0f / (scale_of_code<KIND>((uint32_t)c) * st);
+}
+
+template <int KIND>
+__device__ __forceinline__ void encode_block(const float (&xf)[16], float amax, const float* rtab,
                                              const EncodeParams& prm, uint2& cw, uint32_t& sbyte) {
   constexpr float kSMax = KIND == kWeight ? 30.0f : 448.0f;
   constexpr int kPairs = KIND == kWeight ? 2 : 1;
@@ -331,9 +360,7 @@ __device__ __forceinline__ void encode_block(const float (&xf)[16], float amax, 
   const float sb_real = r * kSMax;
   const uint32_t scode = round_scale<KIND>(sb_real);
   if (scode == 0u) return;  // block underflows to zero
-  const float sb = scale_of_code<KIND>(scode);
-  const float d = sb * st;
-  const float rcp = 1.0f / d;
+  const float rcp = rtab[scode];  // 1 / (sb * st)
   if (!(rcp < INFINITY)) return;  // scale product underflowed: zero block
 
   float y[16];
@@ -517,6 +544,11 @@ __global__ __launch_bounds__(256) void encode_kernel(const T* __restrict__ x, in
   const float st = amax / (6.0f * kSMax);
   if (blockIdx.x == 0 && threadIdx.x == 0) *ts_out = nonfinite ? __builtin_nanf("") : st;
   const bool all_zero = nonfinite || amax == 0.0f;
+  __shared__ float rtab[kScaleCodes<KIND>];
+  if constexpr (!FOS) {
+    build_rcp_table<KIND>(rtab, st);
+    __syncthreads();
+  }
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -542,6 +574,11 @@ __global__ __launch_bounds__(256) void encode_kernel(const T* __restrict__ x, in
   };
   u32x4_t cur[kNI], nxt[kNI];
   load(bb, cur);
+  // Drain the first loads here: otherwise the loop head, which the compiler
+  // enters from two paths, waits (for the later steps) on the previous step's
+  // stores as well.
+#pragma unroll
+  for (int i = 0; i < kNI; i++) asm volatile("" ::"v"(cur[i]));
   uint8_t* stg = stage[wave];
   for (; bb < nblk; bb += step) {
     load(bb + step, nxt);
@@ -559,11 +596,17 @@ __global__ __launch_bounds__(256) void encode_kernel(const T* __restrict__ x, in
     if constexpr (FOS)
       encode_block_fos<KIND>(xf, amax, st, cw, sbyte);
     else
-      encode_block<KIND>(xf, amax, st, prm, cw, sbyte);
-    if (bb + lane < nblk) {
-      codes[bb + lane] = cw;
-      scales[bb + lane] = (uint8_t)sbyte;
-    }
+      encode_block<KIND>(xf, amax, rtab, prm, cw, sbyte);
+    // Buffer stores sized to the wave's valid blocks: lanes past the end are
+    // dropped by the range check, so the stores need no branch (a branch
+    // around them made every step wait for its stores to complete).
+    const int nval = (int)min(nblk - bb, (int64_t)64);
+    __builtin_amdgcn_raw_buffer_store_b64(
+        u32x2_t{cw.x, cw.y}, __builtin_amdgcn_make_buffer_rsrc((void*)(codes + bb), (short)0, nval * 8, 0x00020000),
+        lane * 8, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b8(
+        (uint8_t)sbyte, __builtin_amdgcn_make_buffer_rsrc((void*)(scales + bb), (short)0, nval, 0x00020000), lane,
+        0, 0);
 #pragma unroll
     for (int i = 0; i < kNI; i++) cur[i] = nxt[i];
   }
@@ -648,6 +691,9 @@ __global__ __launch_bounds__(256) void offset_sse_kernel(const T* __restrict__ x
   const bool nonfinite = m >= 0x7F800000u;
   const float amax = u2f(m);
   const float st = amax / (6.0f * 30.0f);
+  __shared__ float rtab[kScaleCodes<kWeight>];
+  build_rcp_table<kWeight>(rtab, st);
+  __syncthreads();
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -689,7 +735,7 @@ __global__ __launch_bounds__(256) void offset_sse_kernel(const T* __restrict__ x
           e.f[1] = prm.f1[o];
           uint2 cw;
           uint32_t sbyte;
-          encode_block<kWeight>(xf, amax, st, e, cw, sbyte);
+          encode_block<kWeight>(xf, amax, rtab, e, cw, sbyte);
           const double sbst = (double)scale_of_byte<kWeight>(sbyte) * st64;
           // the special value's sign is bit 7 of the scale byte, not the code's
           const double svm = (double)((sbyte & 0x40u) ? 0.5f * (float)prm.mag1[o] : prm.m0);
