@@ -38,6 +38,7 @@
 #include <math.h>
 
 #include <mutex>
+#include <type_traits>
 
 namespace rz {
 
@@ -147,17 +148,21 @@ template <> __device__ __forceinline__ uint32_t absbits_finish<_Float16>(uint32_
   return f2u((float)__builtin_bit_cast(_Float16, (uint16_t)m));
 }
 
-template <typename T>
+// KEEP: default-policy loads, so that a tensor that fits the memory-side cache
+// is still there for the encode pass, which reads it again right after this
+// one; larger tensors are streamed (non-temporal loads).
+template <typename T, bool KEEP>
 __global__ __launch_bounds__(256) void amax_partial_kernel(const uint4* __restrict__ x, int64_t nvec,
                                                            uint32_t* __restrict__ partial) {
   uint32_t m = 0;
   const int64_t stride = (int64_t)gridDim.x * 256;
   int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  auto ld = [&](int64_t j) { return KEEP ? x[j] : load_nt16(x + j); };
   for (; i + 3 * stride < nvec; i += 4 * stride) {
-    uint4 a = load_nt16(x + i);
-    uint4 b = load_nt16(x + i + stride);
-    uint4 c = load_nt16(x + i + 2 * stride);
-    uint4 d = load_nt16(x + i + 3 * stride);
+    uint4 a = ld(i);
+    uint4 b = ld(i + stride);
+    uint4 c = ld(i + 2 * stride);
+    uint4 d = ld(i + 3 * stride);
     m = max(m, max(max(absbits_max<T>(a), absbits_max<T>(b)), max(absbits_max<T>(c), absbits_max<T>(d))));
   }
   for (; i < nvec; i += stride) m = max(m, absbits_max<T>(x[i]));
@@ -166,6 +171,18 @@ __global__ __launch_bounds__(256) void amax_partial_kernel(const uint4* __restri
   if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) partial[blockIdx.x] = max(max(sm[0], sm[1]), max(sm[2], sm[3]));
+}
+
+// Tensors up to this size are read with default-policy loads in the amax pass
+// (the 256 MB memory-side cache then still holds them for the encode pass).
+constexpr int64_t kAmaxKeepBytes = 128ll << 20;
+
+template <typename T>
+static void launch_amax_partial(dim3 grid, hipStream_t stream, const uint4* x, int64_t nvec, uint32_t* partial) {
+  if (nvec * 16 <= kAmaxKeepBytes)
+    hipLaunchKernelGGL((amax_partial_kernel<T, true>), grid, dim3(256), 0, stream, x, nvec, partial);
+  else
+    hipLaunchKernelGGL((amax_partial_kernel<T, false>), grid, dim3(256), 0, stream, x, nvec, partial);
 }
 
 // ---- pass 2: block encode ----------------------------------------------------
@@ -185,6 +202,21 @@ template <int KIND> __device__ __forceinline__ uint32_t round_scale(float v) {
   b = (b + 0x7FFFFu + ((b >> 20) & 1u)) & 0xFFF00000u;
   uint32_t code = ((uint32_t)((int)(b >> 23) - 127 + kBias) << 3) | ((b >> 20) & 7u);
   return min(code, kMaxCode);
+}
+
+// round_scale for a block: sb_real = S_MAX * amax_b / amax never exceeds S_MAX.
+// For activations (OCP E4M3) the gfx950 fp32 -> fp8 conversion (scale 1)
+// gives the same code as round_scale on every fp32 value in [0, 448]
+// (nearest-even in the normal and subnormal ranges alike; checked on all of
+// them); weights (E3M3, no hardware format) keep the software rounding.
+template <int KIND> __device__ __forceinline__ uint32_t round_scale_block(float v) {
+  if constexpr (KIND == kAct) {
+    typedef short v2i16 __attribute__((ext_vector_type(2)));
+    const v2i16 r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2i16{0, 0}, v, 0.0f, 1.0f, false);
+    return (uint32_t)(uint16_t)r.x & 0xFFu;
+  } else {
+    return round_scale<KIND>(v);
+  }
 }
 
 template <int KIND> __device__ __forceinline__ float scale_of_code(uint32_t code) {
@@ -230,22 +262,31 @@ __device__ __forceinline__ uint32_t search_fast(const float (&y)[16], float ymax
       sym_done = true;
       if (ymax > prm.lo[0]) {
         float dsum;
+        uint32_t tb[16];
 #pragma unroll
         for (int j = 15; j >= 0; j--) {
           const float u = fabsf(y[j]) - prm.sym_m;
           float t;
           asm("v_fma_f32 %0, |%1|, -2.0, %2 clamp" : "=v"(t) : "v"(u), "v"(prm.sym_h));
-          const float term = __builtin_bit_cast(
-              float, __builtin_bit_cast(uint32_t, t) | (__builtin_bit_cast(uint32_t, y[j]) & 0x80000000u));
+          tb[j] = __builtin_bit_cast(uint32_t, t);
+          const float term = __builtin_bit_cast(float, tb[j] | (__builtin_bit_cast(uint32_t, y[j]) & 0x80000000u));
           dsum = j == 15 ? term : dsum + term;
-          // window mark: min(bits of t, 1) into bit 4 (j % 8) (asm keeps the
-          // compiler from turning it into a compare and a select)
-          uint32_t one;
-          asm("v_min_u32 %0, %1, 1" : "=v"(one) : "v"(__builtin_bit_cast(uint32_t, t)));
-          asm("v_lshl_or_b32 %0, %1, %2, %3"
-              : "=v"(sym_nib[j >> 3])
-              : "v"(one), "i"(4 * (j & 7)), "v"(sym_nib[j >> 3]));
         }
+        // Window marks, two elements per step: a nonzero t is at least 2^-21,
+        // so its upper 16 bits are nonzero.  Elements i and i + 4 of a code
+        // dword have their upper halves gathered into one register, each half
+        // is clamped to 0 / 1, and one shift-or puts them at bits 4i and
+        // 4i + 16 (asm: the compiler would turn these into compares and selects).
+        const uint32_t ones = 0x00010001u;
+#pragma unroll
+        for (int h = 0; h < 2; h++)
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            const uint32_t hi2 = __builtin_amdgcn_perm(tb[8 * h + i + 4], tb[8 * h + i], 0x07060302u);
+            uint32_t mk;
+            asm("v_pk_min_u16 %0, %1, %2" : "=v"(mk) : "v"(hi2), "v"(ones));
+            asm("v_lshl_or_b32 %0, %1, %2, %3" : "=v"(sym_nib[h]) : "v"(mk), "i"(4 * i), "v"(sym_nib[h]));
+          }
         sym_sel = dsum < 0.0f ? 1u : 0u;
       }
     }
@@ -346,8 +387,27 @@ __device__ __forceinline__ void build_rcp_table(float* rtab, float st) {
     rtab[c] = 1.0f / (scale_of_code<KIND>((uint32_t)c) * st);
 }
 
-template <int KIND>
-__device__ __forceinline__ void encode_block(const float (&xf)[16], float amax, const float* rtab,
+// amax_b / amax, the IEEE fp32 quotient.  With FASTDIV (16-bit inputs, amax in
+// [2^-60, 2^60]) it is computed from rinv = 1 / amax (one IEEE division per
+// kernel) by Markstein's correction: q0 = amax_b * rinv, e = amax_b - q0 * amax
+// (exact in an fma), q = q0 + e * rinv.  Markstein's theorem gives the correctly
+// rounded quotient for a correctly rounded reciprocal, a faithful q0 and no
+// underflow; for 8- and 11-bit significands it was also checked on every pair
+// (a CPU model against exact rationals).  Where the operands leave the normal
+// range the quotient is far below 2^-18, whose scale code is 0 either way.
+template <bool FASTDIV>
+__device__ __forceinline__ float block_ratio(float amax_b, float amax, float rinv) {
+  if constexpr (FASTDIV) {
+    const float q0 = amax_b * rinv;
+    const float e = __builtin_fmaf(-q0, amax, amax_b);
+    return __builtin_fmaf(e, rinv, q0);
+  } else {
+    return amax_b / amax;
+  }
+}
+
+template <int KIND, bool FASTDIV = false>
+__device__ __forceinline__ void encode_block(const float (&xf)[16], float amax, float rinv, const float* rtab,
                                              const EncodeParams& prm, uint2& cw, uint32_t& sbyte) {
   constexpr float kSMax = KIND == kWeight ? 30.0f : 448.0f;
   constexpr int kPairs = KIND == kWeight ? 2 : 1;
@@ -356,9 +416,9 @@ __device__ __forceinline__ void encode_block(const float (&xf)[16], float amax, 
   float amax_b = 0.0f;
 #pragma unroll
   for (int j = 0; j < 16; j++) amax_b = fmaxf(amax_b, fabsf(xf[j]));
-  const float r = amax_b / amax;
+  const float r = block_ratio<FASTDIV>(amax_b, amax, rinv);
   const float sb_real = r * kSMax;
-  const uint32_t scode = round_scale<KIND>(sb_real);
+  const uint32_t scode = round_scale_block<KIND>(sb_real);
   if (scode == 0u) return;  // block underflows to zero
   const float rcp = rtab[scode];  // 1 / (sb * st)
   if (!(rcp < INFINITY)) return;  // scale product underflowed: zero block
@@ -532,6 +592,25 @@ __global__ __launch_bounds__(256) void encode_kernel(const T* __restrict__ x, in
   constexpr int kBB = 16 * (int)sizeof(T);  // input bytes per block
   constexpr int kNI = kBB * 64 / 1024;      // 16-byte loads per lane and step
   __shared__ __attribute__((aligned(16))) uint8_t stage[4][64 * kBB];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t step = (int64_t)gridDim.x * 4 * 64;  // blocks per grid step
+  int64_t bb = ((int64_t)blockIdx.x * 4 + wave) * 64;
+  const uint8_t* xb = (const uint8_t*)x;
+  const int64_t total = nblk * kBB;
+  auto load = [&](int64_t b0, u32x4_t (&v)[kNI]) {
+    const int64_t rem = total - b0 * kBB;
+    const int nrec = rem <= 0 ? 0 : (int)min(rem, (int64_t)64 * kBB);
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(xb + (rem <= 0 ? 0 : b0 * kBB)), (short)0, nrec, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < kNI; i++) v[i] = __builtin_amdgcn_raw_buffer_load_b128(r, (i * 64 + lane) * 16, 0, 2);
+  };
+  // The first step's blocks do not depend on the tensor amax: their loads are
+  // in flight while the partials are folded.
+  u32x4_t cur[kNI], nxt[kNI];
+  load(bb, cur);
+
   uint32_t m = 0u;
   for (int i = threadIdx.x; i < npartial; i += 256) m = max(m, partial[i]);
   m = wave_max_u32(m);
@@ -544,16 +623,13 @@ __global__ __launch_bounds__(256) void encode_kernel(const T* __restrict__ x, in
   const float st = amax / (6.0f * kSMax);
   if (blockIdx.x == 0 && threadIdx.x == 0) *ts_out = nonfinite ? __builtin_nanf("") : st;
   const bool all_zero = nonfinite || amax == 0.0f;
+  const float rinv = 1.0f / amax;
   __shared__ float rtab[kScaleCodes<KIND>];
   if constexpr (!FOS) {
     build_rcp_table<KIND>(rtab, st);
     __syncthreads();
   }
 
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t step = (int64_t)gridDim.x * 4 * 64;  // blocks per grid step
-  int64_t bb = ((int64_t)blockIdx.x * 4 + wave) * 64;
   if (all_zero) {
     for (; bb < nblk; bb += step)
       if (bb + lane < nblk) {
@@ -562,53 +638,54 @@ __global__ __launch_bounds__(256) void encode_kernel(const T* __restrict__ x, in
       }
     return;
   }
-  const uint8_t* xb = (const uint8_t*)x;
-  const int64_t total = nblk * kBB;
-  auto load = [&](int64_t b0, u32x4_t (&v)[kNI]) {
-    const int64_t rem = total - b0 * kBB;
-    const int nrec = rem <= 0 ? 0 : (int)min(rem, (int64_t)64 * kBB);
-    const __amdgpu_buffer_rsrc_t r =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(xb + (rem <= 0 ? 0 : b0 * kBB)), (short)0, nrec, 0x00020000);
-#pragma unroll
-    for (int i = 0; i < kNI; i++) v[i] = __builtin_amdgcn_raw_buffer_load_b128(r, (i * 64 + lane) * 16, 0, 2);
-  };
-  u32x4_t cur[kNI], nxt[kNI];
-  load(bb, cur);
   // Drain the first loads here: otherwise the loop head, which the compiler
   // enters from two paths, waits (for the later steps) on the previous step's
   // stores as well.
 #pragma unroll
   for (int i = 0; i < kNI; i++) asm volatile("" ::"v"(cur[i]));
-  uint8_t* stg = stage[wave];
-  for (; bb < nblk; bb += step) {
-    load(bb + step, nxt);
+  auto run = [&](auto fastdiv) {
+    constexpr bool kFastDiv = decltype(fastdiv)::value;
+    uint8_t* stg = stage[wave];
+    for (; bb < nblk; bb += step) {
+      load(bb + step, nxt);
 #pragma unroll
-    for (int i = 0; i < kNI; i++) *(u32x4_t*)(stg + (i * 64 + lane) * 16) = cur[i];
-    wave_lds_sync();
-    u32x4_t q[kBB / 16];
+      for (int i = 0; i < kNI; i++) *(u32x4_t*)(stg + (i * 64 + lane) * 16) = cur[i];
+      wave_lds_sync();
+      u32x4_t q[kBB / 16];
 #pragma unroll
-    for (int i = 0; i < kBB / 16; i++) q[i] = *(const u32x4_t*)(stg + lane * kBB + 16 * i);
-    wave_lds_sync();
-    float xf[16];
-    unpack_block<T>(q, xf);
-    uint2 cw;
-    uint32_t sbyte;
-    if constexpr (FOS)
-      encode_block_fos<KIND>(xf, amax, st, cw, sbyte);
+      for (int i = 0; i < kBB / 16; i++) q[i] = *(const u32x4_t*)(stg + lane * kBB + 16 * i);
+      wave_lds_sync();
+      float xf[16];
+      unpack_block<T>(q, xf);
+      uint2 cw;
+      uint32_t sbyte;
+      if constexpr (FOS)
+        encode_block_fos<KIND>(xf, amax, st, cw, sbyte);
+      else
+        encode_block<KIND, kFastDiv>(xf, amax, rinv, rtab, prm, cw, sbyte);
+      // Buffer stores sized to the wave's valid blocks: lanes past the end are
+      // dropped by the range check, so the stores need no branch (a branch
+      // around them made every step wait for its stores to complete).
+      const int nval = (int)min(nblk - bb, (int64_t)64);
+      __builtin_amdgcn_raw_buffer_store_b64(
+          u32x2_t{cw.x, cw.y}, __builtin_amdgcn_make_buffer_rsrc((void*)(codes + bb), (short)0, nval * 8, 0x00020000),
+          lane * 8, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b8(
+          (uint8_t)sbyte, __builtin_amdgcn_make_buffer_rsrc((void*)(scales + bb), (short)0, nval, 0x00020000), lane,
+          0, 0);
+#pragma unroll
+      for (int i = 0; i < kNI; i++) cur[i] = nxt[i];
+    }
+  };
+  // The Markstein quotient is used for 16-bit inputs whose amax keeps every
+  // operand normal; the test is uniform, so the kernel takes one loop or the other.
+  if constexpr (sizeof(T) == 2 && !FOS) {
+    if (amax >= 0x1p-60f && amax <= 0x1p60f)
+      run(std::true_type{});
     else
-      encode_block<KIND>(xf, amax, rtab, prm, cw, sbyte);
-    // Buffer stores sized to the wave's valid blocks: lanes past the end are
-    // dropped by the range check, so the stores need no branch (a branch
-    // around them made every step wait for its stores to complete).
-    const int nval = (int)min(nblk - bb, (int64_t)64);
-    __builtin_amdgcn_raw_buffer_store_b64(
-        u32x2_t{cw.x, cw.y}, __builtin_amdgcn_make_buffer_rsrc((void*)(codes + bb), (short)0, nval * 8, 0x00020000),
-        lane * 8, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b8(
-        (uint8_t)sbyte, __builtin_amdgcn_make_buffer_rsrc((void*)(scales + bb), (short)0, nval, 0x00020000), lane,
-        0, 0);
-#pragma unroll
-    for (int i = 0; i < kNI; i++) cur[i] = nxt[i];
+      run(std::false_type{});
+  } else {
+    run(std::false_type{});
   }
 }
 
@@ -621,7 +698,7 @@ static hipError_t run_quantize(const T* x, const PackedView& out, uint32_t* part
   int64_t g1 = (nvec + 4 * 256 - 1) / (4 * 256);
   if (g1 < 1) g1 = 1;
   if (g1 > kAmaxMaxPartials) g1 = kAmaxMaxPartials;
-  hipLaunchKernelGGL(amax_partial_kernel<T>, dim3((unsigned)g1), dim3(256), 0, stream,
+  launch_amax_partial<T>(dim3((unsigned)g1), stream,
                      (const uint4*)x, nvec, partial);
   EncodeParams prm;
   const int npairs = KIND == kWeight ? 2 : 1;
@@ -735,7 +812,7 @@ __global__ __launch_bounds__(256) void offset_sse_kernel(const T* __restrict__ x
           e.f[1] = prm.f1[o];
           uint2 cw;
           uint32_t sbyte;
-          encode_block<kWeight>(xf, amax, rtab, e, cw, sbyte);
+          encode_block<kWeight>(xf, amax, 0.0f, rtab, e, cw, sbyte);
           const double sbst = (double)scale_of_byte<kWeight>(sbyte) * st64;
           // the special value's sign is bit 7 of the scale byte, not the code's
           const double svm = (double)((sbyte & 0x40u) ? 0.5f * (float)prm.mag1[o] : prm.m0);
@@ -804,7 +881,7 @@ static hipError_t run_offset_search(const T* x, int64_t n, int off0, double* sse
   if (g1 < 1) g1 = 1;
   if (g1 > kAmaxMaxPartials) g1 = kAmaxMaxPartials;
   if (nvec > 0)
-    hipLaunchKernelGGL(amax_partial_kernel<T>, dim3((unsigned)g1), dim3(256), 0, stream,
+    launch_amax_partial<T>(dim3((unsigned)g1), stream,
                        (const uint4*)x, nvec, partial);
   OffsetSearchParams prm;
   for (int p = 0; p < 2; p++) {
@@ -1072,7 +1149,7 @@ static hipError_t run_quantize_variant(const T* x, const PackedView& out, uint32
   int64_t g1 = (nvec + 4 * 256 - 1) / (4 * 256);
   if (g1 < 1) g1 = 1;
   if (g1 > kAmaxMaxPartials) g1 = kAmaxMaxPartials;
-  hipLaunchKernelGGL(amax_partial_kernel<T>, dim3((unsigned)g1), dim3(256), 0, stream,
+  launch_amax_partial<T>(dim3((unsigned)g1), stream,
                      (const uint4*)x, nvec, partial);
   VariantParams vp;
   const int npairs = KIND == kWeight ? 2 : 1;

@@ -125,6 +125,39 @@ def test_quantize_act_parity(dtype):
     assert_same_encoding(p, ref, as_f32(x), f"act {dtype}")
 
 
+def _e4m3_boundary_blocks(dtype, tensor_max, seed):
+    """Blocks whose maximum sits on every E4M3 rounding midpoint of
+    448 * amax_b / amax, and one step of the input type either side."""
+    vals = np.array([c * 2.0 ** -9 if c < 8 else (8 + (c & 7)) * 2.0 ** ((c >> 3) - 10)
+                     for c in range(127)])
+    mids = (vals[:-1] + vals[1:]) / 2
+    base = torch.from_numpy((mids * tensor_max / 448.0).astype(np.float32)).to(dtype)
+    bits = base.view(torch.int16)
+    tops = torch.cat([bits - 1, bits, bits + 1]).view(dtype).float().numpy()
+    rng = np.random.default_rng(seed)
+    blocks = rng.uniform(-0.5, 0.5, (tops.size + 1, 16)) * np.append(tops, tensor_max)[:, None]
+    blocks[:-1, 0] = tops * np.where(rng.integers(0, 2, tops.size) == 1, -1.0, 1.0)
+    blocks[-1, 3] = tensor_max
+    rows = -(-blocks.size // 64)
+    x = np.zeros(rows * 64, np.float32)
+    x[:blocks.size] = blocks.reshape(-1)
+    return torch.from_numpy(x.reshape(rows, 64)).to(dtype)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("tensor_max", [448.0, 1.0, 37.25])
+def test_quantize_act_scale_code_boundaries(dtype, tensor_max):
+    """Block maxima on every E4M3 rounding midpoint (and one input step either
+    side) give the oracle's scale byte: the activation encoder forms the block
+    ratio with a corrected reciprocal product and rounds it with the fp8
+    conversion for 16-bit inputs."""
+    _need_gpu()
+    x = _e4m3_boundary_blocks(dtype, tensor_max, seed=int(tensor_max * 8))
+    ref = oracle.quantize_act(as_f32(x))
+    p = gpu_encode(oracle.ACT, x, (-2,))
+    assert_same_encoding(p, ref, as_f32(x), f"act scale boundaries {dtype} max {tensor_max}")
+
+
 def test_quantize_act_full_size():
     """Activation quantizer at its full size, X[4096, 8192] bf16."""
     _need_gpu()
