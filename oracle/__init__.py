@@ -188,15 +188,18 @@ class Packed:
         return out
 
 
-MODE_PLAIN, MODE_RAZER, MODE_FOUR_OVER_SIX = 0, 1, 2
+MODE_PLAIN, MODE_RAZER, MODE_FOUR_OVER_SIX, MODE_RAZER_RESCALE = 0, 1, 2, 3
 
 
 def quantize(kind: int, x, offsets, remap: bool = True, four_over_six: bool = False,
-             block: int = 16, scale_fmt: int = SCALE_BYTE) -> Packed:
+             block: int = 16, scale_fmt: int = SCALE_BYTE, rescale: bool = False) -> Packed:
     """Encode x (RaZeR, plain NVFP4 when not remap, or the Four Over Six
     baseline when four_over_six: plain FP4 with a per-block choice of the
     max -> 6 or max -> 4 scale), with `block` elements per block and byte or
-    FP16 group scales."""
+    FP16 group scales.  rescale (RaZeR, 16-element blocks, byte scales): every
+    candidate is tried on its own, one with |v| > 6 at the block scale that maps
+    the block maximum to |v|, and the encoding with the smallest squared error
+    in real units is kept."""
     x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
     if x.ndim != 2:
         raise ValueError("x must be 2-D")
@@ -206,7 +209,8 @@ def quantize(kind: int, x, offsets, remap: bool = True, four_over_six: bool = Fa
     nblk = rows * cols // block if block in BLOCK_SIZES else 0
     scales = np.zeros(nblk, dtype=np.uint16 if scale_fmt == SCALE_F16 else np.uint8)
     ts = np.zeros(1, dtype=np.float32)
-    mode = MODE_FOUR_OVER_SIX if four_over_six else (MODE_RAZER if remap else MODE_PLAIN)
+    mode = (MODE_FOUR_OVER_SIX if four_over_six else
+            (MODE_PLAIN if not remap else MODE_RAZER_RESCALE if rescale else MODE_RAZER))
     rc = lib().rzo_quantize_fmt(kind, _ptr(x), rows, cols, _ptr(off), mode, block, scale_fmt,
                                 _ptr(codes), _ptr(scales), _ptr(ts))
     if rc != 0:
@@ -214,12 +218,14 @@ def quantize(kind: int, x, offsets, remap: bool = True, four_over_six: bool = Fa
     return Packed(kind, rows, cols, offsets, codes, scales, ts[0], block, scale_fmt)
 
 
-def quantize_weight(w, offsets=(-2, 4), remap: bool = True, four_over_six: bool = False) -> Packed:
-    return quantize(WEIGHT, w, offsets, remap, four_over_six)
+def quantize_weight(w, offsets=(-2, 4), remap: bool = True, four_over_six: bool = False,
+                    rescale: bool = False) -> Packed:
+    return quantize(WEIGHT, w, offsets, remap, four_over_six, rescale=rescale)
 
 
-def quantize_act(x, offsets=(-2,), remap: bool = True, four_over_six: bool = False) -> Packed:
-    return quantize(ACT, x, offsets, remap, four_over_six)
+def quantize_act(x, offsets=(-2,), remap: bool = True, four_over_six: bool = False,
+                 rescale: bool = False) -> Packed:
+    return quantize(ACT, x, offsets, remap, four_over_six, rescale=rescale)
 
 
 SECOND_PAIR_OFFSETS = tuple(range(-7, 8))  # offsets tried for the second weight pair

@@ -230,16 +230,23 @@ static int encode_at_scale(int kind, int sfmt, int n, const float* xb, float sb_
  * j = 0 .. n-1.  value * sb * st is exact in fp64 (at most 3 + 11 + 24
  * significant bits); the difference, the square and each partial sum are
  * rounded once each. */
-static double block_sse(int kind, int sfmt, int n, const float* xb, const uint8_t* cb, int scode,
-                        float st) {
+static double block_sse_sv(int kind, int sfmt, int n, const float* xb, const uint8_t* cb, int scode,
+                           float st, double sv) {
   double sb = scode == 0 ? 0.0 : rzo_scale_value_fmt(kind, sfmt, scode);
   double sse = 0.0;
   for (int j = 0; j < n; j++) {
-    double q = rzo_fp4_value(cb[j]) * sb * (double)st;
+    double v = cb[j] == 8 ? sv : rzo_fp4_value(cb[j]);
+    double q = v * sb * (double)st;
     double e = (double)xb[j] - q;
     sse += e * e;
   }
   return sse;
+}
+
+static double block_sse(int kind, int sfmt, int n, const float* xb, const uint8_t* cb, int scode,
+                        float st) {
+  /* plain FP4 codes: code 8 never occurs (a negative zero is written +0) */
+  return block_sse_sv(kind, sfmt, n, xb, cb, scode, st, 0.0);
 }
 
 int rzo_quantize(int kind, const float* x, int64_t rows, int64_t cols, const int8_t* off_half,
@@ -254,7 +261,8 @@ int rzo_quantize_fmt(int kind, const float* x, int64_t rows, int64_t cols, const
   if ((kind != RZO_WEIGHT && kind != RZO_ACT) || rows < 0 || cols < 0 ||
       (block != 16 && block != 32 && block != 64 && block != 128) || cols % block != 0 ||
       (sfmt != RZO_SCALE_BYTE && sfmt != RZO_SCALE_F16) || (sfmt == RZO_SCALE_F16 && kind != RZO_WEIGHT) ||
-      mode < RZO_MODE_PLAIN || mode > RZO_MODE_FOUR_OVER_SIX ||
+      mode < RZO_MODE_PLAIN || mode > RZO_MODE_RAZER_RESCALE ||
+      (mode == RZO_MODE_RAZER_RESCALE && (block != 16 || sfmt != RZO_SCALE_BYTE)) ||
       !off_half || !valid_offsets(kind, off_half))
     return -1;
   int64_t n = rows * cols, nblk = n / block;
@@ -316,8 +324,35 @@ int rzo_quantize_fmt(int kind, const float* x, int64_t rows, int64_t cols, const
     float sb_real = r * smax;
     uint8_t cb[128];
     int sel = 0;
-    int scode = encode_at_scale(kind, sfmt, block, xb, sb_real, st, cand, ncand,
-                                mode == RZO_MODE_RAZER, cb, &sel);
+    int scode = 0;
+    if (mode == RZO_MODE_RAZER_RESCALE) {
+      /* Rescaled large special values (a reading of [notes] Training
+       * strategy, whose best weight pairs include +/-7, +/-8 and +/-9, values
+       * a block scaled max -> 6 almost never reaches): candidate c alone, at
+       * the block scale that maps the maximum to |v_c| when |v_c| > 6.  The
+       * error of each encoding is summed in real units in fp64 in element
+       * order (every term value * sb * st exact), and the smallest wins, ties
+       * to the lowest index.  A candidate whose scale code or scale product
+       * underflows stores the block as zero (error = sum of x^2). */
+      double best = 0.0;
+      for (int c = 0; c < ncand; c++) {
+        double mag = fabs(cand[c]);
+        float sbr = mag > 6.0 ? (sb_real * 6.0f) / (float)mag : sb_real;
+        uint8_t cc[16];
+        int selc = 0;
+        int sc = encode_at_scale(kind, sfmt, 16, xb, sbr, st, &cand[c], 1, 1, cc, &selc);
+        double e = block_sse_sv(kind, sfmt, 16, xb, cc, sc, st, cand[c]);
+        if (c == 0 || e < best) {
+          best = e;
+          sel = c;
+          scode = sc;
+          memcpy(cb, cc, 16);
+        }
+      }
+    } else {
+      scode = encode_at_scale(kind, sfmt, block, xb, sb_real, st, cand, ncand,
+                              mode == RZO_MODE_RAZER, cb, &sel);
+    }
     if (mode == RZO_MODE_FOUR_OVER_SIX) {
       /* [Four Over Six] Technical framework / key innovation: a block may
        * instead be scaled so that its maximum lands on 4 rather than 6 (block

@@ -42,10 +42,16 @@ extern "C" {
 enum { RZO_WEIGHT = 0, RZO_ACT = 1 };
 
 /* Encoder modes: plain NVFP4 (same scale format, no special value), RaZeR
- * (special-value remap), and the Four Over Six baseline (plain FP4; each block
+ * (special-value remap), the Four Over Six baseline (plain FP4; each block
  * takes the max -> 6 or the max -> 4 block scale, whichever has the smaller
- * squared error in real units, ties to max -> 6). */
-enum { RZO_MODE_PLAIN = 0, RZO_MODE_RAZER = 1, RZO_MODE_FOUR_OVER_SIX = 2 };
+ * squared error in real units, ties to max -> 6), and RaZeR with rescaled
+ * large special values: every candidate v is tried on its own, a candidate
+ * with |v| > 6 at the block scale that maps the block maximum to |v| instead
+ * of 6 (sb_real * 6 / |v| in fp32), the others at the usual scale; the block
+ * keeps the candidate whose encoding has the smallest squared error in real
+ * units (fp64, element order), ties to the lowest index.  This mode takes
+ * 16-element blocks with byte scales only. */
+enum { RZO_MODE_PLAIN = 0, RZO_MODE_RAZER = 1, RZO_MODE_FOUR_OVER_SIX = 2, RZO_MODE_RAZER_RESCALE = 3 };
 
 /* Block-scale storage: one byte per block (E3M3 weights / E4M3 activations,
  * metadata in bits 7-6), or the group-scale variant for weights: a 16-bit FP16

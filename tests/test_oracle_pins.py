@@ -831,3 +831,123 @@ def test_sampled_output_helpers_equal_the_full_products():
     yc, nc = oracle.gemm_any(x, pf, ni[:9])
     np.testing.assert_allclose(yc, ya[:, ni[:9]], rtol=1e-12, atol=1e-12 * float(na.max()))
     np.testing.assert_allclose(nc, na[:, ni[:9]], rtol=1e-12)
+
+
+# ---- RaZeR with rescaled large special values ---------------------------------
+# A reading of [notes] Training strategy (best weight pairs +/-7, +/-8, +/-9):
+# every candidate v is tried on its own; one with |v| > 6 at the block scale
+# that maps the block maximum to |v| (S_MAX * amax_b / amax * 6 / |v|), the
+# others at the usual scale; the block keeps the candidate whose encoding has
+# the smallest squared error in real units, ties to the lowest index.
+
+def _rescale_one(kind, xb, exact_sbr, st, v):
+    """One block encoded with the single candidate v at the exact-rational
+    nearest scale code to exact_sbr: closed-form E2M1 rounding of the fp32
+    scaled values, then every element strictly nearer to v than to its FP4
+    rounding takes code 8.  Returns (codes, real decoded values, scale code)."""
+    c = _fos_nearest(kind, exact_sbr)
+    if c == 0:
+        return [0] * len(xb), [0.0] * len(xb), 0
+    sb = np.float32(oracle.scale_value(kind, c))
+    rcp = np.float32(1.0) / (sb * st)
+    if not np.isfinite(rcp):
+        return [0] * len(xb), [0.0] * len(xb), 0
+    codes, vals = [], []
+    for a in (xb * rcp).astype(np.float32):
+        m = _fp4_rne_closed_form(abs(float(a)))
+        q0 = math.copysign(m, float(a)) if m else 0.0
+        if abs(F(float(a)) - F(v)) < abs(F(float(a)) - F(q0)):
+            codes.append(8)
+            vals.append(v * float(sb) * float(st))
+        else:
+            codes.append(0 if m == 0 else (8 if a < 0 else 0) | FP4_SET.index(m))
+            vals.append(q0 * float(sb) * float(st))
+    return codes, vals, c
+
+
+def _rescale_inputs(kind):
+    rng = np.random.default_rng(97 + kind)
+    x = (rng.standard_t(5, (12, 256)) * 0.02).astype(np.float32)
+    if kind == oracle.ACT:
+        x[:, 7] *= 25
+    return x
+
+
+@pytest.mark.parametrize("kind,offs", [(oracle.WEIGHT, (-2, 4)), (oracle.WEIGHT, (-2, 2)),
+                                       (oracle.WEIGHT, (1, 6)), (oracle.ACT, (2,)), (oracle.ACT, (-3,))])
+def test_rescale_mode_is_the_exact_best_single_candidate(kind, offs):
+    # Independent of the oracle's encoder: exact-rational scale codes, closed-form
+    # FP4, exact squared errors.  Blocks within 2^-20 of a scale-rounding
+    # midpoint (the fp32 steps may pick either neighbour) and blocks whose two
+    # best exact errors are within 2^-40 of each other (fp64 sums may order them
+    # either way) are left out.
+    x = _rescale_inputs(kind)
+    p = oracle.quantize(kind, x, offs, rescale=True)
+    smax = F(oracle.scale_max(kind))
+    grid = _fos_grid(kind)
+    mids = [(grid[c] + grid[c + 1]) / 2 for c in range(len(grid) - 1)]
+    st = np.float32(p.tensor_scale)
+    amax = F(float(np.abs(x).max()))
+    cand = []
+    for o in offs:
+        mag = 6.0 + o / 2.0
+        cand += [mag, -mag]
+    codes = p.unpacked_codes().reshape(-1, 16)
+    picked_large = skipped = 0
+    for b in range(codes.shape[0]):
+        xb = x.reshape(-1, 16)[b]
+        base = smax * F(float(np.abs(xb).max())) / amax
+        sbrs = [base * 6 / F(abs(v)) if abs(v) > 6 else base for v in cand]
+        if any(e < smax and min(abs(e - m) for m in mids) <= e * F(1, 2 ** 20) for e in sbrs):
+            skipped += 1
+            continue
+        enc = [_rescale_one(kind, xb, e, st, v) for e, v in zip(sbrs, cand)]
+        errs = [_exact_block_sse(xb, vals) for _, vals, _ in enc]
+        order = sorted(range(len(cand)), key=lambda c: (errs[c], c))
+        if len(order) > 1 and errs[order[1]] - errs[order[0]] <= errs[order[0]] * F(1, 2 ** 40):
+            if errs[order[1]] != errs[order[0]]:
+                skipped += 1
+                continue
+        best = order[0]
+        sbyte = int(p.scales[b])
+        sel = (((sbyte >> 6) & 1) << 1 | (sbyte >> 7)) if kind == oracle.WEIGHT else sbyte >> 7
+        mask = 63 if kind == oracle.WEIGHT else 127
+        k_best, _, c_best = enc[best]
+        if c_best == 0:
+            assert sbyte & mask == 0 and not codes[b].any(), b
+            continue
+        assert sel == best and sbyte & mask == c_best and codes[b].tolist() == k_best, (b, sel, best)
+        picked_large += abs(cand[best]) > 6
+    assert skipped <= codes.shape[0] // 50
+    if any(abs(v) > 6 for v in cand):
+        assert picked_large > 0
+
+
+def test_rescale_mode_without_large_special_values_is_the_default_mode():
+    # With every |v| <= 6 no candidate is rescaled: each block keeps the usual
+    # scale and the candidate with the smallest error, as in the default mode.
+    x = _rescale_inputs(oracle.WEIGHT)
+    for offs in ((-2, -5), (-2, -7), (-1, -3)):
+        a = oracle.quantize_weight(x, offs)
+        b = oracle.quantize_weight(x, offs, rescale=True)
+        assert np.array_equal(a.codes, b.codes) and np.array_equal(a.scales, b.scales)
+
+
+def test_rescale_mode_reaches_large_special_values():
+    # On t(5) weights the fixed scale (max -> 6) almost never lets +/-8 win; with
+    # the rescale it wins a large share of blocks and lowers the tensor error
+    # below every fixed-scale pair with |v| <= 6 tried here.
+    rng = np.random.default_rng(5)
+    w = (rng.standard_t(5, (64, 1024)) * 0.02).astype(np.float32)
+    w64 = w.astype(np.float64)
+
+    def rel(p):
+        return float(((w64 - oracle.dequant_f64(p)) ** 2).sum() / (w64 ** 2).sum())
+
+    fixed8 = oracle.quantize_weight(w, (-2, 4))
+    resc8 = oracle.quantize_weight(w, (-2, 4), rescale=True)
+    share_fixed = float(((fixed8.scales >> 6) & 1).mean())
+    share_resc = float(((resc8.scales >> 6) & 1).mean())
+    assert share_fixed < 0.01 < 0.2 < share_resc
+    best_small = min(rel(oracle.quantize_weight(w, (-2, o))) for o in range(-7, 0))
+    assert rel(resc8) < best_small
