@@ -109,7 +109,8 @@ enum {
    * real units (summed in fp64 in element order; a tie keeps max -> 6).  The
    * tensor scale and the packed layout are unchanged, so every decoding call
    * reads such a tensor as plain NVFP4.  Takes precedence over NO_REMAP.
-   * The quantize calls reject any other flag bit with RAZER_E_INVALID. */
+   * The quantize calls reject any other flag bit than these three with
+   * RAZER_E_INVALID. */
   RAZER_FLAG_FOUR_OVER_SIX = 2u,
   /* Read by the product calls only (the encoders reject it): launch the
    * product with the untrimmed plan -- the K range split over the most waves
@@ -120,7 +121,20 @@ enum {
    * Key design 3).  Outputs agree within the product tolerance (the
    * summation order changes).  razer_gemm then needs
    * razer_workspace_bytes(RAZER_OP_GEMM_UNTRIMMED, ...). */
-  RAZER_FLAG_UNTRIMMED_PLAN = 4u
+  RAZER_FLAG_UNTRIMMED_PLAN = 4u,
+  /* Encode with rescaled large special values (a reading of [notes] Training
+   * strategy, whose best weight pairs include +/-7, +/-8 and +/-9, values a
+   * block scaled so that its maximum maps to 6 almost never reaches): every
+   * candidate special value v is tried on its own -- one with |v| > 6 at the
+   * block scale whose code is nearest to S_MAX * amax_block / amax_tensor *
+   * 6 / |v| (fp32: (sb_real * 6) / |v|), so the block maximum maps to |v|, the
+   * others at the usual scale -- and the block keeps the encoding with the
+   * smallest squared error against the input in real units (fp64, element
+   * order; ties to the lowest candidate index).  Decoding is unchanged (the
+   * scale byte holds the chosen scale and the metadata the chosen value).
+   * 16-element blocks with byte scales only (other layouts:
+   * RAZER_E_UNSUPPORTED); NO_REMAP and FOUR_OVER_SIX take precedence. */
+  RAZER_FLAG_RESCALE_LARGE_SV = 8u
 };
 
 /* Block-scale storage of a packed tensor (razer_packed.scale_fmt). */

@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_HERE, "librazer.so")
 RAZER_OK, RAZER_E_INVALID, RAZER_E_UNSUPPORTED, RAZER_E_HIP = 0, 1, 2, 3
 RAZER_F32, RAZER_F16, RAZER_BF16 = 0, 1, 2
 RAZER_WEIGHT, RAZER_ACT = 0, 1
-RAZER_FLAG_NO_REMAP, RAZER_FLAG_FOUR_OVER_SIX, RAZER_FLAG_UNTRIMMED_PLAN = 1, 2, 4
+RAZER_FLAG_NO_REMAP, RAZER_FLAG_FOUR_OVER_SIX, RAZER_FLAG_UNTRIMMED_PLAN, RAZER_FLAG_RESCALE_LARGE_SV = 1, 2, 4, 8
 RAZER_SCALE_BYTE, RAZER_SCALE_F16 = 0, 1
 BLOCK_SIZES = (16, 32, 64, 128)
 RAZER_OP_QUANTIZE_WEIGHT, RAZER_OP_QUANTIZE_ACT, RAZER_OP_GEMV, RAZER_OP_GEMM = 0, 1, 2, 3
@@ -225,10 +225,12 @@ def _workspace(op, m, n, k, device, workspace):
     return workspace, workspace.numel() * workspace.element_size()
 
 
-def _encoder_flags(remap: bool, four_over_six: bool) -> int:
+def _encoder_flags(remap: bool, four_over_six: bool, rescale: bool = False) -> int:
     if four_over_six:
         return RAZER_FLAG_FOUR_OVER_SIX
-    return 0 if remap else RAZER_FLAG_NO_REMAP
+    if not remap:
+        return RAZER_FLAG_NO_REMAP
+    return RAZER_FLAG_RESCALE_LARGE_SV if rescale else 0
 
 
 def _quantize(fn, op, kind, x, offsets, flags, out, workspace, stream, block, scale_fmt):
@@ -254,23 +256,25 @@ def _quantize(fn, op, kind, x, offsets, flags, out, workspace, stream, block, sc
 def razer_quantize_weight(w: torch.Tensor, offsets=DEFAULT_WEIGHT_OFFSETS, remap: bool = True,
                           out: PackedTensor | None = None, workspace=None, stream=None,
                           four_over_six: bool = False, block: int = 16,
-                          scale_fmt: int = RAZER_SCALE_BYTE):
+                          scale_fmt: int = RAZER_SCALE_BYTE, rescale: bool = False):
     """Offline RaZeR weight encoding of w [N, K] (fp32/fp16/bf16, on the GPU).
     remap=False gives plain NVFP4, four_over_six=True the Four Over Six
-    baseline; block / scale_fmt pick a layout variant; a given `out` carries
-    its own flags and layout instead."""
+    baseline, rescale=True RaZeR with rescaled large special values (a
+    candidate with |v| > 6 maps the block maximum to |v|; 16-element blocks,
+    byte scales); block / scale_fmt pick a layout variant; a given `out`
+    carries its own flags and layout instead."""
     return _quantize(lib().razer_quantize_weight, RAZER_OP_QUANTIZE_WEIGHT, RAZER_WEIGHT, w,
-                     offsets, _encoder_flags(remap, four_over_six), out, workspace, stream, block,
-                     scale_fmt)
+                     offsets, _encoder_flags(remap, four_over_six, rescale), out, workspace, stream,
+                     block, scale_fmt)
 
 
 def razer_quantize_act(x: torch.Tensor, offsets=DEFAULT_ACT_OFFSETS, remap: bool = True,
                        out: PackedTensor | None = None, workspace=None, stream=None,
-                       four_over_six: bool = False, block: int = 16):
+                       four_over_six: bool = False, block: int = 16, rescale: bool = False):
     """Online RaZeR activation encoding of x [rows, cols] (fp16/bf16, on the GPU).
-    remap / four_over_six / block / out as for razer_quantize_weight."""
+    remap / four_over_six / rescale / block / out as for razer_quantize_weight."""
     return _quantize(lib().razer_quantize_act, RAZER_OP_QUANTIZE_ACT, RAZER_ACT, x, offsets,
-                     _encoder_flags(remap, four_over_six), out, workspace, stream, block,
+                     _encoder_flags(remap, four_over_six, rescale), out, workspace, stream, block,
                      RAZER_SCALE_BYTE)
 
 

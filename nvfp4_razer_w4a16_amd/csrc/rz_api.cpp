@@ -74,8 +74,20 @@ rz::PackedView view_of(const razer_packed* p) {
 }
 
 static_assert(RAZER_FLAG_NO_REMAP == rz::kFlagNoRemap && RAZER_FLAG_FOUR_OVER_SIX == rz::kFlagFourOverSix &&
-                  RAZER_FLAG_UNTRIMMED_PLAN == rz::kFlagUntrimmed,
+                  RAZER_FLAG_UNTRIMMED_PLAN == rz::kFlagUntrimmed && RAZER_FLAG_RESCALE_LARGE_SV == rz::kFlagRescale,
               "flag values");
+
+constexpr uint32_t kEncoderFlags = RAZER_FLAG_NO_REMAP | RAZER_FLAG_FOUR_OVER_SIX | RAZER_FLAG_RESCALE_LARGE_SV;
+
+// The encoder flags a packed output may carry: the rescale mode exists for
+// 16-element blocks with byte scales only.
+razer_status check_encoder_flags(const razer_packed* out) {
+  if (out->flags & ~kEncoderFlags) return RAZER_E_INVALID;
+  if ((out->flags & RAZER_FLAG_RESCALE_LARGE_SV) && !((out->block_log2 == 0 || out->block_log2 == 4) &&
+                                                      out->scale_fmt == RAZER_SCALE_BYTE))
+    return RAZER_E_UNSUPPORTED;
+  return RAZER_OK;
+}
 
 // The product kernels read 16-element blocks with byte scales; the GEMV and
 // razer_gemm also read 128-element blocks with FP16 scales.
@@ -92,7 +104,8 @@ razer_status quantize_common(const void* x, razer_dtype dt, const razer_packed* 
                              size_t ws_bytes, void* stream, int kind) {
   razer_status s = check_packed(out, true);
   if (s != RAZER_OK) return s;
-  if (out->flags & ~(uint32_t)(RAZER_FLAG_NO_REMAP | RAZER_FLAG_FOUR_OVER_SIX)) return RAZER_E_INVALID;
+  s = check_encoder_flags(out);
+  if (s != RAZER_OK) return s;
   if (out->kind != kind || !dtype_ok(dt)) return RAZER_E_INVALID;
   const int64_t n = out->rows * out->cols;
   if (n > 0 && (!x || !aligned(x, 16))) return RAZER_E_INVALID;
@@ -121,7 +134,8 @@ razer_status razer_quantize_act_noalloc(const void* x, razer_dtype x_dt, const r
                                         void* stream) {
   razer_status s = check_packed(out, true);
   if (s != RAZER_OK) return s;
-  if (out->flags & ~(uint32_t)(RAZER_FLAG_NO_REMAP | RAZER_FLAG_FOUR_OVER_SIX)) return RAZER_E_INVALID;
+  s = check_encoder_flags(out);
+  if (s != RAZER_OK) return s;
   if (out->kind != RAZER_ACT || !dtype_ok(x_dt)) return RAZER_E_INVALID;
   const int64_t n = out->rows * out->cols;
   if (n > 0 && (!x || !aligned(x, 16))) return RAZER_E_INVALID;

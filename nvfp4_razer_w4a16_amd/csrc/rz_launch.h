@@ -12,6 +12,7 @@ namespace rz {
 constexpr uint32_t kFlagNoRemap = 1u;       // plain NVFP4: no special value
 constexpr uint32_t kFlagFourOverSix = 2u;   // plain FP4, per-block max -> 6 or max -> 4 scale
 constexpr uint32_t kFlagUntrimmed = 4u;     // products: untrimmed launch plan (most splits)
+constexpr uint32_t kFlagRescale = 8u;       // encoders: candidates with |SV| > 6 rescale the block (max -> |SV|)
 
 struct PackedView {
   int kind;          // 0 weight (E3M3, 4 candidates), 1 activation (E4M3, 2 candidates)

@@ -549,6 +549,83 @@ __device__ __forceinline__ void encode_block_fos(const float (&xf)[16], float am
   sbyte = four ? c4 : c6;
 }
 
+// ---- RaZeR with rescaled large special values --------------------------------
+// A reading of "RaZeR ..." (papernotes.org notes), Training strategy: the best
+// weight pairs it reports include +/-7, +/-8 and +/-9, which a block scaled
+// so that its maximum maps to 6 almost never reaches.  Each candidate v is
+// tried on its own: one with |v| > 6 at the block scale nearest to
+// (sb_real * 6) / |v| (the block maximum then maps to |v|), the others at the
+// usual scale; its elements strictly nearer to v than to their FP4 rounding
+// take the special-value code.  The block keeps the encoding with the smallest
+// squared error in real units, summed in fp64 in element order (every decoded
+// value * sb * st is exact in fp64; the difference, the square and each
+// partial sum round once), ties to the lowest candidate index.  A candidate
+// whose scale code or scale product underflows stores the block as zero.
+template <int KIND>
+__device__ __forceinline__ void encode_block_rescale(const float (&xf)[16], float amax, float st,
+                                                     const float* rtab, const EncodeParams& prm, uint2& cw,
+                                                     uint32_t& sbyte) {
+#pragma clang fp contract(off)
+  constexpr float kSMax = KIND == kWeight ? 30.0f : 448.0f;
+  constexpr int kCand = KIND == kWeight ? 4 : 2;
+  float amax_b = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 16; j++) amax_b = fmaxf(amax_b, fabsf(xf[j]));
+  const float r = amax_b / amax;
+  const float sb_real = r * kSMax;
+  double best = 0.0;
+  uint32_t bsel = 0u, bcode = 0u, bw0 = 0u, bw1 = 0u;
+#pragma unroll
+  for (int c = 0; c < kCand; c++) {
+    const int p = c >> 1;
+    const uint32_t neg = (uint32_t)(c & 1);
+    const float mag = 0.5f * (float)prm.mag_x2[p];
+    const float sbr = mag > 6.0f ? (sb_real * 6.0f) / mag : sb_real;
+    uint32_t scode = round_scale_block<KIND>(sbr);
+    uint32_t w[2] = {0u, 0u};
+    const float rcp = scode ? rtab[scode] : 0.0f;
+    if (!(rcp < INFINITY)) scode = 0u;
+    float y[16];
+#pragma unroll
+    for (int j = 0; j < 16; j++) y[j] = xf[j] * rcp;
+    if (scode) {
+      fp4_pack16(y, w);
+      const float lo = prm.lo[p], hi = prm.hi[p];
+#pragma unroll
+      for (int j = 0; j < 16; j++) {
+        const uint32_t sh = 4 * (j & 7);
+        const uint32_t code = (w[j >> 3] >> sh) & 15u;
+        const float aj = fabsf(y[j]);
+        // a moved element lies above 2, so its FP4 code carries the sign
+        const bool hit = aj > lo && aj < hi && (code >> 3) == neg;
+        w[j >> 3] ^= hit ? ((code ^ 8u) << sh) : 0u;
+      }
+    }
+    const double sbst = scode ? (double)scale_of_code<KIND>(scode) * (double)st : 0.0;
+    const double sv = neg ? -(double)mag : (double)mag;
+    double sse = 0.0;
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+      const uint32_t code = (w[j >> 3] >> (4 * (j & 7))) & 15u;
+      const double v = code == 8u ? sv : ((code & 8u) ? -0.5 : 0.5) * (double)fp4_mag_x2(code & 7u);
+      const double e = (double)xf[j] - v * sbst;
+      sse = sse + e * e;
+    }
+    if (c == 0 || sse < best) {
+      best = sse;
+      bsel = (uint32_t)c;
+      bcode = scode;
+      bw0 = w[0];
+      bw1 = w[1];
+    }
+  }
+  cw = make_uint2(bw0, bw1);
+  if (bcode == 0u)
+    sbyte = 0u;  // zero block: no metadata
+  else
+    sbyte = (KIND == kWeight) ? (((bsel & 1u) << 7) | ((bsel >> 1) << 6) | bcode) : ((bsel << 7) | bcode);
+}
+
 // Block values from the 16 input elements' bytes (fp32: 4 x 16 B, 16-bit: 2 x 16 B).
 template <typename T> __device__ __forceinline__ void unpack_block(const u32x4_t* q, float (&v)[16]);
 template <> __device__ __forceinline__ void unpack_block<float>(const u32x4_t* q, float (&v)[16]) {
@@ -582,7 +659,11 @@ template <> __device__ __forceinline__ void unpack_block<_Float16>(const u32x4_t
 // back as one block per lane.  The next step's loads are in flight while a
 // step is encoded; the buffer descriptor is rebased per step, so a read past
 // the tensor returns zero and any tensor size works with 32-bit offsets.
-template <int KIND, typename T, bool FOS>
+// Encode-kernel modes: RaZeR (with the plain-NVFP4 no-remap option), the Four
+// Over Six baseline, RaZeR with rescaled large special values.
+enum { kModeRazer = 0, kModeFos = 1, kModeRescale = 2 };
+
+template <int KIND, typename T, int MODE>
 __global__ __launch_bounds__(256) void encode_kernel(const T* __restrict__ x, int64_t nblk,
                                                      const uint32_t* __restrict__ partial,
                                                      int npartial, uint2* __restrict__ codes,
@@ -625,7 +706,7 @@ __global__ __launch_bounds__(256) void encode_kernel(const T* __restrict__ x, in
   const bool all_zero = nonfinite || amax == 0.0f;
   const float rinv = 1.0f / amax;
   __shared__ float rtab[kScaleCodes<KIND>];
-  if constexpr (!FOS) {
+  if constexpr (MODE != kModeFos) {
     build_rcp_table<KIND>(rtab, st);
     __syncthreads();
   }
@@ -659,8 +740,10 @@ __global__ __launch_bounds__(256) void encode_kernel(const T* __restrict__ x, in
       unpack_block<T>(q, xf);
       uint2 cw;
       uint32_t sbyte;
-      if constexpr (FOS)
+      if constexpr (MODE == kModeFos)
         encode_block_fos<KIND>(xf, amax, st, cw, sbyte);
+      else if constexpr (MODE == kModeRescale)
+        encode_block_rescale<KIND>(xf, amax, st, rtab, prm, cw, sbyte);
       else
         encode_block<KIND, kFastDiv>(xf, amax, rinv, rtab, prm, cw, sbyte);
       // Buffer stores sized to the wave's valid blocks: lanes past the end are
@@ -679,7 +762,7 @@ __global__ __launch_bounds__(256) void encode_kernel(const T* __restrict__ x, in
   };
   // The Markstein quotient is used for 16-bit inputs whose amax keeps every
   // operand normal; the test is uniform, so the kernel takes one loop or the other.
-  if constexpr (sizeof(T) == 2 && !FOS) {
+  if constexpr (sizeof(T) == 2 && MODE == kModeRazer) {
     if (amax >= 0x1p-60f && amax <= 0x1p60f)
       run(std::true_type{});
     else
@@ -722,11 +805,15 @@ static hipError_t run_quantize(const T* x, const PackedView& out, uint32_t* part
   const int64_t cap = (int64_t)device_cu_count() * 8;
   if (g2 > cap) g2 = cap;
   if (g2 < 1) g2 = 1;
+  // Four Over Six takes precedence over the others, no-remap over the rescale
   if (out.flags & kFlagFourOverSix)
-    hipLaunchKernelGGL((encode_kernel<KIND, T, true>), dim3((unsigned)g2), dim3(256), 0, stream, x,
+    hipLaunchKernelGGL((encode_kernel<KIND, T, kModeFos>), dim3((unsigned)g2), dim3(256), 0, stream, x,
+                       nblk, partial, (int)g1, (uint2*)out.codes, out.scales, out.tensor_scale, prm);
+  else if ((out.flags & kFlagRescale) && prm.remap)
+    hipLaunchKernelGGL((encode_kernel<KIND, T, kModeRescale>), dim3((unsigned)g2), dim3(256), 0, stream, x,
                        nblk, partial, (int)g1, (uint2*)out.codes, out.scales, out.tensor_scale, prm);
   else
-    hipLaunchKernelGGL((encode_kernel<KIND, T, false>), dim3((unsigned)g2), dim3(256), 0, stream, x,
+    hipLaunchKernelGGL((encode_kernel<KIND, T, kModeRazer>), dim3((unsigned)g2), dim3(256), 0, stream, x,
                        nblk, partial, (int)g1, (uint2*)out.codes, out.scales, out.tensor_scale, prm);
   return hipGetLastError();
 }

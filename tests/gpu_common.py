@@ -34,12 +34,12 @@ def log(*a):
 
 # ---- helpers -----------------------------------------------------------------
 
-def gpu_encode(kind, x_cpu: torch.Tensor, offsets, remap=True, four_over_six=False):
+def gpu_encode(kind, x_cpu: torch.Tensor, offsets, remap=True, four_over_six=False, rescale=False):
     x = x_cpu.cuda()
     if kind == oracle.WEIGHT:
-        p = rz.razer_quantize_weight(x, offsets, remap, four_over_six=four_over_six)
+        p = rz.razer_quantize_weight(x, offsets, remap, four_over_six=four_over_six, rescale=rescale)
     else:
-        p = rz.razer_quantize_act(x, offsets, remap, four_over_six=four_over_six)
+        p = rz.razer_quantize_act(x, offsets, remap, four_over_six=four_over_six, rescale=rescale)
     torch.cuda.synchronize()
     return p
 

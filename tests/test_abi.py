@@ -81,6 +81,7 @@ FAKE_WS = ctypes.c_void_p(0x5000)
     lambda s: setattr(s, "block_log2", 6),             # cols (32) not a multiple of 64
     lambda s: setattr(s, "scale_fmt", 2),
     lambda s: setattr(s, "flags", 4),                  # unknown encoder flag bit
+    lambda s: setattr(s, "flags", 16),
     lambda s: setattr(s, "flags", 0x80000002),
 ])
 def test_quantize_weight_rejects_bad_packed(mutate):
@@ -88,6 +89,21 @@ def test_quantize_weight_rejects_bad_packed(mutate):
     mutate(s)
     st = rz.lib().razer_quantize_weight(FAKE_X, rz.RAZER_F32, ctypes.byref(s), FAKE_WS, 4096, None)
     assert st == rz.RAZER_E_INVALID
+
+
+def test_rescale_flag_only_on_the_default_layout():
+    # RAZER_FLAG_RESCALE_LARGE_SV encodes 16-element blocks with byte scales;
+    # other layouts are refused before any launch
+    L = rz.lib()
+    for blog2, sfmt in ((5, rz.RAZER_SCALE_BYTE), (7, rz.RAZER_SCALE_F16)):
+        s = _packed(cols=128)
+        s.flags, s.block_log2, s.scale_fmt = rz.RAZER_FLAG_RESCALE_LARGE_SV, blog2, sfmt
+        st = L.razer_quantize_weight(FAKE_X, rz.RAZER_F32, ctypes.byref(s), FAKE_WS, 4096, None)
+        assert st == rz.RAZER_E_UNSUPPORTED
+    a = _packed(kind=rz.RAZER_ACT, cols=64)
+    a.flags, a.block_log2 = rz.RAZER_FLAG_RESCALE_LARGE_SV, 6
+    assert L.razer_quantize_act(FAKE_X, rz.RAZER_BF16, ctypes.byref(a), FAKE_WS, 4096, None) == rz.RAZER_E_UNSUPPORTED
+    assert L.razer_quantize_act_noalloc(FAKE_X, rz.RAZER_BF16, ctypes.byref(a), None) == rz.RAZER_E_UNSUPPORTED
 
 
 def test_quantize_rejects_bad_buffers():

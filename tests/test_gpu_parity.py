@@ -259,6 +259,88 @@ def test_quantize_four_over_six_prefill_weight_sampled():
     torch.cuda.empty_cache()
 
 
+def _rescale_input(kind, dtype, seed):
+    rng = np.random.default_rng(seed)
+    if kind == oracle.WEIGHT:
+        x = (rng.standard_t(5, (48, 512)) * 0.02).astype(np.float32)
+    else:
+        x = rng.standard_normal((48, 512)).astype(np.float32)
+        x[:, 9] *= 30
+    return torch.from_numpy(x).to(dtype)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("kind,offsets", [(oracle.WEIGHT, (-2, 4)), (oracle.WEIGHT, (-2, 2)),
+                                          (oracle.WEIGHT, (1, 6)), (oracle.WEIGHT, (-2, -5)),
+                                          (oracle.ACT, (2,)), (oracle.ACT, (-2,)), (oracle.ACT, (7,))])
+def test_quantize_rescale_parity(kind, offsets, dtype):
+    """RaZeR with rescaled large special values: bytes and tensor scale equal
+    the oracle's, for both kinds and every input type."""
+    _need_gpu()
+    if kind == oracle.ACT and dtype == torch.float32:
+        pytest.skip("activations come in 16-bit types")
+    x = _rescale_input(kind, dtype, 17 + offsets[-1])
+    ref = oracle.quantize(kind, as_f32(x), offsets, rescale=True)
+    p = gpu_encode(kind, x, offsets, rescale=True)
+    assert_same_encoding(p, ref, as_f32(x), f"rescale {kind} {offsets} {dtype}")
+
+
+@pytest.mark.parametrize("name", sorted(EDGE))
+@pytest.mark.parametrize("kind,offsets", [(oracle.WEIGHT, (-2, 4)), (oracle.ACT, (3,))])
+def test_quantize_rescale_edge_cases(name, kind, offsets):
+    _need_gpu()
+    x = EDGE[name]
+    ref = oracle.quantize(kind, x, offsets, rescale=True)
+    p = gpu_encode(kind, torch.from_numpy(x), offsets, rescale=True)
+    assert_same_encoding(p, ref, x, f"rescale edge {name} kind {kind}")
+
+
+def test_quantize_rescale_prefill_weight_sampled():
+    """The rescale mode on the full W[28672, 8192] fp32 weight with pairs
+    (+-5, +-8): the oracle encodes a row sample with the row holding the tensor
+    maximum (same tensor scale) and the GPU rows match it byte for byte."""
+    _need_gpu()
+    w = synth.prefill_weight()
+    log("rescale prefill W: gpu ...")
+    p = gpu_encode(oracle.WEIGHT, torch.from_numpy(w), (-2, 4), rescale=True)
+    rmax = int(np.abs(w).max(axis=1).argmax())
+    rows = sorted(set(np.random.default_rng(93).choice(w.shape[0], 96, replace=False).tolist()) | {rmax, 0, w.shape[0] - 1})
+    log("rescale prefill W: oracle on", len(rows), "rows ...")
+    ref = oracle.quantize_weight(w[rows], (-2, 4), rescale=True)
+    k = w.shape[1]
+    codes = p.codes.cpu().numpy().reshape(w.shape[0], k // 2)[rows]
+    scales = p.scales.cpu().numpy().reshape(w.shape[0], k // 16)[rows]
+    ts = p.tensor_scale.cpu().numpy().view(np.uint32)[0]
+    assert ts == np.array([ref.tensor_scale], np.float32).view(np.uint32)[0]
+    np.testing.assert_array_equal(scales.reshape(-1), ref.scales)
+    np.testing.assert_array_equal(codes.reshape(-1), ref.codes)
+    share8 = float(((scales >> 6) & 1).mean())
+    log(f"rescale prefill W: blocks choosing +-8: {share8:.3f}")
+    assert share8 > 0.1
+    del p
+    torch.cuda.empty_cache()
+
+
+def test_rescaled_weights_decode_through_the_products():
+    """A weight encoded with rescaled large special values goes through the
+    GEMV, the small-batch product and the prefill tile kernel unchanged
+    (decoding reads the scale byte and the metadata as for any RaZeR weight)."""
+    _need_gpu()
+    rng = np.random.default_rng(29)
+    w = (rng.standard_t(5, (1040, 1024)) * 0.02).astype(np.float32)
+    ref = oracle.quantize_weight(w, (-2, 4), rescale=True)
+    p = rz.razer_quantize_weight(torch.from_numpy(w).cuda(), (-2, 4), rescale=True)
+    for m in (1, 4, 16, 256):
+        x = torch.from_numpy(rng.standard_normal((m, 1024)).astype(np.float32)).to(torch.bfloat16)
+        y_ref, nrm = oracle.gemm(as_f32(x), ref)
+        if m == 1:
+            y = rz.razer_gemv(x.reshape(-1).to(torch.float16).cuda(), p, torch.float32).cpu().numpy()[None]
+            y_ref, nrm = oracle.gemm(as_f32(x.to(torch.float16)), ref)
+        else:
+            y = rz.razer_gemm(x.cuda(), p, torch.float32).cpu().numpy()
+        assert_product_close(y, y_ref, nrm, f"rescaled weight m={m}")
+
+
 def test_four_over_six_weights_decode_through_the_products():
     # The Four Over Six layout is plain NVFP4, so the unchanged decoders
     # (dequant, GEMV, GEMM) read it exactly as the oracle's decoder does.
