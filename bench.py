@@ -589,6 +589,24 @@ def bench_rows(torch, rz, synth, args, decode_base):
              "four_over_six": rel_sse(torch, rz, w, wf),
              "razer_pairs_-2_4": rel_sse(torch, rz, w, wp),
              f"razer_pairs_-2_{best}": rel_sse(torch, rz, w, rz.razer_quantize_weight(w, (-2, best)))}
+    # RaZeR with rescaled large special values on the same weight: its encode
+    # time with the pairs (+-5, +-8), and the relative squared error for every
+    # second-pair offset (the offset search composed from encodes and decodes)
+    wr = rz.PackedTensor(rz.RAZER_WEIGHT, 28672, 8192, (-2, 4), dev, rz.RAZER_FLAG_RESCALE_LARGE_SV)
+    t = GraphTimer(torch, lambda: rz.razer_quantize_weight(w, out=wr))
+    ms_r = t.time(3)
+    resc_sse = {o: rel_sse(torch, rz, w, rz.razer_quantize_weight(w, (-2, o), rescale=True))
+                for o in rz.SECOND_PAIR_OFFSETS}
+    best_r = min(resc_sse, key=lambda o: (resc_sse[o], o))
+    resc_row = {"workload": "RaZeR with rescaled large special values (a candidate with |v| > 6 maps the block "
+                            "maximum to |v|) on W [28672,8192] fp32: encode time with pairs (+-5, +-8), relative "
+                            "squared error per second-pair offset (first pair at -2)",
+                "ms": ms_r, "gelem_per_s": 28672 * 8192 / ms_r / 1e6,
+                "rel_sse_by_offset": {str(o): v for o, v in resc_sse.items()},
+                "best_offset": best_r, "rel_sse_best": resc_sse[best_r],
+                "share_of_blocks_on_pair_1_at_+4": float(((wr.scales >> 6) & 1).float().mean()),
+                "fixed_scale_best_rel_sse": err_w[f"razer_pairs_-2_{best}"]}
+    del wr, t
     # layout variants (block sizes 16..128 with byte scales, and the FP16
     # group scale): relative squared error of each encoder on this weight, and
     # the RaZeR encode time of each layout
@@ -648,6 +666,7 @@ def bench_rows(torch, rz, synth, args, decode_base):
     n_el = 28672 * 8192
     rows["offset_search_prefill"] = off_row
     rows["four_over_six_prefill"] = fos_row
+    rows["rescale_large_sv_prefill"] = resc_row
     rows["layout_variants"] = var_row
     rows["quantize_weight_prefill"] = {
         "workload": "W [28672,8192] fp32, 4 candidates", "ms": ms_q, "gelem_per_s": n_el / ms_q / 1e6,
