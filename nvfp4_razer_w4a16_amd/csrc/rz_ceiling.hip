@@ -38,13 +38,20 @@ constexpr int kTileChunks = 1024;  // 16-byte chunks per 16 KiB tile
 __global__ __launch_bounds__(256) void read_kernel(ReadArgs a) {
   const int64_t total = a.end[a.count - 1];
   uint32_t acc = 0u;
+  // The buffer of chunk c, chosen with selects between the (scalar) kernel
+  // arguments: indexing the argument arrays with a per-lane index made the
+  // compiler load the pointer from memory first, one more memory latency on
+  // every load's path.
   auto load = [&](int64_t c) -> u32x4_t {
-    int b = 0;
+    const u32x4_t* base = a.p[0];
+    int64_t off = c;
 #pragma unroll
     for (int i = 1; i < 4; i++)
-      if (i < a.count && c >= a.end[i - 1]) b = i;
-    const int64_t off = c - (b ? a.end[b - 1] : 0);
-    return __builtin_nontemporal_load(a.p[b] + off);
+      if (i < a.count && c >= a.end[i - 1]) {
+        base = a.p[i];
+        off = c - a.end[i - 1];
+      }
+    return __builtin_nontemporal_load(base + off);
   };
   const int64_t c0 = (int64_t)blockIdx.x * kTileChunks + threadIdx.x;
   u32x4_t v[4];
