@@ -10,7 +10,10 @@ token through the L layers = 3L launches replayed from a HIP graph: razer_gemv
 for qkv and down, razer_gemv_group for gate and up (the two read the same x);
 --per-matrix times 4L razer_gemv launches instead (also reported as a row).
 ``value`` is algorithmic GB/s (packed weights + x + y + tensor scale, each
-counted once) over the timed steps.
+counted once) over the timed steps.  Every timed region, the headline's and
+each row's, follows W warmup replays and then at least SETTLE_MS (100 ms) of
+untimed replays, so that the clocks have left their idle state (the JSON line
+gives the number of settling steps); the K timed steps are whole steps.
 
 Also measured in the same run (the ``rows`` object): the weight and activation
 encoders (Gelem/s, GB/s, special-value-search overhead), the small-batch GEMM
@@ -71,9 +74,33 @@ def clone_packed(rz, p):
     return q
 
 
+# Untimed work before every timed region.  After an idle spell the clocks take
+# tens of milliseconds to settle: the decode step replayed right after a one
+# second pause runs 250-290 us per step for its first ten steps and settles at
+# about 226 us after some hundred (about 25 ms); the prefill GEMM dips to
+# 820-870 TFLOP/s before it climbs to about 1080 over some 40 ms.  Timing only
+# steady-state replays keeps those transients out of every figure.
+SETTLE_MS = 100.0
+
+
+def settle(torch, run, min_ms=SETTLE_MS, chunk=8):
+    """Call run() (untimed) in chunks until at least min_ms of wall time have
+    passed, then synchronize; returns the number of calls."""
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        for _ in range(chunk):
+            run()
+        n += chunk
+        torch.cuda.synchronize()
+        if (time.perf_counter() - t0) * 1e3 >= min_ms:
+            return n
+
+
 class GraphTimer:
     """Capture fn() (a batch of launches on the current stream) in a HIP graph
-    and time replays with events on that stream."""
+    and time replays with events on that stream, after warmup replays and
+    SETTLE_MS of untimed ones."""
 
     def __init__(self, torch, fn, warmup=2):
         self.torch = torch
@@ -89,11 +116,13 @@ class GraphTimer:
             fn()
         torch.cuda.synchronize()
 
-    def time(self, iters, warmup=1):
+    def time(self, iters, warmup=1, settle_ms=SETTLE_MS):
         t = self.torch
         for _ in range(warmup):
             self.g.replay()
         t.cuda.synchronize()
+        if settle_ms > 0:
+            settle(t, self.g.replay, settle_ms)
         st = t.cuda.current_stream()
         e0, e1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
         e0.record(st)
@@ -405,6 +434,7 @@ def mfma_loop_ceiling(torch, cus, reps=5, iters=20000):
     for _ in range(2):
         L.rzc_mfma_loop(iters // 4, wgs, sink.data_ptr(), st.cuda_stream)
     torch.cuda.synchronize()
+    settle(torch, lambda: L.rzc_mfma_loop(iters // 4, wgs, sink.data_ptr(), st.cuda_stream))
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(st)
     for _ in range(reps):
@@ -696,6 +726,7 @@ def bench_rows(torch, rz, synth, args, decode_base):
     for _ in range(3):
         torch.mm(x, out.t(), out=y)
     torch.cuda.synchronize()
+    settle(torch, lambda: torch.mm(x, out.t(), out=y))
     st = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(st)
@@ -816,7 +847,8 @@ def main():
     for _ in range(args.warmup):
         timer.g.replay()
     torch.cuda.synchronize()
-    ms_step = timer.time(args.steps, warmup=0)
+    settle_steps = settle(torch, timer.g.replay)  # untimed: the clocks settle
+    ms_step = timer.time(args.steps, warmup=0, settle_ms=0)
     value = step_bytes / ms_step / 1e6  # GB/s
     log(f"decode: {ms_step * 1e3:.1f} us/step, {value:.0f} GB/s")
 
@@ -891,6 +923,7 @@ def main():
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "settle": {"ms": SETTLE_MS, "untimed_steps": settle_steps},
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp16",
         "data": "synthetic (seeded Philox; Student-t(5)*0.02 weights, N(0,1) fp16 x with 8 channels x20)",
         "config": {"workload": f"llama3-8b decode GEMV: qkv 6144x4096, gate 14336x4096, "
