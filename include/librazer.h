@@ -254,7 +254,11 @@ razer_status razer_gemv_group(const void* x, razer_dtype x_dt, const razer_packe
  * kind, default layout or 128-element blocks with FP16 scales.  y: device
  * [m, N] in F32, F16 or BF16.  m >= 1; m == 1 runs the GEMV path.  ws: at least
  * razer_workspace_bytes(RAZER_OP_GEMM, m, N, K) bytes (enough for either
- * layout). */
+ * layout).  For m >= 256 (the 256x256-tile kernel) the workspace is optional:
+ * NULL, smaller or not 16-byte aligned, the product runs without it; with it,
+ * when the tile count leaves a last round of tiles on at most half of the
+ * compute units, those tiles are computed as two K halves (fp32 partial tiles
+ * in ws, then added in one more launch). */
 razer_status razer_gemm(const void* x, razer_dtype x_dt, int64_t m, const razer_packed* w, void* y,
                         razer_dtype y_dt, void* ws, size_t ws_bytes, void* stream);
 

@@ -299,13 +299,19 @@ __device__ __forceinline__ uint32_t decode_one_pair(uint32_t w, int sel, float s
 // F16S: weights in the 128-element FP16-scale layout; a K step of 64 lies in
 // one 128-element block, so one scale word per weight row and step gives both
 // coefficients (computed from the word instead of the table).
+//
+// Workgroups 0 .. full-1 compute tiles 0 .. full-1 over all of K.  Any further
+// workgroup j = blockIdx.x - full takes K half j % 2 of tile full + j / 2 and
+// writes its (scaled) fp32 sums, unconverted, to the 256x256 slot j of part;
+// tail_fold_kernel adds the two halves of each such tile into y.
 template <typename XT, int KIND, typename OT, bool F16S = false>
 __global__ __launch_bounds__(512) void gemm_tile256_kernel(const XT* __restrict__ x, int64_t m,
                                                       const uint8_t* __restrict__ codes,
                                                       const uint8_t* __restrict__ scales,
                                                       const float* __restrict__ ts,
                                                       const float* __restrict__ ts2, int64_t n,
-                                                      int64_t k, float m0, float m1, OT* __restrict__ y) {
+                                                      int64_t k, float m0, float m1, OT* __restrict__ y,
+                                                      int64_t full, float* __restrict__ part) {
   typedef typename Mfma32<XT>::V V;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   XT* As = (XT*)smem;
@@ -314,9 +320,18 @@ __global__ __launch_bounds__(512) void gemm_tile256_kernel(const XT* __restrict_
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 2, wn = wave & 3;
   const int64_t ntn = (n + kTN - 1) / kTN;
-  const int64_t m_base = (int64_t)(blockIdx.x / ntn) * kTM;
-  const int64_t n_base = (int64_t)(blockIdx.x % ntn) * kTN;
-  const int ktiles = (int)(k / kTK);
+  int64_t tile = blockIdx.x;
+  int kt0 = 0, ktiles = (int)(k / kTK), slot = -1;
+  if (tile >= full) {  // one K half of a tail tile
+    const int64_t j = tile - full;
+    const int h0 = ktiles / 2;
+    tile = full + j / 2;
+    slot = (int)j;
+    kt0 = (j & 1) ? h0 : 0;
+    ktiles = (j & 1) ? ktiles - h0 : h0;
+  }
+  const int64_t m_base = (tile / ntn) * kTM;
+  const int64_t n_base = (tile % ntn) * kTN;
   if (tid < 256) {
     const uint32_t b = (uint32_t)tid;
     const float sb = scale_of_byte<KIND>(b);
@@ -355,7 +370,7 @@ __global__ __launch_bounds__(512) void gemm_tile256_kernel(const XT* __restrict_
   const int co = br < rows_n ? (int)((int64_t)br * (k / 2)) + 16 * bh : kOob;
   const int so = br < rows_n ? (int)((int64_t)br * srb) : kOob;
   auto gload = [&](int kt, Stage& r) {
-    const int k0 = kt * kTK;
+    const int k0 = (kt0 + kt) * kTK;
     if constexpr (F16S)
       r.s = __builtin_amdgcn_raw_buffer_load_b16(sr, so, (k0 / 128) * 2, 0);
     else
@@ -462,6 +477,21 @@ __global__ __launch_bounds__(512) void gemm_tile256_kernel(const XT* __restrict_
   // ts2: a second factor applied after the weight's tensor scale (the
   // activations' tensor scale of the W4A4 product), 1 when absent
   const float scale = *ts, scale2 = ts2 ? *ts2 : 1.0f;
+  if (slot >= 0) {  // a K half: the whole 256x256 slot, rows and columns past m, n included
+    float* p = part + (int64_t)slot * (kTM * kTN);
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int j = 0; j < 2; j++) {
+        const int lc = wn * 64 + j * 32 + (lane & 31);
+#pragma unroll
+        for (int e = 0; e < 16; e++) {
+          const int lr = wm * 128 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+          p[lr * kTN + lc] = (acc[i][j][e] * scale) * scale2;
+        }
+      }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; i++)
 #pragma unroll
@@ -473,6 +503,26 @@ __global__ __launch_bounds__(512) void gemm_tile256_kernel(const XT* __restrict_
         if (gr < m && gc < n) y[gr * n + gc] = from_f32<OT>((acc[i][j][e] * scale) * scale2);
       }
     }
+}
+
+// y of the tail tiles: the sum of the two K halves' slots.  blockIdx.y = tail
+// tile t (tile full + t), blockIdx.x = 1024-element run of it; a thread adds
+// four consecutive columns of one row.
+template <typename OT>
+__global__ __launch_bounds__(256) void tail_fold_kernel(const float* __restrict__ part, int64_t full,
+                                                     int64_t m, int64_t n, OT* __restrict__ y) {
+  const int64_t t = blockIdx.y, tile = full + t, ntn = (n + kTN - 1) / kTN;
+  const int64_t m_base = (tile / ntn) * kTM, n_base = (tile % ntn) * kTN;
+  const int idx = (blockIdx.x * 256 + threadIdx.x) * 4;
+  const float4 a = *(const float4*)(part + (2 * t) * (kTM * kTN) + idx);
+  const float4 b = *(const float4*)(part + (2 * t + 1) * (kTM * kTN) + idx);
+  const int64_t gr = m_base + idx / kTN, gc = n_base + idx % kTN;
+  if (gr >= m) return;
+  const float v[4] = {a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w};
+  OT* yr = y + gr * n;
+#pragma unroll
+  for (int e = 0; e < 4; e++)
+    if (gc + e < n) yr[gc + e] = from_f32<OT>(v[e]);
 }
 
 // ---- small M (2..32): weight-streaming MFMA with split K -------------------------
@@ -933,18 +983,38 @@ size_t gemm_ws_need(int64_t m, int64_t n, int64_t k, bool f16s, bool untrimmed) 
 
 // Enough for either layout (two rows need no workspace on the default layout
 // but may on the FP16-scale one).
+size_t prefill_ws_bytes(int64_t m, int64_t n, int64_t k);
+
 size_t gemm_ws_bytes(int64_t m, int64_t n, int64_t k) {
   const size_t a = gemm_ws_need(m, n, k, false), b = gemm_ws_need(m, n, k, true);
-  return a > b ? a : b;
+  const size_t c = prefill_ws_bytes(m, n, k);
+  return a > b ? (a > c ? a : c) : (b > c ? b : c);
 }
 
 static bool tile256_fits(int64_t m, int64_t k, size_t xsize) {
   return m >= kTM && k % kTK == 0 && (int64_t)kTM * k * (int64_t)xsize < (1LL << 30);
 }
 
+// One 256x256 tile per CU at a time: a tile count just past a multiple of the
+// CU count leaves a last round that runs on few CUs.  When that round would
+// fill at most half of them, its tiles are split into two K halves (twice the
+// workgroups, half the steps each), which costs two fp32 partial tiles per
+// tail tile in the workspace and one fold launch.  Returns the tail tiles.
+static int64_t tail_tiles(int64_t m, int64_t n, int64_t k) {
+  const int64_t tiles = ((m + kTM - 1) / kTM) * ((n + kTN - 1) / kTN), cus = device_cu_count();
+  const int64_t tail = tiles % cus;
+  if (tiles <= cus || tail == 0 || 2 * tail > cus || k / kTK < 2) return 0;
+  return tail;
+}
+
+size_t prefill_ws_bytes(int64_t m, int64_t n, int64_t k) {
+  if (!tile256_fits(m, k, 2)) return 0;
+  return (size_t)tail_tiles(m, n, k) * 2 * kTM * kTN * sizeof(float);
+}
+
 template <typename XT, int KIND, typename OT, bool F16S = false>
 static hipError_t run_tile256(const XT* x, int64_t m, const PackedView& w, OT* y, const float* ts2,
-                              hipStream_t stream) {
+                              void* ws, size_t wsb, hipStream_t stream) {
   const int64_t n = w.rows, k = w.cols;
   const float m0 = 6.0f + 0.5f * (float)w.off_half[0];
   const float m1 = 6.0f + 0.5f * (float)w.off_half[KIND == kWeight ? 1 : 0];
@@ -953,8 +1023,15 @@ static hipError_t run_tile256(const XT* x, int64_t m, const PackedView& w, OT* y
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const int64_t tiles = ((m + kTM - 1) / kTM) * ((n + kTN - 1) / kTN);
-  hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(512), lds, stream, x, m, w.codes, w.scales,
-                     w.tensor_scale, ts2, n, k, m0, m1, y);
+  // the tail split only with a workspace that holds its partial tiles
+  int64_t tail = tail_tiles(m, n, k);
+  if (!ws || ((uintptr_t)ws & 15) || wsb < (size_t)tail * 2 * kTM * kTN * sizeof(float)) tail = 0;
+  const int64_t full = tiles - tail;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(full + 2 * tail)), dim3(512), lds, stream, x, m, w.codes, w.scales,
+                     w.tensor_scale, ts2, n, k, m0, m1, y, full, (float*)ws);
+  if (tail > 0)
+    hipLaunchKernelGGL(tail_fold_kernel<OT>, dim3(kTM * kTN / 1024, (unsigned)tail), dim3(256), 0, stream,
+                       (const float*)ws, full, m, n, y);
   return hipGetLastError();
 }
 
@@ -998,14 +1075,14 @@ static hipError_t run_batch(const XT* x, int64_t m, const PackedView& w, OT* y, 
 // fits, else the generic tile kernel.
 template <typename XT, int KIND, typename OT>
 static hipError_t run_gemm_f16s(const XT* x, int64_t m, const PackedView& w, OT* y, void* ws,
-                                hipStream_t stream) {
+                                size_t wsb, hipStream_t stream) {
   const int64_t n = w.rows, k = w.cols;
   if (k % 128 != 0) return hipErrorInvalidValue;
   if (KIND == kWeight && fp16s_supported(m, n, k))
     return launch_bdiag(x, __is_same(XT, __bf16) ? kBF16 : kF16, m, w, y,
                         sizeof(OT) == 4 ? kF32 : __is_same(OT, _Float16) ? kF16 : kBF16, stream);
   if (use_batch_f16s(m, k)) return run_batch<XT, KIND, OT, true>(x, m, w, y, ws, stream);
-  if (tile256_fits(m, k, sizeof(XT))) return run_tile256<XT, KIND, OT, true>(x, m, w, y, nullptr, stream);
+  if (tile256_fits(m, k, sizeof(XT))) return run_tile256<XT, KIND, OT, true>(x, m, w, y, nullptr, ws, wsb, stream);
   const float m0 = 6.0f + 0.5f * (float)w.off_half[0];
   const float m1 = 6.0f + 0.5f * (float)w.off_half[KIND == kWeight ? 1 : 0];
   dim3 grid((unsigned)((n + kBN - 1) / kBN), (unsigned)((m + kBM - 1) / kBM));
@@ -1015,9 +1092,9 @@ static hipError_t run_gemm_f16s(const XT* x, int64_t m, const PackedView& w, OT*
 }
 
 template <typename XT, int KIND, typename OT>
-static hipError_t run_gemm(const XT* x, int64_t m, const PackedView& w, OT* y, void* ws,
+static hipError_t run_gemm(const XT* x, int64_t m, const PackedView& w, OT* y, void* ws, size_t wsb,
                            hipStream_t stream) {
-  if (!default_layout(w)) return run_gemm_f16s<XT, KIND, OT>(x, m, w, y, ws, stream);
+  if (!default_layout(w)) return run_gemm_f16s<XT, KIND, OT>(x, m, w, y, ws, wsb, stream);
   const int64_t n = w.rows, k = w.cols;
   const float m0 = 6.0f + 0.5f * (float)w.off_half[0];
   const float m1 = 6.0f + 0.5f * (float)w.off_half[KIND == kWeight ? 1 : 0];
@@ -1039,7 +1116,7 @@ static hipError_t run_gemm(const XT* x, int64_t m, const PackedView& w, OT* y, v
                        p.split, mn, w.tensor_scale, y);
     return hipGetLastError();
   }
-  if (tile256_fits(m, k, sizeof(XT))) return run_tile256<XT, KIND, OT>(x, m, w, y, nullptr, stream);
+  if (tile256_fits(m, k, sizeof(XT))) return run_tile256<XT, KIND, OT>(x, m, w, y, nullptr, ws, wsb, stream);
   dim3 grid((unsigned)((n + kBN - 1) / kBN), (unsigned)((m + kBM - 1) / kBM));
   hipLaunchKernelGGL((gemm_kernel<XT, KIND, OT>), grid, dim3(256), 0, stream, x, m, w.codes,
                      w.scales, w.tensor_scale, n, k, m0, m1, y);
@@ -1048,18 +1125,18 @@ static hipError_t run_gemm(const XT* x, int64_t m, const PackedView& w, OT* y, v
 
 template <typename XT, int KIND>
 static hipError_t gemm_out_dispatch(const XT* x, int64_t m, const PackedView& w, void* y,
-                                    int y_dtype, void* ws, hipStream_t stream) {
-  if (y_dtype == kF32) return run_gemm<XT, KIND>(x, m, w, (float*)y, ws, stream);
-  if (y_dtype == kF16) return run_gemm<XT, KIND>(x, m, w, (_Float16*)y, ws, stream);
-  return run_gemm<XT, KIND>(x, m, w, (__bf16*)y, ws, stream);
+                                    int y_dtype, void* ws, size_t wsb, hipStream_t stream) {
+  if (y_dtype == kF32) return run_gemm<XT, KIND>(x, m, w, (float*)y, ws, wsb, stream);
+  if (y_dtype == kF16) return run_gemm<XT, KIND>(x, m, w, (_Float16*)y, ws, wsb, stream);
+  return run_gemm<XT, KIND>(x, m, w, (__bf16*)y, ws, wsb, stream);
 }
 
 template <typename XT, int KIND>
 static hipError_t tile256_out_dispatch(const XT* x, int64_t m, const PackedView& w, void* y, int y_dtype,
                                        const float* ts2, hipStream_t stream) {
-  if (y_dtype == kF32) return run_tile256<XT, KIND>(x, m, w, (float*)y, ts2, stream);
-  if (y_dtype == kF16) return run_tile256<XT, KIND>(x, m, w, (_Float16*)y, ts2, stream);
-  return run_tile256<XT, KIND>(x, m, w, (__bf16*)y, ts2, stream);
+  if (y_dtype == kF32) return run_tile256<XT, KIND>(x, m, w, (float*)y, ts2, nullptr, 0, stream);
+  if (y_dtype == kF16) return run_tile256<XT, KIND>(x, m, w, (_Float16*)y, ts2, nullptr, 0, stream);
+  return run_tile256<XT, KIND>(x, m, w, (__bf16*)y, ts2, nullptr, 0, stream);
 }
 
 bool gemm_prefill_fits(int64_t m, int64_t k, int x_dtype) { return tile256_fits(m, k, 2); }
@@ -1076,16 +1153,16 @@ hipError_t launch_gemm_prefill_scaled(const void* x, int x_dtype, int64_t m, con
 }
 
 hipError_t launch_gemm(const void* x, int x_dtype, int64_t m, const PackedView& w, void* y,
-                       int y_dtype, void* ws, size_t, hipStream_t stream) {
+                       int y_dtype, void* ws, size_t wsb, hipStream_t stream) {
   if (default_layout(w) && use_bdiag(m, w.rows, w.cols)) return launch_bdiag(x, x_dtype, m, w, y, y_dtype, stream);
   if (default_layout(w) && use_smallm(m, w.rows, w.cols)) return launch_smallm(x, x_dtype, m, w, y, y_dtype, stream);
   if (!default_layout(w) && (w.blog2 != 7 || w.sfmt != 1)) return hipErrorNotSupported;
   if (x_dtype == kF16) {
-    if (w.kind == kWeight) return gemm_out_dispatch<_Float16, kWeight>((const _Float16*)x, m, w, y, y_dtype, ws, stream);
-    return gemm_out_dispatch<_Float16, kAct>((const _Float16*)x, m, w, y, y_dtype, ws, stream);
+    if (w.kind == kWeight) return gemm_out_dispatch<_Float16, kWeight>((const _Float16*)x, m, w, y, y_dtype, ws, wsb, stream);
+    return gemm_out_dispatch<_Float16, kAct>((const _Float16*)x, m, w, y, y_dtype, ws, wsb, stream);
   }
-  if (w.kind == kWeight) return gemm_out_dispatch<__bf16, kWeight>((const __bf16*)x, m, w, y, y_dtype, ws, stream);
-  return gemm_out_dispatch<__bf16, kAct>((const __bf16*)x, m, w, y, y_dtype, ws, stream);
+  if (w.kind == kWeight) return gemm_out_dispatch<__bf16, kWeight>((const __bf16*)x, m, w, y, y_dtype, ws, wsb, stream);
+  return gemm_out_dispatch<__bf16, kAct>((const __bf16*)x, m, w, y, y_dtype, ws, wsb, stream);
 }
 
 }  // namespace rz

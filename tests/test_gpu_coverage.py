@@ -153,6 +153,43 @@ def test_gemm_prefill_every_tile_column_and_random_outputs():
     assert_product_close(got, yp, np_, "prefill out f32 (random outputs)")
 
 
+@pytest.mark.parametrize("m,n,k,xdt", [(505, 256 * 130 - 100, 128, torch.bfloat16),
+                                       (300, 256 * 129 + 1, 192, torch.float16)])
+def test_gemm_prefill_tail_split_ragged(m, n, k, xdt):
+    """260 tiles of 256x256 on 256 compute units: the last four tiles run as two
+    K halves (one and one, or one and two K steps) folded by a second launch.
+    Those tiles hold the ragged last rows and columns.  Checked against the
+    oracle on every column of the tail tiles plus sampled others, for f32 and
+    bf16 outputs, with the workspace (split) and with a 16-byte one (unsplit)."""
+    _need_gpu()
+    rng = np.random.default_rng(m + n + k)
+    w = (rng.standard_t(4, (n, k)) * 0.015).astype(np.float32)
+    x = torch.from_numpy(rng.normal(0, 1, (m, k)).astype(np.float32)).to(xdt)
+    ref = oracle.quantize_weight(w, (-2, -5))
+    ntn = (n + 255) // 256
+    tiles = ((m + 255) // 256) * ntn
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    tail = tiles % cus if tiles > cus and 2 * (tiles % cus) <= cus else 0
+    first = (tiles - tail) % ntn * 256 if tail else n
+    cols = np.unique(np.concatenate([np.arange(first, n), rng.choice(first, 64, replace=False)]))
+    need = rz.razer_workspace_bytes(rz.RAZER_OP_GEMM, m, n, k)
+    log(f"tail split {m}x{n}x{k}: {tiles} tiles, {tail} split, workspace {need} bytes, "
+        f"{cols.size} columns checked")
+    assert need == tail * 2 * 256 * 256 * 4
+    y_ref, nrm = oracle.gemm(as_f32(x), ref, cols)
+    t = to_device(ref)
+    ci = torch.from_numpy(cols).cuda()
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    for odt in (torch.float32, torch.bfloat16):
+        for ws in (None, small):
+            y = rz.razer_gemm(x.cuda(), t, odt, workspace=ws)
+            torch.cuda.synchronize()
+            got = y[:, ci].float().cpu().double().numpy()
+            what = f"prefill tail {m}x{n}x{k} out {odt} " + ("split" if ws is None else "unsplit")
+            assert_product_close(got, y_ref, nrm, what, odt)
+            assert torch.isfinite(y).all(), what
+
+
 def test_gemm_w4a4_prefill_every_tile_column_and_random_outputs():
     """W4A4 at the prefill shape: the activation encoded by the oracle, the
     same tile columns and random outputs as the W4A16 prefill, bf16 and f32."""
