@@ -983,8 +983,6 @@ size_t gemm_ws_need(int64_t m, int64_t n, int64_t k, bool f16s, bool untrimmed) 
 
 // Enough for either layout (two rows need no workspace on the default layout
 // but may on the FP16-scale one).
-size_t prefill_ws_bytes(int64_t m, int64_t n, int64_t k);
-
 size_t gemm_ws_bytes(int64_t m, int64_t n, int64_t k) {
   const size_t a = gemm_ws_need(m, n, k, false), b = gemm_ws_need(m, n, k, true);
   const size_t c = prefill_ws_bytes(m, n, k);
@@ -1133,23 +1131,23 @@ static hipError_t gemm_out_dispatch(const XT* x, int64_t m, const PackedView& w,
 
 template <typename XT, int KIND>
 static hipError_t tile256_out_dispatch(const XT* x, int64_t m, const PackedView& w, void* y, int y_dtype,
-                                       const float* ts2, hipStream_t stream) {
-  if (y_dtype == kF32) return run_tile256<XT, KIND>(x, m, w, (float*)y, ts2, nullptr, 0, stream);
-  if (y_dtype == kF16) return run_tile256<XT, KIND>(x, m, w, (_Float16*)y, ts2, nullptr, 0, stream);
-  return run_tile256<XT, KIND>(x, m, w, (__bf16*)y, ts2, nullptr, 0, stream);
+                                       const float* ts2, void* ws, size_t wsb, hipStream_t stream) {
+  if (y_dtype == kF32) return run_tile256<XT, KIND>(x, m, w, (float*)y, ts2, ws, wsb, stream);
+  if (y_dtype == kF16) return run_tile256<XT, KIND>(x, m, w, (_Float16*)y, ts2, ws, wsb, stream);
+  return run_tile256<XT, KIND>(x, m, w, (__bf16*)y, ts2, ws, wsb, stream);
 }
 
 bool gemm_prefill_fits(int64_t m, int64_t k, int x_dtype) { return tile256_fits(m, k, 2); }
 
 hipError_t launch_gemm_prefill_scaled(const void* x, int x_dtype, int64_t m, const PackedView& w, void* y,
-                                      int y_dtype, const float* ts2, hipStream_t stream) {
+                                      int y_dtype, const float* ts2, void* ws, size_t wsb, hipStream_t stream) {
   if (!tile256_fits(m, w.cols, 2)) return hipErrorNotSupported;
   if (x_dtype == kF16) {
-    if (w.kind == kWeight) return tile256_out_dispatch<_Float16, kWeight>((const _Float16*)x, m, w, y, y_dtype, ts2, stream);
-    return tile256_out_dispatch<_Float16, kAct>((const _Float16*)x, m, w, y, y_dtype, ts2, stream);
+    if (w.kind == kWeight) return tile256_out_dispatch<_Float16, kWeight>((const _Float16*)x, m, w, y, y_dtype, ts2, ws, wsb, stream);
+    return tile256_out_dispatch<_Float16, kAct>((const _Float16*)x, m, w, y, y_dtype, ts2, ws, wsb, stream);
   }
-  if (w.kind == kWeight) return tile256_out_dispatch<__bf16, kWeight>((const __bf16*)x, m, w, y, y_dtype, ts2, stream);
-  return tile256_out_dispatch<__bf16, kAct>((const __bf16*)x, m, w, y, y_dtype, ts2, stream);
+  if (w.kind == kWeight) return tile256_out_dispatch<__bf16, kWeight>((const __bf16*)x, m, w, y, y_dtype, ts2, ws, wsb, stream);
+  return tile256_out_dispatch<__bf16, kAct>((const __bf16*)x, m, w, y, y_dtype, ts2, ws, wsb, stream);
 }
 
 hipError_t launch_gemm(const void* x, int x_dtype, int64_t m, const PackedView& w, void* y,

@@ -67,10 +67,12 @@ hipError_t launch_gemv_group(const void* x, int x_dtype, const PackedView* w, vo
 inline bool default_layout(const PackedView& v) { return v.blog2 == 4 && v.sfmt == 0; }
 
 // The prefill (M >= 256, K % 64 == 0) product with a second scale factor
-// applied after the weight's tensor scale in the epilogue.
+// applied after the weight's tensor scale in the epilogue.  ws (optional, at
+// least prefill_ws_bytes) holds the partial tiles of the last round's K split.
 bool gemm_prefill_fits(int64_t m, int64_t k, int x_dtype);
+size_t prefill_ws_bytes(int64_t m, int64_t n, int64_t k);
 hipError_t launch_gemm_prefill_scaled(const void* x, int x_dtype, int64_t m, const PackedView& w, void* y,
-                                      int y_dtype, const float* ts2, hipStream_t stream);
+                                      int y_dtype, const float* ts2, void* ws, size_t wsb, hipStream_t stream);
 hipError_t launch_gemv(const void* x, int x_dtype, const PackedView& w, void* y, int y_dtype,
                        void* ws, size_t ws_bytes, hipStream_t stream);
 

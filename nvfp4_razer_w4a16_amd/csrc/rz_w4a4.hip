@@ -15,7 +15,8 @@
 // For prefill shapes passes 2 and 3 are one: the product's epilogue multiplies
 // by st_w, then by st_x, and rounds once (the same operations in the same
 // order).  Every pass is one of this library's kernels; the workspace holds the
-// fp16 activations, the fp32 product and the product's own workspace.
+// fp16 activations, the fp32 product and the product's own workspace (prefill
+// shapes: the fp16 activations and the product's workspace).
 #include "rz_device.h"
 #include "rz_launch.h"
 
@@ -45,6 +46,8 @@ size_t product_ws(int64_t m, int64_t n, int64_t k) { return m == 1 ? gemv_ws_byt
 
 size_t gemm_w4a4_ws_bytes(int64_t m, int64_t n, int64_t k) {
   if (m <= 0 || n <= 0 || k <= 0) return 0;
+  // prefill shapes write y from the product's epilogue: no fp32 product buffer
+  if (gemm_prefill_fits(m, k, kF16)) return up((size_t)m * (size_t)k * 2) + up(prefill_ws_bytes(m, n, k));
   return up((size_t)m * (size_t)k * 2) + up((size_t)m * (size_t)n * 4) + up(product_ws(m, n, k));
 }
 
@@ -53,16 +56,19 @@ hipError_t launch_gemm_w4a4(const PackedView& x, const PackedView& w, void* y, i
   const int64_t m = x.rows, k = x.cols, n = w.rows;
   if (m == 0 || n == 0) return hipSuccess;
   uint8_t* base = (uint8_t*)ws;
-  void* xb = base;                                             // fp16 [m, k]
-  float* y32 = (float*)(base + up((size_t)m * k * 2));         // fp32 [m, n]
-  void* pws = base + up((size_t)m * k * 2) + up((size_t)m * n * 4);
-  const size_t pws_bytes = ws_bytes - (up((size_t)m * k * 2) + up((size_t)m * n * 4));
+  void* xb = base;  // fp16 [m, k]
+  const size_t xb_bytes = up((size_t)m * k * 2);
   hipError_t e = launch_dequant_unscaled(x, xb, kF16, stream);
   if (e != hipSuccess) return e;
   // prefill shapes: the product's epilogue applies st_x after st_w and writes
-  // y directly -- the same two fp32 multiplies and one rounding as passes 2-3
+  // y directly -- the same two fp32 multiplies and one rounding as passes 2-3;
+  // the rest of the workspace serves the product's tail split
   if (gemm_prefill_fits(m, k, kF16))
-    return launch_gemm_prefill_scaled(xb, kF16, m, w, y, y_dtype, x.tensor_scale, stream);
+    return launch_gemm_prefill_scaled(xb, kF16, m, w, y, y_dtype, x.tensor_scale, base + xb_bytes,
+                                      ws_bytes - xb_bytes, stream);
+  float* y32 = (float*)(base + xb_bytes);  // fp32 [m, n]
+  void* pws = base + xb_bytes + up((size_t)m * n * 4);
+  const size_t pws_bytes = ws_bytes - (xb_bytes + up((size_t)m * n * 4));
   e = m == 1 ? launch_gemv(xb, kF16, w, y32, kF32, pws, pws_bytes, stream)
              : launch_gemm(xb, kF16, m, w, y32, kF32, pws, pws_bytes, stream);
   if (e != hipSuccess) return e;
