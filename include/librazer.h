@@ -293,7 +293,10 @@ razer_status razer_weight_offset_sse(const void* w, razer_dtype w_dt, int64_t ro
                                      void* stream);
 
 /* Workspace bytes an operation needs for the given sizes (m rows of x, n
- * weight rows / output features, k reduction length).  0 means none. */
+ * weight rows / output features, k reduction length).  0 means none.  For
+ * RAZER_OP_GEMM with m >= 256 the figure is what the prefill kernel's tail
+ * split uses (it depends on the current device's compute-unit count); that
+ * workspace is optional there. */
 size_t razer_workspace_bytes(int op, int64_t m, int64_t n, int64_t k);
 
 /* Static, human-readable name of a status code. */
