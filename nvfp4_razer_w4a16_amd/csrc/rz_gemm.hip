@@ -514,15 +514,23 @@ __global__ __launch_bounds__(256) void tail_fold_kernel(const float* __restrict_
   const int64_t t = blockIdx.y, tile = full + t, ntn = (n + kTN - 1) / kTN;
   const int64_t m_base = (tile / ntn) * kTM, n_base = (tile % ntn) * kTN;
   const int idx = (blockIdx.x * 256 + threadIdx.x) * 4;
-  const float4 a = *(const float4*)(part + (2 * t) * (kTM * kTN) + idx);
-  const float4 b = *(const float4*)(part + (2 * t + 1) * (kTM * kTN) + idx);
+  const uint4 a = load_nt16(part + (2 * t) * (kTM * kTN) + idx);  // read once
+  const uint4 b = load_nt16(part + (2 * t + 1) * (kTM * kTN) + idx);
   const int64_t gr = m_base + idx / kTN, gc = n_base + idx % kTN;
   if (gr >= m) return;
-  const float v[4] = {a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w};
-  OT* yr = y + gr * n;
+  const float v[4] = {__uint_as_float(a.x) + __uint_as_float(b.x), __uint_as_float(a.y) + __uint_as_float(b.y),
+                      __uint_as_float(a.z) + __uint_as_float(b.z), __uint_as_float(a.w) + __uint_as_float(b.w)};
+  OT* yp = y + gr * n + gc;
+  if (gc + 4 <= n && ((uintptr_t)yp & (4 * sizeof(OT) - 1)) == 0) {  // one aligned vector store
+    struct alignas(4 * sizeof(OT)) Q { OT e[4]; } q;
 #pragma unroll
-  for (int e = 0; e < 4; e++)
-    if (gc + e < n) yr[gc + e] = from_f32<OT>(v[e]);
+    for (int e = 0; e < 4; e++) q.e[e] = from_f32<OT>(v[e]);
+    *(Q*)yp = q;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; e++)
+      if (gc + e < n) yp[e] = from_f32<OT>(v[e]);
+  }
 }
 
 // ---- small M (2..32): weight-streaming MFMA with split K -------------------------
